@@ -1,0 +1,280 @@
+"""Pins of the oracle's key/value encoders, scores and attention.
+
+Checks are independent restatements (numpy matmuls, numpy bit unpacking,
+numpy float16, brute-force nearest centroid), statistical properties the pages
+claim (the QJL correction makes the inner-product estimate unbiased), closed
+forms, or figures printed on the pages.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+KAPPA = lambda m: math.sqrt(math.pi / 2.0) / m
+
+
+def _unpack_le(packed, per_vec, width):
+    """LSB-first bit-stream -> integers, via numpy.unpackbits (independent)."""
+    bits = np.unpackbits(packed, axis=1, bitorder="little")[:, : per_vec * width]
+    bits = bits.reshape(packed.shape[0], per_vec, width).astype(np.uint32)
+    return (bits << np.arange(width, dtype=np.uint32)).sum(axis=2)
+
+
+# -------------------------------------------------------------- packing
+@pytest.mark.parametrize("width,per", [(1, 128), (2, 128), (3, 128), (4, 64), (5, 256),
+                                       (6, 64), (7, 256), (8, 32)])
+def test_pack_roundtrip_and_bit_order(width, per):
+    rng = np.random.default_rng(width * 1000 + per)
+    vals = rng.integers(0, 1 << width, size=(17, per), dtype=np.uint32)
+    packed = O.pack(vals, width)
+    assert packed.shape == (17, (per * width + 7) // 8)
+    assert np.array_equal(O.unpack(packed, per, width), vals)
+    assert np.array_equal(_unpack_le(packed, per, width), vals)
+
+
+def test_four_two_bit_values_per_byte(golden_dir):
+    figs = json.load(open(os.path.join(golden_dir, "page_figures.json")))
+    per_byte = figs["values_per_byte_2bit"]["value"]
+    vals = np.array([[1, 2, 3, 0]], np.uint32)
+    packed = O.pack(vals, 2)
+    assert packed.shape[1] * per_byte == vals.shape[1]
+    assert packed[0, 0] == (1 | 2 << 2 | 3 << 4 | 0 << 6)
+
+
+# ----------------------------------------------------------------- keys
+def _keys(n, d, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal((n, d)) * scale
+
+
+@pytest.mark.parametrize("d,bits,kind", [(128, 2, "dense"), (128, 3, "hadamard"),
+                                         (64, 4, "dense"), (256, 7, "dense")])
+def test_key_encode_restated(d, bits, kind):
+    rot = O.rotation(42, d, kind)
+    k = _keys(300, d, 1, 3.0)
+    kc = O.compress_keys(k, bits, rot, keep_aux=True)
+    c, t = O.codebook(d, bits)
+    n = np.linalg.norm(k, axis=1)
+    y = (k / n[:, None]) @ rot.pi.T
+    assert np.abs(kc.y - y).max() < 1e-13
+    assert np.abs(np.linalg.norm(kc.y, axis=1) - 1).max() < 1e-12
+    idx = _unpack_le(kc.codes, d, bits)
+    # nearest centroid off ties
+    near = np.abs(y[:, :, None] - c[None, None, :]).argmin(axis=2)
+    dist_to_t = np.abs(y[:, :, None] - t[None, None, :]).min(axis=2)
+    safe = dist_to_t > 1e-12
+    assert np.array_equal(idx[safe], near[safe])
+    r = y - c[idx]
+    assert np.abs(kc.rho - np.linalg.norm(r, axis=1)).max() < 1e-13
+    z = r @ rot.s.T
+    assert np.abs(kc.z - z).max() < 1e-12
+    sg = _unpack_le(kc.signs, d, 1)
+    assert np.array_equal(sg[np.abs(z) > 1e-12], (z >= 0)[np.abs(z) > 1e-12].astype(np.uint32))
+    assert np.array_equal(kc.knorm, n.astype(np.float32))
+    assert np.array_equal(kc.rnorm, np.linalg.norm(r, axis=1).astype(np.float32))
+
+
+def test_zero_key():
+    d, bits = 128, 2
+    rot = O.rotation(3, d)
+    kc = O.compress_keys(np.zeros((1, d)), bits, rot, keep_aux=True)
+    c, _ = O.codebook(d, bits)
+    L = 1 << bits
+    assert np.all(_unpack_le(kc.codes, d, bits) == L // 2 - 1)
+    assert kc.knorm[0] == 0.0
+    assert abs(kc.rnorm[0] - math.sqrt(d) * abs(c[L // 2 - 1])) < 1e-6
+    q = np.random.default_rng(0).standard_normal((2, d))
+    assert np.all(O.scores(q, kc, bits, rot) == 0.0)
+
+
+def test_boundary_tie_goes_to_lower_cell():
+    # a key whose rotated coordinate 0 sits exactly on boundary t_2 = 0
+    d, bits = 4, 2
+    rot = O.rotation(1, d)
+    # choose u = Pi^T e_1 -> y = e_1, so y_0 = 0 (a boundary) and y_1 = 1
+    u = rot.pi.T @ np.eye(d)[1]
+    kc = O.compress_keys(u[None, :], bits, rot, keep_aux=True)
+    idx = _unpack_le(kc.codes, d, bits)[0]
+    if abs(kc.y[0, 0]) == 0.0:
+        assert idx[0] == 1
+    # sign(0) = +1 with an all-zero residual row of S cannot be built from
+    # seeds; check the encoder rule on the recorded z instead
+    sg = _unpack_le(kc.signs, d, 1)[0]
+    assert np.array_equal(sg, (kc.z[0] >= 0).astype(np.uint32))
+
+
+# ----------------------------------------------------------- estimator
+@pytest.mark.parametrize("d,bits,kind", [(128, 2, "dense"), (128, 2, "hadamard"), (256, 7, "dense")])
+def test_score_equals_inner_product_with_explicit_reconstruction(d, bits, kind):
+    rot = O.rotation(8, d, kind)
+    k = _keys(64, d, 2, 5.0)
+    q = np.random.default_rng(3).standard_normal((4, d))
+    kc = O.compress_keys(k, bits, rot)
+    c, _ = O.codebook(d, bits)
+    idx = _unpack_le(kc.codes, d, bits)
+    sg = _unpack_le(kc.signs, d, 1) * 2.0 - 1.0
+    m = rot.s.shape[0]
+    yhat = c[idx] + KAPPA(m) * kc.rnorm.astype(np.float64)[:, None] * (sg @ rot.s)
+    khat = kc.knorm.astype(np.float64)[:, None] * (yhat @ rot.pi)      # n Pi^T (...)
+    want = q @ khat.T
+    got = O.scores(q, kc, bits, rot)
+    scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(k, axis=1)[None, :]
+    assert np.abs(got - want).max() < 1e-12 * scale.max()
+
+
+def _mc_errors(n_seeds, d=128, bits=2):
+    rng = np.random.default_rng(2024)
+    k = rng.standard_normal((1, d))
+    q = k[0] * 0.8 + 0.6 * rng.standard_normal(d)
+    truth = float(q @ k[0])
+    full, mse, bound = [], [], []
+    for s in range(n_seeds):
+        rot = O.rotation(10_000 + s, d)
+        kc = O.compress_keys(k, bits, rot, keep_aux=True)
+        sc, t1, _ = O.scores(q[None, :], kc, bits, rot, terms=True)
+        full.append(sc[0, 0] - truth)
+        mse.append(t1[0, 0] - truth)
+        m = rot.s.shape[0]
+        bound.append(math.pi / (2 * m) * float(q @ q) * kc.rho[0] ** 2 * float(kc.knorm[0]) ** 2)
+    return np.array(full), np.array(mse), np.array(bound)
+
+
+def test_qjl_estimator_unbiased_and_mse_only_biased():
+    full, mse, bound = _mc_errors(1500)
+    n = len(full)
+    # unbiased: |mean| < 3 sigma / sqrt(N)
+    assert abs(full.mean()) < 3 * full.std() / math.sqrt(n), (full.mean(), full.std())
+    # power: the estimator without the QJL term is biased under the same test
+    assert abs(mse.mean()) > 3 * mse.std() / math.sqrt(n), (mse.mean(), mse.std())
+    # variance at most the QJL bound pi/(2m) ||q||^2 ||r||^2 ||k||^2 (+ MC slack)
+    assert full.var() <= 1.15 * bound.mean()
+
+
+def test_scores_linear_in_query():
+    d, bits = 128, 3
+    rot = O.rotation(5, d)
+    kc = O.compress_keys(_keys(50, d, 4), bits, rot)
+    q = np.random.default_rng(9).standard_normal((1, d))
+    a = O.scores(q, kc, bits, rot)
+    b = O.scores(2.5 * q, kc, bits, rot)
+    assert np.abs(b - 2.5 * a).max() < 1e-12 * np.abs(a).max()
+
+
+# ---------------------------------------------------------------- values
+def test_fp16_conversion_matches_numpy():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 5, 4000),
+                        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 6.1e-5, 5.96e-8, 2.98e-8,
+                         2.9802322387695312e-08, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11]])
+    got = O.f64_to_f16_bits(x)
+    want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.f16_bits_to_f64(want), want.view(np.float16).astype(np.float64))
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (4, 32), (2, 64), (4, 128)])
+def test_value_encode_restated(bits, group):
+    d = 128
+    v = np.random.default_rng(bits + group).standard_normal((200, d)).astype(np.float32).astype(np.float64)
+    vc = O.compress_values(v, bits, group, keep_aux=True)
+    L = (1 << bits) - 1
+    vg = v.reshape(200, d // group, group)
+    mn, mx = vg.min(axis=2), vg.max(axis=2)
+    sc = ((mx - mn) / L).astype(np.float16)
+    ze = mn.astype(np.float16)
+    assert np.array_equal(vc.params[..., 0], sc.view(np.uint16))
+    assert np.array_equal(vc.params[..., 1], ze.view(np.uint16))
+    scd, zed = sc.astype(np.float64)[..., None], ze.astype(np.float64)[..., None]
+    codes = np.clip(np.rint((vg - zed) / scd), 0, L).reshape(200, d).astype(np.uint32)
+    assert np.array_equal(_unpack_le(vc.codes, d, bits), codes)
+    vhat = O.dequant_values(vc, d, bits, group).reshape(200, d // group, group)
+    bound = scd / 2 + np.abs(zed - mn[..., None]) + L * np.abs(scd - ((mx - mn) / L)[..., None])
+    assert np.all(np.abs(vg - vhat) <= bound * (1 + 1e-12) + 1e-15)
+
+
+def test_constant_group_exact():
+    d = 64
+    v = np.full((3, d), 0.5)
+    v[1] = -2.25
+    v[2, :32] = 1.0
+    vc = O.compress_values(v, 2, 32)
+    assert np.all(vc.params[[0, 1], :, 0] == 0)
+    assert np.all(O.dequant_values(vc, d, 2, 32)[:2] == v[:2])
+    assert np.all(_unpack_le(vc.codes, d, 2)[:2] == 0)
+
+
+def test_value_cos_sim_near_page_figures(golden_dir):
+    figs = json.load(open(os.path.join(golden_dir, "page_figures.json")))["value_cos_sim"]
+    v = np.random.default_rng(0).standard_normal((4000, 128))
+    for bits, want, tol in [(2, figs["bits2"], 0.02), (4, figs["bits4"], 0.003)]:
+        vhat = O.dequant_values(O.compress_values(v, bits, 32), 128, bits, 32)
+        cs = (v * vhat).sum(1) / np.linalg.norm(v, axis=1) / np.linalg.norm(vhat, axis=1)
+        assert abs(cs.mean() - want) < tol, (bits, cs.mean(), want)
+
+
+# -------------------------------------------------------------- attention
+def _setup(T, d=128, bits=2, vbits=2, group=32, kscale=1.0, seed=0):
+    rng = np.random.default_rng(seed)
+    rot = O.rotation(seed + 100, d)
+    k = rng.standard_normal((T, d)) * kscale
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((4, d))
+    return rot, O.compress_keys(k, bits, rot), O.compress_values(v, vbits, group), q
+
+
+def test_attention_is_softmax_of_scores_times_dequantized_values():
+    d, bits, vbits, g = 128, 2, 4, 32
+    for kscale in (1.0, 60.0):
+        rot, kc, vc, q = _setup(257, d, bits, vbits, g, kscale)
+        sc = O.scores(q, kc, bits, rot) / math.sqrt(d)
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        want = p @ O.dequant_values(vc, d, vbits, g)
+        got = O.attend(q, kc, bits, rot, vc, vbits, g)
+        assert np.abs(got - want).max() < 1e-12
+
+
+def test_attention_single_key_and_equal_keys():
+    d = 128
+    rot, kc, vc, q = _setup(1, d)
+    vhat = O.dequant_values(vc, d, 2, 32)
+    assert np.abs(O.attend(q, kc, 2, rot, vc, 2, 32) - vhat[0]).max() < 1e-15
+    # five copies of one key: softmax is uniform, output is the mean value
+    rng = np.random.default_rng(1)
+    k = np.repeat(rng.standard_normal((1, d)), 5, axis=0)
+    v = rng.standard_normal((5, d))
+    kc = O.compress_keys(k, 2, rot)
+    vc = O.compress_values(v, 2, 32)
+    want = O.dequant_values(vc, d, 2, 32).mean(axis=0)
+    assert np.abs(O.attend(q, kc, 2, rot, vc, 2, 32) - want[None]).max() < 1e-14
+
+
+def test_attention_empty_cache_gives_zeros():
+    rot, kc, vc, q = _setup(4)
+    empty_k = O.KeyCache(kc.codes[:0], kc.signs[:0], kc.knorm[:0], kc.rnorm[:0])
+    empty_v = O.ValueCache(vc.codes[:0], vc.params[:0])
+    assert np.all(O.attend(q, empty_k, 2, rot, empty_v, 2, 32) == 0.0)
+
+
+# ------------------------------------------------------------ cache size
+def test_qwen25_3b_8k_cache_size_matches_page(golden_dir):
+    fig = json.load(open(os.path.join(golden_dir, "page_figures.json")))["kv_cache_qwen25_3b_8k_3bit"]
+    layers, heads, tokens, d = 36, 2, 8192, 128
+    per_tok = O.key_bytes_per_vector(d, 2, d) + O.value_bytes_per_vector(d, 2, 32)
+    packed = layers * heads * tokens * per_tok
+    dense = layers * heads * tokens * d * 2 * 2        # K and V in bf16
+    assert packed == 61_341_696 and dense == 301_989_888
+    ratio, page = packed / dense, fig["after_mb"] / fig["before_mb"]
+    assert abs(ratio / page - 1) < 0.03, (ratio, page)
+
+
+def test_capacity_ratio_consistent_with_page(golden_dir):
+    # K 2+1 bits / V 2-bit g32 gives 4.92x over bf16: the page's 70B capacity
+    # estimate (TQ3 / FP16) is the same ratio to within rounding of its figures
+    fig = json.load(open(os.path.join(golden_dir, "page_figures.json")))["context_capacity_70b"]
+    per_tok = O.key_bytes_per_vector(128, 2, 128) + O.value_bytes_per_vector(128, 2, 32)
+    ours = 2 * 128 * 2 / per_tok
+    assert abs(ours / (fig["tq3_k"] / fig["fp16_k"]) - 1) < 0.01
