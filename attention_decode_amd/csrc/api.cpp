@@ -1,0 +1,560 @@
+// C ABI of libtq: argument validation, handle lifetime, workspace carve-up and
+// the launch of the HIP kernels.  Nothing here computes on the data path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+tq_status fail(tq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+tq_status fail(tq_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+tq_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(TQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(tq_dtype t)
+{
+    switch (t) {
+    case TQ_F32: return 4;
+    case TQ_BF16: return 2;
+    case TQ_F16: return 2;
+    }
+    return 0;
+}
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------- profiling
+struct ProfRecord {
+    const char *name;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_live;
+std::vector<ProfRecord> g_prof_free;
+
+}  // namespace
+
+namespace tq {
+
+void prof_begin(const char *name, hipStream_t stream, void **token)
+{
+    *token = nullptr;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof_on) return;
+    ProfRecord r;
+    if (!g_prof_free.empty()) {
+        r = g_prof_free.back();
+        g_prof_free.pop_back();
+    } else {
+        if (hipEventCreate(&r.start) != hipSuccess) return;
+        if (hipEventCreate(&r.stop) != hipSuccess) return;
+    }
+    r.name = name;
+    hipEventRecord(r.start, stream);
+    g_prof_live.push_back(r);
+    *token = reinterpret_cast<void *>(g_prof_live.size());   // 1-based index
+}
+
+void prof_end(void *token, hipStream_t stream)
+{
+    if (!token) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    const size_t idx = reinterpret_cast<size_t>(token) - 1;
+    if (idx < g_prof_live.size()) hipEventRecord(g_prof_live[idx].stop, stream);
+}
+
+}  // namespace tq
+
+extern "C" {
+
+const char *tq_last_error(void) { return g_error.c_str(); }
+
+tq_status tq_profile_enable(int on)
+{
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_on = on != 0;
+    return TQ_OK;
+}
+
+tq_status tq_profile_read(const char *name, double *total_ms, int64_t *launches)
+{
+    if (!name || !total_ms || !launches) return fail(TQ_EINVAL, "tq_profile_read: NULL argument");
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    double sum = 0.0;
+    int64_t count = 0;
+    std::vector<ProfRecord> keep;
+    for (ProfRecord &r : g_prof_live) {
+        if (std::strstr(r.name, name) == nullptr) {
+            keep.push_back(r);
+            continue;
+        }
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "tq_profile_read: hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "tq_profile_read: hipEventElapsedTime");
+        sum += ms;
+        ++count;
+        g_prof_free.push_back(r);
+    }
+    g_prof_live.swap(keep);
+    *total_ms = sum;
+    *launches = count;
+    return TQ_OK;
+}
+
+// ------------------------------------------------------------------ codebook
+tq_status tq_codebook_host(int d, int bits, double *centroids, double *boundaries)
+{
+    if (d < 3 || d > 4096) return fail(TQ_EINVAL, "codebook: d=%d outside [3, 4096]", d);
+    if (bits < 1 || bits > 8) return fail(TQ_EINVAL, "codebook: bits=%d outside [1, 8]", bits);
+    if (!centroids || !boundaries) return fail(TQ_EINVAL, "codebook: NULL output");
+    double res = 0.0;
+    const tq_status st = tq::lloyd_max_codebook(d, bits, centroids, boundaries, &res);
+    if (st != TQ_OK) return fail(st, "codebook: Lloyd-Max residual %.3g after the iteration cap", res);
+    return TQ_OK;
+}
+
+tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
+{
+    if (!out) return fail(TQ_EINVAL, "tq_build_codebook: NULL out");
+    *out = nullptr;
+    auto *cb = new (std::nothrow) tq_codebook;
+    if (!cb) return fail(TQ_ENOMEM, "tq_build_codebook: host allocation failed");
+    cb->d = d;
+    cb->bits = bits;
+    const int L = 1 << (bits < 1 ? 1 : bits > 8 ? 8 : bits);
+    cb->centroids.assign(L, 0.0);
+    cb->boundaries.assign(L - 1, 0.0);
+    tq_status st = tq_codebook_host(d, bits, cb->centroids.data(), cb->boundaries.data());
+    if (st != TQ_OK) {
+        delete cb;
+        return st;
+    }
+    std::vector<float> host(2 * L);
+    for (int i = 0; i < L; ++i) host[i] = static_cast<float>(cb->centroids[i]);
+    for (int i = 0; i < L - 1; ++i) host[L + i] = static_cast<float>(cb->boundaries[i]);
+    host[2 * L - 1] = INFINITY;
+    hipError_t e = hipGetDevice(&cb->device);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&cb->d_centroids), sizeof(float) * 2 * L);
+    if (e == hipSuccess)
+        e = hipMemcpy(cb->d_centroids, host.data(), sizeof(float) * 2 * L, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (cb->d_centroids) hipFree(cb->d_centroids);
+        delete cb;
+        return hip_fail(e, "tq_build_codebook: device upload");
+    }
+    cb->d_boundaries = cb->d_centroids + L;
+    *out = cb;
+    return TQ_OK;
+}
+
+void tq_codebook_free(tq_codebook *cb)
+{
+    if (!cb) return;
+    if (cb->d_centroids) hipFree(cb->d_centroids);
+    delete cb;
+}
+
+tq_status tq_codebook_tables(const tq_codebook *cb, double *centroids, double *boundaries)
+{
+    if (!cb || !centroids || !boundaries) return fail(TQ_EINVAL, "tq_codebook_tables: NULL argument");
+    std::memcpy(centroids, cb->centroids.data(), sizeof(double) * cb->centroids.size());
+    std::memcpy(boundaries, cb->boundaries.data(), sizeof(double) * cb->boundaries.size());
+    return TQ_OK;
+}
+
+// ------------------------------------------------------------------ rotation
+tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, double *s)
+{
+    if (d < 2 || d > 4096) return fail(TQ_EINVAL, "rotation: d=%d outside [2, 4096]", d);
+    if (kind != TQ_ROT_DENSE && kind != TQ_ROT_HADAMARD) return fail(TQ_EINVAL, "rotation: bad kind %d", kind);
+    if (kind == TQ_ROT_HADAMARD && (d & (d - 1)) != 0)
+        return fail(TQ_EUNSUPPORTED, "rotation: Hadamard needs a power-of-two d, got %d", d);
+    if (pi) {
+        if (kind == TQ_ROT_DENSE) tq::dense_rotation(seed, d, pi);
+        else tq::hadamard_rotation(seed, d, pi);
+    }
+    if (s) tq::qjl_projection(seed, d, d, s);
+    return TQ_OK;
+}
+
+tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation **out)
+{
+    if (!out) return fail(TQ_EINVAL, "tq_make_rotation: NULL out");
+    *out = nullptr;
+    if (!supported_d(d)) return fail(TQ_EUNSUPPORTED, "tq_make_rotation: d=%d not in {64, 128, 256}", d);
+    const size_t dd = static_cast<size_t>(d) * d;
+    std::vector<double> pi(dd), s(dd);
+    tq_status st = tq_rotation_host(seed, d, kind, pi.data(), s.data());
+    if (st != TQ_OK) return st;
+    std::vector<float> host(4 * dd + d);
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            host[i * d + j] = static_cast<float>(pi[i * d + j]);            // Pi
+            host[dd + j * d + i] = static_cast<float>(pi[i * d + j]);       // Pi^T
+            host[2 * dd + i * d + j] = static_cast<float>(s[i * d + j]);    // S
+            host[3 * dd + j * d + i] = static_cast<float>(s[i * d + j]);    // S^T
+        }
+    if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 4 * dd);
+    else for (int j = 0; j < d; ++j) host[4 * dd + j] = 1.0f;
+    auto *rot = new (std::nothrow) tq_rotation;
+    if (!rot) return fail(TQ_ENOMEM, "tq_make_rotation: host allocation failed");
+    rot->seed = seed;
+    rot->d = d;
+    rot->m = d;
+    rot->kind = kind;
+    hipError_t e = hipGetDevice(&rot->device);
+    if (e == hipSuccess) e = hipMalloc(&rot->d_block, sizeof(float) * host.size());
+    if (e == hipSuccess) e = hipMemcpy(rot->d_block, host.data(), sizeof(float) * host.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (rot->d_block) hipFree(rot->d_block);
+        delete rot;
+        return hip_fail(e, "tq_make_rotation: device upload");
+    }
+    float *base = static_cast<float *>(rot->d_block);
+    rot->d_pi = base;
+    rot->d_piT = base + dd;
+    rot->d_s = base + 2 * dd;
+    rot->d_sT = base + 3 * dd;
+    rot->d_dsign = base + 4 * dd;
+    *out = rot;
+    return TQ_OK;
+}
+
+void tq_rotation_free(tq_rotation *rot)
+{
+    if (!rot) return;
+    if (rot->d_block) hipFree(rot->d_block);
+    delete rot;
+}
+
+// ------------------------------------------------------------------ sizes
+size_t tq_key_plane_bytes(const tq_key_fmt *fmt, int64_t n_vec, int plane)
+{
+    if (!fmt || n_vec < 0 || fmt->d <= 0 || fmt->mse_bits <= 0 || fmt->qjl_m < 0) return 0;
+    const size_t n = static_cast<size_t>(n_vec);
+    switch (plane) {
+    case 0: return n * ((static_cast<size_t>(fmt->d) * fmt->mse_bits + 7) / 8);
+    case 1: return n * ((static_cast<size_t>(fmt->qjl_m) + 7) / 8);
+    case 2: return n * sizeof(float);
+    case 3: return n * sizeof(float);
+    }
+    return 0;
+}
+
+size_t tq_val_plane_bytes(const tq_val_fmt *fmt, int64_t n_vec, int plane)
+{
+    if (!fmt || n_vec < 0 || fmt->d <= 0 || fmt->bits <= 0 || fmt->group <= 0 || fmt->d % fmt->group)
+        return 0;
+    const size_t n = static_cast<size_t>(n_vec);
+    switch (plane) {
+    case 0: return n * ((static_cast<size_t>(fmt->d) * fmt->bits + 7) / 8);
+    case 1: return n * (static_cast<size_t>(fmt->d) / fmt->group) * 2 * sizeof(uint16_t);
+    }
+    return 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+tq_status check_key_fmt(const tq_key_fmt *f, const char *who)
+{
+    if (!f) return fail(TQ_EINVAL, "%s: NULL key format", who);
+    if (!f->cb || !f->rot) return fail(TQ_EINVAL, "%s: key format without codebook or rotation", who);
+    if (!supported_d(f->d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not in {64, 128, 256}", who, f->d);
+    if (f->mse_bits < 1 || f->mse_bits > 7)
+        return fail(TQ_EUNSUPPORTED, "%s: mse_bits=%d not in [1, 7]", who, f->mse_bits);
+    if (f->qjl_m != f->d) return fail(TQ_EUNSUPPORTED, "%s: qjl_m=%d must equal d=%d", who, f->qjl_m, f->d);
+    if (f->cb->d != f->d || f->cb->bits != f->mse_bits)
+        return fail(TQ_EINVAL, "%s: codebook is for (d=%d, bits=%d), format wants (%d, %d)", who,
+                    f->cb->d, f->cb->bits, f->d, f->mse_bits);
+    if (f->rot->d != f->d || f->rot->m != f->qjl_m)
+        return fail(TQ_EINVAL, "%s: rotation is for d=%d, format wants %d", who, f->rot->d, f->d);
+    return TQ_OK;
+}
+
+tq_status check_val_fmt(const tq_val_fmt *f, const char *who)
+{
+    if (!f) return fail(TQ_EINVAL, "%s: NULL value format", who);
+    if (!supported_d(f->d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not in {64, 128, 256}", who, f->d);
+    if (f->bits != 2 && f->bits != 4) return fail(TQ_EUNSUPPORTED, "%s: value bits=%d not in {2, 4}", who, f->bits);
+    if (f->group != 32 && f->group != 64 && f->group != 128)
+        return fail(TQ_EUNSUPPORTED, "%s: group=%d not in {32, 64, 128}", who, f->group);
+    if (f->group > f->d || f->d % f->group) return fail(TQ_EINVAL, "%s: group=%d does not divide d=%d", who, f->group, f->d);
+    return TQ_OK;
+}
+
+tq_status check_dtype(tq_dtype t, const char *who)
+{
+    if (dtype_size(t) == 0) return fail(TQ_EINVAL, "%s: bad dtype %d", who, static_cast<int>(t));
+    return TQ_OK;
+}
+
+tq_status check_input(const void *x, tq_dtype dt, int B, int H, int64_t T, int64_t sb, int64_t sh,
+                      int64_t st, int d, const char *who)
+{
+    if (B < 1 || H < 1 || T < 0) return fail(TQ_EINVAL, "%s: bad shape B=%d H=%d T=%lld", who, B, H, (long long)T);
+    if (T > 0 && !x) return fail(TQ_EINVAL, "%s: NULL input", who);
+    if (sb < 0 || sh < 0 || st < 0) return fail(TQ_EINVAL, "%s: negative stride", who);
+    if (T > 0 && st < d) return fail(TQ_EINVAL, "%s: token stride %lld overlaps a %d-channel row", who, (long long)st, d);
+    const size_t es = dtype_size(dt);
+    if (!aligned16(x) || (sb * es) % 16 || (sh * es) % 16 || (st * es) % 16)
+        return fail(TQ_EALIGN, "%s: input pointer and strides must be 16-byte aligned", who);
+    if (static_cast<int64_t>(B) * H * T > (int64_t(1) << 40))
+        return fail(TQ_EINVAL, "%s: too many vectors", who);
+    return TQ_OK;
+}
+
+tq_status check_kcache(const tq_kcache &kc, const char *who)
+{
+    if (!kc.codes || !kc.signs || !kc.knorm || !kc.rnorm) return fail(TQ_EINVAL, "%s: NULL key plane", who);
+    if (!aligned16(kc.codes) || !aligned16(kc.signs) || !aligned16(kc.knorm) || !aligned16(kc.rnorm))
+        return fail(TQ_EALIGN, "%s: key planes must be 16-byte aligned", who);
+    return TQ_OK;
+}
+
+tq_status check_vcache(const tq_vcache &vc, const char *who)
+{
+    if (!vc.codes || !vc.params) return fail(TQ_EINVAL, "%s: NULL value plane", who);
+    if (!aligned16(vc.codes) || !aligned16(vc.params)) return fail(TQ_EALIGN, "%s: value planes must be 16-byte aligned", who);
+    return TQ_OK;
+}
+
+#define TQ_TRY(expr)                         \
+    do {                                     \
+        const tq_status st_ = (expr);        \
+        if (st_ != TQ_OK) return st_;        \
+    } while (0)
+
+struct AttendLayout {
+    size_t qprep, ml, acc, total;
+};
+
+AttendLayout attend_layout(int d, int m, int B, int Hq, int splits)
+{
+    AttendLayout L;
+    const size_t rows = static_cast<size_t>(B) * Hq;
+    L.qprep = 0;
+    L.ml = align256(rows * (d + m) * sizeof(float));
+    L.acc = L.ml + align256(rows * splits * 2 * sizeof(float));
+    L.total = L.acc + align256(rows * splits * d * sizeof(float));
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
+                           int64_t T, int64_t sb, int64_t sh, int64_t st, tq_kcache out, void *stream)
+{
+    const char *who = "tq_compress_keys";
+    TQ_TRY(check_key_fmt(fmt, who));
+    TQ_TRY(check_dtype(dtype, who));
+    TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
+    if (T == 0) return TQ_OK;
+    TQ_TRY(check_kcache(out, who));
+    tq::KeyLaunch a{};
+    a.k = k;
+    a.dtype = dtype;
+    a.B = B;
+    a.H = Hkv;
+    a.T = T;
+    a.sb = sb;
+    a.sh = sh;
+    a.st = st;
+    a.d = fmt->d;
+    a.bits = fmt->mse_bits;
+    a.m = fmt->qjl_m;
+    a.hadamard = fmt->rot->kind == TQ_ROT_HADAMARD;
+    a.piT = fmt->rot->d_piT;
+    a.sT = fmt->rot->d_sT;
+    a.dsign = fmt->rot->d_dsign;
+    a.centroids = fmt->cb->d_centroids;
+    a.boundaries = fmt->cb->d_boundaries;
+    a.out = out;
+    const hipError_t e = tq::launch_compress_keys(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv,
+                             int64_t T, int64_t sb, int64_t sh, int64_t st, tq_vcache out, void *stream)
+{
+    const char *who = "tq_compress_values";
+    TQ_TRY(check_val_fmt(fmt, who));
+    TQ_TRY(check_dtype(dtype, who));
+    TQ_TRY(check_input(v, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
+    if (T == 0) return TQ_OK;
+    TQ_TRY(check_vcache(out, who));
+    tq::ValueLaunch a{};
+    a.v = v;
+    a.dtype = dtype;
+    a.B = B;
+    a.H = Hkv;
+    a.T = T;
+    a.sb = sb;
+    a.sh = sh;
+    a.st = st;
+    a.d = fmt->d;
+    a.bits = fmt->bits;
+    a.group = fmt->group;
+    a.out = out;
+    const hipError_t e = tq::launch_compress_values(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq,
+                                     int Hkv, int64_t T, const tq_kcache &kc, const char *who)
+{
+    TQ_TRY(check_key_fmt(fmt, who));
+    TQ_TRY(check_dtype(dtype, who));
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 0) return fail(TQ_EINVAL, "%s: bad shape", who);
+    if (Hq % Hkv) return fail(TQ_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
+    if (!q) return fail(TQ_EINVAL, "%s: NULL query", who);
+    if (!aligned16(q)) return fail(TQ_EALIGN, "%s: query must be 16-byte aligned", who);
+    if (static_cast<int64_t>(B) * Hkv * T > (int64_t(1) << 40)) return fail(TQ_EINVAL, "%s: too many keys", who);
+    if (T > 0) TQ_TRY(check_kcache(kc, who));
+    return TQ_OK;
+}
+
+size_t tq_scores_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq)
+{
+    if (!fmt || B < 1 || Hq < 1) return 0;
+    return align256(static_cast<size_t>(B) * Hq * (fmt->d + fmt->qjl_m) * sizeof(float));
+}
+
+tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq, int Hkv,
+                    int64_t T, tq_kcache kc, float *scores, void *ws, size_t ws_bytes, void *stream)
+{
+    const char *who = "tq_scores";
+    TQ_TRY(check_decode_common(fmt, q, dtype, B, Hq, Hkv, T, kc, who));
+    if (T == 0) return TQ_OK;
+    if (!scores || !ws) return fail(TQ_EINVAL, "%s: NULL scores or workspace", who);
+    if (!aligned16(scores) || !aligned16(ws)) return fail(TQ_EALIGN, "%s: scores/workspace must be 16-byte aligned", who);
+    const size_t need = tq_scores_workspace_bytes(fmt, B, Hq);
+    if (ws_bytes < need) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, need);
+    tq::DecodeLaunch a{};
+    a.q = q;
+    a.dtype = dtype;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.d = fmt->d;
+    a.bits = fmt->mse_bits;
+    a.m = fmt->qjl_m;
+    a.piT = fmt->rot->d_piT;
+    a.sT = fmt->rot->d_sT;
+    a.centroids = fmt->cb->d_centroids;
+    a.kc = kc;
+    a.qprep = static_cast<float *>(ws);
+    a.scores = scores;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = tq::launch_qprep(a, s);
+    if (e == hipSuccess) e = tq::launch_scores(a, s);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+int tq_attend_splits(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T)
+{
+    if (!fmt || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < 0) return 0;
+    const int G = Hq / Hkv, gc = tq::query_chunk(G);
+    const int64_t units = static_cast<int64_t>(B) * Hkv * (G / gc);
+    const int64_t tiles = (T + tq::kDecodeTile - 1) / tq::kDecodeTile;
+    int64_t want = (1024 + units - 1) / units;          // about four workgroups per CU
+    if (want > tiles) want = tiles;
+    if (want > 1024) want = 1024;
+    return want < 1 ? 1 : static_cast<int>(want);
+}
+
+size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits)
+{
+    if (!fmt || B < 1 || Hq < 1) return 0;
+    const int splits = n_splits > 0 ? n_splits : tq_attend_splits(fmt, B, Hq, Hkv, T);
+    if (splits < 1) return 0;
+    return attend_layout(fmt->d, fmt->qjl_m, B, Hq, splits).total;
+}
+
+tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
+                           int B, int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
+                           int n_splits, void *ws, size_t ws_bytes, float *out, void *stream)
+{
+    const char *who = "tq_attend_decode";
+    TQ_TRY(check_decode_common(kfmt, q, dtype, B, Hq, Hkv, T, kc, who));
+    TQ_TRY(check_val_fmt(vfmt, who));
+    if (vfmt->d != kfmt->d) return fail(TQ_EINVAL, "%s: key d=%d and value d=%d differ", who, kfmt->d, vfmt->d);
+    if (!out) return fail(TQ_EINVAL, "%s: NULL output", who);
+    if (!aligned16(out)) return fail(TQ_EALIGN, "%s: output must be 16-byte aligned", who);
+    if (n_splits < 0 || n_splits > 65535) return fail(TQ_EINVAL, "%s: n_splits=%d outside [0, 65535]", who, n_splits);
+    if (!(softmax_scale >= 0.0f) || !std::isfinite(softmax_scale))
+        return fail(TQ_EINVAL, "%s: softmax_scale must be finite and >= 0", who);
+    tq::DecodeLaunch a{};
+    a.q = q;
+    a.dtype = dtype;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.d = kfmt->d;
+    a.bits = kfmt->mse_bits;
+    a.m = kfmt->qjl_m;
+    a.out = out;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        const hipError_t e = tq::launch_attend(a, s);
+        return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+    }
+    TQ_TRY(check_vcache(vc, who));
+    if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
+    if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
+    const int splits = n_splits > 0 ? n_splits : tq_attend_splits(kfmt, B, Hq, Hkv, T);
+    const AttendLayout L = attend_layout(kfmt->d, kfmt->qjl_m, B, Hq, splits);
+    if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
+    a.piT = kfmt->rot->d_piT;
+    a.sT = kfmt->rot->d_sT;
+    a.centroids = kfmt->cb->d_centroids;
+    a.kc = kc;
+    a.vbits = vfmt->bits;
+    a.group = vfmt->group;
+    a.vc = vc;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : static_cast<float>(1.0 / std::sqrt(double(kfmt->d)));
+    a.splits = splits;
+    char *base = static_cast<char *>(ws);
+    a.qprep = reinterpret_cast<float *>(base + L.qprep);
+    a.part_ml = reinterpret_cast<float *>(base + L.ml);
+    a.part_acc = reinterpret_cast<float *>(base + L.acc);
+    hipError_t e = tq::launch_qprep(a, s);
+    if (e == hipSuccess) e = tq::launch_attend(a, s);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+}  // extern "C"

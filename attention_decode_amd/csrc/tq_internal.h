@@ -1,0 +1,100 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of libtq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tq.h"
+
+struct tq_codebook {
+    int d = 0, bits = 0;
+    std::vector<double> centroids, boundaries;   // fp64 host tables
+    float *d_centroids = nullptr;                // device fp32 [2^bits]
+    float *d_boundaries = nullptr;               // device fp32 [2^bits - 1]
+    int device = 0;
+};
+
+struct tq_rotation {
+    uint64_t seed = 0;
+    int d = 0, m = 0;
+    tq_rot_kind kind = TQ_ROT_DENSE;
+    // device fp32 tables (one allocation, carved up)
+    float *d_pi = nullptr;      // [d][d]  y = Pi u, row-major
+    float *d_piT = nullptr;     // [d][d]  transpose of Pi
+    float *d_s = nullptr;       // [m][d]  QJL projection
+    float *d_sT = nullptr;      // [d][m]  transpose of S
+    float *d_dsign = nullptr;   // [d]     Hadamard signs (+-1), dense: unused
+    void *d_block = nullptr;
+    int device = 0;
+};
+
+namespace tq {
+
+// ---- host math (host_math.cpp)
+uint64_t rng_draw(uint64_t seed, int stream, uint64_t k);
+double rng_normal(uint64_t seed, int stream, uint64_t n);
+tq_status lloyd_max_codebook(int d, int bits, double *centroids, double *boundaries,
+                             double *residual_out);
+void dense_rotation(uint64_t seed, int d, double *pi);
+void hadamard_signs(uint64_t seed, int d, float *signs);
+void hadamard_rotation(uint64_t seed, int d, double *pi);
+void qjl_projection(uint64_t seed, int m, int d, double *s);
+
+// ---- kernel launchers.  All return hipSuccess or the launch error.
+struct KeyLaunch {
+    const void *k;
+    tq_dtype dtype;
+    int B, H;
+    int64_t T, sb, sh, st;      // element strides
+    int d, bits, m;
+    bool hadamard;
+    const float *piT, *sT, *dsign, *centroids, *boundaries;
+    tq_kcache out;
+};
+hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
+
+struct ValueLaunch {
+    const void *v;
+    tq_dtype dtype;
+    int B, H;
+    int64_t T, sb, sh, st;
+    int d, bits, group;
+    tq_vcache out;
+};
+hipError_t launch_compress_values(const ValueLaunch &a, hipStream_t stream);
+
+struct DecodeLaunch {
+    const void *q;              // [B, Hq, d]
+    tq_dtype dtype;
+    int B, Hq, Hkv;
+    int64_t T;
+    int d, bits, m;
+    const float *piT, *sT, *centroids;
+    tq_kcache kc;
+    // attention only
+    int vbits, group;
+    tq_vcache vc;
+    float scale;
+    int splits;
+    // workspace carve-up
+    float *qprep;               // [B, Hq, d + m]
+    float *part_ml;             // [B, Hq, splits, 2]
+    float *part_acc;            // [B, Hq, splits, d]
+    float *scores;              // tq_scores output [B, Hq, T]
+    float *out;                 // [B, Hq, d]
+};
+hipError_t launch_qprep(const DecodeLaunch &a, hipStream_t stream);
+hipError_t launch_scores(const DecodeLaunch &a, hipStream_t stream);
+hipError_t launch_attend(const DecodeLaunch &a, hipStream_t stream);
+
+// query-chunk size the decode kernels use for a GQA group of G heads
+int query_chunk(int G);
+constexpr int kDecodeTile = 256;   // keys per decode tile
+
+// ---- profiling hooks (api.cpp)
+void prof_begin(const char *name, hipStream_t stream, void **token);
+void prof_end(void *token, hipStream_t stream);
+
+}  // namespace tq

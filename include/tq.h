@@ -1,0 +1,199 @@
+/*
+ * libtq: TurboQuant KV-cache compression and decode attention for AMD MI355X
+ * (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The method (pages "turboquant-pytorch", section "What it does", and the
+ * discosf.com TurboQuant article, section "TurboQuant in one sentence",
+ * steps 1-4):
+ *   keys   : normalise, rotate by a random orthogonal matrix Pi, quantise each
+ *            rotated coordinate with a Lloyd-Max codebook, and keep one sign
+ *            bit per row of a Gaussian QJL projection S of the residual;
+ *   values : min-max quantise each group of g channels to 2 or 4 bits with an
+ *            fp16 scale and zero, packed four (or two) codes per byte;
+ *   decode : score the query against the packed keys directly (asymmetric
+ *            estimator), softmax, and sum the dequantised values.
+ *
+ * Conventions shared by every call
+ *  - Device pointers are caller-owned (allocated by the caller, e.g. PyTorch),
+ *    must be 16-byte aligned, and are never freed by libtq.  libtq allocates
+ *    device memory only inside tq_build_codebook and tq_make_rotation.
+ *  - Calls that launch work are asynchronous on `stream` (a hipStream_t; NULL
+ *    is the default stream) and return after the launch.  A device fault shows
+ *    up at the caller's next synchronisation.
+ *  - Every argument is validated before anything is launched.  On any status
+ *    other than TQ_OK nothing was launched, and tq_last_error() returns a
+ *    thread-local message.  Nothing throws across this interface.
+ *  - Handles are immutable after creation and safe to share across streams;
+ *    freeing a handle while a launch that uses it is in flight is an error of
+ *    the caller.
+ *  - Packed planes are laid out [B, Hkv, T, row] with rows contiguous in T.
+ *    Bit-streams are LSB-first: element j of width w occupies bits
+ *    [w*j, w*j + w) of the row read as little-endian bytes.
+ *  - Grouped-query attention: query head hq reads KV head hq / (Hq / Hkv).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_EINVAL = 1,        /* an argument is out of range or inconsistent   */
+    TQ_EUNSUPPORTED = 2,  /* a valid combination this build does not serve  */
+    TQ_EALIGN = 3,        /* a device pointer or stride is not 16-B aligned  */
+    TQ_ENOMEM = 4,        /* handle allocation failed, or workspace too small*/
+    TQ_EHIP = 5,          /* the HIP runtime reported an error                */
+    TQ_ENOTCONV = 6       /* the codebook iteration did not converge          */
+} tq_status;
+
+typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot_kind;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef struct tq_codebook tq_codebook;   /* opaque, immutable */
+typedef struct tq_rotation tq_rotation;   /* opaque, immutable */
+
+/* Key format: d channels, mse_bits Lloyd-Max bits per coordinate, qjl_m sign
+   rows (this build: qjl_m == d), the codebook for (d, mse_bits) and the
+   rotation (Pi and S) for d. */
+typedef struct {
+    int d;
+    int mse_bits;
+    int qjl_m;
+    const tq_codebook *cb;
+    const tq_rotation *rot;
+} tq_key_fmt;
+
+/* Value format: d channels, bits per code (2 or 4), group size g (g | d,
+   g in {32, 64, 128}). */
+typedef struct {
+    int d;
+    int bits;
+    int group;
+} tq_val_fmt;
+
+/* Packed key cache planes (device, caller-owned), per vector:
+   codes d*mse_bits/8 B, signs qjl_m/8 B, knorm fp32 ||k||, rnorm fp32 ||r||. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *signs;
+    float *knorm;
+    float *rnorm;
+} tq_kcache;
+
+/* Packed value cache planes (device, caller-owned), per vector:
+   codes d*bits/8 B, params d/g pairs of fp16 bit patterns (scale, zero). */
+typedef struct {
+    uint8_t *codes;
+    uint16_t *params;
+} tq_vcache;
+
+/* ------------------------------------------------------------------ setup */
+
+/* Lloyd-Max codebook for one coordinate of a uniformly random unit vector in
+   R^d, whose density is proportional to (1 - x^2)^((d-3)/2) on [-1, 1]
+   ("turboquant-pytorch": build the optimal codebook with the Lloyd-Max
+   quantizer for vector dimension d; discosf article step 2).  2^bits
+   centroids, 2^bits - 1 boundaries (midpoints).  d in [3, 4096], bits in
+   [1, 8].  Host work of a few ms; the tables are copied to the current device.
+   *out receives a new handle; free it with tq_codebook_free. */
+tq_status tq_build_codebook(int d, int bits, tq_codebook **out);
+void tq_codebook_free(tq_codebook *cb);
+/* fp64 tables of a handle: centroids[2^bits], boundaries[2^bits - 1] (host). */
+tq_status tq_codebook_tables(const tq_codebook *cb, double *centroids, double *boundaries);
+/* The same computation without any device: fills the host arrays. */
+tq_status tq_codebook_host(int d, int bits, double *centroids, double *boundaries);
+
+/* Random rotation Pi and QJL projection S (m = d rows, iid N(0,1)) from a seed
+   ("turboquant-pytorch", random orthogonal rotations and QJL; discosf article
+   steps 1 and 3).  TQ_ROT_DENSE: Haar-random orthogonal matrix, the Q factor
+   of a Gaussian matrix with a positive-diagonal R.  TQ_ROT_HADAMARD:
+   H D / sqrt(d), H the Sylvester Walsh-Hadamard matrix and D random signs (the
+   O(d log d) rotation the tproger.ru article, section "Implementations",
+   names); d must be a power of two.  Random numbers: SplitMix64 counter
+   generator, stream 0 = Gaussian matrix for Pi, 1 = signs of D, 2 = S;
+   Box-Muller, row-major fill.  d in {64, 128, 256}.  Allocates device
+   copies on the current device. */
+tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation **out);
+void tq_rotation_free(tq_rotation *rot);
+/* Host-only: fp64 Pi [d*d] (y = Pi u, row-major) and S [d*d]; either may be
+   NULL.  d in [2, 4096] (power of two for Hadamard). */
+tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, double *s);
+
+/* Bytes of one plane for n_vec vectors.  Key planes: 0 codes, 1 signs,
+   2 knorm, 3 rnorm.  Value planes: 0 codes, 1 params.  0 on a bad argument. */
+size_t tq_key_plane_bytes(const tq_key_fmt *fmt, int64_t n_vec, int plane);
+size_t tq_val_plane_bytes(const tq_val_fmt *fmt, int64_t n_vec, int plane);
+
+/* -------------------------------------------------------------- hot path */
+
+/* Compress keys k[B, Hkv, T, d] (element strides sb, sh, st; channel stride
+   1; dtype f32/bf16/f16) into the planes of `out` (discosf article steps 1-3):
+   n = ||k||, y = Pi k / n, idx_j = #{boundaries < y_j}, r = y - c[idx],
+   sign_i = [(S r)_i >= 0], stored with fp32 n and fp32 ||r||.  A zero key
+   stores n = 0 and the codes of y = 0.  T = 0 is a no-op.  Strides must be
+   multiples of 16 bytes. */
+tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
+                           int64_t T, int64_t sb, int64_t sh, int64_t st, tq_kcache out,
+                           void *stream);
+
+/* Compress values v[B, Hkv, T, d] (discosf article step 4): per token and
+   group of g channels, fp16 scale = (max - min)/(2^bits - 1) and fp16 zero =
+   min (round to nearest even), code = clamp(round_half_even((v - zero) /
+   scale), 0, 2^bits - 1), or 0 when the scale is 0. */
+tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv,
+                             int64_t T, int64_t sb, int64_t sh, int64_t st, tq_vcache out,
+                             void *stream);
+
+/* Asymmetric scores of queries q[B, Hq, d] (contiguous) against the packed
+   keys ("turboquant-pytorch": attention scores computed directly on the
+   compressed keys):
+     score_t = ||k_t|| ( sum_j (Pi q)_j c[idx_tj]
+                         + sqrt(pi/2)/m ||r_t|| sum_i (S Pi q)_i (2 s_ti - 1) ).
+   scores: device fp32 [B, Hq, T].  ws: device workspace of at least
+   tq_scores_workspace_bytes() bytes. */
+size_t tq_scores_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq);
+tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq, int Hkv,
+                    int64_t T, tq_kcache kc, float *scores, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Decode attention over the packed cache without dequantising the keys
+   ("turboquant-pytorch", example requests: attention over the compressed
+   cache without full key dequantisation):
+     lambda_t = softmax_scale * score_t, p = softmax(lambda),
+     out = sum_t p_t (code_t * scale + zero).
+   softmax_scale 0 means 1/sqrt(d).  out: device fp32 [B, Hq, d].  T = 0
+   writes zeros.  n_splits 0 picks the split count; otherwise the token axis
+   is cut into n_splits ranges whose partial results are merged with a
+   log-sum-exp combine.  ws: device workspace of at least
+   tq_attend_workspace_bytes() bytes (same n_splits). */
+int tq_attend_splits(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T);
+size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
+                                 int n_splits);
+tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q,
+                           tq_dtype dtype, int B, int Hq, int Hkv, int64_t T, tq_kcache kc,
+                           tq_vcache vc, float softmax_scale, int n_splits, void *ws,
+                           size_t ws_bytes, float *out, void *stream);
+
+/* ------------------------------------------------------------- utilities */
+
+/* Thread-local message describing the last non-OK status of this thread. */
+const char *tq_last_error(void);
+
+/* Kernel timing for measurement.  While enabled, libtq records a pair of HIP
+   events around every launch of its kernels on the launch stream.
+   tq_profile_read synchronises on those events and returns, for kernels whose
+   name contains `name`, the summed duration in ms and the launch count, then
+   clears their records.  Off by default; enabling it adds two event records
+   per launch. */
+tq_status tq_profile_enable(int on);
+tq_status tq_profile_read(const char *name, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

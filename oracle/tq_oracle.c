@@ -581,19 +581,28 @@ void orc_scores(int d, int bits, int m, const double *pi, const double *s,
             sq[h * m + i] = acc;
         }
     }
-#pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < T; t++) {
-        const uint8_t *cr = codes + t * code_bytes, *sr = signs + t * sign_bytes;
-        for (int h = 0; h < nq; h++) {
-            double a = 0.0, b = 0.0;
-            for (int j = 0; j < d; j++) a += qrot[h * d + j] * centroids[orc_get_bits(cr, j, bits)];
-            for (int i = 0; i < m; i++) b += sq[h * m + i] * (orc_get_bits(sr, i, 1) ? 1.0 : -1.0);
+#pragma omp parallel
+    {
+        unsigned *idx = (unsigned *)malloc(sizeof(unsigned) * d);
+        double *sgn = (double *)malloc(sizeof(double) * m);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; t++) {
+            const uint8_t *cr = codes + t * code_bytes, *sr = signs + t * sign_bytes;
+            for (int j = 0; j < d; j++) idx[j] = orc_get_bits(cr, j, bits);
+            for (int i = 0; i < m; i++) sgn[i] = orc_get_bits(sr, i, 1) ? 1.0 : -1.0;
             double n = (double)knorm[t], rho = (double)rnorm[t];
-            double t1 = n * a, t2 = n * kappa * rho * b;
-            scores[(int64_t)h * T + t] = t1 + t2;
-            if (term_mse) term_mse[(int64_t)h * T + t] = t1;
-            if (term_qjl) term_qjl[(int64_t)h * T + t] = t2;
+            for (int h = 0; h < nq; h++) {
+                double a = 0.0, b = 0.0;
+                for (int j = 0; j < d; j++) a += qrot[h * d + j] * centroids[idx[j]];
+                for (int i = 0; i < m; i++) b += sq[h * m + i] * sgn[i];
+                double t1 = n * a, t2 = n * kappa * rho * b;
+                scores[(int64_t)h * T + t] = t1 + t2;
+                if (term_mse) term_mse[(int64_t)h * T + t] = t1;
+                if (term_qjl) term_qjl[(int64_t)h * T + t] = t2;
+            }
         }
+        free(idx);
+        free(sgn);
     }
     free(qrot);
     free(sq);
@@ -617,7 +626,7 @@ void orc_attend(int d, int bits, int m, const double *pi, const double *s,
     orc_scores(d, bits, m, pi, s, centroids, q, nq, codes, signs, knorm, rnorm, T, sc, NULL, NULL);
     int64_t vbytes = ((int64_t)d * vbits + 7) / 8;
     int ng = d / group;
-#pragma omp parallel for schedule(static)
+    /* softmax weights per query head (max subtracted) */
     for (int h = 0; h < nq; h++) {
         double *lam = sc + (int64_t)h * T;
         double mx = -INFINITY;
@@ -630,16 +639,17 @@ void orc_attend(int d, int bits, int m, const double *pi, const double *s,
             lam[t] = exp(lam[t] - mx);
             den += lam[t];
         }
-        double *o = out + (int64_t)h * d;
+        for (int64_t t = 0; t < T; t++) lam[t] /= den;
+    }
+    /* out[h][j] = sum_t p[h][t] v_hat[t][j]; channels split across threads, t in order */
+#pragma omp parallel for schedule(static)
+    for (int j = 0; j < d; j++) {
+        int g = j / group;
         for (int64_t t = 0; t < T; t++) {
-            double p = lam[t] / den;
-            const uint8_t *row = vcodes + t * vbytes;
-            for (int j = 0; j < d; j++) {
-                int g = j / group;
-                double sv = orc_f16_to_f64(vparams[(t * ng + g) * 2 + 0]);
-                double zv = orc_f16_to_f64(vparams[(t * ng + g) * 2 + 1]);
-                o[j] += p * (orc_get_bits(row, j, vbits) * sv + zv);
-            }
+            double sv = orc_f16_to_f64(vparams[(t * ng + g) * 2 + 0]);
+            double zv = orc_f16_to_f64(vparams[(t * ng + g) * 2 + 1]);
+            double vh = orc_get_bits(vcodes + t * vbytes, j, vbits) * sv + zv;
+            for (int h = 0; h < nq; h++) out[(int64_t)h * d + j] += sc[(int64_t)h * T + t] * vh;
         }
     }
     free(sc);

@@ -1,0 +1,147 @@
+"""libtq vs the fp64 oracle on the GPU, through the C ABI.
+
+Reduced-size cases keep each workload's format, dtype and statistics with a
+token count that spans several tiles and ends in a ragged tail; the oracle
+checks every output.  Full-size cases run in the launch configuration the
+benchmark times and check sampled outputs (compression) or whole sampled
+(sequence, KV head) units (decode, on a seeded random packed cache).
+"""
+import numpy as np
+import pytest
+
+import attention_decode_amd as tq
+from attention_decode_amd import workloads as W
+import oracle as O
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "tiny": dict(T=512),
+    "qwen25-3b-8k": dict(T=1000, layers=1),
+    "batched-8b-32k": dict(T=777, B=2),
+    "long-1m": dict(T=1500),
+    "asym-d256": dict(T=300, B=2),
+}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _reduced(name):
+    return W.WORKLOADS[name].with_T(**REDUCED[name])
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_compress_matches_oracle(torch_cuda, name):
+    torch = torch_cuda
+    w = _reduced(name)
+    layer = 3 if w.layers > 1 or name == "qwen25-3b-8k" else 0
+    print(f"[parity] compress {name} B={w.B} T={w.T} layer={layer}", flush=True)
+    fm = P.Formats(w, layer)
+    k, v = W.make_keys(w, layer), W.make_values(w, layer)
+    kc, vc = P.gpu_compress(fm, k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    stats = P.compare_keys(fm, kc, P.f64(k).reshape(-1, w.d))
+    vflips = P.compare_values(fm, vc, P.f64(v).reshape(-1, w.d))
+    print(f"[parity] {name}: {stats} value flips {vflips}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_decode_on_oracle_cache(torch_cuda, name):
+    torch = torch_cuda
+    w = _reduced(name)
+    print(f"[parity] decode {name} B={w.B} T={w.T}", flush=True)
+    fm = P.Formats(w, 0)
+    k, v, q = W.make_keys(w), W.make_values(w), W.make_queries(w)
+    ok = O.compress_keys(P.f64(k).reshape(-1, w.d), w.k_bits, fm.orot)
+    ov = O.compress_values(P.f64(v).reshape(-1, w.d), w.v_bits, w.group)
+    shape = (w.B, w.Hkv, w.T)
+    kc, vc = P.to_device_cache(ok, ov, shape, "cuda")
+    qd = q.cuda()
+    sc = tq.tq_scores(fm.kf, qd, kc, w.Hkv, w.T)
+    out = tq.tq_attend_decode(fm.kf, fm.vf, qd, kc, vc, w.Hkv, w.T)
+    torch.cuda.synchronize()
+    qn = P.f64(q)
+    osc, oat = P.oracle_units(fm, qn, ok, ov, shape)
+    r = P.check_scores(sc.double().cpu().numpy(), osc, qn, ok.knorm.reshape(shape), w.Hkv)
+    e = P.check_attention(out.double().cpu().numpy(), oat)
+    print(f"[parity] {name}: score err {r:.3g} x bound, attention max abs err {e:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+def test_split_count_invariance(torch_cuda, splits):
+    torch = torch_cuda
+    w = _reduced("long-1m")
+    fm = P.Formats(w, 0)
+    k, v, q = W.make_keys(w, device="cuda"), W.make_values(w, device="cuda"), W.make_queries(w, device="cuda")
+    kc, vc = P.gpu_compress(fm, k, v)
+    ref = tq.tq_attend_decode(fm.kf, fm.vf, q, kc, vc, w.Hkv, w.T, n_splits=1)
+    out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc, vc, w.Hkv, w.T, n_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, ref, atol=1e-5, rtol=1e-5), (out - ref).abs().max()
+
+
+def test_edge_cases(torch_cuda):
+    torch = torch_cuda
+    w = W.WORKLOADS["tiny"].with_T(3)
+    fm = P.Formats(w, 0)
+    # zero key, a key with one nonzero channel, a constant value row
+    k = torch.zeros((1, 1, 3, 128), dtype=torch.float32)
+    k[0, 0, 1, 5] = 2.0
+    k[0, 0, 2] = torch.randn(128)
+    v = torch.randn((1, 1, 3, 128), dtype=torch.float32)
+    v[0, 0, 0] = 0.75
+    kc, vc = P.gpu_compress(fm, k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    P.compare_keys(fm, kc, P.f64(k).reshape(-1, 128))
+    P.compare_values(fm, vc, P.f64(v).reshape(-1, 128))
+    # T = 1: attention returns the single dequantised value
+    q = torch.randn((1, 4, 128)).cuda()
+    kc1 = tq.KeyCache(kc.codes[:, :, 2:3].contiguous(), kc.signs[:, :, 2:3].contiguous(),
+                      kc.knorm[:, :, 2:3].contiguous(), kc.rnorm[:, :, 2:3].contiguous())
+    vc1 = tq.ValueCache(vc.codes[:, :, 0:1].contiguous(), vc.params[:, :, 0:1].contiguous())
+    out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc1, vc1, 1, 1)
+    torch.cuda.synchronize()
+    assert torch.all(out.cpu() == 0.75)
+    # T = 0: zeros, and compression is a no-op
+    out0 = torch.full((1, 4, 128), 7.0, device="cuda")
+    tq.tq_attend_decode(fm.kf, fm.vf, q, kc1, vc1, 1, 0, out=out0)
+    torch.cuda.synchronize()
+    assert torch.all(out0 == 0)
+
+
+def test_strided_layouts_agree(torch_cuda):
+    torch = torch_cuda
+    w = W.WORKLOADS["batched-8b-32k"].with_T(300, B=2)
+    fm = P.Formats(w, 0)
+    k = W.make_keys(w, device="cuda")
+    v = W.make_values(w, device="cuda")
+    kc, vc = P.gpu_compress(fm, k, v)
+    # the same tensors stored token-major ([B, T, H, d]) and viewed as [B, H, T, d]
+    k2 = k.transpose(1, 2).contiguous().transpose(1, 2)
+    v2 = v.transpose(1, 2).contiguous().transpose(1, 2)
+    kc2, vc2 = P.gpu_compress(fm, k2, v2)
+    torch.cuda.synchronize()
+    for a, b in [(kc.codes, kc2.codes), (kc.signs, kc2.signs), (kc.knorm, kc2.knorm),
+                 (kc.rnorm, kc2.rnorm), (vc.codes, vc2.codes), (vc.params, vc2.params)]:
+        assert torch.equal(a, b)
+
+
+def test_deterministic(torch_cuda):
+    torch = torch_cuda
+    w = _reduced("asym-d256")
+    fm = P.Formats(w, 0)
+    k, v, q = W.make_keys(w, device="cuda"), W.make_values(w, device="cuda"), W.make_queries(w, device="cuda")
+    a = P.gpu_compress(fm, k, v)
+    b = P.gpu_compress(fm, k, v)
+    o1 = tq.tq_attend_decode(fm.kf, fm.vf, q, a[0], a[1], w.Hkv, w.T)
+    o2 = tq.tq_attend_decode(fm.kf, fm.vf, q, a[0], a[1], w.Hkv, w.T)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].codes, b[0].codes) and torch.equal(a[0].signs, b[0].signs)
+    assert torch.equal(a[1].codes, b[1].codes) and torch.equal(a[1].params, b[1].params)
+    assert torch.equal(o1, o2)
