@@ -1,0 +1,226 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic input already in
+HBM: compress every layer's keys and values into the packed planes, then run
+one decode-attention step (query prep, split-K attention, combine) per layer
+straight from the packed cache.
+
+Prints ONE JSON line.  `value` is decode-attention throughput in GB/s of
+packed KV read (packed K + V bytes of all layers / decode time of the step);
+keys and values compressed per second are reported beside it.  `roofline`
+covers the split-K decode-attention kernel: algorithmic bytes per launch /
+its mean launch duration (HIP events recorded by libtq around each launch on
+the launch stream) against the 8 TB/s HBM peak.  `cpu_baseline` times the
+fp64 oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen25-3b-8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Layer:
+    """Inputs, formats and packed planes of one layer."""
+
+    def __init__(self, w, layer, tq, W, torch):
+        self.cb = tq.tq_build_codebook(w.d, w.k_bits)
+        self.rot = tq.tq_make_rotation(w.rotation_seed(layer), w.d, w.rot)
+        self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot)
+        self.vf = tq.ValueFormat(w.d, w.v_bits, w.group)
+        self.k = W.make_keys(w, layer, device="cuda")
+        self.v = W.make_values(w, layer, device="cuda")
+        self.q = W.make_queries(w, layer, device="cuda")
+        self.kc = tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T)
+        self.vc = tq.alloc_value_cache(self.vf, w.B, w.Hkv, w.T)
+        self.splits = tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, w.T)
+        n = tq.tq_attend_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, w.T, self.splits)
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle (as is) on a bounded sample of the workload: one (sequence,
+    KV head) unit's keys compressed, then decode attention of its G query heads
+    over the oracle-packed unit, repeated over units until the time budget."""
+    import numpy as np
+    import oracle as O
+    from attention_decode_amd import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    small = w.with_T(min(w.T, 8192), B=1, layers=1)
+    rot = O.rotation(w.rotation_seed(0), w.d, w.rot)
+    O.codebook(w.d, w.k_bits)
+    k = W.make_keys(small, 0).double().numpy()[0]
+    v = W.make_values(small, 0).double().numpy()[0]
+    q = W.make_queries(small, 0).double().numpy()[0]
+    key_time = dec_time = 0.0
+    keys = units = 0
+    h = 0
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < seconds and h < small.Hkv:
+        # compress a bounded slice of keys, then decode over the unit
+        n_keys = small.T
+        t0 = time.perf_counter()
+        ok = O.compress_keys(k[h, :n_keys], w.k_bits, rot)
+        key_time += time.perf_counter() - t0
+        keys += n_keys
+        ov = O.compress_values(v[h, :n_keys], w.v_bits, w.group)
+        t0 = time.perf_counter()
+        O.attend(q[h * w.G:(h + 1) * w.G], ok, w.k_bits, rot, ov, w.v_bits, w.group)
+        dec_time += time.perf_counter() - t0
+        units += n_keys
+        h += 1
+    packed = units * (w.key_bytes() + w.value_bytes())
+    return {
+        "value": packed / dec_time / 1e9, "unit": "GB/s", "cores": min(threads, cores), "kind": "oracle",
+        "sample": f"{h} (sequence, KV head) units x {min(w.T, 8192)} tokens of {w.name}: fp64 oracle "
+                  f"key compression then decode attention of {w.G} query heads",
+        "keys_compressed_per_s": keys / key_time,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence / KV head with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import attention_decode_amd as tq
+    from attention_decode_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.WORKLOADS[args.workload]
+    print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
+          file=sys.stderr, flush=True)
+    layers = [Layer(w, l, tq, W, torch) for l in range(w.layers)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        for L in layers:
+            tq.tq_compress_keys(L.kf, L.k, L.kc)
+        if ev:
+            ev[1].record(stream)
+        for L in layers:
+            tq.tq_compress_values(L.vf, L.v, L.vc)
+        if ev:
+            ev[2].record(stream)
+        for L in layers:
+            tq.tq_attend_decode(L.kf, L.vf, L.q, L.kc, L.vc, w.Hkv, w.T, out=L.out, ws=L.ws,
+                                n_splits=L.splits)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    tq.tq_profile_enable(True)
+    tq.tq_profile_read("")            # drop anything recorded before the timed region
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tq.tq_profile_enable(False)
+    attn_ms, attn_n = tq.tq_profile_read("tq_attend_splitk")
+    kq_ms, kq_n = tq.tq_profile_read("tq_compress_keys")
+    vq_ms, vq_n = tq.tq_profile_read("tq_compress_values")
+    tq.tq_profile_read("")
+
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    v_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    d_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    packed = w.packed_bytes()
+    vectors = w.vectors()
+    value = packed / (d_ms * 1e-3) / 1e9
+    # split-K attention kernel: algorithmic bytes per launch = packed K + V of one
+    # layer + q-prep rows read + split partials written
+    per_layer_keys = w.B * w.Hkv * w.T
+    splits = layers[0].splits
+    attn_bytes = (per_layer_keys * (w.key_bytes() + w.value_bytes())
+                  + w.B * w.Hq * 2 * w.d * 4 + w.B * w.Hq * splits * (w.d + 2) * 4)
+    attn_avg_s = attn_ms * 1e-3 / max(attn_n, 1)
+    achieved = attn_bytes / attn_avg_s / 1e9
+    result = {
+        "metric": "decode attention GB/s of packed KV read (% of HBM peak); keys compressed/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and statistics of the workload, no model weights)",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "kv_heads": w.Hkv,
+                   "q_heads": w.Hq, "tokens": w.T, "head_dim": w.d, "input_dtype": w.dtype,
+                   "k_bits": f"{w.k_bits}+1 (Lloyd-Max + QJL sign)", "rotation": w.rot,
+                   "v_bits": w.v_bits, "v_group": w.group, "attn_splits": splits},
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "decode_ms_per_step": round(d_ms, 4),
+        "compress_keys_ms_per_step": round(k_ms, 4),
+        "compress_values_ms_per_step": round(v_ms, 4),
+        "keys_compressed_per_s": vectors / (k_ms * 1e-3),
+        "values_compressed_per_s": vectors / (v_ms * 1e-3),
+        "packed_bytes_per_step": packed,
+        "roofline": {"bound": "hbm", "kernel": "tq_attend_splitk", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": attn_bytes,
+                     "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n},
+        "kernel_avg_us": {"tq_compress_keys": round(kq_ms * 1e3 / max(kq_n, 1), 3),
+                          "tq_compress_values": round(vq_ms * 1e3 / max(vq_n, 1), 3),
+                          "tq_attend_splitk": round(attn_avg_s * 1e6, 3)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

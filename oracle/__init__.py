@@ -78,6 +78,8 @@ def _l():
     lib.orc_unpack.argtypes = [_u8p, i64, i32, i32, _u32p]
     lib.orc_compress_keys.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _f64p, _f64p, i64,
                                       _u8p, _u8p, _f32p, _f32p, vp, vp, vp]
+    lib.orc_key_residual_signs.argtypes = [i32, i32, _f64p, _f64p, _f64p, _u32p, _u8p, _f64p,
+                                           ctypes.POINTER(ctypes.c_double)]
     lib.orc_compress_values.argtypes = [i32, i32, i32, _f64p, i64, _u8p, _u16p, vp]
     lib.orc_dequant_values.argtypes = [i32, i32, i32, _u8p, _u16p, i64, _f64p]
     lib.orc_scores.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _f64p, i32,
@@ -233,6 +235,19 @@ def compress_keys(k: np.ndarray, bits: int, rot: Rotation, keep_aux: bool = Fals
     _l().orc_compress_keys(d, bits, m, np.ascontiguousarray(rot.pi), np.ascontiguousarray(rot.s),
                            c, t, k, n, codes, signs, kn, rn, _ptr(y), _ptr(z), _ptr(rho))
     return KeyCache(codes, signs, kn, rn, y, z, rho)
+
+
+def key_residual_signs(y: np.ndarray, idx: np.ndarray, bits: int, rot: Rotation):
+    """Signs (packed), z and ||r|| of one key for rotated vector y and codes idx."""
+    d = y.shape[0]
+    m = rot.s.shape[0]
+    c, _ = codebook(d, bits)
+    signs = np.zeros((m + 7) // 8, np.uint8)
+    z = np.zeros(m)
+    rho = ctypes.c_double()
+    _l().orc_key_residual_signs(d, m, np.ascontiguousarray(rot.s), c, np.ascontiguousarray(y, np.float64),
+                                np.ascontiguousarray(idx, np.uint32), signs, z, ctypes.byref(rho))
+    return signs, z, rho.value
 
 
 # -------------------------------------------------------------------- values

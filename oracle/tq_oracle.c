@@ -492,6 +492,31 @@ void orc_compress_keys(int d, int bits, int m, const double *pi, const double *s
     }
 }
 
+/* Residual, QJL signs and ||r|| of one key for a given rotated vector y and a
+   given code vector idx (the second half of the key encoder).  Used to derive
+   the alternative encoding of a key when a rotated coordinate sits on a
+   decision boundary and either adjacent cell is a valid code. */
+void orc_key_residual_signs(int d, int m, const double *s, const double *centroids,
+                            const double *y, const uint32_t *idx, uint8_t *signs,
+                            double *z_out, double *rho_out)
+{
+    double *r = (double *)malloc(sizeof(double) * d);
+    double rho2 = 0.0;
+    for (int j = 0; j < d; j++) {
+        r[j] = y[j] - centroids[idx[j]];
+        rho2 += r[j] * r[j];
+    }
+    memset(signs, 0, (size_t)((m + 7) / 8));
+    for (int i = 0; i < m; i++) {
+        double z = 0.0;
+        for (int j = 0; j < d; j++) z += s[(size_t)i * d + j] * r[j];
+        if (z >= 0.0) orc_put_bits(signs, i, 1, 1u);
+        if (z_out) z_out[i] = z;
+    }
+    *rho_out = sqrt(rho2);
+    free(r);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Value compression: asymmetric min-max quantization per group of `group`   */
 /* consecutive channels of one token, fp16 scale and zero, codes packed      */

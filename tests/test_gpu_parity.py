@@ -102,9 +102,9 @@ def test_edge_cases(torch_cuda):
     P.compare_values(fm, vc, P.f64(v).reshape(-1, 128))
     # T = 1: attention returns the single dequantised value
     q = torch.randn((1, 4, 128)).cuda()
-    kc1 = tq.KeyCache(kc.codes[:, :, 2:3].contiguous(), kc.signs[:, :, 2:3].contiguous(),
-                      kc.knorm[:, :, 2:3].contiguous(), kc.rnorm[:, :, 2:3].contiguous())
-    vc1 = tq.ValueCache(vc.codes[:, :, 0:1].contiguous(), vc.params[:, :, 0:1].contiguous())
+    kc1 = tq.KeyCache(kc.codes[:, :, 2:3].clone(), kc.signs[:, :, 2:3].clone(),
+                      kc.knorm[:, :, 2:3].clone(), kc.rnorm[:, :, 2:3].clone())
+    vc1 = tq.ValueCache(vc.codes[:, :, 0:1].clone(), vc.params[:, :, 0:1].clone())
     out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc1, vc1, 1, 1)
     torch.cuda.synchronize()
     assert torch.all(out.cpu() == 0.75)

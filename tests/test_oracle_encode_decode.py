@@ -77,6 +77,25 @@ def test_key_encode_restated(d, bits, kind):
     assert np.array_equal(kc.rnorm, np.linalg.norm(r, axis=1).astype(np.float32))
 
 
+def test_residual_signs_routine_reproduces_encoder():
+    d, bits = 128, 3
+    rot = O.rotation(77, d)
+    kc = O.compress_keys(_keys(20, d, 5), bits, rot, keep_aux=True)
+    idx = _unpack_le(kc.codes, d, bits)
+    c, _ = O.codebook(d, bits)
+    for r in range(20):
+        sg, z, rho = O.key_residual_signs(kc.y[r], idx[r], bits, rot)
+        assert np.array_equal(sg, kc.signs[r]) and np.array_equal(z, kc.z[r]) and rho == kc.rho[r]
+    # an alternative code vector: restated residual, projection and signs
+    alt = idx[0].copy()
+    alt[3] = (alt[3] + 1) % (1 << bits)
+    sg, z, rho = O.key_residual_signs(kc.y[0], alt, bits, rot)
+    res = kc.y[0] - c[alt]
+    assert abs(rho - np.linalg.norm(res)) < 1e-14
+    assert np.abs(z - rot.s @ res).max() < 1e-12
+    assert np.array_equal(_unpack_le(sg[None], d, 1)[0], (z >= 0).astype(np.uint32))
+
+
 def test_zero_key():
     d, bits = 128, 2
     rot = O.rotation(3, d)
