@@ -37,7 +37,26 @@ def parse():
     ap.add_argument("--workload", default="qwen25-3b-8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (to calibrate HBM byte counters)")
     return ap.parse_args()
+
+
+def calib_copy(torch):
+    """A plain copy kernel of known size: reads and writes 1 GiB per launch."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                      "launches": 15, "copy_GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 class Layer:
@@ -124,6 +143,9 @@ def main():
     from attention_decode_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy:
+        calib_copy(torch)
+        return
     w = W.WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
           file=sys.stderr, flush=True)
