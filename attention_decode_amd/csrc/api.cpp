@@ -355,18 +355,55 @@ tq_status check_vcache(const tq_vcache &vc, const char *who)
         if (st_ != TQ_OK) return st_;        \
     } while (0)
 
-struct AttendLayout {
-    size_t qprep, ml, acc, total;
+// Decode path and split count for a shape: the matrix-core path when the key
+// format allows it, else the general kernel.
+struct DecodePlan {
+    bool mfma = false;
+    int gc = 0, nqc = 0, mt = 0, units = 0, splits = 0, steps = 0;
 };
 
-AttendLayout attend_layout(int d, int m, int B, int Hq, int splits)
+DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits)
+{
+    DecodePlan p;
+    const int G = Hq / Hkv;
+    p.mfma = tq::mfma_decode_supported(fmt->d, fmt->mse_bits, G, 2, 32);
+    p.gc = p.mfma ? tq::mfma_query_chunk(G) : tq::query_chunk(G);
+    p.nqc = G / p.gc;
+    p.mt = (p.gc + 3) / 4;
+    p.units = B * Hkv * p.nqc;
+    p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits) : 0;
+    const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;
+    const int64_t tiles = (T + tile - 1) / tile;
+    int64_t want = (1024 + p.units - 1) / p.units;      // about four workgroups per CU
+    if (want > tiles) want = tiles;
+    if (want > 1024) want = 1024;
+    p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);
+    return p;
+}
+
+struct AttendLayout {
+    size_t qprep, aops, qscal, counters, ml, acc, total;
+};
+
+AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePlan &p)
 {
     AttendLayout L;
     const size_t rows = static_cast<size_t>(B) * Hq;
-    L.qprep = 0;
-    L.ml = align256(rows * (d + m) * sizeof(float));
-    L.acc = L.ml + align256(rows * splits * 2 * sizeof(float));
-    L.total = L.acc + align256(rows * splits * d * sizeof(float));
+    const int d = fmt->d, m = fmt->qjl_m;
+    size_t off = 0;
+    L.qprep = off;
+    off += align256(rows * (d + m) * sizeof(float));
+    L.aops = off;
+    off += align256(static_cast<size_t>(p.units) * p.mt * p.steps * 64 * 16);
+    L.qscal = off;
+    off += align256(rows * 4 * sizeof(float));
+    L.counters = off;
+    off += align256(static_cast<size_t>(p.units) * sizeof(int));
+    L.ml = off;
+    off += align256(rows * p.splits * 2 * sizeof(float));
+    L.acc = off;
+    off += align256(rows * p.splits * d * sizeof(float));
+    L.total = off;
     return L;
 }
 
@@ -487,21 +524,14 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
 int tq_attend_splits(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T)
 {
     if (!fmt || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < 0) return 0;
-    const int G = Hq / Hkv, gc = tq::query_chunk(G);
-    const int64_t units = static_cast<int64_t>(B) * Hkv * (G / gc);
-    const int64_t tiles = (T + tq::kDecodeTile - 1) / tq::kDecodeTile;
-    int64_t want = (1024 + units - 1) / units;          // about four workgroups per CU
-    if (want > tiles) want = tiles;
-    if (want > 1024) want = 1024;
-    return want < 1 ? 1 : static_cast<int>(want);
+    return decode_plan(fmt, B, Hq, Hkv, T, 0).splits;
 }
 
 size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits)
 {
-    if (!fmt || B < 1 || Hq < 1) return 0;
-    const int splits = n_splits > 0 ? n_splits : tq_attend_splits(fmt, B, Hq, Hkv, T);
-    if (splits < 1) return 0;
-    return attend_layout(fmt->d, fmt->qjl_m, B, Hq, splits).total;
+    if (!fmt || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < 0) return 0;
+    const DecodePlan p = decode_plan(fmt, B, Hq, Hkv, T, n_splits);
+    return attend_layout(fmt, B, Hq, p).total;
 }
 
 tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
@@ -536,8 +566,8 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     TQ_TRY(check_vcache(vc, who));
     if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
     if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
-    const int splits = n_splits > 0 ? n_splits : tq_attend_splits(kfmt, B, Hq, Hkv, T);
-    const AttendLayout L = attend_layout(kfmt->d, kfmt->qjl_m, B, Hq, splits);
+    const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits);
+    const AttendLayout L = attend_layout(kfmt, B, Hq, plan);
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;
     a.sT = kfmt->rot->d_sT;
@@ -547,13 +577,25 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     a.group = vfmt->group;
     a.vc = vc;
     a.scale = softmax_scale > 0.0f ? softmax_scale : static_cast<float>(1.0 / std::sqrt(double(kfmt->d)));
-    a.splits = splits;
+    a.splits = plan.splits;
     char *base = static_cast<char *>(ws);
     a.qprep = reinterpret_cast<float *>(base + L.qprep);
     a.part_ml = reinterpret_cast<float *>(base + L.ml);
     a.part_acc = reinterpret_cast<float *>(base + L.acc);
-    hipError_t e = tq::launch_qprep(a, s);
-    if (e == hipSuccess) e = tq::launch_attend(a, s);
+    a.mf.gc = plan.gc;
+    a.mf.nqc = plan.nqc;
+    a.mf.mt = plan.mt;
+    a.mf.units = plan.units;
+    a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
+    a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
+    a.mf.counters = reinterpret_cast<int *>(base + L.counters);
+    hipError_t e;
+    if (plan.mfma) {
+        e = tq::launch_decode_mfma(a, s);
+    } else {
+        e = tq::launch_qprep(a, s);
+        if (e == hipSuccess) e = tq::launch_attend(a, s);
+    }
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
 

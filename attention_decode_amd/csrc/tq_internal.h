@@ -65,6 +65,17 @@ struct ValueLaunch {
 };
 hipError_t launch_compress_values(const ValueLaunch &a, hipStream_t stream);
 
+// extra state of the matrix-core decode path
+struct MfmaArgs {
+    int gc = 0;                 // query heads per unit (<= 8)
+    int nqc = 0;                // query chunks per KV head
+    int mt = 0;                 // 4-query row tiles of the score product
+    int units = 0;              // B * Hkv * nqc
+    uint32_t *aops = nullptr;   // [units][mt][steps][64 lanes][4 dwords] score digit operands
+    float *qscal = nullptr;     // [B, Hq, 4] fixed-point scales, constant terms
+    int *counters = nullptr;    // [units] split-completion counters
+};
+
 struct DecodeLaunch {
     const void *q;              // [B, Hq, d]
     tq_dtype dtype;
@@ -84,6 +95,7 @@ struct DecodeLaunch {
     float *part_acc;            // [B, Hq, splits, d]
     float *scores;              // tq_scores output [B, Hq, T]
     float *out;                 // [B, Hq, d]
+    MfmaArgs mf;
 };
 hipError_t launch_qprep(const DecodeLaunch &a, hipStream_t stream);
 hipError_t launch_scores(const DecodeLaunch &a, hipStream_t stream);
@@ -92,6 +104,13 @@ hipError_t launch_attend(const DecodeLaunch &a, hipStream_t stream);
 // query-chunk size the decode kernels use for a GQA group of G heads
 int query_chunk(int G);
 constexpr int kDecodeTile = 256;   // keys per decode tile
+
+// matrix-core decode path (k_attend_mfma.hip): keys with 1-2 bits, d 128/256
+constexpr int kMfmaTile = 64;      // keys per tile
+bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
+int mfma_query_chunk(int G);
+int mfma_score_steps(int d, int bits);
+hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream);
 
 // ---- profiling hooks (api.cpp)
 void prof_begin(const char *name, hipStream_t stream, void **token);
