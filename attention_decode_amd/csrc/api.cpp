@@ -215,7 +215,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
     std::vector<double> pi(dd), s(dd);
     tq_status st = tq_rotation_host(seed, d, kind, pi.data(), s.data());
     if (st != TQ_OK) return st;
-    std::vector<float> host(4 * dd + d);
+    std::vector<float> host(5 * dd + d);
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
             host[i * d + j] = static_cast<float>(pi[i * d + j]);            // Pi
@@ -223,8 +223,15 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
             host[2 * dd + i * d + j] = static_cast<float>(s[i * d + j]);    // S
             host[3 * dd + j * d + i] = static_cast<float>(s[i * d + j]);    // S^T
         }
-    if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 4 * dd);
-    else for (int j = 0; j < d; ++j) host[4 * dd + j] = 1.0f;
+    // (S Pi)^T in fp64, rounded once: Sq = S (Pi q) = (S Pi) q
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += s[static_cast<size_t>(i) * d + k] * pi[static_cast<size_t>(k) * d + j];
+            host[4 * dd + static_cast<size_t>(j) * d + i] = static_cast<float>(acc);
+        }
+    if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 5 * dd);
+    else for (int j = 0; j < d; ++j) host[5 * dd + j] = 1.0f;
     auto *rot = new (std::nothrow) tq_rotation;
     if (!rot) return fail(TQ_ENOMEM, "tq_make_rotation: host allocation failed");
     rot->seed = seed;
@@ -244,7 +251,8 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
     rot->d_piT = base + dd;
     rot->d_s = base + 2 * dd;
     rot->d_sT = base + 3 * dd;
-    rot->d_dsign = base + 4 * dd;
+    rot->d_spiT = base + 4 * dd;
+    rot->d_dsign = base + 5 * dd;
     *out = rot;
     return TQ_OK;
 }
@@ -376,7 +384,8 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     const int64_t tiles = (T + tile - 1) / tile;
     int64_t want = (1024 + p.units - 1) / p.units;      // about four workgroups per CU
     if (want > tiles) want = tiles;
-    if (want > 1024) want = 1024;
+    // the matrix-core kernel merges its splits in one wave per query
+    if (want > (p.mfma ? tq::kMfmaMaxSplits : 1024)) want = p.mfma ? tq::kMfmaMaxSplits : 1024;
     p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);
     return p;
 }
@@ -567,10 +576,14 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
     if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
     const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits);
+    if (plan.mfma && plan.splits > tq::kMfmaMaxSplits)
+        return fail(TQ_EUNSUPPORTED, "%s: n_splits=%d above %d for this key format", who, plan.splits,
+                    tq::kMfmaMaxSplits);
     const AttendLayout L = attend_layout(kfmt, B, Hq, plan);
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;
     a.sT = kfmt->rot->d_sT;
+    a.spiT = kfmt->rot->d_spiT;
     a.centroids = kfmt->cb->d_centroids;
     a.kc = kc;
     a.vbits = vfmt->bits;

@@ -89,130 +89,130 @@ __device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(p->
 __device__ __forceinline__ float load1(const f16_t *p) { return f16_bits_to_f32(p->bits); }
 
 // ---------------------------------------------------------------- q-prep
-// One workgroup per unit: q_rot = Pi q and Sq = S q_rot for the unit's query
-// heads, then the fixed-point digit operands of both score products, the
-// per-query scalars, and a zeroed split counter.
+// One workgroup per query row (b, hq): q_rot = Pi q and Sq = (S Pi) q as two
+// coalesced float4 matrix-vector products with every load of a pass in
+// flight, then this query's fixed-point digit operands (its four rows of the
+// score products), its scalars, and (first query of a unit) the zeroed split
+// counter and the zero rows of absent queries.
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void k_qprep_mfma(DecodeLaunch a)
 {
-    __shared__ float qs[kMaxG][256];
-    __shared__ float qr[kMaxG][256];
-    __shared__ float sq[kMaxG][256];
-    __shared__ int s_fc[kMaxG], s_fs[kMaxG];
+    __shared__ float qs[256];
+    __shared__ float part[2][8][256];
+    __shared__ float qr[256], sq[256];
+    __shared__ float red[4];
     __shared__ float s_acoef[2];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int D = a.d, M = a.m, GC = a.mf.gc, nqc = a.mf.nqc, MT = a.mf.mt;
-    const int unit = blockIdx.x;
-    const int qc = unit % nqc;
-    const int64_t bh = unit / nqc;
-    const int b = static_cast<int>(bh / a.Hkv), hkv = static_cast<int>(bh % a.Hkv);
-    const int hq0 = hkv * (a.Hq / a.Hkv) + qc * GC;
+    const int D = a.d, M = a.m;
+    const int64_t row = blockIdx.x;                 // b * Hq + hq
+    const int b = static_cast<int>(row / a.Hq), hq = static_cast<int>(row % a.Hq);
+    const int G = a.Hq / a.Hkv, hkv = hq / G, gi = hq % G;
+    const int GC = a.mf.gc, qc = gi / GC, g = gi % GC;
+    const int MT = a.mf.mt;
+    const int unit = (b * a.Hkv + hkv) * a.mf.nqc + qc;
 
-    for (int i = tid; i < GC * D; i += kThreads) {
-        const int g = i / D, j = i % D;
-        qs[g][j] = load1(static_cast<const TIn *>(a.q) + (static_cast<int64_t>(b) * a.Hq + hq0 + g) * D + j);
-    }
+    for (int i = tid; i < D; i += kThreads) qs[i] = load1(static_cast<const TIn *>(a.q) + row * D + i);
     if (tid == 0) {
         // bit-affine form of the codebook (exact for symmetric codebooks)
         s_acoef[0] = a.centroids[1] - a.centroids[0];
         s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
     }
     __syncthreads();
-    if (tid < D) {
-        float acc[kMaxG];
-#pragma unroll
-        for (int g = 0; g < kMaxG; ++g) acc[g] = 0.0f;
-        for (int j = 0; j < D; ++j) {
-            const float p = a.piT[j * D + tid];
-#pragma unroll
-            for (int g = 0; g < kMaxG; ++g)
-                if (g < GC) acc[g] = fmaf(p, qs[g][j], acc[g]);
+    {
+        const int NQ = D / 4, RG = kThreads / NQ;
+        const int c4 = tid % NQ, rg = tid / NQ;
+        const float4 *p1 = reinterpret_cast<const float4 *>(a.piT);
+        const float4 *p2 = reinterpret_cast<const float4 *>(a.spiT);
+        float4 y1 = make_float4(0.f, 0.f, 0.f, 0.f), y2 = y1;
+#pragma unroll 16
+        for (int jj = rg; jj < D; jj += RG) {
+            const float4 u = p1[jj * NQ + c4], v = p2[jj * NQ + c4];
+            const float qj = qs[jj];
+            y1.x = fmaf(u.x, qj, y1.x); y1.y = fmaf(u.y, qj, y1.y);
+            y1.z = fmaf(u.z, qj, y1.z); y1.w = fmaf(u.w, qj, y1.w);
+            y2.x = fmaf(v.x, qj, y2.x); y2.y = fmaf(v.y, qj, y2.y);
+            y2.z = fmaf(v.z, qj, y2.z); y2.w = fmaf(v.w, qj, y2.w);
         }
-#pragma unroll
-        for (int g = 0; g < kMaxG; ++g)
-            if (g < GC) qr[g][tid] = acc[g];
+        *reinterpret_cast<float4 *>(&part[0][rg][4 * c4]) = y1;
+        *reinterpret_cast<float4 *>(&part[1][rg][4 * c4]) = y2;
+        __syncthreads();
+        if (tid < D) {
+            float s1 = 0.0f, s2 = 0.0f;
+            for (int r = 0; r < RG; ++r) {
+                s1 += part[0][r][tid];
+                s2 += part[1][r][tid];
+            }
+            qr[tid] = s1;
+            sq[tid] = s2;
+        }
     }
     __syncthreads();
-    if (tid < M) {
-        float acc[kMaxG];
-#pragma unroll
-        for (int g = 0; g < kMaxG; ++g) acc[g] = 0.0f;
-        for (int j = 0; j < D; ++j) {
-            const float p = a.sT[j * M + tid];
-#pragma unroll
-            for (int g = 0; g < kMaxG; ++g)
-                if (g < GC) acc[g] = fmaf(p, qr[g][j], acc[g]);
+    if (wave < 2) {
+        const float *v = wave == 0 ? qr : sq;
+        const int n = wave == 0 ? D : M;
+        float mx = 0.0f, sum = 0.0f;
+        for (int j = lane; j < n; j += 64) {
+            mx = fmaxf(mx, fabsf(v[j]));
+            sum += v[j];
         }
-#pragma unroll
-        for (int g = 0; g < kMaxG; ++g)
-            if (g < GC) sq[g][tid] = acc[g];
-    }
-    __syncthreads();
-    // per-query scalars: fixed-point exponents, constant code term, sum of Sq
-    for (int g = wave; g < GC; g += kThreads / 64) {
-        float mq = 0.0f, sum_q = 0.0f, ms = 0.0f, sum_s = 0.0f;
-        for (int j = lane; j < D; j += 64) {
-            mq = fmaxf(mq, fabsf(qr[g][j]));
-            sum_q += qr[g][j];
-        }
-        for (int i = lane; i < M; i += 64) {
-            ms = fmaxf(ms, fabsf(sq[g][i]));
-            sum_s += sq[g][i];
-        }
-        mq = wave_max(mq);
-        ms = wave_max(ms);
-        sum_q = wave_sum(sum_q);
-        sum_s = wave_sum(sum_s);
+        mx = wave_max(mx);
+        sum = wave_sum(sum);
         if (lane == 0) {
-            const float mw = mq * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1]));
-            int ec = 0, es = 0;
-            frexpf(mw, &ec);      // mw < 2^ec
-            frexpf(ms, &es);
-            const int fc = (mw > 0.0f) ? 26 - ec : 0;
-            const int fs = (ms > 0.0f) ? 26 - es : 0;
-            s_fc[g] = fc;
-            s_fs[g] = fs;
-            float *sc = a.mf.qscal + (static_cast<int64_t>(b) * a.Hq + hq0 + g) * 4;
-            sc[0] = ldexpf(1.0f, -fc);
-            sc[1] = a.centroids[0] * sum_q;
-            sc[2] = ldexpf(1.0f, -fs);
-            sc[3] = sum_s;
+            red[2 * wave] = mx;
+            red[2 * wave + 1] = sum;
         }
     }
     __syncthreads();
-    // digit operands: dword (mt, step, lane, r) holds elements e = 4r..4r+3 of
-    // lane's 16-element k-block; row i = lane % 16 = 4 (query) + digit
+    const float mw = red[0] * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1]));
+    int ec = 0, es = 0;
+    frexpf(mw, &ec);          // mw < 2^ec
+    frexpf(red[2], &es);
+    const int fc = (mw > 0.0f) ? 26 - ec : 0;
+    const int fs = (red[2] > 0.0f) ? 26 - es : 0;
+    if (tid == 0) {
+        float *sc = a.mf.qscal + row * 4;
+        sc[0] = ldexpf(1.0f, -fc);
+        sc[1] = a.centroids[0] * red[1];
+        sc[2] = ldexpf(1.0f, -fs);
+        sc[3] = red[3];
+    }
+    // this query's digit rows: lanes 16 kb + 4 (g % 4) + digit of row tile g / 4;
+    // dword r of a lane holds elements 4r..4r+3 of its 16-element k-block
     const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
     const int S = 2 * nc + 2 * ns;
     uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
-    for (int w = tid; w < MT * S * 256; w += kThreads) {
-        const int r = w % 4, l = (w / 4) % 64, s = (w / 256) % S, mt = w / (256 * S);
-        const int i = l % 16, kb = l / 16;
-        const int g = 4 * mt + i / 4, limb = i % 4;
+    for (int w = tid; w < S * 64; w += kThreads) {
+        const int r = w % 4, limb = (w / 4) % 4, kb = (w / 16) % 4, s = w / 64;
+        const int l = 16 * kb + 4 * (g % 4) + limb;
         uint32_t dw = 0;
-        if (g < GC) {
 #pragma unroll
-            for (int K = 0; K < 4; ++K) {
-                float wv;
-                int f;
-                if (s < 2 * nc) {
-                    const int u = s / 2, h = s % 2;
-                    const int bit = 32 * (kb * nc + u) + 8 * K + 4 * h + r;
-                    wv = qr[g][bit / a.bits] * s_acoef[bit % a.bits];
-                    f = s_fc[g];
-                } else {
-                    const int s2 = s - 2 * nc, u = s2 / 2, h = s2 % 2;
-                    const int bit = 32 * (kb * ns + u) + 8 * K + 4 * h + r;
-                    wv = sq[g][bit];
-                    f = s_fs[g];
-                }
-                const int x = static_cast<int>(rintf(ldexpf(wv, f)));
-                dw |= (static_cast<uint32_t>(digit7(x, limb)) & 0xffu) << (8 * K);
+        for (int K = 0; K < 4; ++K) {
+            float wv;
+            int f;
+            if (s < 2 * nc) {
+                const int u = s / 2, h = s % 2;
+                const int bit = 32 * (kb * nc + u) + 8 * K + 4 * h + r;
+                wv = qr[bit / a.bits] * s_acoef[bit % a.bits];
+                f = fc;
+            } else {
+                const int s2 = s - 2 * nc, u = s2 / 2, h = s2 % 2;
+                const int bit = 32 * (kb * ns + u) + 8 * K + 4 * h + r;
+                wv = sq[bit];
+                f = fs;
             }
+            const int x = static_cast<int>(rintf(ldexpf(wv, f)));
+            dw |= (static_cast<uint32_t>(digit7(x, limb)) & 0xffu) << (8 * K);
         }
-        out[w] = dw;
+        out[((g / 4) * S + s) * 256 + l * 4 + r] = dw;
     }
-    if (tid == 0) a.mf.counters[unit] = 0;
+    if (g == 0) {
+        // rows of absent queries (unit with fewer than four query heads) stay zero
+        for (int w = tid; w < S * 64 * 4; w += kThreads) {
+            const int l = (w / 4) % 64;
+            if ((l % 16) / 4 >= GC) out[(w / 256) * 256 + (w % 256)] = 0u;
+        }
+        if (tid == 0) a.mf.counters[unit] = 0;
+    }
 }
 
 // ------------------------------------------------------------ attention
@@ -232,9 +232,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
 
     __shared__ float lam[GCMAX][kKeys];
     __shared__ float s_alpha[GCMAX], s_m[GCMAX], s_l[GCMAX];
+    __shared__ float pmax[4][GCMAX], psum[4][GCMAX];
     __shared__ float zsum[GCMAX][kMaxNG];
     __shared__ __align__(16) unsigned char vtile[kKeys * VSTR];
-    __shared__ float vsc[kKeys * kMaxNG], vze[kKeys * kMaxNG];
+    __shared__ float2 vsz[kKeys * kMaxNG];       // (scale, zero) per (key, group)
     // value-product A fragments: [group][k-step][lane][4 dwords of fp16 pairs]
     __shared__ __align__(16) uint32_t afr[kMaxNG][2][64][4];
     __shared__ int s_last;
@@ -281,63 +282,92 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
         s_m[tid] = -INFINITY;
         s_l[tid] = 0.0f;
     }
-    // softmax state (wave w owns queries w and w + 4) and zero-point sums
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-    float zacc[2][kMaxNG];
+    // softmax state of this lane's (query 4 mt + rb, key column j): running max
+    // (identical in all lanes of a query), this lane's share of the running sum
+    // and of the zero-point sums
+    float m_run[MT], l_run[MT];
+    float zacc[MT][kMaxNG];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int mt = 0; mt < MT; ++mt) {
+        m_run[mt] = -INFINITY;
+        l_run[mt] = 0.0f;
 #pragma unroll
-        for (int gg = 0; gg < kMaxNG; ++gg) zacc[q][gg] = 0.0f;
+        for (int gg = 0; gg < kMaxNG; ++gg) zacc[mt][gg] = 0.0f;
+    }
     // lane (channel column, rb) accumulates queries 2 rb and 2 rb + 1
     float oacc[NTW][2];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) oacc[x][0] = oacc[x][1] = 0.0f;
     __syncthreads();
 
-    for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kKeys) {
+    // Register prefetch of one tile: value code chunk, value params, the key
+    // row slices of this lane's key.  The next tile's loads are issued before
+    // the current tile is computed, so their latency hides behind the work.
+    constexpr int VCH = kKeys * VB / 16;          // 16-byte value chunks per tile
+    constexpr int VCPT = (VCH + kThreads - 1) / kThreads;   // chunks per thread
+    struct Prefetch {
+        uint4 vcode[VCPT];
+        uint32_t vpar[2];
+        uint32_t cw[NC], sw[NS];
+        float nrm, rho;
+    };
+    auto fetch = [&](int64_t tile0, Prefetch &pf) {
         const int ntile = static_cast<int>(t_end - tile0 < kKeys ? t_end - tile0 : kKeys);
         const int64_t n0 = bh * a.T + tile0;
+#pragma unroll
+        for (int k = 0; k < VCPT; ++k) {
+            const int i = tid + k * kThreads;
+            pf.vcode[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < VCH && i / (VB / 16) < ntile) pf.vcode[k] = reinterpret_cast<const uint4 *>(a.vc.codes + n0 * VB)[i];
+        }
+        const uint32_t *par = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = tid + k * kThreads;
+            pf.vpar[k] = (i < ntile * NG) ? par[i] : 0u;
+        }
+        const int t = 16 * wave + j;
+        const bool valid = t < ntile;
+        const int64_t n = n0 + (valid ? t : 0);
+        const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
+#pragma unroll
+        for (int u = 0; u < NC; ++u) pf.cw[u] = valid ? crow[u] : 0u;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) pf.sw[u] = valid ? srow[u] : 0u;
+        pf.nrm = valid ? a.kc.knorm[n] : 0.0f;
+        pf.rho = valid ? a.kc.rnorm[n] : 0.0f;
+    };
+    Prefetch pre;
+    if (t_begin < t_end) fetch(t_begin, pre);
+
+    for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kKeys) {
+        const int ntile = static_cast<int>(t_end - tile0 < kKeys ? t_end - tile0 : kKeys);
+        const Prefetch cur = pre;
+        if (tile0 + kKeys < t_end) fetch(tile0 + kKeys, pre);
         // ---- stage the value tile (code rows, fp32 scale / zero)
-        {
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.vc.codes + n0 * VB);
-            for (int i = tid; i < kKeys * (VB / 16); i += kThreads) {
-                const int t = i / (VB / 16), c16 = i % (VB / 16);
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (t < ntile) v = src[i];
-                *reinterpret_cast<uint4 *>(vtile + t * VSTR + c16 * 16) = v;
-            }
-            const uint32_t *par = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
-            for (int i = tid; i < kKeys * NG; i += kThreads) {
-                float sc = 0.0f, ze = 0.0f;
-                if (i < ntile * NG) {
-                    const uint32_t w = par[i];
-                    sc = f16_bits_to_f32(w & 0xffffu);
-                    ze = f16_bits_to_f32(w >> 16);
-                }
-                vsc[i] = sc;
-                vze[i] = ze;
-            }
+#pragma unroll
+        for (int k = 0; k < VCPT; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < VCH) *reinterpret_cast<uint4 *>(vtile + (i / (VB / 16)) * VSTR + (i % (VB / 16)) * 16) = cur.vcode[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < kKeys * NG)
+                vsz[i] = make_float2(f16_bits_to_f32(cur.vpar[k] & 0xffffu), f16_bits_to_f32(cur.vpar[k] >> 16));
         }
         // ---- scores of keys 16 wave + j: 4 lanes (kb) split each key row
+        float lamr[MT];
         {
             const int t = 16 * wave + j;
             const bool valid = t < ntile;
-            const int64_t n = n0 + (valid ? t : 0);
-            uint32_t cw[NC], sw[NS];
-            const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
-            const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
-#pragma unroll
-            for (int u = 0; u < NC; ++u) cw[u] = valid ? crow[u] : 0u;
-#pragma unroll
-            for (int u = 0; u < NS; ++u) sw[u] = valid ? srow[u] : 0u;
-            const float nrm = valid ? a.kc.knorm[n] : 0.0f;
-            const float rho = valid ? a.kc.rnorm[n] : 0.0f;
             v4i accc[MT], accs[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) accc[mt] = accs[mt] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int s = 0; s < SC; ++s) {
-                const uint32_t dw = cw[s / 2];
+                const uint32_t dw = cur.cw[s / 2];
                 const int h = 4 * (s % 2);
                 const v4i bop = {static_cast<int>((dw >> h) & 0x01010101u), static_cast<int>((dw >> (h + 1)) & 0x01010101u),
                                  static_cast<int>((dw >> (h + 2)) & 0x01010101u), static_cast<int>((dw >> (h + 3)) & 0x01010101u)};
@@ -347,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
             }
 #pragma unroll
             for (int s = 0; s < SS; ++s) {
-                const uint32_t dw = sw[s / 2];
+                const uint32_t dw = cur.sw[s / 2];
                 const int h = 4 * (s % 2);
                 const v4i bop = {static_cast<int>((dw >> h) & 0x01010101u), static_cast<int>((dw >> (h + 1)) & 0x01010101u),
                                  static_cast<int>((dw >> (h + 2)) & 0x01010101u), static_cast<int>((dw >> (h + 3)) & 0x01010101u)};
@@ -355,52 +385,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
                 for (int mt = 0; mt < MT; ++mt)
                     accs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][SC + s], bop, accs[mt], 0, 0, 0);
             }
-            // lane (key j, row block rb) holds the four digits of query 4 mt + rb
+            // lane (key j, row block rb) holds the four digits of query 4 mt + rb;
+            // per-wave partial maxima over the 16 key columns
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
+                const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
+                const float score = cur.nrm * fmaf(kappa * cur.rho, dsign, dcode);
+                lamr[mt] = (valid && 4 * mt + rb < GC) ? a.scale * score : -INFINITY;
+                float pm = lamr[mt];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) pm = fmaxf(pm, __shfl_xor(pm, off));
+                if (j == 0) pmax[wave][4 * mt + rb] = pm;
+            }
+        }
+        __syncthreads();
+        // ---- online softmax and value-product operands, per (query, key) lane:
+        // p = e^(lambda - m), w = p * scale as fp16 hi + lo into row 2 g + part of
+        // the A fragment at the token's k position (tr-read order {0,2|1,3|4,6|5,7})
+        {
+            const int t = 16 * wave + j;
+            const int ks = t / 32, kbq = (t % 32) / 8, tau = t % 8;
+            const int u = 2 * (tau / 4) + (tau % 2), half = (tau % 4) / 2;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int g = 4 * mt + rb;
                 if (g < GC) {
-                    const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
-                    const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
-                    const float score = nrm * fmaf(kappa * rho, dsign, dcode);
-                    lam[g][t] = valid ? a.scale * score : -INFINITY;
+                    const float tmax = fmaxf(fmaxf(pmax[0][g], pmax[1][g]), fmaxf(pmax[2][g], pmax[3][g]));
+                    const float m_new = fmaxf(m_run[mt], tmax);
+                    float alpha = 1.0f, p = 0.0f;
+                    if (m_new != -INFINITY) {
+                        alpha = __expf(m_run[mt] - m_new);
+                        p = __expf(lamr[mt] - m_new);
+                    }
+                    m_run[mt] = m_new;
+                    l_run[mt] = fmaf(l_run[mt], alpha, p);
+                    if (wave == 0 && j == 0) s_alpha[g] = alpha;
+                    uint16_t *arow = reinterpret_cast<uint16_t *>(&afr[0][ks][16 * kbq + 2 * g][u]) + half;
+#pragma unroll
+                    for (int gg = 0; gg < kMaxNG; ++gg) {
+                        if (gg < NG) {
+                            const float2 sz = vsz[t * NG + gg];
+                            zacc[mt][gg] = fmaf(p, sz.y, zacc[mt][gg] * alpha);
+                            const float w = p * sz.x;
+                            const auto hi = __builtin_amdgcn_cvt_pkrtz(w, 0.0f);
+                            const auto lo = __builtin_amdgcn_cvt_pkrtz(w - static_cast<float>(hi[0]), 0.0f);
+                            // afr[gg][ks][row][u]: rows 2 g (hi) and 2 g + 1 (lo)
+                            arow[gg * (2 * 64 * 4 * 2)] = __builtin_bit_cast(uint32_t, hi) & 0xffffu;
+                            arow[gg * (2 * 64 * 4 * 2) + 4 * 2] = __builtin_bit_cast(uint32_t, lo) & 0xffffu;
+                        }
+                    }
                 }
             }
-        }
-        __syncthreads();
-        // ---- online softmax: wave w updates queries w, w + 4; lane = key
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int g = wave + 4 * q;
-            if (g < GC) {
-                const float x = lam[g][lane];
-                const float m_new = fmaxf(m_run[q], wave_max(x));
-                float alpha = 1.0f, p = 0.0f;
-                if (m_new != -INFINITY) {
-                    alpha = expf(m_run[q] - m_new);
-                    p = expf(x - m_new);
-                }
-                l_run[q] = fmaf(l_run[q], alpha, wave_sum(p));
-                m_run[q] = m_new;
-                lam[g][lane] = p;
-                if (lane == 0) s_alpha[g] = alpha;
-#pragma unroll
-                for (int gg = 0; gg < kMaxNG; ++gg)
-                    if (gg < NG) zacc[q][gg] = fmaf(p, vze[lane * NG + gg], zacc[q][gg] * alpha);
-            }
-        }
-        __syncthreads();
-        // ---- value-product operands: w = p * scale as fp16 hi + lo, rows 2 g + part.
-        // Lane (row, kb) k-step ks holds tokens 32 ks + 8 kb + {0,2 | 1,3 | 4,6 | 5,7}
-        // in its four dwords (the order the code operand below produces).
-        for (int it = tid; it < GC * NG * 32; it += kThreads) {
-            const int u = it % 4, kbq = (it / 4) % 4, ks = (it / 16) % 2, gg = (it / 32) % NG, g = it / (32 * NG);
-            const int ta = 32 * ks + 8 * kbq + 4 * (u / 2) + (u % 2), tb = ta + 2;
-            const float wa = lam[g][ta] * vsc[ta * NG + gg], wb = lam[g][tb] * vsc[tb * NG + gg];
-            const auto hi = __builtin_amdgcn_cvt_pkrtz(wa, wb);
-            const auto lo = __builtin_amdgcn_cvt_pkrtz(wa - static_cast<float>(hi[0]), wb - static_cast<float>(hi[1]));
-            afr[gg][ks][16 * kbq + 2 * g][u] = __builtin_bit_cast(uint32_t, hi);
-            afr[gg][ks][16 * kbq + 2 * g + 1][u] = __builtin_bit_cast(uint32_t, lo);
         }
         __syncthreads();
         // ---- value product: wave w handles channel tiles w, w + 4, ...
@@ -444,21 +480,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
         __syncthreads();
     }
 
-    // ---- this split's partials: m, l per query; acc[c] = value sum + zero-point sum
+    // ---- this split's partials: m, l per query; acc[c] = value sum + zero-point sum.
+    // l and the zero-point sums are spread over the 16 key columns of each wave
+    // and over the 4 waves: reduce across j, then across waves.
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int g = wave + 4 * q;
-        if (g < GC) {
+    for (int mt = 0; mt < MT; ++mt) {
+        const int g = 4 * mt + rb;
+        float l = l_run[mt];
 #pragma unroll
-            for (int gg = 0; gg < kMaxNG; ++gg)
-                if (gg < NG) {
-                    const float z = wave_sum(zacc[q][gg]);
-                    if (lane == 0) zsum[g][gg] = z;
-                }
-            if (lane == 0) {
-                s_m[g] = m_run[q];
-                s_l[g] = l_run[q];
+        for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off);
+        if (j == 0 && g < GC) psum[wave][g] = l;
+        if (wave == 0 && j == 0 && g < GC) s_m[g] = m_run[mt];
+#pragma unroll
+        for (int gg = 0; gg < kMaxNG; ++gg) {
+            if (gg < NG) {
+                float z = zacc[mt][gg];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) z += __shfl_xor(z, off);
+                if (j == 0 && g < GC) vsz[(wave * GCMAX + g) * kMaxNG + gg].x = z;
             }
+        }
+    }
+    __syncthreads();
+    if (tid < GC) {
+        s_l[tid] = psum[0][tid] + psum[1][tid] + psum[2][tid] + psum[3][tid];
+        for (int gg = 0; gg < NG; ++gg) {
+            float z = 0.0f;
+            for (int w = 0; w < 4; ++w) z += vsz[(w * GCMAX + tid) * kMaxNG + gg].x;
+            zsum[tid][gg] = z;
         }
     }
     __syncthreads();
@@ -487,23 +536,45 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    for (int i = tid; i < GC * D; i += kThreads) {
-        const int g = i / D, c = i % D;
-        const float *ml = a.part_ml + (row0 + g) * a.splits * 2;
-        const float *pa = a.part_acc + (row0 + g) * a.splits * D;
-        float mx = -INFINITY;
-        for (int s = 0; s < a.splits; ++s)
-            if (__builtin_nontemporal_load(ml + 2 * s + 1) > 0.0f) mx = fmaxf(mx, __builtin_nontemporal_load(ml + 2 * s));
-        float den = 0.0f, num = 0.0f;
-        for (int s = 0; s < a.splits; ++s) {
-            const float l = __builtin_nontemporal_load(ml + 2 * s + 1);
-            if (l > 0.0f) {
-                const float w = expf(__builtin_nontemporal_load(ml + 2 * s) - mx);
-                den = fmaf(l, w, den);
-                num = fmaf(__builtin_nontemporal_load(pa + static_cast<int64_t>(s) * D + c), w, num);
+    // pass 1: one wave per query turns the split maxima and sums into weights
+    // w_s = e^(m_s - M) / sum_s' l_s' e^(m_s' - M)   (splits <= 64, lane = split)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int g = wave + 4 * q;
+        if (g < GC) {
+            const float *ml = a.part_ml + (row0 + g) * a.splits * 2;
+            float m = -INFINITY, l = 0.0f;
+            if (lane < a.splits) {
+                m = ml[2 * lane];
+                l = ml[2 * lane + 1];
+            }
+            const float mx = wave_max(l > 0.0f ? m : -INFINITY);
+            const float w = (l > 0.0f) ? expf(m - mx) : 0.0f;
+            const float den = wave_sum(l * w);
+            lam[g][lane] = den > 0.0f ? w / den : 0.0f;
+        }
+    }
+    __syncthreads();
+    // pass 2: out[g][c..c+3] = sum_s w_s acc_s[c..c+3], sixteen splits' loads in flight
+    for (int i = tid; i < GC * (D / 4); i += kThreads) {
+        const int g = i / (D / 4), c4 = i % (D / 4);
+        const float4 *pa = reinterpret_cast<const float4 *>(a.part_acc + (row0 + g) * a.splits * D) + c4;
+        float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int s0 = 0; s0 < a.splits; s0 += 16) {
+            float4 v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                v[k] = (s0 + k < a.splits) ? pa[static_cast<int64_t>(s0 + k) * (D / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const float w = (s0 + k < a.splits) ? lam[g][s0 + k] : 0.0f;
+                o.x = fmaf(w, v[k].x, o.x);
+                o.y = fmaf(w, v[k].y, o.y);
+                o.z = fmaf(w, v[k].z, o.z);
+                o.w = fmaf(w, v[k].w, o.w);
             }
         }
-        a.out[(row0 + g) * D + c] = den > 0.0f ? num / den : 0.0f;
+        reinterpret_cast<float4 *>(a.out + (row0 + g) * D)[c4] = o;
     }
     if (tid == 0) a.mf.counters[unit] = 0;
 }
@@ -558,7 +629,7 @@ int mfma_score_steps(int d, int bits) { return 2 * code_dwords(d, bits) + 2 * si
 
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
 {
-    const dim3 qgrid(static_cast<unsigned>(a.mf.units));
+    const dim3 qgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq));
     void *tok;
     prof_begin("tq_qprep", stream, &tok);
     switch (a.dtype) {

@@ -26,6 +26,7 @@ struct tq_rotation {
     float *d_s = nullptr;       // [m][d]  QJL projection
     float *d_sT = nullptr;      // [d][m]  transpose of S
     float *d_dsign = nullptr;   // [d]     Hadamard signs (+-1), dense: unused
+    float *d_spiT = nullptr;    // [d][m]  transpose of S Pi (Sq = S Pi q in one product)
     void *d_block = nullptr;
     int device = 0;
 };
@@ -83,6 +84,7 @@ struct DecodeLaunch {
     int64_t T;
     int d, bits, m;
     const float *piT, *sT, *centroids;
+    const float *spiT;          // (S Pi)^T, [d][m]
     tq_kcache kc;
     // attention only
     int vbits, group;
@@ -107,6 +109,7 @@ constexpr int kDecodeTile = 256;   // keys per decode tile
 
 // matrix-core decode path (k_attend_mfma.hip): keys with 1-2 bits, d 128/256
 constexpr int kMfmaTile = 64;      // keys per tile
+constexpr int kMfmaMaxSplits = 64; // splits merged by one wave per query
 bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
 int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits);
