@@ -16,6 +16,33 @@ namespace {
 
 thread_local std::string g_error;
 
+// bf16 bits of a value, round to nearest even (finite inputs)
+uint16_t bf16_rne(double x)
+{
+    const float f = static_cast<float>(x);
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+double bf16_value(uint16_t h)
+{
+    const uint32_t u = static_cast<uint32_t>(h) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// split x into `parts` bf16 terms, each the rounding of what is left
+void bf16_split(double x, int parts, uint16_t *out)
+{
+    for (int p = 0; p < parts; ++p) {
+        out[p] = bf16_rne(x);
+        x -= bf16_value(out[p]);
+    }
+}
+
 tq_status fail(tq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 tq_status fail(tq_status st, const char *fmt, ...)
 {
@@ -246,6 +273,42 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
         delete rot;
         return hip_fail(e, "tq_make_rotation: device upload");
     }
+    // operand fragments of the matrix-core compressor: Pi as three bf16 terms
+    // (about 24 significant bits, so y keeps fp32 accuracy), S as two (16 bits;
+    // the residual is split in two as well, see the key kernel)
+    const int ks_n = d / 32, rt_n = d / 16;
+    std::vector<uint16_t> frag(static_cast<size_t>(rt_n) * ks_n * 5 * 512);
+    uint16_t *pif = frag.data(), *sfr = frag.data() + static_cast<size_t>(rt_n) * ks_n * 3 * 512;
+    for (int rt = 0; rt < rt_n; ++rt)
+        for (int ks = 0; ks < ks_n; ++ks)
+            for (int lane = 0; lane < 64; ++lane)
+                for (int el = 0; el < 8; ++el) {
+                    const int row = 16 * rt + lane % 16, kb = lane / 16;
+                    uint16_t parts[3];
+                    const double pv = pi[static_cast<size_t>(row) * d + 32 * ks + 8 * kb + el];
+                    if (kind == TQ_ROT_HADAMARD) {
+                        // the +-1 sign matrix H D, exact in one part; 1/sqrt(d) is applied in fp32
+                        parts[0] = bf16_rne(pv > 0.0 ? 1.0 : -1.0);
+                        parts[1] = parts[2] = 0;
+                    } else {
+                        bf16_split(pv, 3, parts);
+                    }
+                    for (int p = 0; p < 3; ++p) pif[(((rt * ks_n + ks) * 3 + p) * 64 + lane) * 8 + el] = parts[p];
+                    const int col = 16 * (2 * ks + el / 4) + 4 * kb + el % 4;
+                    bf16_split(s[static_cast<size_t>(row) * d + col], 2, parts);
+                    for (int p = 0; p < 2; ++p) sfr[(((rt * ks_n + ks) * 2 + p) * 64 + lane) * 8 + el] = parts[p];
+                }
+    e = hipMalloc(&rot->d_frag_block, sizeof(uint16_t) * frag.size());
+    if (e == hipSuccess)
+        e = hipMemcpy(rot->d_frag_block, frag.data(), sizeof(uint16_t) * frag.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (rot->d_frag_block) hipFree(rot->d_frag_block);
+        hipFree(rot->d_block);
+        delete rot;
+        return hip_fail(e, "tq_make_rotation: fragment upload");
+    }
+    rot->d_pifrag = static_cast<uint16_t *>(rot->d_frag_block);
+    rot->d_sfrag = rot->d_pifrag + static_cast<size_t>(rt_n) * ks_n * 3 * 512;
     float *base = static_cast<float *>(rot->d_block);
     rot->d_pi = base;
     rot->d_piT = base + dd;
@@ -261,6 +324,7 @@ void tq_rotation_free(tq_rotation *rot)
 {
     if (!rot) return;
     if (rot->d_block) hipFree(rot->d_block);
+    if (rot->d_frag_block) hipFree(rot->d_frag_block);
     delete rot;
 }
 
@@ -447,6 +511,8 @@ tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype,
     a.dsign = fmt->rot->d_dsign;
     a.centroids = fmt->cb->d_centroids;
     a.boundaries = fmt->cb->d_boundaries;
+    a.pifrag = fmt->rot->d_pifrag;
+    a.sfrag = fmt->rot->d_sfrag;
     a.out = out;
     const hipError_t e = tq::launch_compress_keys(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);

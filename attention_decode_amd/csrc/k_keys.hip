@@ -1,245 +1,309 @@
-// Key compression for gfx950: norm, rotation, Lloyd-Max codes, residual norm
-// and QJL signs, packed into the four key planes.  One 256-thread workgroup
-// owns a tile of TK = 8192/D keys (32 KB of fp32 in LDS); the dense rotation
-// and the QJL projection are fp32 tile products whose second operand (Pi^T or
-// S^T) is streamed through LDS in 32-row chunks; the Hadamard rotation is an
-// in-place butterfly on the LDS tile.  Method: discosf.com TurboQuant article,
-// section "TurboQuant in one sentence", steps 1-3.
+// Key compression for gfx950 on the matrix cores: norm, rotation, Lloyd-Max
+// codes, residual norm and QJL signs, packed into the four key planes.
+// Method: discosf.com TurboQuant article, section "TurboQuant in one sentence",
+// steps 1-3 (y = Pi k/||k||, nearest-centroid codes, signs of S r with
+// r = y - c[idx]).
+//
+// One 256-thread workgroup encodes 64 keys (four 16-key tiles).  Both products
+// run as v_mfma_f32_16x16x32_bf16 with the keys / residuals as the B operand
+// (lane = key column) and the matrix as the A operand, so that every A
+// fragment read from L2 serves 64 keys; the four waves split the output rows.
+//
+// Accuracy: the bf16 operands are made exact or near-fp32 by splitting.
+//   * y:  Pi = P0 + P1 + P2 (three bf16 terms, about 24 significant bits); a
+//         bf16 key is one exact term, an fp16 key two, an fp32 key three.  The
+//         products kept are those whose term ranks sum to at most 2, i.e. every
+//         product down to about 2^-24 of the leading one.  The Hadamard sign
+//         matrix H D is exact in one term and its 1/sqrt(d) joins 1/||k||.
+//   * z:  S = S0 + S1, r = R0 + R1 (16 bits each); S0 R0 + S0 R1 + S1 R0 leaves
+//         an error near 2^-16 of |z| per term, far inside the resolution at
+//         which a sign can legitimately flip.
+// All sums accumulate in fp32 inside the MFMA; ||k|| and ||r|| are summed in
+// fp64 from the fp32 values.
 #include "tq_internal.h"
 #include "tq_device.h"
 
 namespace tq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 32;   // rows of the streamed operand per LDS stage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
-struct KeyTile {
-    static constexpr int TK = 8192 / D;        // keys per workgroup
-    static constexpr int LPR = kThreads / TK;  // lanes per key row (2, 4, 8)
-    static constexpr int OC = D / 16;          // outputs per thread in the products
-    static constexpr int KR = TK / 16;         // key rows per thread in the products
-    static constexpr int LD = D + 1;           // padded LDS row
-};
+constexpr int kThreads = 256;
+constexpr int kKT = 4;              // 16-key tiles per workgroup
+constexpr int kKeys = 16 * kKT;     // keys per workgroup
+
+// bf16 terms that represent one input element exactly
+template <typename TIn> struct KeyTerms;
+template <> struct KeyTerms<bf16_t> { static constexpr int n = 1; };
+template <> struct KeyTerms<f16_t> { static constexpr int n = 2; };
+template <> struct KeyTerms<float> { static constexpr int n = 3; };
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4 &a, const uint4 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// split eight fp32 values into NT bf16x8 terms (x = t0 + t1 + ...)
+template <int NT>
+__device__ __forceinline__ void split_terms(const float (&x)[8], uint4 (&t)[NT])
+{
+    float rem[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rem[e] = x[e];
+#pragma unroll
+    for (int p = 0; p < NT; ++p) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = bf16_rne_bits(rem[e]);
+            rem[e] -= bf16_bits_f32(h[e]);
+        }
+        t[p] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+}
+
+// eight consecutive channels of one key as B-operand terms, plus their sum of squares
+__device__ __forceinline__ void key_frag(const bf16_t *p, bool valid, uint4 (&t)[1], double &ss)
+{
+    t[0] = valid ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_to_f32(w[i] & 0xffffu), hi = bf16_to_f32(w[i] >> 16);
+        ss += static_cast<double>(lo * lo) + static_cast<double>(hi * hi);   // squares exact in fp32
+    }
+}
+
+template <typename TIn, int NT>
+__device__ __forceinline__ void key_frag(const TIn *p, bool valid, uint4 (&t)[NT], double &ss)
+{
+    float x[8];
+    if (valid) {
+        load8_as_f32(p, x);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);
+    split_terms<NT>(x, t);
+}
 
 struct KeySmem {
-    float *u;         // [TK][D+1]  input -> rotated -> residual
-    float *chunk;     // [kChunk][D]
-    uint8_t *code8;   // [TK][D]
-    uint8_t *sign8;   // [TK][D]
-    float *inv_n;     // [TK]
-    float *knorm;     // [TK]
-    float *rnorm;     // [TK]
-    float *cent;      // [256]
-    float *bnd;       // [256]
+    uint4 *rfrag;       // [kKT][KS][2][64]  residual B operands (two bf16 terms)
+    uint32_t *cw;       // [kKeys][D * bits / 32]  code words
+    uint32_t *sw;       // [kKeys][D / 32]         sign words
+    double *rho2;       // [4 waves][kKeys]
+    float *knorm;       // [kKeys]
+    float *cent;        // [256]
+    float *bnd;         // [256]
 };
 
-// acc[kr][c] += U[ty*KR + kr][j] * Op[j][tx + 16 c] over j, Op streamed from global
 template <int D>
-__device__ __forceinline__ void tile_product(const KeySmem &s, const float *__restrict__ op,
-                                             float (&acc)[KeyTile<D>::KR][KeyTile<D>::OC])
+constexpr size_t key_smem_bytes()
 {
-    using KT = KeyTile<D>;
-    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-#pragma unroll
-    for (int kr = 0; kr < KT::KR; ++kr)
-#pragma unroll
-        for (int c = 0; c < KT::OC; ++c) acc[kr][c] = 0.0f;
-    for (int j0 = 0; j0 < D; j0 += kChunk) {
-        __syncthreads();
-        // stage rows j0 .. j0+kChunk of the operand (each row D floats)
-        const float4 *src = reinterpret_cast<const float4 *>(op + static_cast<size_t>(j0) * D);
-        float4 *dst = reinterpret_cast<float4 *>(s.chunk);
-        for (int i = tid; i < kChunk * D / 4; i += kThreads) dst[i] = src[i];
-        __syncthreads();
-#pragma unroll 4
-        for (int jj = 0; jj < kChunk; ++jj) {
-            float a[KT::KR], b[KT::OC];
-#pragma unroll
-            for (int kr = 0; kr < KT::KR; ++kr) a[kr] = s.u[(ty * KT::KR + kr) * KT::LD + j0 + jj];
-#pragma unroll
-            for (int c = 0; c < KT::OC; ++c) b[c] = s.chunk[jj * D + tx + 16 * c];
-#pragma unroll
-            for (int kr = 0; kr < KT::KR; ++kr)
-#pragma unroll
-                for (int c = 0; c < KT::OC; ++c) acc[kr][c] = fmaf(a[kr], b[c], acc[kr][c]);
-        }
-    }
+    return sizeof(uint4) * kKT * (D / 32) * 2 * 64 + sizeof(uint32_t) * kKeys * (D / 4 + D / 32)
+           + sizeof(double) * 4 * kKeys + sizeof(float) * (kKeys + 512);
 }
 
 template <int D, typename TIn>
 __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
-    using KT = KeyTile<D>;
+    constexpr int KS = D / 32;           // k-steps of 32 channels
+    constexpr int RTW = D / 64;          // 16-row output tiles per wave
+    constexpr int NK = KeyTerms<TIn>::n;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     KeySmem s;
     {
         unsigned char *p = smem_raw;
-        s.u = reinterpret_cast<float *>(p);        p += sizeof(float) * KT::TK * KT::LD;
-        s.chunk = reinterpret_cast<float *>(p);    p += sizeof(float) * kChunk * D;
-        s.inv_n = reinterpret_cast<float *>(p);    p += sizeof(float) * KT::TK;
-        s.knorm = reinterpret_cast<float *>(p);    p += sizeof(float) * KT::TK;
-        s.rnorm = reinterpret_cast<float *>(p);    p += sizeof(float) * KT::TK;
-        s.cent = reinterpret_cast<float *>(p);     p += sizeof(float) * 256;
-        s.bnd = reinterpret_cast<float *>(p);      p += sizeof(float) * 256;
-        s.code8 = p;                               p += KT::TK * D;
-        s.sign8 = p;
+        s.rfrag = reinterpret_cast<uint4 *>(p);   p += sizeof(uint4) * kKT * KS * 2 * 64;
+        s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
+        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * (D / 4);
+        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * (D / 32);
+        s.knorm = reinterpret_cast<float *>(p);   p += sizeof(float) * kKeys;
+        s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
+        s.bnd = reinterpret_cast<float *>(p);
     }
-    const int tid = threadIdx.x;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * KT::TK;
-    const int L = 1 << a.bits;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kb = lane >> 4;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kKeys;
+    const int bits = a.bits, L = 1 << bits;
+    const int CW = D * bits / 32, SWN = D / 32;
 
+    for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
+    for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
     for (int i = tid; i < L; i += kThreads) s.cent[i] = a.centroids[i];
     for (int i = tid; i < L - 1; i += kThreads) s.bnd[i] = a.boundaries[i];
 
-    // ---- 1. load the key tile as fp32 (8 channels per access)
-    for (int i = tid; i < KT::TK * D / 8; i += kThreads) {
-        const int r = i / (D / 8), j = (i % (D / 8)) * 8;
-        const int64_t n = n0 + r;
-        float v[8];
-        if (n < n_total) {
-            const int64_t t = n % a.T, bh = n / a.T;
-            const int64_t b = bh / a.H, h = bh % a.H;
-            const TIn *src = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st + j;
-            load8_as_f32(src, v);
-        } else {
+    // rows of this lane's four keys
+    const TIn *kp[kKT];
+    bool valid[kKT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s.u[r * KT::LD + j + e] = v[e];
+    for (int kt = 0; kt < kKT; ++kt) {
+        const int64_t n = n0 + 16 * kt + col;
+        valid[kt] = n < n_total;
+        const int64_t nn = valid[kt] ? n : 0;
+        const int64_t t = nn % a.T, bh = nn / a.T;
+        const int64_t b = bh / a.H, h = bh % a.H;
+        kp[kt] = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st + 8 * kb;
     }
-    __syncthreads();
 
-    // ---- 2. ||k|| in fp64, LPR lanes per row
-    {
-        const int r = tid / KT::LPR, part = tid % KT::LPR;
-        double acc = 0.0;
-        for (int j = part; j < D; j += KT::LPR) {
-            const double x = s.u[r * KT::LD + j];
-            acc = fma(x, x, acc);
-        }
+    // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r
+    const uint4 *pif = reinterpret_cast<const uint4 *>(a.pifrag);
+    const uint4 *sfr = reinterpret_cast<const uint4 *>(a.sfrag);
+    f32x4 acc[RTW][kKT];
 #pragma unroll
-        for (int off = KT::LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, KT::LPR);
-        if (part == 0) {
-            const double n = sqrt(acc);
-            s.knorm[r] = static_cast<float>(n);
-            s.inv_n[r] = (n > 0.0) ? static_cast<float>((a.hadamard ? 1.0 / sqrt(double(D)) : 1.0) / n)
-                                   : 0.0f;
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. rotation: y = Pi k / n
-    if (!a.hadamard) {
-        float acc[KT::KR][KT::OC];
-        tile_product<D>(s, a.piT, acc);
-        __syncthreads();
-        const int tx = tid % 16, ty = tid / 16;
+    for (int j = 0; j < RTW; ++j)
 #pragma unroll
-        for (int kr = 0; kr < KT::KR; ++kr) {
-            const int r = ty * KT::KR + kr;
-            const float sc = s.inv_n[r];
+        for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    double ss[kKT] = {0.0, 0.0, 0.0, 0.0};
+    const int npp = a.hadamard ? 1 : 3;
+#pragma unroll 2
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 kf[kKT][NK];
 #pragma unroll
-            for (int c = 0; c < KT::OC; ++c) s.u[r * KT::LD + tx + 16 * c] = acc[kr][c] * sc;
-        }
-    } else {
-        // y = H (D k) / (sqrt(d) n): sign flip, then log2(d) butterfly stages
-        for (int i = tid; i < KT::TK * D; i += kThreads) {
-            const int r = i / D, j = i % D;
-            s.u[r * KT::LD + j] *= a.dsign[j];
-        }
-        for (int h = 1; h < D; h <<= 1) {
-            __syncthreads();
-            for (int p = tid; p < KT::TK * D / 2; p += kThreads) {
-                const int r = p / (D / 2), q = p % (D / 2);
-                const int j = (q / h) * 2 * h + (q % h);
-                float *row = s.u + r * KT::LD;
-                const float x = row[j], y = row[j + h];
-                row[j] = x + y;
-                row[j + h] = x - y;
+        for (int kt = 0; kt < kKT; ++kt) key_frag(kp[kt] + 32 * ks, valid[kt], kf[kt], ss[kt]);
+#pragma unroll
+        for (int j = 0; j < RTW; ++j) {
+            const int rt = wave * RTW + j;
+            for (int pp = 0; pp < npp; ++pp) {
+                const uint4 af = pif[((rt * KS + ks) * 3 + pp) * 64 + lane];
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq) {
+                    if (!a.hadamard && pp + kq > 2) continue;
+#pragma unroll
+                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af, kf[kt][kq], acc[j][kt]);
+                }
             }
         }
-        __syncthreads();
-        for (int i = tid; i < KT::TK * D; i += kThreads) {
-            const int r = i / D, j = i % D;
-            s.u[r * KT::LD + j] *= s.inv_n[r];
+    }
+
+    // ---- 2. ||k|| (fp64 over the four lanes that hold one key)
+    float inv_n[kKT];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+        double t = ss[kt];
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        const double n = sqrt(t);
+        inv_n[kt] = (n > 0.0) ? static_cast<float>((a.hadamard ? 1.0 / sqrt(double(D)) : 1.0) / n) : 0.0f;
+        if (wave == 0 && kb == 0) s.knorm[16 * kt + col] = static_cast<float>(n);
+    }
+    __syncthreads();   // cleared words, codebook tables
+
+    // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+        const int key = 16 * kt + col;
+        double rr = 0.0;
+#pragma unroll
+        for (int j = 0; j < RTW; ++j) {
+            const int rt = wave * RTW + j;
+            uint32_t chunk = 0, rh[4], rl[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float y = acc[j][kt][r] * inv_n[kt];
+                int pos = 0;
+                for (int step = L >> 1; step > 0; step >>= 1)
+                    if (s.bnd[pos + step - 1] < y) pos += step;
+                const float res = y - s.cent[pos];
+                rr = fma(static_cast<double>(res), static_cast<double>(res), rr);
+                chunk |= static_cast<uint32_t>(pos) << (bits * r);
+                rh[r] = bf16_rne_bits(res);
+                rl[r] = bf16_rne_bits(res - bf16_bits_f32(rh[r]));
+            }
+            // 4 codes of `bits` bits at bit offset bits (16 rt + 4 kb) of the key's stream
+            const int off = bits * (16 * rt + 4 * kb), w = off >> 5, sh = off & 31;
+            atomicOr(&s.cw[key * CW + w], chunk << sh);
+            if (sh + 4 * bits > 32) atomicOr(&s.cw[key * CW + w + 1], chunk >> (32 - sh));
+            // residual as B operand of k-step rt/2: elements 4 (rt % 2) + r of this lane
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 0) * 64 + lane]);
+            uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 1) * 64 + lane]);
+            const int hw = 2 * (rt & 1);
+            *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(rh[0] | (rh[1] << 16), rh[2] | (rh[3] << 16));
+            *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(rl[0] | (rl[1] << 16), rl[2] | (rl[3] << 16));
+        }
+        rr += __shfl_xor(rr, 16);
+        rr += __shfl_xor(rr, 32);
+        if (kb == 0) s.rho2[wave * kKeys + key] = rr;
+    }
+    __syncthreads();
+
+    // ---- 4. z = S r on this wave's rows; signs [z >= 0]
+    f32x4 zacc[RTW][kKT];
+#pragma unroll
+    for (int j = 0; j < RTW; ++j)
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 rf[kKT][2];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+            rf[kt][0] = s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + lane];
+            rf[kt][1] = s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < RTW; ++j) {
+            const int rt = wave * RTW + j;
+            const uint4 s0 = sfr[((rt * KS + ks) * 2 + 0) * 64 + lane];
+            const uint4 s1 = sfr[((rt * KS + ks) * 2 + 1) * 64 + lane];
+#pragma unroll
+            for (int kt = 0; kt < kKT; ++kt) {
+                zacc[j][kt] = mfma_bf16(s0, rf[kt][0], zacc[j][kt]);
+                zacc[j][kt] = mfma_bf16(s0, rf[kt][1], zacc[j][kt]);
+                zacc[j][kt] = mfma_bf16(s1, rf[kt][0], zacc[j][kt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RTW; ++j) {
+        const int rt = wave * RTW + j;
+        const int off = 16 * rt + 4 * kb;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+            uint32_t nib = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
+            atomicOr(&s.sw[(16 * kt + col) * SWN + (off >> 5)], nib << (off & 31));
         }
     }
     __syncthreads();
 
-    // ---- 4. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
-    {
-        const int r = tid / KT::LPR, part = tid % KT::LPR;
-        double acc = 0.0;
-        for (int j = part; j < D; j += KT::LPR) {
-            const float y = s.u[r * KT::LD + j];
-            int pos = 0;
-            for (int step = L >> 1; step > 0; step >>= 1)
-                if (s.bnd[pos + step - 1] < y) pos += step;
-            const float res = y - s.cent[pos];
-            s.u[r * KT::LD + j] = res;
-            s.code8[r * D + j] = static_cast<uint8_t>(pos);
-            acc = fma(double(res), double(res), acc);
-        }
-#pragma unroll
-        for (int off = KT::LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, KT::LPR);
-        if (part == 0) s.rnorm[r] = static_cast<float>(sqrt(acc));
-    }
-    __syncthreads();
-
-    // ---- 5. QJL signs of z = S r
-    {
-        float acc[KT::KR][KT::OC];
-        tile_product<D>(s, a.sT, acc);
-        const int tx = tid % 16, ty = tid / 16;
-#pragma unroll
-        for (int kr = 0; kr < KT::KR; ++kr)
-#pragma unroll
-            for (int c = 0; c < KT::OC; ++c)
-                s.sign8[(ty * KT::KR + kr) * D + tx + 16 * c] = acc[kr][c] >= 0.0f ? 1 : 0;
-    }
-    __syncthreads();
-
-    // ---- 6. pack and store (rows of consecutive keys are contiguous)
-    const int wc = D * a.bits / 32, ws = D / 32;
-    uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * wc;
-    for (int i = tid; i < KT::TK * wc; i += kThreads) {
-        const int r = i / wc, w = i % wc;
-        if (n0 + r >= n_total) continue;
-        codes[i] = pack_word(s.code8 + r * D, w, a.bits);
-    }
-    uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * ws;
-    for (int i = tid; i < KT::TK * ws; i += kThreads) {
-        const int r = i / ws, w = i % ws;
-        if (n0 + r >= n_total) continue;
-        signs[i] = pack_word(s.sign8 + r * D, w, 1);
-    }
-    if (tid < KT::TK && n0 + tid < n_total) {
+    // ---- 5. store the WG's keys (contiguous rows of every plane)
+    const int nk = static_cast<int>(n_total - n0 < kKeys ? n_total - n0 : kKeys);
+    uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
+    for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
+    uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
+    for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+    if (tid < nk) {
         a.out.knorm[n0 + tid] = s.knorm[tid];
-        a.out.rnorm[n0 + tid] = s.rnorm[tid];
+        const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
+        a.out.rnorm[n0 + tid] = static_cast<float>(sqrt(r2));
     }
-}
-
-template <int D>
-size_t key_smem_bytes()
-{
-    using KT = KeyTile<D>;
-    return sizeof(float) * (KT::TK * KT::LD + kChunk * D + 3 * KT::TK + 512) + 2 * KT::TK * D;
 }
 
 template <int D, typename TIn>
 hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
 {
-    using KT = KeyTile<D>;
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
-    const size_t smem = key_smem_bytes<D>();
+    constexpr size_t smem = key_smem_bytes<D>();
     auto kern = k_compress_keys<D, TIn>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const int64_t blocks = (n + KT::TK - 1) / KT::TK;
+    const int64_t blocks = (n + kKeys - 1) / kKeys;
     void *tok;
     prof_begin("tq_compress_keys", stream, &tok);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, stream, a, n);

@@ -27,6 +27,14 @@ struct tq_rotation {
     float *d_sT = nullptr;      // [d][m]  transpose of S
     float *d_dsign = nullptr;   // [d]     Hadamard signs (+-1), dense: unused
     float *d_spiT = nullptr;    // [d][m]  transpose of S Pi (Sq = S Pi q in one product)
+    // bf16 operand fragments of the matrix-core key compressor, in lane order
+    // (16x16x32 MFMA A operand: lane = row % 16 + 16 * k-block, 8 elements):
+    //   pifrag [d/16 row tiles][d/32 k-steps][3 parts][64][8]: Pi = hi + mid + lo
+    //   sfrag  [m/16 row tiles][d/32 k-steps][2 parts][64][8]: S = hi + mid, with
+    //          k element e of k-block kb at coordinate 16 (2 ks + e/4) + 4 kb + e%4
+    uint16_t *d_pifrag = nullptr;
+    uint16_t *d_sfrag = nullptr;
+    void *d_frag_block = nullptr;
     void *d_block = nullptr;
     int device = 0;
 };
@@ -52,6 +60,7 @@ struct KeyLaunch {
     int d, bits, m;
     bool hadamard;
     const float *piT, *sT, *dsign, *centroids, *boundaries;
+    const uint16_t *pifrag, *sfrag;
     tq_kcache out;
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
