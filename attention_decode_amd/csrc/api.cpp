@@ -448,14 +448,13 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     const int64_t tiles = (T + tile - 1) / tile;
     int64_t want = (1024 + p.units - 1) / p.units;      // about four workgroups per CU
     if (want > tiles) want = tiles;
-    // the matrix-core kernel merges its splits in one wave per query
-    if (want > (p.mfma ? tq::kMfmaMaxSplits : 1024)) want = p.mfma ? tq::kMfmaMaxSplits : 1024;
+    if (want > 1024) want = 1024;
     p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);
     return p;
 }
 
 struct AttendLayout {
-    size_t qprep, aops, qscal, counters, ml, acc, total;
+    size_t qprep, aops, qscal, ml, acc, total;
 };
 
 AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePlan &p)
@@ -470,8 +469,6 @@ AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePla
     off += align256(static_cast<size_t>(p.units) * p.mt * p.steps * 64 * 16);
     L.qscal = off;
     off += align256(rows * 4 * sizeof(float));
-    L.counters = off;
-    off += align256(static_cast<size_t>(p.units) * sizeof(int));
     L.ml = off;
     off += align256(rows * p.splits * 2 * sizeof(float));
     L.acc = off;
@@ -642,9 +639,6 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
     if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
     const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits);
-    if (plan.mfma && plan.splits > tq::kMfmaMaxSplits)
-        return fail(TQ_EUNSUPPORTED, "%s: n_splits=%d above %d for this key format", who, plan.splits,
-                    tq::kMfmaMaxSplits);
     const AttendLayout L = attend_layout(kfmt, B, Hq, plan);
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;
@@ -667,7 +661,6 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     a.mf.units = plan.units;
     a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
-    a.mf.counters = reinterpret_cast<int *>(base + L.counters);
     hipError_t e;
     if (plan.mfma) {
         e = tq::launch_decode_mfma(a, s);

@@ -7,10 +7,11 @@
 //   c[b0 + 2 b1] = c[0] + (c[1] - c[0]) b0 + (c[2] - c[0]) b1,
 // so sum_j q_rot[j] c[idx_j] is a weighted sum of the raw bits of the code
 // row, and sum_i Sq_i s_i a weighted sum of the raw sign bits.  Each bit is an
-// exact int8 operand ((dword >> k) & 0x01010101 yields four of them), and the
-// weights are fixed point with four balanced 7-bit digits, so a
-// v_mfma_i32_16x16x64_i8 accumulates every limb exactly in int32.  Matrix rows
-// are (query, digit), columns are keys.
+// exact int8 operand: dword & (0x01010101 << k) yields four of them as bytes
+// of value 2^k (-128 for k = 7), and the weight of that position carries
+// 2^-k (negated for k = 7).  The weights are fixed point with four balanced
+// 7-bit digits, so a v_mfma_i32_16x16x64_i8 accumulates every limb exactly in
+// int32.  Matrix rows are (query, digit), columns are keys.
 //
 // Values (discosf.com TurboQuant article, step 4).  out[g][c] =
 //   sum_t p[g][t] scale[t][grp(c)] code[t][c] + sum_t p[g][t] zero[t][grp(c)].
@@ -19,13 +20,15 @@
 // columns are channels.  The code operand is the code itself as the bits of an
 // fp16 subnormal (value code * 2^-24, exact; the product is scaled back by
 // 2^24), taken straight from the packed bytes: the LDS transpose read
-// (ds_read_b64_tr_b8) gives each lane one byte column over eight tokens and a
-// shift and mask leave one field per half.  The zero-point sum is a per-lane
-// running sum reduced once per split.
+// (ds_read_b64_tr_b8) gives each lane one byte column over eight tokens, and a
+// mask leaves one field per half in place (field f of a byte reads as
+// code * 2^(bits f), undone when the accumulator is read out).  The
+// zero-point sum is a per-lane running sum reduced once per split.
 //
 // One 256-thread workgroup owns one (sequence, KV head, query chunk) and one
-// token range; tiles of 64 keys.  The last workgroup of a unit to finish
-// merges the splits (log-sum-exp), so one launch does the whole decode step.
+// token range; every wave runs its own 32-key tiles without workgroup
+// barriers.  Split partials (max, sum, weighted values) are merged by
+// log-sum-exp in a second, small kernel (none with a single split).
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -41,7 +44,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kThreads = 256;
-constexpr int kKeys = 64;          // keys per tile
 constexpr int kMaxG = 8;           // query heads per unit
 constexpr int kMaxNG = 8;          // value groups per vector (d / group)
 
@@ -62,12 +64,12 @@ __device__ __forceinline__ int digit7(int x, int k)
     return (k == 3) ? x : d;
 }
 
-// value of a limb-row quadruple: c0 + 128 c1 + 128^2 c2 + 128^3 c3 (each |c| < 2^24)
+// value of a limb-row quadruple: c0 + 128 c1 + 128^2 c2 + 128^3 c3 (each |c| < 2^23,
+// so the two pair sums are exact in int32)
 __device__ __forceinline__ float limbs_to_float(v4i c)
 {
-    return static_cast<float>(c[0]) +
-           128.0f * (static_cast<float>(c[1]) +
-                     128.0f * (static_cast<float>(c[2]) + 128.0f * static_cast<float>(c[3])));
+    const int lo = c[0] + (c[1] << 7), hi = c[2] + (c[3] << 7);
+    return fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
 }
 
 __device__ __forceinline__ float wave_max(float x)
@@ -200,7 +202,11 @@ __global__ __launch_bounds__(kThreads) void k_qprep_mfma(DecodeLaunch a)
                 wv = sq[bit];
                 f = fs;
             }
-            const int x = static_cast<int>(rintf(ldexpf(wv, f)));
+            // the key bit arrives as byte 2^sh (masked in place, not shifted):
+            // weight w 2^-sh, negated for sh = 7 where the byte reads as -128
+            const int sh = 4 * (s % 2) + r;
+            int x = static_cast<int>(rintf(ldexpf(wv, f - sh)));
+            if (sh == 7) x = -x;
             dw |= (static_cast<uint32_t>(digit7(x, limb)) & 0xffu) << (8 * K);
         }
         out[((g / 4) * S + s) * 256 + l * 4 + r] = dw;
@@ -211,46 +217,91 @@ __global__ __launch_bounds__(kThreads) void k_qprep_mfma(DecodeLaunch a)
             const int l = (w / 4) % 64;
             if ((l % 16) / 4 >= GC) out[(w / 256) * 256 + (w % 256)] = 0u;
         }
-        if (tid == 0) a.mf.counters[unit] = 0;
     }
 }
 
 // ------------------------------------------------------------ attention
+// 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+
+// k-slot order of a 32-token wave tile in the value product: slot 2j holds
+// token j, slot 2j + 1 token 16 + j, so that the lane owning key column j of
+// both score tiles writes its two tokens as one packed fp16 pair.
+__device__ __forceinline__ int slot_token(int slot) { return (slot & 1) ? 16 + (slot >> 1) : (slot >> 1); }
+
+// One 256-thread workgroup owns one (sequence, KV head, query chunk) and one
+// token range; each wave walks its own 32-key tiles (wave w takes tiles w,
+// w + 4, ...) with its own online-softmax state and value accumulators, so
+// the tile loop has no workgroup barrier.  Loads of the next tile are issued
+// before the current one is computed (two register buffers in turn).  The
+// four waves are merged in LDS at the end; with one split the workgroup
+// writes the normalised output, else its partial (max, sum, weighted values).
 template <int BITS, int D, int MT, int VBITS>
-__global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, float kappa, int64_t chunk)
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NC = code_dwords(D, BITS), NS = sign_dwords(D);
     constexpr int SC = 2 * NC, SS = 2 * NS, S = SC + SS;
-    constexpr int GCMAX = 4 * MT;
+    constexpr int TK = 32;                       // keys per wave tile
     constexpr int VB = D * VBITS / 8;            // value code bytes per token
     constexpr int VSTR = VB + 16;                // LDS row stride (odd multiple of 16 B)
-    constexpr int NCB = VB / 16;                 // 16-column blocks of value bytes
+    constexpr int NCB = VB / 16;                 // 16-byte column blocks of a value row
     constexpr int NF = 8 / VBITS;                // code fields per byte
     constexpr int NTILE = NCB * NF;              // 16-channel tiles of the value product
-    constexpr int NTW = (NTILE + 3) / 4;         // tiles per wave
-    constexpr uint32_t VMASK = VBITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+    constexpr bool kTwoGroups = NF * 16 > 32;    // a tile can span two value groups (group >= 32)
+    constexpr int VCL = TK * VB / 16 / 64;       // 16-byte value chunks per lane per tile
+    constexpr int NGM = D / 32;                  // most value groups per row (group >= 32)
+    constexpr int PD = TK * NGM / 64;            // (scale, zero) dwords per lane per tile
+    constexpr int VT_BYTES = TK * VSTR;
+    constexpr int AF_BYTES = NGM * 64 * 16;
+    constexpr int PS_BYTES = TK * NGM * 4;
+    constexpr int WAVE_BYTES = VT_BYTES + AF_BYTES + PS_BYTES;
+    constexpr int MERGE_BYTES = 4 * kMaxG * D * 4;
+    constexpr int SMEM = (4 * WAVE_BYTES > MERGE_BYTES) ? 4 * WAVE_BYTES : MERGE_BYTES;
 
-    __shared__ float lam[GCMAX][kKeys];
-    __shared__ float s_alpha[GCMAX], s_m[GCMAX], s_l[GCMAX];
-    __shared__ float pmax[4][GCMAX], psum[4][GCMAX];
-    __shared__ float zsum[GCMAX][kMaxNG];
-    __shared__ __align__(16) unsigned char vtile[kKeys * VSTR];
-    __shared__ float2 vsz[kKeys * kMaxNG];       // (scale, zero) per (key, group)
-    // value-product A fragments: [group][k-step][lane][4 dwords of fp16 pairs]
-    __shared__ __align__(16) uint32_t afr[kMaxNG][2][64][4];
-    __shared__ int s_last;
+    __shared__ __align__(16) unsigned char smem[SMEM];
+    __shared__ float s_alpha[4][kMaxG];
+    __shared__ float s_wm[4][kMaxG], s_wl[4][kMaxG];
+    __shared__ float s_wz[4][kMaxG][kMaxNG];
 
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int GC = a.mf.gc, nqc = a.mf.nqc, G = a.Hq / a.Hkv;
-    const int NG = D / a.group;
+    const int GC = a.mf.gc, nqc = a.mf.nqc;
+    const int NG = D / a.group;                  // 1, 2, 4 or 8
+    const int lg_ng = __builtin_ctz(NG);
     const int unit = blockIdx.y, split = blockIdx.x;
     const int qc = unit % nqc;
     const int64_t bh = unit / nqc;
     const int b = static_cast<int>(bh / a.Hkv), hkv = static_cast<int>(bh % a.Hkv);
+    const int G = a.Hq / a.Hkv;
     const int hq0 = hkv * G + qc * GC;
     const int64_t row0 = static_cast<int64_t>(b) * a.Hq + hq0;
     const int64_t t_begin = static_cast<int64_t>(split) * chunk;
     const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
+    const int j = lane % 16, kb = lane / 16;
+
+    unsigned char *vt = smem + wave * WAVE_BYTES;
+    uint32_t *afr = reinterpret_cast<uint32_t *>(vt + VT_BYTES);              // [NGM][64 lanes][4]
+    uint32_t *pst = reinterpret_cast<uint32_t *>(vt + VT_BYTES + AF_BYTES);   // [TK][NGM]
 
     // score operands of this unit (loop invariant)
     v4i aop[MT][S];
@@ -261,11 +312,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
 #pragma unroll
             for (int s = 0; s < S; ++s) aop[mt][s] = src[(mt * S + s) * 64 + lane];
     }
-    const int j = lane % 16, kb = lane / 16, rb = lane / 16;
     float fc[MT], cc[MT], fs[MT], ssq[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int g = 4 * mt + rb;
+        const int g = 4 * mt + kb;
         if (g < GC) {
             const float *sc = a.mf.qscal + (row0 + g) * 4;
             fc[mt] = sc[0];
@@ -276,307 +326,343 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeLaunch a, flo
             fc[mt] = cc[mt] = fs[mt] = ssq[mt] = 0.0f;
         }
     }
-    // rows of absent queries stay zero in the value operands
-    for (int i = tid; i < kMaxNG * 2 * 64 * 4; i += kThreads) (&afr[0][0][0][0])[i] = 0u;
-    if (tid < GCMAX) {
-        s_m[tid] = -INFINITY;
-        s_l[tid] = 0.0f;
-    }
-    // softmax state of this lane's (query 4 mt + rb, key column j): running max
-    // (identical in all lanes of a query), this lane's share of the running sum
-    // and of the zero-point sums
+    // value-product A rows of absent queries stay zero; alphas of absent queries are 1
+    for (int i = lane; i < NGM * 64 * 4; i += 64) afr[i] = 0u;
+    if (lane < kMaxG) s_alpha[wave][lane] = 1.0f;
+
     float m_run[MT], l_run[MT];
-    float zacc[MT][kMaxNG];
+    float zacc[MT][NGM];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         m_run[mt] = -INFINITY;
         l_run[mt] = 0.0f;
 #pragma unroll
-        for (int gg = 0; gg < kMaxNG; ++gg) zacc[mt][gg] = 0.0f;
+        for (int gg = 0; gg < NGM; ++gg) zacc[mt][gg] = 0.0f;
     }
-    // lane (channel column, rb) accumulates queries 2 rb and 2 rb + 1
-    float oacc[NTW][2];
+    // value-product accumulators, rows (query 2 kb + r / 2, fp16 part r % 2),
+    // column j = byte column 16 cb + j, field f; acc1 for tiles whose second
+    // half of columns lies in the next value group
+    v4f acc0[NTILE], acc1[kTwoGroups ? NTILE : 1];
 #pragma unroll
-    for (int x = 0; x < NTW; ++x) oacc[x][0] = oacc[x][1] = 0.0f;
-    __syncthreads();
+    for (int nt = 0; nt < NTILE; ++nt) acc0[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int nt = 0; nt < (kTwoGroups ? NTILE : 1); ++nt) acc1[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Register prefetch of one tile: value code chunk, value params, the key
-    // row slices of this lane's key.  The next tile's loads are issued before
-    // the current tile is computed, so their latency hides behind the work.
-    constexpr int VCH = kKeys * VB / 16;          // 16-byte value chunks per tile
-    constexpr int VCPT = (VCH + kThreads - 1) / kThreads;   // chunks per thread
+    // tr-read row of this lane in every value block: k-slot 8 kb + e holds the
+    // token of slot order; lanes 2r, 2r + 1 address read row r, and row r lands
+    // in half e(r) of the operand with e = {0, 2, 1, 3, 4, 6, 5, 7}
+    const int rr = j / 2;
+    const int e_of_r = (rr & 4) | ((rr & 1) << 1) | ((rr >> 1) & 1);
+    const unsigned char *tr_base = vt + slot_token(8 * kb + e_of_r) * VSTR + 8 * (j % 2);
+
     struct Prefetch {
-        uint4 vcode[VCPT];
-        uint32_t vpar[2];
-        uint32_t cw[NC], sw[NS];
-        float nrm, rho;
+        uint32_t cw[2][NC], sw[2][NS];
+        float nrm[2], rho[2];
+        v4i vcode[VCL];
+        uint32_t par[PD];
     };
+    const int64_t first = t_begin + TK * wave;
+    // Loads of one tile, all unconditional: rows past the valid range are
+    // clamped to the last valid row and masked where they are used; a tile
+    // past the end reloads the wave's first tile.
     auto fetch = [&](int64_t tile0, Prefetch &pf) {
-        const int ntile = static_cast<int>(t_end - tile0 < kKeys ? t_end - tile0 : kKeys);
-        const int64_t n0 = bh * a.T + tile0;
+        const int64_t tc = tile0 < t_end ? tile0 : first;
+        const int nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
+        const int64_t n0 = bh * a.T + tc;
 #pragma unroll
-        for (int k = 0; k < VCPT; ++k) {
-            const int i = tid + k * kThreads;
-            pf.vcode[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < VCH && i / (VB / 16) < ntile) pf.vcode[k] = reinterpret_cast<const uint4 *>(a.vc.codes + n0 * VB)[i];
+        for (int c = 0; c < 2; ++c) {
+            const int t = 16 * c + j;
+            const int64_t n = n0 + (t < nv ? t : nv - 1);
+            const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
+            const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
+#pragma unroll
+            for (int u = 0; u < NC; ++u) pf.cw[c][u] = crow[u];
+#pragma unroll
+            for (int u = 0; u < NS; ++u) pf.sw[c][u] = srow[u];
+            pf.nrm[c] = a.kc.knorm[n];
+            pf.rho[c] = a.kc.rnorm[n];
         }
-        const uint32_t *par = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
+        const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int i = tid + k * kThreads;
-            pf.vpar[k] = (i < ntile * NG) ? par[i] : 0u;
+        for (int v = 0; v < VCL; ++v) {
+            const int i = lane + 64 * v;
+            const int tok = i / (VB / 16);
+            pf.vcode[v] = vsrc[(tok < nv ? tok : nv - 1) * (VB / 16) + i % (VB / 16)];
         }
-        const int t = 16 * wave + j;
-        const bool valid = t < ntile;
-        const int64_t n = n0 + (valid ? t : 0);
-        const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
+        const uint32_t *psrc = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
+        const int plim = nv * NG - 1;
 #pragma unroll
-        for (int u = 0; u < NC; ++u) pf.cw[u] = valid ? crow[u] : 0u;
-#pragma unroll
-        for (int u = 0; u < NS; ++u) pf.sw[u] = valid ? srow[u] : 0u;
-        pf.nrm = valid ? a.kc.knorm[n] : 0.0f;
-        pf.rho = valid ? a.kc.rnorm[n] : 0.0f;
+        for (int k = 0; k < PD; ++k) {
+            const int idx = lane + 64 * k;
+            pf.par[k] = psrc[idx < plim ? idx : plim];
+        }
     };
-    Prefetch pre;
-    if (t_begin < t_end) fetch(t_begin, pre);
 
-    for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kKeys) {
-        const int ntile = static_cast<int>(t_end - tile0 < kKeys ? t_end - tile0 : kKeys);
-        const Prefetch cur = pre;
-        if (tile0 + kKeys < t_end) fetch(tile0 + kKeys, pre);
-        // ---- stage the value tile (code rows, fp32 scale / zero)
+    auto compute = [&](int64_t tile0, const Prefetch &cur) {
+        const int nv = static_cast<int>(t_end - tile0 < TK ? t_end - tile0 : TK);
+        // ---- value codes and (scale, zero) words of the tile into this wave's LDS
 #pragma unroll
-        for (int k = 0; k < VCPT; ++k) {
-            const int i = tid + k * kThreads;
-            if (i < VCH) *reinterpret_cast<uint4 *>(vtile + (i / (VB / 16)) * VSTR + (i % (VB / 16)) * 16) = cur.vcode[k];
+        for (int v = 0; v < VCL; ++v) {
+            const int i = lane + 64 * v;
+            *reinterpret_cast<v4i *>(vt + (i / (VB / 16)) * VSTR + (i % (VB / 16)) * 16) = cur.vcode[v];
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int i = tid + k * kThreads;
-            if (i < kKeys * NG)
-                vsz[i] = make_float2(f16_bits_to_f32(cur.vpar[k] & 0xffffu), f16_bits_to_f32(cur.vpar[k] >> 16));
+        for (int k = 0; k < PD; ++k) {
+            const int idx = lane + 64 * k;
+            if (idx < TK * NG) pst[(idx >> lg_ng) * NGM + (idx & (NG - 1))] = idx < nv * NG ? cur.par[k] : 0u;
         }
-        // ---- scores of keys 16 wave + j: 4 lanes (kb) split each key row
-        float lamr[MT];
-        {
-            const int t = 16 * wave + j;
-            const bool valid = t < ntile;
+
+        // ---- scores of keys j and 16 + j: B bytes are raw key bits at weight
+        // 2^k (mask without shift; the digit rows carry the 2^-k)
+        float lamv[MT][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
             v4i accc[MT], accs[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) accc[mt] = accs[mt] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int s = 0; s < SC; ++s) {
-                const uint32_t dw = cur.cw[s / 2];
+                const uint32_t dw = cur.cw[c][s / 2];
                 const int h = 4 * (s % 2);
-                const v4i bop = {static_cast<int>((dw >> h) & 0x01010101u), static_cast<int>((dw >> (h + 1)) & 0x01010101u),
-                                 static_cast<int>((dw >> (h + 2)) & 0x01010101u), static_cast<int>((dw >> (h + 3)) & 0x01010101u)};
+                const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                                 static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     accc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][s], bop, accc[mt], 0, 0, 0);
             }
 #pragma unroll
             for (int s = 0; s < SS; ++s) {
-                const uint32_t dw = cur.sw[s / 2];
+                const uint32_t dw = cur.sw[c][s / 2];
                 const int h = 4 * (s % 2);
-                const v4i bop = {static_cast<int>((dw >> h) & 0x01010101u), static_cast<int>((dw >> (h + 1)) & 0x01010101u),
-                                 static_cast<int>((dw >> (h + 2)) & 0x01010101u), static_cast<int>((dw >> (h + 3)) & 0x01010101u)};
+                const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                                 static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     accs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][SC + s], bop, accs[mt], 0, 0, 0);
             }
-            // lane (key j, row block rb) holds the four digits of query 4 mt + rb;
-            // per-wave partial maxima over the 16 key columns
+            // lane (key column j, row block kb) holds the four digits of query 4 mt + kb
+            const bool valid = 16 * c + j < nv;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
                 const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
-                const float score = cur.nrm * fmaf(kappa * cur.rho, dsign, dcode);
-                lamr[mt] = (valid && 4 * mt + rb < GC) ? a.scale * score : -INFINITY;
-                float pm = lamr[mt];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) pm = fmaxf(pm, __shfl_xor(pm, off));
-                if (j == 0) pmax[wave][4 * mt + rb] = pm;
+                const float score = cur.nrm[c] * fmaf(kappa * cur.rho[c], dsign, dcode);
+                lamv[mt][c] = (valid && 4 * mt + kb < GC) ? a.scale * score : -INFINITY;
             }
         }
-        __syncthreads();
-        // ---- online softmax and value-product operands, per (query, key) lane:
-        // p = e^(lambda - m), w = p * scale as fp16 hi + lo into row 2 g + part of
-        // the A fragment at the token's k position (tr-read order {0,2|1,3|4,6|5,7})
-        {
-            const int t = 16 * wave + j;
-            const int ks = t / 32, kbq = (t % 32) / 8, tau = t % 8;
-            const int u = 2 * (tau / 4) + (tau % 2), half = (tau % 4) / 2;
+
+        // ---- online softmax (per query, over the 16 lanes of its row block)
+        bool grow = false;
+        float m_new[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            m_new[mt] = fmaxf(m_run[mt], row16_max(fmaxf(lamv[mt][0], lamv[mt][1])));
+            grow |= m_new[mt] > m_run[mt];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // the running maximum moved: rescale this wave's sums and accumulators
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int g = 4 * mt + rb;
-                if (g < GC) {
-                    const float tmax = fmaxf(fmaxf(pmax[0][g], pmax[1][g]), fmaxf(pmax[2][g], pmax[3][g]));
-                    const float m_new = fmaxf(m_run[mt], tmax);
-                    float alpha = 1.0f, p = 0.0f;
-                    if (m_new != -INFINITY) {
-                        alpha = __expf(m_run[mt] - m_new);
-                        p = __expf(lamr[mt] - m_new);
-                    }
-                    m_run[mt] = m_new;
-                    l_run[mt] = fmaf(l_run[mt], alpha, p);
-                    if (wave == 0 && j == 0) s_alpha[g] = alpha;
-                    uint16_t *arow = reinterpret_cast<uint16_t *>(&afr[0][ks][16 * kbq + 2 * g][u]) + half;
+                const float alpha = (m_new[mt] > m_run[mt]) ? __expf(m_run[mt] - m_new[mt]) : 1.0f;
+                l_run[mt] *= alpha;
 #pragma unroll
-                    for (int gg = 0; gg < kMaxNG; ++gg) {
-                        if (gg < NG) {
-                            const float2 sz = vsz[t * NG + gg];
-                            zacc[mt][gg] = fmaf(p, sz.y, zacc[mt][gg] * alpha);
-                            const float w = p * sz.x;
-                            const auto hi = __builtin_amdgcn_cvt_pkrtz(w, 0.0f);
-                            const auto lo = __builtin_amdgcn_cvt_pkrtz(w - static_cast<float>(hi[0]), 0.0f);
-                            // afr[gg][ks][row][u]: rows 2 g (hi) and 2 g + 1 (lo)
-                            arow[gg * (2 * 64 * 4 * 2)] = __builtin_bit_cast(uint32_t, hi) & 0xffffu;
-                            arow[gg * (2 * 64 * 4 * 2) + 4 * 2] = __builtin_bit_cast(uint32_t, lo) & 0xffffu;
-                        }
-                    }
+                for (int gg = 0; gg < NGM; ++gg) zacc[mt][gg] *= alpha;
+                if (j == 0) s_alpha[wave][4 * mt + kb] = alpha;
+                m_run[mt] = m_new[mt];
+            }
+            const float a0 = s_alpha[wave][2 * kb], a1 = s_alpha[wave][2 * kb + 1];
+#pragma unroll
+            for (int nt = 0; nt < NTILE; ++nt) {
+                acc0[nt][0] *= a0; acc0[nt][1] *= a0; acc0[nt][2] *= a1; acc0[nt][3] *= a1;
+            }
+#pragma unroll
+            for (int nt = 0; nt < (kTwoGroups ? NTILE : 1); ++nt) {
+                acc1[nt][0] *= a0; acc1[nt][1] *= a0; acc1[nt][2] *= a1; acc1[nt][3] *= a1;
+            }
+        }
+        float p[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float mref = m_run[mt] == -INFINITY ? 0.0f : m_run[mt];
+            p[mt][0] = __expf(lamv[mt][0] - mref);
+            p[mt][1] = __expf(lamv[mt][1] - mref);
+            l_run[mt] += p[mt][0] + p[mt][1];
+        }
+
+        // ---- value-product A operand: p * scale as fp16 hi + lo in rows 2 q and
+        // 2 q + 1, tokens j and 16 + j packed in dword j % 4 of k-block j / 4
+        uint32_t pr[2][NGM];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int k = 0; k < NGM / 4; ++k) {
+                const v4i w4 = *reinterpret_cast<const v4i *>(pst + (16 * c + j) * NGM + 4 * k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pr[c][4 * k + e] = static_cast<uint32_t>(w4[e]);
+            }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int q = 4 * mt + kb;
+            uint32_t *dst = afr + ((2 * q + 16 * (j / 4)) * 4 + (j % 4));
+#pragma unroll
+            for (int gg = 0; gg < NGM; ++gg) {
+                if (gg < NG) {
+                    const float w0 = p[mt][0] * f16_bits_to_f32(pr[0][gg] & 0xffffu);
+                    const float w1 = p[mt][1] * f16_bits_to_f32(pr[1][gg] & 0xffffu);
+                    zacc[mt][gg] = fmaf(p[mt][0], f16_bits_to_f32(pr[0][gg] >> 16),
+                                        fmaf(p[mt][1], f16_bits_to_f32(pr[1][gg] >> 16), zacc[mt][gg]));
+                    const auto hi = __builtin_amdgcn_cvt_pkrtz(w0, w1);
+                    const auto lo = __builtin_amdgcn_cvt_pkrtz(w0 - static_cast<float>(hi[0]), w1 - static_cast<float>(hi[1]));
+                    dst[gg * 256] = __builtin_bit_cast(uint32_t, hi);
+                    dst[gg * 256 + 4] = __builtin_bit_cast(uint32_t, lo);
                 }
             }
         }
-        __syncthreads();
-        // ---- value product: wave w handles channel tiles w, w + 4, ...
+
+        // ---- value product over the 32 tokens, all channel tiles
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int nt = wave + 4 * x;
-            if (nt < NTILE) {
-                const int cb = nt / NF, f = nt % NF;
-                const int pl = lane % 16;
-                const int sh = VBITS * f;
-                const uint32_t fm = (VBITS == 4 ? 0x000F000Fu : 0x00030003u);
-                // column i = byte column 16 cb + i -> channel NF (16 cb + i) + f
-                const int ch = NF * (16 * cb + j) + f;
-                const int g_lo = (NF * 16 * cb) / a.group;
-                const bool two = NF * 16 > a.group;          // the tile spans two value groups
-                v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int g_lo = (NF * 16 * cb) >> (__builtin_ctz(a.group));
+            const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + g_lo * 256 + lane * 4));
+            v8h af1 = af0;
+            if (kTwoGroups && NF * 16 > a.group)
+                af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + (g_lo + 1) * 256 + lane * 4));
+            const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(tr_base + 16 * cb));
+            const uint32_t x0 = static_cast<uint32_t>(raw.x), x1 = static_cast<uint32_t>(raw.y);
+            const uint32_t y0 = x0 >> 8, y1 = x1 >> 8;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const unsigned char *base = vtile + (32 * ks + 8 * kb + pl / 2) * VSTR + 16 * cb + 8 * (pl % 2);
-                    const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(base));
-                    const uint32_t x0 = static_cast<uint32_t>(raw.x), x1 = static_cast<uint32_t>(raw.y);
-                    const v4i bop = {static_cast<int>((x0 >> sh) & fm), static_cast<int>((x0 >> (8 + sh)) & fm),
-                                     static_cast<int>((x1 >> sh) & fm), static_cast<int>((x1 >> (8 + sh)) & fm)};
-                    const v8h bh = __builtin_bit_cast(v8h, bop);
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(&afr[g_lo][ks][lane][0])), bh, acc0, 0, 0, 0);
-                    if (two)
-                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(&afr[g_lo + 1][ks][lane][0])), bh, acc1, 0, 0, 0);
-                }
-                const v4f acc = (two && ch / a.group != g_lo) ? acc1 : acc0;
-                // rows 4 rb .. 4 rb + 3 = (query 2 rb, hi), (2 rb, lo), (2 rb + 1, hi), (2 rb + 1, lo)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int g = 2 * rb + q;
-                    const float alpha = (g < GC) ? s_alpha[g] : 1.0f;
-                    oacc[x][q] = fmaf(oacc[x][q], alpha, 16777216.0f * (acc[2 * q] + acc[2 * q + 1]));
-                }
+            for (int f = 0; f < NF; ++f) {
+                // field f of every byte, in place: the fp16 subnormal code * 2^(VBITS f - 24)
+                const uint32_t fm = (VBITS == 4 ? 0x000F000Fu : 0x00030003u) << (VBITS * f);
+                const v4i bop = {static_cast<int>(x0 & fm), static_cast<int>(y0 & fm),
+                                 static_cast<int>(x1 & fm), static_cast<int>(y1 & fm)};
+                const v8h bv = __builtin_bit_cast(v8h, bop);
+                const int nt = cb * NF + f;
+                acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af0, bv, acc0[nt], 0, 0, 0);
+                if (kTwoGroups && NF * 16 > a.group)
+                    acc1[kTwoGroups ? nt : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bv, acc1[kTwoGroups ? nt : 0], 0, 0, 0);
             }
         }
-        __syncthreads();
+    };
+
+    // two tiles per trip, the loads of each issued one tile ahead; an odd
+    // last tile is computed after the loop
+    if (first < t_end) {
+        Prefetch pa, pb;
+        fetch(first, pa);
+        int64_t t = first;
+        for (; t + 4 * TK < t_end; t += 8 * TK) {
+            fetch(t + 4 * TK, pb);
+            compute(t, pa);
+            fetch(t + 8 * TK, pa);
+            compute(t + 4 * TK, pb);
+        }
+        if (t < t_end) compute(t, pa);
     }
 
-    // ---- this split's partials: m, l per query; acc[c] = value sum + zero-point sum.
-    // l and the zero-point sums are spread over the 16 key columns of each wave
-    // and over the 4 waves: reduce across j, then across waves.
+    // ---- merge the four waves: m, l, zero-point sums and value sums per query
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int g = 4 * mt + rb;
-        float l = l_run[mt];
+        const int g = 4 * mt + kb;
+        const float l = row16_sum(l_run[mt]);
+        if (j == 0) {
+            s_wm[wave][g] = m_run[mt];
+            s_wl[wave][g] = l;
+        }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off);
-        if (j == 0 && g < GC) psum[wave][g] = l;
-        if (wave == 0 && j == 0 && g < GC) s_m[g] = m_run[mt];
+        for (int gg = 0; gg < NGM; ++gg) {
+            const float z = row16_sum(zacc[mt][gg]);
+            if (j == 0) s_wz[wave][g][gg] = z;
+        }
+    }
+    __syncthreads();        // every wave is done with its tile buffers
+    float *wo = reinterpret_cast<float *>(smem);      // [4 waves][kMaxG][D]
 #pragma unroll
-        for (int gg = 0; gg < kMaxNG; ++gg) {
-            if (gg < NG) {
-                float z = zacc[mt][gg];
+    for (int nt = 0; nt < NTILE; ++nt) {
+        const int cb = nt / NF, f = nt % NF;
+        const int ch = NF * (16 * cb + j) + f;
+        const int g_lo = (NF * 16 * cb) / a.group;
+        const v4f acc = (kTwoGroups && NF * 16 > a.group && ch / a.group != g_lo) ? acc1[kTwoGroups ? nt : 0] : acc0[nt];
+        const float sc = 16777216.0f / static_cast<float>(1 << (VBITS * f));
 #pragma unroll
-                for (int off = 1; off < 16; off <<= 1) z += __shfl_xor(z, off);
-                if (j == 0 && g < GC) vsz[(wave * GCMAX + g) * kMaxNG + gg].x = z;
+        for (int qq = 0; qq < 2; ++qq) {
+            const int g = 2 * kb + qq;
+            wo[(wave * kMaxG + g) * D + ch] = sc * (acc[2 * qq] + acc[2 * qq + 1]);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < GC * D; i += kThreads) {
+        const int g = i / D, ch = i % D, grp = ch / a.group;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_wm[w][g]);
+        float l = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float e = (s_wm[w][g] == -INFINITY) ? 0.0f : __expf(s_wm[w][g] - mx);
+            l = fmaf(e, s_wl[w][g], l);
+            o = fmaf(e, wo[(w * kMaxG + g) * D + ch] + s_wz[w][g][grp], o);
+        }
+        if (a.splits == 1) {
+            a.out[(row0 + g) * D + ch] = l > 0.0f ? o / l : 0.0f;
+        } else {
+            a.part_acc[((row0 + g) * a.splits + split) * D + ch] = o;
+            if (ch == 0) {
+                a.part_ml[((row0 + g) * a.splits + split) * 2 + 0] = mx;
+                a.part_ml[((row0 + g) * a.splits + split) * 2 + 1] = l;
             }
         }
     }
+}
+
+// ------------------------------------------------------------ split merge
+// One workgroup per query row: out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
+// (M the largest split maximum), split weights staged through LDS 256 at a time.
+__global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
+{
+    __shared__ float red[kThreads / 64];
+    __shared__ float wts[kThreads];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int64_t row = blockIdx.x;
+    const int S = a.splits, D = a.d;
+    const float *ml = a.part_ml + row * S * 2;
+    float mx = -INFINITY;
+    for (int s = tid; s < S; s += kThreads)
+        if (ml[2 * s + 1] > 0.0f) mx = fmaxf(mx, ml[2 * s]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
-    if (tid < GC) {
-        s_l[tid] = psum[0][tid] + psum[1][tid] + psum[2][tid] + psum[3][tid];
-        for (int gg = 0; gg < NG; ++gg) {
-            float z = 0.0f;
-            for (int w = 0; w < 4; ++w) z += vsz[(w * GCMAX + tid) * kMaxNG + gg].x;
-            zsum[tid][gg] = z;
-        }
-    }
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
+    float l = 0.0f;
+    for (int s = tid; s < S; s += kThreads)
+        if (ml[2 * s + 1] > 0.0f) l = fmaf(ml[2 * s + 1], __expf(ml[2 * s] - mx), l);
+    l = wave_sum(l);
+    if (lane == 0) red[wave] = l;
+    __syncthreads();
+    l = red[0] + red[1] + red[2] + red[3];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float *pa = a.part_acc + row * S * D;
+    float o = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += kThreads) {
+        __syncthreads();
+        const int s = s0 + tid;
+        wts[tid] = (s < S && ml[2 * s + 1] > 0.0f) ? __expf(ml[2 * s] - mx) * inv : 0.0f;
+        __syncthreads();
+        const int n = S - s0 < kThreads ? S - s0 : kThreads;
+        if (tid < D) {
+            int k = 0;
+            for (; k + 8 <= n; k += 8) {
+                float v[8];
 #pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int nt = wave + 4 * x;
-        if (nt < NTILE) {
-            const int cb = nt / NF, f = nt % NF;
-            const int ch = NF * (16 * cb + j) + f;
+                for (int u = 0; u < 8; ++u) v[u] = pa[static_cast<int64_t>(s0 + k + u) * D + tid];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int g = 2 * rb + q;
-                if (g < GC)
-                    a.part_acc[((row0 + g) * a.splits + split) * D + ch] = oacc[x][q] + zsum[g][ch / a.group];
+                for (int u = 0; u < 8; ++u) o = fmaf(wts[k + u], v[u], o);
             }
+            for (; k < n; ++k) o = fmaf(wts[k], pa[static_cast<int64_t>(s0 + k) * D + tid], o);
         }
     }
-    if (tid < GC) {
-        a.part_ml[((row0 + tid) * a.splits + split) * 2 + 0] = s_m[tid];
-        a.part_ml[((row0 + tid) * a.splits + split) * 2 + 1] = s_l[tid];
-    }
-    // ---- the last workgroup of this unit merges the splits
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.mf.counters + unit, 1) == a.splits - 1) ? 1 : 0;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // pass 1: one wave per query turns the split maxima and sums into weights
-    // w_s = e^(m_s - M) / sum_s' l_s' e^(m_s' - M)   (splits <= 64, lane = split)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int g = wave + 4 * q;
-        if (g < GC) {
-            const float *ml = a.part_ml + (row0 + g) * a.splits * 2;
-            float m = -INFINITY, l = 0.0f;
-            if (lane < a.splits) {
-                m = ml[2 * lane];
-                l = ml[2 * lane + 1];
-            }
-            const float mx = wave_max(l > 0.0f ? m : -INFINITY);
-            const float w = (l > 0.0f) ? expf(m - mx) : 0.0f;
-            const float den = wave_sum(l * w);
-            lam[g][lane] = den > 0.0f ? w / den : 0.0f;
-        }
-    }
-    __syncthreads();
-    // pass 2: out[g][c..c+3] = sum_s w_s acc_s[c..c+3], sixteen splits' loads in flight
-    for (int i = tid; i < GC * (D / 4); i += kThreads) {
-        const int g = i / (D / 4), c4 = i % (D / 4);
-        const float4 *pa = reinterpret_cast<const float4 *>(a.part_acc + (row0 + g) * a.splits * D) + c4;
-        float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int s0 = 0; s0 < a.splits; s0 += 16) {
-            float4 v[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                v[k] = (s0 + k < a.splits) ? pa[static_cast<int64_t>(s0 + k) * (D / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float w = (s0 + k < a.splits) ? lam[g][s0 + k] : 0.0f;
-                o.x = fmaf(w, v[k].x, o.x);
-                o.y = fmaf(w, v[k].y, o.y);
-                o.z = fmaf(w, v[k].z, o.z);
-                o.w = fmaf(w, v[k].w, o.w);
-            }
-        }
-        reinterpret_cast<float4 *>(a.out + (row0 + g) * D)[c4] = o;
-    }
-    if (tid == 0) a.mf.counters[unit] = 0;
+    if (tid < D) a.out[row * D + tid] = o;
 }
 
 template <int BITS, int D, int MT, int VBITS>
@@ -586,6 +672,12 @@ hipError_t launch_mfma_t(const DecodeLaunch &a, hipStream_t stream, float kappa,
     void *tok;
     prof_begin("tq_attend_splitk", stream, &tok);
     hipLaunchKernelGGL((k_attend_mfma<BITS, D, MT, VBITS>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    prof_end(tok, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    prof_begin("tq_merge_splits", stream, &tok);
+    hipLaunchKernelGGL(k_merge_splits, dim3(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq)), dim3(kThreads), 0,
+                       stream, a);
     prof_end(tok, stream);
     return hipGetLastError();
 }
@@ -641,8 +733,8 @@ hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / a.m);
-    const int64_t tiles = (a.T + kKeys - 1) / kKeys;
-    const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kKeys;
+    const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
+    const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kMfmaTile;
     return a.bits == 1 ? launch_mfma_d<1>(a, stream, kappa, chunk) : launch_mfma_d<2>(a, stream, kappa, chunk);
 }
 

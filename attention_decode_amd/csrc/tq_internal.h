@@ -83,7 +83,6 @@ struct MfmaArgs {
     int units = 0;              // B * Hkv * nqc
     uint32_t *aops = nullptr;   // [units][mt][steps][64 lanes][4 dwords] score digit operands
     float *qscal = nullptr;     // [B, Hq, 4] fixed-point scales, constant terms
-    int *counters = nullptr;    // [units] split-completion counters
 };
 
 struct DecodeLaunch {
@@ -117,8 +116,7 @@ int query_chunk(int G);
 constexpr int kDecodeTile = 256;   // keys per decode tile
 
 // matrix-core decode path (k_attend_mfma.hip): keys with 1-2 bits, d 128/256
-constexpr int kMfmaTile = 64;      // keys per tile
-constexpr int kMfmaMaxSplits = 64; // splits merged by one wave per query
+constexpr int kMfmaTile = 128;     // keys per workgroup step (four waves x 32)
 bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
 int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits);

@@ -122,9 +122,9 @@ def test_split_policy_and_workspace():
     # one long sequence with 8 KV heads spreads over many splits
     s = lib.tq_attend_splits(ctypes.byref(kf), 1, 64, 8, 1 << 20)
     assert 64 <= s <= 1024
-    # never more splits than tiles: 64 keys on the matrix-core path (1-2 bit
+    # never more splits than tiles: 128 keys on the matrix-core path (1-2 bit
     # keys), 256 on the general path (3-bit keys here)
-    assert lib.tq_attend_splits(ctypes.byref(kf), 1, 4, 1, 300) == 5
+    assert lib.tq_attend_splits(ctypes.byref(kf), 1, 4, 1, 300) == 3
     kf3 = _kf(mse_bits=3)
     assert lib.tq_attend_splits(ctypes.byref(kf3), 1, 4, 1, 300) == 2
     assert lib.tq_attend_splits(ctypes.byref(kf), 1, 4, 1, 0) == 1
