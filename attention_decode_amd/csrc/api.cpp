@@ -441,7 +441,7 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     p.mfma = tq::mfma_decode_supported(fmt->d, fmt->mse_bits, G, 2, 32);
     p.gc = p.mfma ? tq::mfma_query_chunk(G) : tq::query_chunk(G);
     p.nqc = G / p.gc;
-    p.mt = (p.gc + 3) / 4;
+    p.mt = p.mfma ? tq::mfma_row_tiles(fmt->mse_bits, p.gc) : (p.gc + 3) / 4;
     p.units = B * Hkv * p.nqc;
     p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits) : 0;
     const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;

@@ -51,19 +51,6 @@ constexpr int kMaxNG = 8;          // value groups per vector (d / group)
 __host__ __device__ constexpr int code_dwords(int d, int bits) { return d * bits / 128; }
 __host__ __device__ constexpr int sign_dwords(int d) { return d / 128; }
 
-// balanced base-128 digit k of x (|x| < 2^27): x = sum_k digit_k 128^k, digits in [-64, 64]
-__device__ __forceinline__ int digit7(int x, int k)
-{
-    int d = 0;
-#pragma unroll
-    for (int i = 0; i <= 3; ++i) {
-        d = ((x + 64) & 127) - 64;
-        if (i == k) break;
-        x = (x - d) >> 7;
-    }
-    return (k == 3) ? x : d;
-}
-
 // value of a limb-row quadruple: c0 + 128 c1 + 128^2 c2 + 128^3 c3 (each |c| < 2^23,
 // so the two pair sums are exact in int32)
 __device__ __forceinline__ float limbs_to_float(v4i c)
@@ -86,149 +73,260 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-__device__ __forceinline__ float load1(const float *p) { return *p; }
-__device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(p->bits); }
-__device__ __forceinline__ float load1(const f16_t *p) { return f16_bits_to_f32(p->bits); }
-
-// ---------------------------------------------------------------- q-prep
-// One workgroup per query row (b, hq): q_rot = Pi q and Sq = (S Pi) q as two
-// coalesced float4 matrix-vector products with every load of a pass in
-// flight, then this query's fixed-point digit operands (its four rows of the
-// score products), its scalars, and (first query of a unit) the zeroed split
-// counter and the zero rows of absent queries.
-template <typename TIn>
-__global__ __launch_bounds__(kThreads) void k_qprep_mfma(DecodeLaunch a)
-{
-    __shared__ float qs[256];
-    __shared__ float part[2][8][256];
-    __shared__ float qr[256], sq[256];
-    __shared__ float red[4];
-    __shared__ float s_acoef[2];
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int D = a.d, M = a.m;
-    const int64_t row = blockIdx.x;                 // b * Hq + hq
-    const int b = static_cast<int>(row / a.Hq), hq = static_cast<int>(row % a.Hq);
-    const int G = a.Hq / a.Hkv, hkv = hq / G, gi = hq % G;
-    const int GC = a.mf.gc, qc = gi / GC, g = gi % GC;
-    const int MT = a.mf.mt;
-    const int unit = (b * a.Hkv + hkv) * a.mf.nqc + qc;
-
-    for (int i = tid; i < D; i += kThreads) qs[i] = load1(static_cast<const TIn *>(a.q) + row * D + i);
-    if (tid == 0) {
-        // bit-affine form of the codebook (exact for symmetric codebooks)
-        s_acoef[0] = a.centroids[1] - a.centroids[0];
-        s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
-    }
-    __syncthreads();
-    {
-        const int NQ = D / 4, RG = kThreads / NQ;
-        const int c4 = tid % NQ, rg = tid / NQ;
-        const float4 *p1 = reinterpret_cast<const float4 *>(a.piT);
-        const float4 *p2 = reinterpret_cast<const float4 *>(a.spiT);
-        float4 y1 = make_float4(0.f, 0.f, 0.f, 0.f), y2 = y1;
-#pragma unroll 16
-        for (int jj = rg; jj < D; jj += RG) {
-            const float4 u = p1[jj * NQ + c4], v = p2[jj * NQ + c4];
-            const float qj = qs[jj];
-            y1.x = fmaf(u.x, qj, y1.x); y1.y = fmaf(u.y, qj, y1.y);
-            y1.z = fmaf(u.z, qj, y1.z); y1.w = fmaf(u.w, qj, y1.w);
-            y2.x = fmaf(v.x, qj, y2.x); y2.y = fmaf(v.y, qj, y2.y);
-            y2.z = fmaf(v.z, qj, y2.z); y2.w = fmaf(v.w, qj, y2.w);
-        }
-        *reinterpret_cast<float4 *>(&part[0][rg][4 * c4]) = y1;
-        *reinterpret_cast<float4 *>(&part[1][rg][4 * c4]) = y2;
-        __syncthreads();
-        if (tid < D) {
-            float s1 = 0.0f, s2 = 0.0f;
-            for (int r = 0; r < RG; ++r) {
-                s1 += part[0][r][tid];
-                s2 += part[1][r][tid];
-            }
-            qr[tid] = s1;
-            sq[tid] = s2;
-        }
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const float *v = wave == 0 ? qr : sq;
-        const int n = wave == 0 ? D : M;
-        float mx = 0.0f, sum = 0.0f;
-        for (int j = lane; j < n; j += 64) {
-            mx = fmaxf(mx, fabsf(v[j]));
-            sum += v[j];
-        }
-        mx = wave_max(mx);
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            red[2 * wave] = mx;
-            red[2 * wave + 1] = sum;
-        }
-    }
-    __syncthreads();
-    const float mw = red[0] * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1]));
-    int ec = 0, es = 0;
-    frexpf(mw, &ec);          // mw < 2^ec
-    frexpf(red[2], &es);
-    const int fc = (mw > 0.0f) ? 26 - ec : 0;
-    const int fs = (red[2] > 0.0f) ? 26 - es : 0;
-    if (tid == 0) {
-        float *sc = a.mf.qscal + row * 4;
-        sc[0] = ldexpf(1.0f, -fc);
-        sc[1] = a.centroids[0] * red[1];
-        sc[2] = ldexpf(1.0f, -fs);
-        sc[3] = red[3];
-    }
-    // this query's digit rows: lanes 16 kb + 4 (g % 4) + digit of row tile g / 4;
-    // dword r of a lane holds elements 4r..4r+3 of its 16-element k-block
-    const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
-    const int S = 2 * nc + 2 * ns;
-    uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
-    for (int w = tid; w < S * 64; w += kThreads) {
-        const int r = w % 4, limb = (w / 4) % 4, kb = (w / 16) % 4, s = w / 64;
-        const int l = 16 * kb + 4 * (g % 4) + limb;
-        uint32_t dw = 0;
-#pragma unroll
-        for (int K = 0; K < 4; ++K) {
-            float wv;
-            int f;
-            if (s < 2 * nc) {
-                const int u = s / 2, h = s % 2;
-                const int bit = 32 * (kb * nc + u) + 8 * K + 4 * h + r;
-                wv = qr[bit / a.bits] * s_acoef[bit % a.bits];
-                f = fc;
-            } else {
-                const int s2 = s - 2 * nc, u = s2 / 2, h = s2 % 2;
-                const int bit = 32 * (kb * ns + u) + 8 * K + 4 * h + r;
-                wv = sq[bit];
-                f = fs;
-            }
-            // the key bit arrives as byte 2^sh (masked in place, not shifted):
-            // weight w 2^-sh, negated for sh = 7 where the byte reads as -128
-            const int sh = 4 * (s % 2) + r;
-            int x = static_cast<int>(rintf(ldexpf(wv, f - sh)));
-            if (sh == 7) x = -x;
-            dw |= (static_cast<uint32_t>(digit7(x, limb)) & 0xffu) << (8 * K);
-        }
-        out[((g / 4) * S + s) * 256 + l * 4 + r] = dw;
-    }
-    if (g == 0) {
-        // rows of absent queries (unit with fewer than four query heads) stay zero
-        for (int w = tid; w < S * 64 * 4; w += kThreads) {
-            const int l = (w / 4) % 64;
-            if ((l % 16) / 4 >= GC) out[(w / 256) * 256 + (w % 256)] = 0u;
-        }
-    }
-}
-
-// ------------------------------------------------------------ attention
-// 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(p->bits); }
+__device__ __forceinline__ float load1(const f16_t *p) { return f16_bits_to_f32(p->bits); }
+
+// ---------------------------------------------------------------- q-prep
+// One workgroup per unit (sequence, KV head, query chunk).  q_rot = Pi q and
+// Sq = (S Pi) q for the unit's GC queries: thread (column block c4, row group
+// rg = tid % 8) sums rows rg, rg + 8, ... of four adjacent columns of Pi^T
+// and of (S Pi)^T for every query (each matrix row is one coalesced read
+// shared by all queries); the eight row groups of a column block are
+// adjacent lanes, summed with DPP.  Leaves qv[g] = [q_rot | Sq].
+template <typename TIn>
+__device__ void rotate_unit_queries(const DecodeLaunch &a, int GC, int64_t row0, float (*qs)[256], float (*qv)[512])
+{
+    const int tid = threadIdx.x;
+    const int D = a.d, M = a.m;
+    for (int i = tid; i < GC * D; i += kThreads)
+        qs[i / D][i % D] = load1(static_cast<const TIn *>(a.q) + (row0 + i / D) * D + i % D);
+    __syncthreads();
+    const int rg = tid % 8;
+    for (int c4 = tid / 8; c4 < D / 4; c4 += kThreads / 8) {
+        float acc[2][4][kMaxG];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int g = 0; g < kMaxG; ++g) acc[m][e][g] = 0.0f;
+        const float4 *p1 = reinterpret_cast<const float4 *>(a.piT) + c4;
+        const float4 *p2 = reinterpret_cast<const float4 *>(a.spiT) + c4;
+        for (int j0 = 0; j0 < D; j0 += 64) {
+            float4 u[8], v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int jj = j0 + rg + 8 * i;
+                u[i] = p1[static_cast<int64_t>(jj) * (D / 4)];
+                v[i] = p2[static_cast<int64_t>(jj) * (M / 4)];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int jj = j0 + rg + 8 * i;
+#pragma unroll
+                for (int g = 0; g < kMaxG; ++g) {
+                    if (g < GC) {
+                        const float qj = qs[g][jj];
+                        acc[0][0][g] = fmaf(u[i].x, qj, acc[0][0][g]);
+                        acc[0][1][g] = fmaf(u[i].y, qj, acc[0][1][g]);
+                        acc[0][2][g] = fmaf(u[i].z, qj, acc[0][2][g]);
+                        acc[0][3][g] = fmaf(u[i].w, qj, acc[0][3][g]);
+                        acc[1][0][g] = fmaf(v[i].x, qj, acc[1][0][g]);
+                        acc[1][1][g] = fmaf(v[i].y, qj, acc[1][1][g]);
+                        acc[1][2][g] = fmaf(v[i].z, qj, acc[1][2][g]);
+                        acc[1][3][g] = fmaf(v[i].w, qj, acc[1][3][g]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int g = 0; g < kMaxG; ++g) {
+                    if (g < GC) {
+                        float x = acc[m][e][g];
+                        x += dpp<0xB1>(x);          // xor 1
+                        x += dpp<0x4E>(x);          // xor 2
+                        x += dpp<0x141>(x);         // half-row mirror: lane i <-> 7 - i
+                        if (rg == 0) qv[g][m * D + 4 * c4 + e] = x;
+                    }
+                }
+    }
+    __syncthreads();
+}
+
+// unit index -> first query row
+__device__ __forceinline__ int64_t unit_row0(const DecodeLaunch &a, int unit)
+{
+    const int qc = unit % a.mf.nqc, bh = unit / a.mf.nqc;
+    const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+    return static_cast<int64_t>(b) * a.Hq + hkv * (a.Hq / a.Hkv) + qc * a.mf.gc;
+}
+
+// Bit-plane score operands (keys with 1 or 2 bits): per query the fixed-point
+// scales and constant terms, and the int8 digit rows of the score products.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void k_qprep_bits(DecodeLaunch a)
+{
+    __shared__ float qs[kMaxG][256];
+    __shared__ float qv[kMaxG][512];           // [q_rot (D) | Sq (M)] per query
+    __shared__ int s_f[kMaxG][2];              // fixed-point exponents (code rows, sign rows)
+    __shared__ float s_acoef[2];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int D = a.d, M = a.m;
+    const int GC = a.mf.gc, MT = a.mf.mt;
+    const int unit = blockIdx.x;
+    const int64_t row0 = unit_row0(a, unit);
+    if (tid == 0) {
+        // bit-affine form of the codebook (exact for symmetric codebooks)
+        s_acoef[0] = a.centroids[1] - a.centroids[0];
+        s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
+    }
+    rotate_unit_queries<TIn>(a, GC, row0, qs, qv);
+    // per-query maxima and sums, one wave per query
+    for (int g = wave; g < GC; g += 4) {
+        float mc = 0.0f, sc = 0.0f, ms = 0.0f, ss = 0.0f;
+        for (int j = lane; j < D; j += 64) {
+            mc = fmaxf(mc, fabsf(qv[g][j]));
+            sc += qv[g][j];
+        }
+        for (int i = lane; i < M; i += 64) {
+            ms = fmaxf(ms, fabsf(qv[g][D + i]));
+            ss += qv[g][D + i];
+        }
+        mc = wave_max(mc);
+        sc = wave_sum(sc);
+        ms = wave_max(ms);
+        ss = wave_sum(ss);
+        if (lane == 0) {
+            const float mw = mc * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1]));
+            int ec = 0, es = 0;
+            frexpf(mw, &ec);          // mw < 2^ec
+            frexpf(ms, &es);
+            const int fc = (mw > 0.0f) ? 26 - ec : 0;
+            const int fs = (ms > 0.0f) ? 26 - es : 0;
+            s_f[g][0] = fc;
+            s_f[g][1] = fs;
+            float *sc4 = a.mf.qscal + (row0 + g) * 4;
+            sc4[0] = ldexpf(1.0f, -fc);
+            sc4[1] = a.centroids[0] * sc;
+            sc4[2] = ldexpf(1.0f, -fs);
+            sc4[3] = ss;
+        }
+    }
+    __syncthreads();
+    // digit rows: query g uses lanes 16 kb + 4 (g % 4) + digit of row tile g / 4;
+    // dword r of a lane holds elements 4r..4r+3 of its 16-element k-block
+    const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
+    const int S = 2 * nc + 2 * ns;
+    uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
+    // one work item per (query, step, k-block, dword): four weights, each split
+    // into its four balanced digits, give the item's dword in all four limb rows
+    for (int w = tid; w < MT * 4 * S * 16; w += kThreads) {
+        const int r = w % 4, kb = (w / 4) % 4, s = (w / 16) % S, g = w / (16 * S);
+        uint32_t dw[4] = {0u, 0u, 0u, 0u};
+        if (g < GC) {
+#pragma unroll
+            for (int K = 0; K < 4; ++K) {
+                float wv;
+                int f;
+                if (s < 2 * nc) {
+                    const int u = s / 2, h = s % 2;
+                    const int bit = 32 * (kb * nc + u) + 8 * K + 4 * h + r;
+                    wv = qv[g][bit >> (a.bits - 1)] * s_acoef[bit & (a.bits - 1)];   // bits is 1 or 2
+                    f = s_f[g][0];
+                } else {
+                    const int s2 = s - 2 * nc, u = s2 / 2, h = s2 % 2;
+                    const int bit = 32 * (kb * ns + u) + 8 * K + 4 * h + r;
+                    wv = qv[g][D + bit];
+                    f = s_f[g][1];
+                }
+                // the key bit arrives as byte 2^sh (masked in place, not shifted):
+                // weight w 2^-sh, negated for sh = 7 where the byte reads as -128
+                const int sh = 4 * (s % 2) + r;
+                int x = static_cast<int>(rintf(ldexpf(wv, f - sh)));
+                if (sh == 7) x = -x;
+#pragma unroll
+                for (int limb = 0; limb < 3; ++limb) {
+                    const int d = ((x + 64) & 127) - 64;
+                    dw[limb] |= (static_cast<uint32_t>(d) & 0xffu) << (8 * K);
+                    x = (x - d) >> 7;
+                }
+                dw[3] |= (static_cast<uint32_t>(x) & 0xffu) << (8 * K);
+            }
+        }
+#pragma unroll
+        for (int limb = 0; limb < 4; ++limb) {
+            const int l = 16 * kb + 4 * (g % 4) + limb;
+            out[((g / 4) * S + s) * 256 + l * 4 + r] = dw[limb];
+        }
+    }
+}
+
+// Table score operands (keys with 3 to 8 bits): q_rot and Sq scaled by a power
+// of two to a largest magnitude below 2^10, as fp16 hi + lo rows (2 q, 2 q + 1)
+// of the A operands of v_mfma_f32_16x16x32_f16; k-block kb of step ks holds
+// coordinates kb d/4 + 8 ks + e.  Scales: qscal = {2^-(fq + kCodeExp), 2^-fs}.
+constexpr int kCodeExp = 10;       // centroid tables hold c * 2^kCodeExp
+
+__device__ __forceinline__ uint32_t f16_rn_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void k_qprep_lut(DecodeLaunch a)
+{
+    __shared__ float qs[kMaxG][256];
+    __shared__ float qv[kMaxG][512];
+    __shared__ int s_f[kMaxG][2];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int D = a.d, M = a.m;
+    const int GC = a.mf.gc;
+    const int unit = blockIdx.x;
+    const int64_t row0 = unit_row0(a, unit);
+    rotate_unit_queries<TIn>(a, GC, row0, qs, qv);
+    for (int g = wave; g < GC; g += 4) {
+        float mc = 0.0f, ms = 0.0f;
+        for (int j = lane; j < D; j += 64) mc = fmaxf(mc, fabsf(qv[g][j]));
+        for (int i = lane; i < M; i += 64) ms = fmaxf(ms, fabsf(qv[g][D + i]));
+        mc = wave_max(mc);
+        ms = wave_max(ms);
+        if (lane == 0) {
+            int ec = 0, es = 0;
+            frexpf(mc, &ec);
+            frexpf(ms, &es);
+            const int fq = (mc > 0.0f) ? 10 - ec : 0;
+            const int fs = (ms > 0.0f) ? 10 - es : 0;
+            s_f[g][0] = fq;
+            s_f[g][1] = fs;
+            float *sc4 = a.mf.qscal + (row0 + g) * 4;
+            sc4[0] = ldexpf(1.0f, -(fq + kCodeExp));
+            sc4[1] = ldexpf(1.0f, -fs);
+            sc4[2] = 0.0f;
+            sc4[3] = 0.0f;
+        }
+    }
+    __syncthreads();
+    // aops[unit][part (code, sign)][ks][lane][4 dwords]
+    const int KS = D / 32;
+    uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * 2 * KS * 256;
+    for (int w = tid; w < 2 * KS * 256; w += kThreads) {
+        const int r = w % 4, l = (w / 4) % 64, ks = (w / 256) % KS, part = w / (256 * KS);
+        const int row = l % 16, kb = l / 16, g = row / 2, lo = row % 2;
+        uint32_t dw = 0u;
+        if (g < GC) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int coord = kb * (D / 4) + 8 * ks + 2 * r + h;
+                const float x = ldexpf(qv[g][part * D + coord], s_f[g][part]);
+                const _Float16 xh = static_cast<_Float16>(x);
+                const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
+                dw |= bits << (16 * h);
+            }
+        }
+        out[w] = dw;
+    }
+}
+
+// ------------------------------------------------------------ attention
+// 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
 __device__ __forceinline__ float row16_max(float x)
 {
     x = fmaxf(x, dpp<0xB1>(x));
@@ -245,10 +343,237 @@ __device__ __forceinline__ float row16_sum(float x)
     return x + dpp<0x140>(x);
 }
 
+// Orders this wave's LDS writes before its later LDS reads by other lanes (and
+// the reverse): a compiler-level fence at wavefront scope, free at run time,
+// since one wave's LDS operations execute in order.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // k-slot order of a 32-token wave tile in the value product: slot 2j holds
 // token j, slot 2j + 1 token 16 + j, so that the lane owning key column j of
 // both score tiles writes its two tokens as one packed fp16 pair.
 __device__ __forceinline__ int slot_token(int slot) { return (slot & 1) ? 16 + (slot >> 1) : (slot >> 1); }
+
+// Key words of the two keys (columns j and 16 + j of a wave tile) that lane
+// (j, kb) reads: the kb-th quarter of the code row and of the sign row.
+template <int BITS, int D>
+struct KeyWords {
+    static constexpr int NC = D * BITS / 128, NS = D / 128;
+    uint32_t cw[2][NC], sw[2][NS];
+    float nrm[2], rho[2];
+    __device__ void load(const DecodeLaunch &a, int64_t n, int c, int kb)
+    {
+        const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
+#pragma unroll
+        for (int u = 0; u < NC; ++u) cw[c][u] = crow[u];
+#pragma unroll
+        for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
+        nrm[c] = a.kc.knorm[n];
+        rho[c] = a.kc.rnorm[n];
+    }
+};
+
+// Bit-plane scores (1-2 bit keys).  Rows of the int8 products are (query,
+// digit), four queries per 16-row tile: lane (j, kb) scores query 4 slot + kb.
+template <int BITS, int D, int MT>
+struct ScoreBits {
+    static constexpr int NQ = MT;
+    static constexpr int TAB_BYTES = 0;
+    static constexpr int NC = D * BITS / 128, NS = D / 128;
+    static constexpr int SC = 2 * NC, SS = 2 * NS, S = SC + SS;
+    v4i aop[MT][S];
+    float fc[MT], cc[MT], fs[MT], ssq[MT];
+
+    __device__ static int query(int slot, int kb) { return 4 * slot + kb; }
+
+    // value of a per-slot quantity for query q, fetched from a lane of the
+    // row block that scores q (block q % 4, slot q / 4)
+    __device__ static float for_query(const float (&v)[MT], int q, int j)
+    {
+        float r = 1.0f;
+#pragma unroll
+        for (int s = 0; s < MT; ++s) {
+            const float t = __shfl(v[s], 16 * (q % 4) + j);
+            if (q / 4 == s) r = t;
+        }
+        return r;
+    }
+
+    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, unsigned char *)
+    {
+        const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * MT * S * 64;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s = 0; s < S; ++s) aop[mt][s] = src[(mt * S + s) * 64 + lane];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int g = 4 * mt + kb;
+            const bool ok = g < GC;
+            const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
+            fc[mt] = ok ? sc[0] : 0.0f;
+            cc[mt] = ok ? sc[1] : 0.0f;
+            fs[mt] = ok ? sc[2] : 0.0f;
+            ssq[mt] = ok ? sc[3] : 0.0f;
+        }
+    }
+
+    // B bytes are raw key bits at weight 2^k (mask without shift; the digit
+    // rows carry the 2^-k); returns n (sum q_rot c + kappa rho sum Sq (2s - 1)) per slot
+    __device__ void scores(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[MT]) const
+    {
+        v4i accc[MT], accs[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) accc[mt] = accs[mt] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < SC; ++s) {
+            const uint32_t dw = kw.cw[c][s / 2];
+            const int h = 4 * (s % 2);
+            const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                             static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) accc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][s], bop, accc[mt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < SS; ++s) {
+            const uint32_t dw = kw.sw[c][s / 2];
+            const int h = 4 * (s % 2);
+            const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                             static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                accs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][SC + s], bop, accs[mt], 0, 0, 0);
+        }
+        // lane (key column j, row block kb) holds the four digits of query 4 mt + kb
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
+            const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
+            sc[mt] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
+        }
+    }
+};
+
+// Table scores (3-8 bit keys).  The key's centroids are looked up in LDS as
+// fp16 hi + lo (c * 2^kCodeExp; two coordinates per lookup up to 5 bits, so
+// each lookup yields one packed dword of the hi and one of the lo operand),
+// its sign bytes as eight fp16 +-1; the products run on
+// v_mfma_f32_16x16x32_f16 with rows (query, hi/lo): lane (j, kb) scores
+// queries 2 kb and 2 kb + 1.
+template <int BITS, int D>
+struct ScoreLut {
+    static constexpr int NQ = 2;
+    static constexpr int KS = D / 32;
+    static constexpr bool PAIR = BITS <= 5;
+    static constexpr int CODE_TAB = PAIR ? (1 << (2 * BITS)) * 8 : (1 << BITS) * 4;
+    static constexpr int SIGN_TAB = 256 * 16;
+    static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB;
+    v8h acode[KS], asign[KS];
+    float scc[2], scs[2];
+    const unsigned char *tab;
+
+    __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
+
+    // queries 2 kb and 2 kb + 1 are this lane's own slots
+    __device__ static float for_query(const float (&v)[2], int q, int) { return v[q % 2]; }
+
+    // builds the tables (all threads; the caller synchronises) and loads the operands
+    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, unsigned char *lds)
+    {
+        tab = lds;
+        const int tid = threadIdx.x;
+        constexpr int L = 1 << BITS;
+        if (PAIR) {
+            uint2 *t2 = reinterpret_cast<uint2 *>(lds);
+            for (int i = tid; i < L * L; i += kThreads) {
+                const float c0 = ldexpf(a.centroids[i & (L - 1)], kCodeExp), c1 = ldexpf(a.centroids[i >> BITS], kCodeExp);
+                const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
+                const uint32_t hh = __builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+                const uint32_t ll = f16_rn_bits(c0 - static_cast<float>(h0)) | (f16_rn_bits(c1 - static_cast<float>(h1)) << 16);
+                t2[i] = make_uint2(hh, ll);
+            }
+        } else {
+            uint32_t *t1 = reinterpret_cast<uint32_t *>(lds);
+            for (int i = tid; i < L; i += kThreads) {
+                const float c0 = ldexpf(a.centroids[i], kCodeExp);
+                const _Float16 h0 = static_cast<_Float16>(c0);
+                t1[i] = __builtin_bit_cast(uint16_t, h0) | (f16_rn_bits(c0 - static_cast<float>(h0)) << 16);
+            }
+        }
+        uint32_t *ts = reinterpret_cast<uint32_t *>(lds + CODE_TAB);
+        for (int i = tid; i < 256 * 4; i += kThreads) {
+            const int e = i / 4, r = i % 4;
+            const uint32_t lo = ((e >> (2 * r)) & 1) ? 0x3C00u : 0xBC00u;
+            const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
+            ts[i] = lo | (hi << 16);
+        }
+        const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * 2 * KS * 64;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acode[ks] = __builtin_bit_cast(v8h, src[ks * 64 + lane]);
+            asign[ks] = __builtin_bit_cast(v8h, src[(KS + ks) * 64 + lane]);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int g = 2 * kb + qq;
+            const bool ok = g < GC;
+            const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
+            scc[qq] = ok ? sc[0] : 0.0f;
+            scs[qq] = ok ? sc[1] : 0.0f;
+        }
+    }
+
+    // field of `width` bits at bit offset o of a lane's word array (o, width constant)
+    template <int NW>
+    __device__ static uint32_t field(const uint32_t (&w)[NW], int o, int width)
+    {
+        const int i = o / 32, s = o % 32;
+        const uint32_t mask = (1u << width) - 1u;
+        if (s + width <= 32 || i + 1 >= NW) return (w[i] >> s) & mask;
+        return __builtin_amdgcn_alignbit(w[i + 1], w[i], s) & mask;
+    }
+
+    __device__ void scores(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[2]) const
+    {
+        const uint2 *t2 = reinterpret_cast<const uint2 *>(tab);
+        const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
+        const v4i *ts = reinterpret_cast<const v4i *>(tab + CODE_TAB);
+        v4f accc = {0.0f, 0.0f, 0.0f, 0.0f}, accs = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            v4i bhi, blo;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (PAIR) {
+                    const uint2 t = t2[field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS)];
+                    bhi[p] = static_cast<int>(t.x);
+                    blo[p] = static_cast<int>(t.y);
+                } else {
+                    const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS)];
+                    const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS)];
+                    bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
+                    blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
+                }
+            }
+            accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode[ks], __builtin_bit_cast(v8h, bhi), accc, 0, 0, 0);
+            accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode[ks], __builtin_bit_cast(v8h, blo), accc, 0, 0, 0);
+            const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
+            accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign[ks], __builtin_bit_cast(v8h, ts[sb]), accs, 0, 0, 0);
+        }
+        // rows 4 kb + r: (query 2 kb + r / 2, part r % 2)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const float dcode = (accc[2 * qq] + accc[2 * qq + 1]) * scc[qq];
+            const float dsign = (accs[2 * qq] + accs[2 * qq + 1]) * scs[qq];
+            sc[qq] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
+        }
+    }
+};
 
 // One 256-thread workgroup owns one (sequence, KV head, query chunk) and one
 // token range; each wave walks its own 32-key tiles (wave w takes tiles w,
@@ -257,11 +582,10 @@ __device__ __forceinline__ int slot_token(int slot) { return (slot & 1) ? 16 + (
 // before the current one is computed (two register buffers in turn).  The
 // four waves are merged in LDS at the end; with one split the workgroup
 // writes the normalised output, else its partial (max, sum, weighted values).
-template <int BITS, int D, int MT, int VBITS>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(DecodeLaunch a, float kappa, int64_t chunk)
+template <class SCORE, int BITS, int D, int VBITS>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
-    constexpr int NC = code_dwords(D, BITS), NS = sign_dwords(D);
-    constexpr int SC = 2 * NC, SS = 2 * NS, S = SC + SS;
+    constexpr int NQ = SCORE::NQ;
     constexpr int TK = 32;                       // keys per wave tile
     constexpr int VB = D * VBITS / 8;            // value code bytes per token
     constexpr int VSTR = VB + 16;                // LDS row stride (odd multiple of 16 B)
@@ -280,7 +604,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
     constexpr int SMEM = (4 * WAVE_BYTES > MERGE_BYTES) ? 4 * WAVE_BYTES : MERGE_BYTES;
 
     __shared__ __align__(16) unsigned char smem[SMEM];
-    __shared__ float s_alpha[4][kMaxG];
+    __shared__ __align__(16) unsigned char stab[SCORE::TAB_BYTES > 0 ? SCORE::TAB_BYTES : 16];
     __shared__ float s_wm[4][kMaxG], s_wl[4][kMaxG];
     __shared__ float s_wz[4][kMaxG][kMaxNG];
 
@@ -289,12 +613,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
     const int NG = D / a.group;                  // 1, 2, 4 or 8
     const int lg_ng = __builtin_ctz(NG);
     const int unit = blockIdx.y, split = blockIdx.x;
-    const int qc = unit % nqc;
     const int64_t bh = unit / nqc;
-    const int b = static_cast<int>(bh / a.Hkv), hkv = static_cast<int>(bh % a.Hkv);
-    const int G = a.Hq / a.Hkv;
-    const int hq0 = hkv * G + qc * GC;
-    const int64_t row0 = static_cast<int64_t>(b) * a.Hq + hq0;
+    const int64_t row0 = unit_row0(a, unit);
     const int64_t t_begin = static_cast<int64_t>(split) * chunk;
     const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
     const int j = lane % 16, kb = lane / 16;
@@ -303,41 +623,20 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
     uint32_t *afr = reinterpret_cast<uint32_t *>(vt + VT_BYTES);              // [NGM][64 lanes][4]
     uint32_t *pst = reinterpret_cast<uint32_t *>(vt + VT_BYTES + AF_BYTES);   // [TK][NGM]
 
-    // score operands of this unit (loop invariant)
-    v4i aop[MT][S];
-    {
-        const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * MT * S * 64;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int s = 0; s < S; ++s) aop[mt][s] = src[(mt * S + s) * 64 + lane];
-    }
-    float fc[MT], cc[MT], fs[MT], ssq[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int g = 4 * mt + kb;
-        if (g < GC) {
-            const float *sc = a.mf.qscal + (row0 + g) * 4;
-            fc[mt] = sc[0];
-            cc[mt] = sc[1];
-            fs[mt] = sc[2];
-            ssq[mt] = sc[3];
-        } else {
-            fc[mt] = cc[mt] = fs[mt] = ssq[mt] = 0.0f;
-        }
-    }
-    // value-product A rows of absent queries stay zero; alphas of absent queries are 1
+    SCORE score;
+    score.init(a, unit, row0, lane, kb, GC, stab);
+    // value-product A rows of absent queries stay zero
     for (int i = lane; i < NGM * 64 * 4; i += 64) afr[i] = 0u;
-    if (lane < kMaxG) s_alpha[wave][lane] = 1.0f;
+    if (SCORE::TAB_BYTES > 0) __syncthreads();   // score tables built by all threads
 
-    float m_run[MT], l_run[MT];
-    float zacc[MT][NGM];
+    float m_run[NQ], l_run[NQ];
+    float zacc[NQ][NGM];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        m_run[mt] = -INFINITY;
-        l_run[mt] = 0.0f;
+    for (int sl = 0; sl < NQ; ++sl) {
+        m_run[sl] = -INFINITY;
+        l_run[sl] = 0.0f;
 #pragma unroll
-        for (int gg = 0; gg < NGM; ++gg) zacc[mt][gg] = 0.0f;
+        for (int gg = 0; gg < NGM; ++gg) zacc[sl][gg] = 0.0f;
     }
     // value-product accumulators, rows (query 2 kb + r / 2, fp16 part r % 2),
     // column j = byte column 16 cb + j, field f; acc1 for tiles whose second
@@ -356,8 +655,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
     const unsigned char *tr_base = vt + slot_token(8 * kb + e_of_r) * VSTR + 8 * (j % 2);
 
     struct Prefetch {
-        uint32_t cw[2][NC], sw[2][NS];
-        float nrm[2], rho[2];
+        KeyWords<BITS, D> kw;
         v4i vcode[VCL];
         uint32_t par[PD];
     };
@@ -372,15 +670,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int t = 16 * c + j;
-            const int64_t n = n0 + (t < nv ? t : nv - 1);
-            const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
-            const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
-#pragma unroll
-            for (int u = 0; u < NC; ++u) pf.cw[c][u] = crow[u];
-#pragma unroll
-            for (int u = 0; u < NS; ++u) pf.sw[c][u] = srow[u];
-            pf.nrm[c] = a.kc.knorm[n];
-            pf.rho[c] = a.kc.rnorm[n];
+            pf.kw.load(a, n0 + (t < nv ? t : nv - 1), c, kb);
         }
         const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
@@ -400,6 +690,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
 
     auto compute = [&](int64_t tile0, const Prefetch &cur) {
         const int nv = static_cast<int>(t_end - tile0 < TK ? t_end - tile0 : TK);
+        wave_sync();        // the previous tile's LDS reads come before these writes
         // ---- value codes and (scale, zero) words of the tile into this wave's LDS
 #pragma unroll
         for (int v = 0; v < VCL; ++v) {
@@ -411,82 +702,56 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
             const int idx = lane + 64 * k;
             if (idx < TK * NG) pst[(idx >> lg_ng) * NGM + (idx & (NG - 1))] = idx < nv * NG ? cur.par[k] : 0u;
         }
+        wave_sync();        // staged rows are read by other lanes below
 
-        // ---- scores of keys j and 16 + j: B bytes are raw key bits at weight
-        // 2^k (mask without shift; the digit rows carry the 2^-k)
-        float lamv[MT][2];
+        // ---- scores of keys j and 16 + j for this lane's queries
+        float lamv[NQ][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            v4i accc[MT], accs[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) accc[mt] = accs[mt] = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int s = 0; s < SC; ++s) {
-                const uint32_t dw = cur.cw[c][s / 2];
-                const int h = 4 * (s % 2);
-                const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
-                                 static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    accc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][s], bop, accc[mt], 0, 0, 0);
-            }
-#pragma unroll
-            for (int s = 0; s < SS; ++s) {
-                const uint32_t dw = cur.sw[c][s / 2];
-                const int h = 4 * (s % 2);
-                const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
-                                 static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    accs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mt][SC + s], bop, accs[mt], 0, 0, 0);
-            }
-            // lane (key column j, row block kb) holds the four digits of query 4 mt + kb
+            float sc[NQ];
+            score.scores(cur.kw, c, kappa, sc);
             const bool valid = 16 * c + j < nv;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
-                const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
-                const float score = cur.nrm[c] * fmaf(kappa * cur.rho[c], dsign, dcode);
-                lamv[mt][c] = (valid && 4 * mt + kb < GC) ? a.scale * score : -INFINITY;
-            }
+            for (int sl = 0; sl < NQ; ++sl)
+                lamv[sl][c] = (valid && SCORE::query(sl, kb) < GC) ? a.scale * sc[sl] : -INFINITY;
         }
 
         // ---- online softmax (per query, over the 16 lanes of its row block)
         bool grow = false;
-        float m_new[MT];
+        float m_new[NQ];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            m_new[mt] = fmaxf(m_run[mt], row16_max(fmaxf(lamv[mt][0], lamv[mt][1])));
-            grow |= m_new[mt] > m_run[mt];
+        for (int sl = 0; sl < NQ; ++sl) {
+            m_new[sl] = fmaxf(m_run[sl], row16_max(fmaxf(lamv[sl][0], lamv[sl][1])));
+            grow |= m_new[sl] > m_run[sl];
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             // the running maximum moved: rescale this wave's sums and accumulators
+            float alpha[NQ];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float alpha = (m_new[mt] > m_run[mt]) ? __expf(m_run[mt] - m_new[mt]) : 1.0f;
-                l_run[mt] *= alpha;
+            for (int sl = 0; sl < NQ; ++sl) {
+                alpha[sl] = (m_new[sl] > m_run[sl]) ? __expf(m_run[sl] - m_new[sl]) : 1.0f;
+                l_run[sl] *= alpha[sl];
 #pragma unroll
-                for (int gg = 0; gg < NGM; ++gg) zacc[mt][gg] *= alpha;
-                if (j == 0) s_alpha[wave][4 * mt + kb] = alpha;
-                m_run[mt] = m_new[mt];
+                for (int gg = 0; gg < NGM; ++gg) zacc[sl][gg] *= alpha[sl];
+                m_run[sl] = m_new[sl];
             }
-            const float a0 = s_alpha[wave][2 * kb], a1 = s_alpha[wave][2 * kb + 1];
+            // value rows of this lane: queries 2 kb and 2 kb + 1
+            const float a0 = SCORE::for_query(alpha, 2 * kb, j), a1 = SCORE::for_query(alpha, 2 * kb + 1, j);
+            const v4f av = {a0, a0, a1, a1};
 #pragma unroll
-            for (int nt = 0; nt < NTILE; ++nt) {
-                acc0[nt][0] *= a0; acc0[nt][1] *= a0; acc0[nt][2] *= a1; acc0[nt][3] *= a1;
-            }
+            for (int nt = 0; nt < NTILE; ++nt) acc0[nt] = acc0[nt] * av;
+            if constexpr (kTwoGroups) {
 #pragma unroll
-            for (int nt = 0; nt < (kTwoGroups ? NTILE : 1); ++nt) {
-                acc1[nt][0] *= a0; acc1[nt][1] *= a0; acc1[nt][2] *= a1; acc1[nt][3] *= a1;
+                for (int nt = 0; nt < NTILE; ++nt) acc1[nt] = acc1[nt] * av;
             }
         }
-        float p[MT][2];
+        float p[NQ][2];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const float mref = m_run[mt] == -INFINITY ? 0.0f : m_run[mt];
-            p[mt][0] = __expf(lamv[mt][0] - mref);
-            p[mt][1] = __expf(lamv[mt][1] - mref);
-            l_run[mt] += p[mt][0] + p[mt][1];
+        for (int sl = 0; sl < NQ; ++sl) {
+            const float mref = m_run[sl] == -INFINITY ? 0.0f : m_run[sl];
+            p[sl][0] = __expf(lamv[sl][0] - mref);
+            p[sl][1] = __expf(lamv[sl][1] - mref);
+            l_run[sl] += p[sl][0] + p[sl][1];
         }
 
         // ---- value-product A operand: p * scale as fp16 hi + lo in rows 2 q and
@@ -501,16 +766,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
                 for (int e = 0; e < 4; ++e) pr[c][4 * k + e] = static_cast<uint32_t>(w4[e]);
             }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int q = 4 * mt + kb;
+        for (int sl = 0; sl < NQ; ++sl) {
+            const int q = SCORE::query(sl, kb);
             uint32_t *dst = afr + ((2 * q + 16 * (j / 4)) * 4 + (j % 4));
 #pragma unroll
             for (int gg = 0; gg < NGM; ++gg) {
                 if (gg < NG) {
-                    const float w0 = p[mt][0] * f16_bits_to_f32(pr[0][gg] & 0xffffu);
-                    const float w1 = p[mt][1] * f16_bits_to_f32(pr[1][gg] & 0xffffu);
-                    zacc[mt][gg] = fmaf(p[mt][0], f16_bits_to_f32(pr[0][gg] >> 16),
-                                        fmaf(p[mt][1], f16_bits_to_f32(pr[1][gg] >> 16), zacc[mt][gg]));
+                    const float w0 = p[sl][0] * f16_bits_to_f32(pr[0][gg] & 0xffffu);
+                    const float w1 = p[sl][1] * f16_bits_to_f32(pr[1][gg] & 0xffffu);
+                    zacc[sl][gg] = fmaf(p[sl][0], f16_bits_to_f32(pr[0][gg] >> 16),
+                                        fmaf(p[sl][1], f16_bits_to_f32(pr[1][gg] >> 16), zacc[sl][gg]));
                     const auto hi = __builtin_amdgcn_cvt_pkrtz(w0, w1);
                     const auto lo = __builtin_amdgcn_cvt_pkrtz(w0 - static_cast<float>(hi[0]), w1 - static_cast<float>(hi[1]));
                     dst[gg * 256] = __builtin_bit_cast(uint32_t, hi);
@@ -519,6 +784,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
             }
         }
 
+        wave_sync();        // the A operand is read by other lanes below
         // ---- value product over the 32 tokens, all channel tiles
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
@@ -539,8 +805,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
                 const v8h bv = __builtin_bit_cast(v8h, bop);
                 const int nt = cb * NF + f;
                 acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af0, bv, acc0[nt], 0, 0, 0);
-                if (kTwoGroups && NF * 16 > a.group)
-                    acc1[kTwoGroups ? nt : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bv, acc1[kTwoGroups ? nt : 0], 0, 0, 0);
+                if constexpr (kTwoGroups) {
+                    if (NF * 16 > a.group) acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bv, acc1[nt], 0, 0, 0);
+                }
             }
         }
     };
@@ -562,16 +829,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
 
     // ---- merge the four waves: m, l, zero-point sums and value sums per query
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int g = 4 * mt + kb;
-        const float l = row16_sum(l_run[mt]);
+    for (int sl = 0; sl < NQ; ++sl) {
+        const int g = SCORE::query(sl, kb);
+        const float l = row16_sum(l_run[sl]);
         if (j == 0) {
-            s_wm[wave][g] = m_run[mt];
+            s_wm[wave][g] = m_run[sl];
             s_wl[wave][g] = l;
         }
 #pragma unroll
         for (int gg = 0; gg < NGM; ++gg) {
-            const float z = row16_sum(zacc[mt][gg]);
+            const float z = row16_sum(zacc[sl][gg]);
             if (j == 0) s_wz[wave][g][gg] = z;
         }
     }
@@ -582,7 +849,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend_mfma(Deco
         const int cb = nt / NF, f = nt % NF;
         const int ch = NF * (16 * cb + j) + f;
         const int g_lo = (NF * 16 * cb) / a.group;
-        const v4f acc = (kTwoGroups && NF * 16 > a.group && ch / a.group != g_lo) ? acc1[kTwoGroups ? nt : 0] : acc0[nt];
+        v4f acc = acc0[nt];
+        if constexpr (kTwoGroups) {
+            const v4f alt = acc1[nt];
+            if (NF * 16 > a.group && ch / a.group != g_lo) acc = alt;
+        }
         const float sc = 16777216.0f / static_cast<float>(1 << (VBITS * f));
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
@@ -665,13 +936,13 @@ __global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
     if (tid < D) a.out[row * D + tid] = o;
 }
 
-template <int BITS, int D, int MT, int VBITS>
-hipError_t launch_mfma_t(const DecodeLaunch &a, hipStream_t stream, float kappa, int64_t chunk)
+template <class SCORE, int BITS, int D, int VBITS>
+hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kappa, int64_t chunk)
 {
     const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(a.mf.units));
     void *tok;
     prof_begin("tq_attend_splitk", stream, &tok);
-    hipLaunchKernelGGL((k_attend_mfma<BITS, D, MT, VBITS>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
     prof_end(tok, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
@@ -682,23 +953,46 @@ hipError_t launch_mfma_t(const DecodeLaunch &a, hipStream_t stream, float kappa,
     return hipGetLastError();
 }
 
-template <int BITS, int D, int MT>
-hipError_t launch_mfma_v(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
+template <class SCORE, int BITS, int D>
+hipError_t launch_attend_v(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
-    return a.vbits == 2 ? launch_mfma_t<BITS, D, MT, 2>(a, s, kappa, chunk)
-                        : launch_mfma_t<BITS, D, MT, 4>(a, s, kappa, chunk);
+    return a.vbits == 2 ? launch_attend_t<SCORE, BITS, D, 2>(a, s, kappa, chunk)
+                        : launch_attend_t<SCORE, BITS, D, 4>(a, s, kappa, chunk);
 }
 
 template <int BITS, int D>
-hipError_t launch_mfma_m(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
+hipError_t launch_attend_b(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
-    return a.mf.mt == 1 ? launch_mfma_v<BITS, D, 1>(a, s, kappa, chunk) : launch_mfma_v<BITS, D, 2>(a, s, kappa, chunk);
+    if constexpr (BITS <= 2) {
+        return a.mf.mt == 1 ? launch_attend_v<ScoreBits<BITS, D, 1>, BITS, D>(a, s, kappa, chunk)
+                            : launch_attend_v<ScoreBits<BITS, D, 2>, BITS, D>(a, s, kappa, chunk);
+    } else {
+        return launch_attend_v<ScoreLut<BITS, D>, BITS, D>(a, s, kappa, chunk);
+    }
 }
 
-template <int BITS>
-hipError_t launch_mfma_d(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
+template <int D>
+hipError_t launch_attend_d(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
-    return a.d == 128 ? launch_mfma_m<BITS, 128>(a, s, kappa, chunk) : launch_mfma_m<BITS, 256>(a, s, kappa, chunk);
+    switch (a.bits) {
+    case 1: return launch_attend_b<1, D>(a, s, kappa, chunk);
+    case 2: return launch_attend_b<2, D>(a, s, kappa, chunk);
+    case 3: return launch_attend_b<3, D>(a, s, kappa, chunk);
+    case 4: return launch_attend_b<4, D>(a, s, kappa, chunk);
+    case 5: return launch_attend_b<5, D>(a, s, kappa, chunk);
+    case 6: return launch_attend_b<6, D>(a, s, kappa, chunk);
+    case 7: return launch_attend_b<7, D>(a, s, kappa, chunk);
+    case 8: return launch_attend_b<8, D>(a, s, kappa, chunk);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename TIn>
+void launch_qprep_t(const DecodeLaunch &a, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(a.mf.units));
+    if (a.bits <= 2) hipLaunchKernelGGL(k_qprep_bits<TIn>, grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(k_qprep_lut<TIn>, grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -707,7 +1001,7 @@ bool mfma_decode_supported(int d, int bits, int G, int vbits, int group)
 {
     (void)group;
     const int gc = mfma_query_chunk(G);
-    return (d == 128 || d == 256) && (bits == 1 || bits == 2) && gc >= 1 && (vbits == 2 || vbits == 4);
+    return (d == 128 || d == 256) && bits >= 1 && bits <= 8 && gc >= 1 && (vbits == 2 || vbits == 4);
 }
 
 int mfma_query_chunk(int G)
@@ -717,17 +1011,18 @@ int mfma_query_chunk(int G)
     return gc;
 }
 
-int mfma_score_steps(int d, int bits) { return 2 * code_dwords(d, bits) + 2 * sign_dwords(d); }
+int mfma_row_tiles(int bits, int gc) { return bits <= 2 ? (gc + 3) / 4 : 1; }
+
+int mfma_score_steps(int d, int bits) { return bits <= 2 ? 2 * code_dwords(d, bits) + 2 * sign_dwords(d) : 2 * (d / 32); }
 
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
 {
-    const dim3 qgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq));
     void *tok;
     prof_begin("tq_qprep", stream, &tok);
     switch (a.dtype) {
-    case TQ_F32: hipLaunchKernelGGL(k_qprep_mfma<float>, qgrid, dim3(kThreads), 0, stream, a); break;
-    case TQ_BF16: hipLaunchKernelGGL(k_qprep_mfma<bf16_t>, qgrid, dim3(kThreads), 0, stream, a); break;
-    case TQ_F16: hipLaunchKernelGGL(k_qprep_mfma<f16_t>, qgrid, dim3(kThreads), 0, stream, a); break;
+    case TQ_F32: launch_qprep_t<float>(a, stream); break;
+    case TQ_BF16: launch_qprep_t<bf16_t>(a, stream); break;
+    case TQ_F16: launch_qprep_t<f16_t>(a, stream); break;
     }
     prof_end(tok, stream);
     hipError_t e = hipGetLastError();
@@ -735,7 +1030,7 @@ hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
     const float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / a.m);
     const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
     const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kMfmaTile;
-    return a.bits == 1 ? launch_mfma_d<1>(a, stream, kappa, chunk) : launch_mfma_d<2>(a, stream, kappa, chunk);
+    return a.d == 128 ? launch_attend_d<128>(a, stream, kappa, chunk) : launch_attend_d<256>(a, stream, kappa, chunk);
 }
 
 }  // namespace tq

@@ -115,11 +115,12 @@ hipError_t launch_attend(const DecodeLaunch &a, hipStream_t stream);
 int query_chunk(int G);
 constexpr int kDecodeTile = 256;   // keys per decode tile
 
-// matrix-core decode path (k_attend_mfma.hip): keys with 1-2 bits, d 128/256
+// matrix-core decode path (k_attend_mfma.hip): d 128/256, any key bits
 constexpr int kMfmaTile = 128;     // keys per workgroup step (four waves x 32)
 bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
 int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits);
+int mfma_row_tiles(int bits, int gc);
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream);
 
 // ---- profiling hooks (api.cpp)

@@ -10,7 +10,8 @@ packed KV read (packed K + V bytes of all layers / decode time of the step);
 keys and values compressed per second are reported beside it.  `roofline`
 covers the split-K decode-attention kernel: algorithmic bytes per launch /
 its mean launch duration (HIP events recorded by libtq around each launch on
-the launch stream) against the 8 TB/s HBM peak.  `cpu_baseline` times the
+the launch stream, in a separate pass after the timed region) against the
+8 TB/s HBM peak.  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -175,8 +176,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    tq.tq_profile_enable(True)
-    tq.tq_profile_read("")            # drop anything recorded before the timed region
+    # timed region: plain launches, phase boundaries marked by stream events only
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -184,8 +184,16 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # per-kernel launch durations: a separate pass with libtq's per-launch events
+    tq.tq_profile_enable(True)
+    tq.tq_profile_read("")
+    for _ in range(max(1, min(args.steps, 5))):
+        step()
+    torch.cuda.synchronize()
     tq.tq_profile_enable(False)
     attn_ms, attn_n = tq.tq_profile_read("tq_attend_splitk")
+    qp_ms, qp_n = tq.tq_profile_read("tq_qprep")
+    mg_ms, mg_n = tq.tq_profile_read("tq_merge_splits")
     kq_ms, kq_n = tq.tq_profile_read("tq_compress_keys")
     vq_ms, vq_n = tq.tq_profile_read("tq_compress_values")
     tq.tq_profile_read("")
@@ -236,7 +244,9 @@ def main():
                      "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n},
         "kernel_avg_us": {"tq_compress_keys": round(kq_ms * 1e3 / max(kq_n, 1), 3),
                           "tq_compress_values": round(vq_ms * 1e3 / max(vq_n, 1), 3),
-                          "tq_attend_splitk": round(attn_avg_s * 1e6, 3)},
+                          "tq_qprep": round(qp_ms * 1e3 / max(qp_n, 1), 3),
+                          "tq_attend_splitk": round(attn_avg_s * 1e6, 3),
+                          "tq_merge_splits": round(mg_ms * 1e3 / max(mg_n, 1), 3) if mg_n else None},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -122,11 +122,13 @@ def test_split_policy_and_workspace():
     # one long sequence with 8 KV heads spreads over many splits
     s = lib.tq_attend_splits(ctypes.byref(kf), 1, 64, 8, 1 << 20)
     assert 64 <= s <= 1024
-    # never more splits than tiles: 128 keys on the matrix-core path (1-2 bit
-    # keys), 256 on the general path (3-bit keys here)
+    # never more splits than tiles: 128 keys on the matrix-core path (d 128 and
+    # 256, any key bits), 256 on the general path (d 64 here)
     assert lib.tq_attend_splits(ctypes.byref(kf), 1, 4, 1, 300) == 3
     kf3 = _kf(mse_bits=3)
-    assert lib.tq_attend_splits(ctypes.byref(kf3), 1, 4, 1, 300) == 2
+    assert lib.tq_attend_splits(ctypes.byref(kf3), 1, 4, 1, 300) == 3
+    kf64 = _kf(d=64, mse_bits=3, qjl_m=64)
+    assert lib.tq_attend_splits(ctypes.byref(kf64), 1, 4, 1, 300) == 2
     assert lib.tq_attend_splits(ctypes.byref(kf), 1, 4, 1, 0) == 1
     assert lib.tq_attend_splits(ctypes.byref(kf), 1, 5, 2, 100) == 0      # Hq % Hkv != 0
     ws = lib.tq_attend_workspace_bytes(ctypes.byref(kf), 2, 8, 2, 1000, 3)

@@ -25,7 +25,12 @@ CASES = [
     (256, 1, "hadamard", 2, 2, 2, 64, 129, "iid", "bfloat16"),     # GQA 1
     (128, 2, "hadamard", 1, 6, 4, 128, 517, "iid", "bfloat16"),    # GQA 6 -> chunks of 2
     (128, 2, "dense", 1, 16, 2, 128, 300, "scaled", "bfloat16"),   # GQA 16 -> two chunks of 8, one-hot regime
-    (128, 3, "dense", 1, 8, 2, 64, 400, "iid", "bfloat16"),        # 3-bit keys (general kernel)
+    (128, 3, "dense", 1, 8, 2, 64, 400, "iid", "bfloat16"),        # 3-bit keys (pair table)
+    (128, 4, "dense", 2, 8, 4, 32, 450, "iid", "bfloat16"),        # 4-bit keys (pair table)
+    (128, 5, "hadamard", 1, 4, 2, 64, 290, "iid", "bfloat16"),     # 5-bit keys (largest pair table)
+    (128, 6, "dense", 1, 2, 4, 32, 333, "iid", "float32"),         # 6-bit keys (single-code table)
+    (256, 7, "dense", 2, 4, 4, 32, 260, "scaled", "bfloat16"),     # 7-bit keys (largest format), d 256
+    (256, 3, "dense", 1, 8, 2, 32, 500, "iid", "bfloat16"),        # 3-bit keys, d 256, two-group value tiles
     (64, 2, "dense", 1, 4, 2, 32, 260, "iid", "float32"),          # d 64 (general kernel)
 ]
 
