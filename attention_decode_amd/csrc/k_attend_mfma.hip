@@ -358,6 +358,14 @@ __device__ __forceinline__ void wave_sync()
 // both score tiles writes its two tokens as one packed fp16 pair.
 __device__ __forceinline__ int slot_token(int slot) { return (slot & 1) ? 16 + (slot >> 1) : (slot >> 1); }
 
+// base + a 32-bit byte offset: with a wave-uniform base the load takes the
+// base from scalar registers and the offset from one VGPR
+template <class T>
+__device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off)
+{
+    return reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(base) + off);
+}
+
 // Key words of the two keys (columns j and 16 + j of a wave tile) that lane
 // (j, kb) reads: the kb-th quarter of the code row and of the sign row.
 template <int BITS, int D>
@@ -365,16 +373,14 @@ struct KeyWords {
     static constexpr int NC = D * BITS / 128, NS = D / 128;
     uint32_t cw[2][NC], sw[2][NS];
     float nrm[2], rho[2];
-    __device__ void load(const DecodeLaunch &a, int64_t n, int c, int kb)
+    __device__ void load(const uint32_t *crow, const uint32_t *srow, const float *np, const float *rp, int c)
     {
-        const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32) + kb * NC;
-        const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (D / 32) + kb * NS;
 #pragma unroll
         for (int u = 0; u < NC; ++u) cw[c][u] = crow[u];
 #pragma unroll
         for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
-        nrm[c] = a.kc.knorm[n];
-        rho[c] = a.kc.rnorm[n];
+        nrm[c] = *np;
+        rho[c] = *rp;
     }
 };
 
@@ -470,12 +476,27 @@ struct ScoreLut {
     static constexpr int NQ = 2;
     static constexpr int KS = D / 32;
     static constexpr bool PAIR = BITS <= 5;
-    static constexpr int CODE_TAB = PAIR ? (1 << (2 * BITS)) * 8 : (1 << BITS) * 4;
+    // pair mode: a hi table and a lo table of packed (coordinate 2p, 2p + 1)
+    // fp16 pairs, so each lookup lands in its operand register; single mode:
+    // one table of (hi | lo << 16) per code
+    static constexpr int NENT = PAIR ? (1 << (2 * BITS)) : (1 << BITS);
+    static constexpr int NTAB = PAIR ? 2 : 1;
+    // copies of the code tables, interleaved entry-major so that lane l reads
+    // copy l % COPIES: with 64 copies every lane owns its bank (no conflicts)
+    static constexpr int COPIES_RAW = 32768 / (NENT * 4 * NTAB);
+    static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 4 ? 4 : 1));
+    static constexpr int TAB1 = NENT * 4 * COPIES;                     // bytes of one code table
+    // the lo table starts 16 bytes past a multiple of 256 so that a hi and a lo
+    // lookup cannot be fused into one two-address read (which would land both
+    // in adjacent registers and cost moves into the two operand quads)
+    static constexpr int LO_OFF = TAB1 + 16;
+    static constexpr int CODE_TAB = PAIR ? LO_OFF + TAB1 : TAB1;
     static constexpr int SIGN_TAB = 256 * 16;
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB;
     v8h acode[KS], asign[KS];
     float scc[2], scs[2];
     const unsigned char *tab;
+    int copy;                  // this lane's table copy
 
     __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
 
@@ -486,23 +507,24 @@ struct ScoreLut {
     __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, unsigned char *lds)
     {
         tab = lds;
+        copy = lane % COPIES;
         const int tid = threadIdx.x;
         constexpr int L = 1 << BITS;
         if (PAIR) {
-            uint2 *t2 = reinterpret_cast<uint2 *>(lds);
-            for (int i = tid; i < L * L; i += kThreads) {
+            uint32_t *th = reinterpret_cast<uint32_t *>(lds), *tl = reinterpret_cast<uint32_t *>(lds + LO_OFF);
+            for (int x = tid; x < L * L * COPIES; x += kThreads) {
+                const int i = x / COPIES;
                 const float c0 = ldexpf(a.centroids[i & (L - 1)], kCodeExp), c1 = ldexpf(a.centroids[i >> BITS], kCodeExp);
                 const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
-                const uint32_t hh = __builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-                const uint32_t ll = f16_rn_bits(c0 - static_cast<float>(h0)) | (f16_rn_bits(c1 - static_cast<float>(h1)) << 16);
-                t2[i] = make_uint2(hh, ll);
+                th[x] = __builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+                tl[x] = f16_rn_bits(c0 - static_cast<float>(h0)) | (f16_rn_bits(c1 - static_cast<float>(h1)) << 16);
             }
         } else {
             uint32_t *t1 = reinterpret_cast<uint32_t *>(lds);
-            for (int i = tid; i < L; i += kThreads) {
-                const float c0 = ldexpf(a.centroids[i], kCodeExp);
+            for (int x = tid; x < L * COPIES; x += kThreads) {
+                const float c0 = ldexpf(a.centroids[x / COPIES], kCodeExp);
                 const _Float16 h0 = static_cast<_Float16>(c0);
-                t1[i] = __builtin_bit_cast(uint16_t, h0) | (f16_rn_bits(c0 - static_cast<float>(h0)) << 16);
+                t1[x] = __builtin_bit_cast(uint16_t, h0) | (f16_rn_bits(c0 - static_cast<float>(h0)) << 16);
             }
         }
         uint32_t *ts = reinterpret_cast<uint32_t *>(lds + CODE_TAB);
@@ -540,8 +562,8 @@ struct ScoreLut {
 
     __device__ void scores(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[2]) const
     {
-        const uint2 *t2 = reinterpret_cast<const uint2 *>(tab);
         const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
+        const uint32_t *tl = reinterpret_cast<const uint32_t *>(tab + LO_OFF);
         const v4i *ts = reinterpret_cast<const v4i *>(tab + CODE_TAB);
         v4f accc = {0.0f, 0.0f, 0.0f, 0.0f}, accs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -550,12 +572,12 @@ struct ScoreLut {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 if (PAIR) {
-                    const uint2 t = t2[field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS)];
-                    bhi[p] = static_cast<int>(t.x);
-                    blo[p] = static_cast<int>(t.y);
+                    const uint32_t e = field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS) * COPIES + copy;
+                    bhi[p] = static_cast<int>(t1[e]);
+                    blo[p] = static_cast<int>(tl[e]);
                 } else {
-                    const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS)];
-                    const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS)];
+                    const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS) * COPIES + copy];
+                    const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS) * COPIES + copy];
                     bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
                     blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
                 }
@@ -608,7 +630,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
     __shared__ float s_wm[4][kMaxG], s_wl[4][kMaxG];
     __shared__ float s_wz[4][kMaxG][kMaxNG];
 
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // wave-uniform: tile bases stay scalar
     const int GC = a.mf.gc, nqc = a.mf.nqc;
     const int NG = D / a.group;                  // 1, 2, 4 or 8
     const int lg_ng = __builtin_ctz(NG);
@@ -647,6 +670,18 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
 #pragma unroll
     for (int nt = 0; nt < (kTwoGroups ? NTILE : 1); ++nt) acc1[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // A-operand slots of the value product are swizzled (slot of lane L is
+    // L ^ ((L >> 4) & 3)) so that the writes of one row block spread over all
+    // banks; this lane's write offsets (rows 2 q, 2 q + 1 of its query slots)
+    // and read offset are fixed.
+    auto aslot = [](int L) { return L ^ ((L >> 4) & 3); };
+    int awr[NQ][2];
+#pragma unroll
+    for (int sl = 0; sl < NQ; ++sl)
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+            awr[sl][part] = aslot(2 * SCORE::query(sl, kb) + part + 16 * (j / 4)) * 4 + (j % 4);
+    const int ard = aslot(lane) * 4;
     // tr-read row of this lane in every value block: k-slot 8 kb + e holds the
     // token of slot order; lanes 2r, 2r + 1 address read row r, and row r lands
     // in half e(r) of the operand with e = {0, 2, 1, 3, 4, 6, 5, 7}
@@ -666,25 +701,32 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
     auto fetch = [&](int64_t tile0, Prefetch &pf) {
         const int64_t tc = tile0 < t_end ? tile0 : first;
         const int nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
-        const int64_t n0 = bh * a.T + tc;
+        const int64_t n0 = bh * a.T + tc;            // wave-uniform row of the tile
+        const uint32_t *cbase = reinterpret_cast<const uint32_t *>(a.kc.codes) + n0 * (D * BITS / 32);
+        const uint32_t *sbase = reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32);
+        const float *nbase = a.kc.knorm + n0, *rbase = a.kc.rnorm + n0;
+        // lane offsets are 32-bit unsigned so that the loads take the uniform base
+        // from scalar registers
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int t = 16 * c + j;
-            pf.kw.load(a, n0 + (t < nv ? t : nv - 1), c, kb);
+            const uint32_t t = static_cast<uint32_t>(16 * c + j < nv ? 16 * c + j : nv - 1);
+            pf.kw.load(at_bytes(cbase, 4u * (t * (D * BITS / 32) + kb * KeyWords<BITS, D>::NC)),
+                       at_bytes(sbase, 4u * (t * (D / 32) + kb * KeyWords<BITS, D>::NS)),
+                       at_bytes(nbase, 4u * t), at_bytes(rbase, 4u * t), c);
         }
         const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
         for (int v = 0; v < VCL; ++v) {
-            const int i = lane + 64 * v;
-            const int tok = i / (VB / 16);
-            pf.vcode[v] = vsrc[(tok < nv ? tok : nv - 1) * (VB / 16) + i % (VB / 16)];
+            const uint32_t i = static_cast<uint32_t>(lane + 64 * v);
+            const uint32_t tok = i / (VB / 16);
+            pf.vcode[v] = *at_bytes(vsrc, 16u * ((tok < static_cast<uint32_t>(nv) ? tok : nv - 1) * (VB / 16) + i % (VB / 16)));
         }
         const uint32_t *psrc = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
-        const int plim = nv * NG - 1;
+        const uint32_t plim = static_cast<uint32_t>(nv * NG - 1);
 #pragma unroll
         for (int k = 0; k < PD; ++k) {
-            const int idx = lane + 64 * k;
-            pf.par[k] = psrc[idx < plim ? idx : plim];
+            const uint32_t idx = static_cast<uint32_t>(lane + 64 * k);
+            pf.par[k] = *at_bytes(psrc, 4u * (idx < plim ? idx : plim));
         }
     };
 
@@ -767,8 +809,6 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
             }
 #pragma unroll
         for (int sl = 0; sl < NQ; ++sl) {
-            const int q = SCORE::query(sl, kb);
-            uint32_t *dst = afr + ((2 * q + 16 * (j / 4)) * 4 + (j % 4));
 #pragma unroll
             for (int gg = 0; gg < NGM; ++gg) {
                 if (gg < NG) {
@@ -778,8 +818,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
                                         fmaf(p[sl][1], f16_bits_to_f32(pr[1][gg] >> 16), zacc[sl][gg]));
                     const auto hi = __builtin_amdgcn_cvt_pkrtz(w0, w1);
                     const auto lo = __builtin_amdgcn_cvt_pkrtz(w0 - static_cast<float>(hi[0]), w1 - static_cast<float>(hi[1]));
-                    dst[gg * 256] = __builtin_bit_cast(uint32_t, hi);
-                    dst[gg * 256 + 4] = __builtin_bit_cast(uint32_t, lo);
+                    afr[gg * 256 + awr[sl][0]] = __builtin_bit_cast(uint32_t, hi);
+                    afr[gg * 256 + awr[sl][1]] = __builtin_bit_cast(uint32_t, lo);
                 }
             }
         }
@@ -789,10 +829,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int g_lo = (NF * 16 * cb) >> (__builtin_ctz(a.group));
-            const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + g_lo * 256 + lane * 4));
+            const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + g_lo * 256 + ard));
             v8h af1 = af0;
             if (kTwoGroups && NF * 16 > a.group)
-                af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + (g_lo + 1) * 256 + lane * 4));
+                af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + (g_lo + 1) * 256 + ard));
             const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(tr_base + 16 * cb));
             const uint32_t x0 = static_cast<uint32_t>(raw.x), x1 = static_cast<uint32_t>(raw.y);
             const uint32_t y0 = x0 >> 8, y1 = x1 >> 8;
@@ -812,19 +852,40 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
         }
     };
 
-    // two tiles per trip, the loads of each issued one tile ahead; an odd
-    // last tile is computed after the loop
+    // Register ring of prefetched tiles: the loads of each tile are issued
+    // DEPTH - 1 tiles ahead of its use, so that a wave keeps that many tiles
+    // of HBM reads in flight behind its compute (d 256 keeps two buffers:
+    // its registers are the limit there).  Tiles left after the unrolled trips
+    // are computed from the buffers that already hold them.
+    constexpr int STEP = 4 * TK;
     if (first < t_end) {
-        Prefetch pa, pb;
-        fetch(first, pa);
-        int64_t t = first;
-        for (; t + 4 * TK < t_end; t += 8 * TK) {
-            fetch(t + 4 * TK, pb);
-            compute(t, pa);
-            fetch(t + 8 * TK, pa);
-            compute(t + 4 * TK, pb);
+        if constexpr (D == 256) {
+            Prefetch pa, pb;
+            fetch(first, pa);
+            int64_t t = first;
+            for (; t + STEP < t_end; t += 2 * STEP) {
+                fetch(t + STEP, pb);
+                compute(t, pa);
+                fetch(t + 2 * STEP, pa);
+                compute(t + STEP, pb);
+            }
+            if (t < t_end) compute(t, pa);
+        } else {
+            Prefetch p0, p1, p2;
+            fetch(first, p0);
+            fetch(first + STEP, p1);
+            int64_t t = first;
+            for (; t + 2 * STEP < t_end; t += 3 * STEP) {
+                fetch(t + 2 * STEP, p2);
+                compute(t, p0);
+                fetch(t + 3 * STEP, p0);
+                compute(t + STEP, p1);
+                fetch(t + 4 * STEP, p1);
+                compute(t + 2 * STEP, p2);
+            }
+            if (t < t_end) compute(t, p0);
+            if (t + STEP < t_end) compute(t + STEP, p1);
         }
-        if (t < t_end) compute(t, pa);
     }
 
     // ---- merge the four waves: m, l, zero-point sums and value sums per query
