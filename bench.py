@@ -79,6 +79,28 @@ class Layer:
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
 
 
+def measured_traffic(w):
+    """HBM bytes per launch of the split-K attention kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a plain 1 GiB copy), or None when there is no summary
+    for this workload or the kernel source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{w.name}.txt")
+    src = os.path.join(ROOT, "attention_decode_amd", "csrc", "k_attend_mfma.hip")
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#") and not line.startswith("tq::"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return (float(fields["attend_fetch_kib"]) * float(fields["fetch_factor"])
+                + float(fields["attend_write_kib"]) * float(fields["write_factor"])) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle (as is) on a bounded sample of the workload: one (sequence,
     KV head) unit's keys compressed, then decode attention of its G query heads
@@ -240,7 +262,7 @@ def main():
         "packed_bytes_per_step": packed,
         "roofline": {"bound": "hbm", "kernel": "tq_attend_splitk", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": attn_bytes,
+                     "traffic": measured_traffic(w), "bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n},
         "kernel_avg_us": {"tq_compress_keys": round(kq_ms * 1e3 / max(kq_n, 1), 3),
                           "tq_compress_values": round(vq_ms * 1e3 / max(vq_n, 1), 3),
