@@ -199,6 +199,45 @@ tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
         return hip_fail(e, "tq_build_codebook: device upload");
     }
     cb->d_boundaries = cb->d_centroids + L;
+    if (L >= 8) {
+        // grid over the fp32 boundaries the kernel compares with: cell c starts a
+        // bound below #{t_i < y}; its widened range holds at most two boundaries
+        const double lo = host[L], hi = host[L + L - 2];
+        std::vector<uint8_t> grid;
+        int ng = 0;
+        for (int n = 64; n <= tq::kMaxGrid && ng == 0; n *= 2) {
+            const double w = (hi - lo) / n;
+            grid.assign(n, 0);
+            bool ok = true;
+            for (int c = 0; c < n && ok; ++c) {
+                const double a = lo + (c - 0.02) * w, b = lo + (c + 1.02) * w;
+                int below = 0, inside = 0;
+                for (int i = 0; i < L - 1; ++i) {
+                    if (host[L + i] < a) ++below;
+                    else if (host[L + i] < b) ++inside;
+                }
+                grid[c] = static_cast<uint8_t>(below);
+                ok = inside <= 2;
+            }
+            if (ok) ng = n;
+        }
+        if (ng == 0) {
+            hipFree(cb->d_centroids);
+            delete cb;
+            return fail(TQ_EUNSUPPORTED, "tq_build_codebook: no code grid up to %d cells", tq::kMaxGrid);
+        }
+        cb->ngrid = ng;
+        cb->grid_lo = static_cast<float>(lo);
+        cb->grid_scale = static_cast<float>(ng / (hi - lo));
+        e = hipMalloc(reinterpret_cast<void **>(&cb->d_grid), ng);
+        if (e == hipSuccess) e = hipMemcpy(cb->d_grid, grid.data(), ng, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            if (cb->d_grid) hipFree(cb->d_grid);
+            hipFree(cb->d_centroids);
+            delete cb;
+            return hip_fail(e, "tq_build_codebook: grid upload");
+        }
+    }
     *out = cb;
     return TQ_OK;
 }
@@ -207,6 +246,7 @@ void tq_codebook_free(tq_codebook *cb)
 {
     if (!cb) return;
     if (cb->d_centroids) hipFree(cb->d_centroids);
+    if (cb->d_grid) hipFree(cb->d_grid);
     delete cb;
 }
 
@@ -508,6 +548,10 @@ tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype,
     a.dsign = fmt->rot->d_dsign;
     a.centroids = fmt->cb->d_centroids;
     a.boundaries = fmt->cb->d_boundaries;
+    a.grid = fmt->cb->d_grid;
+    a.ngrid = fmt->cb->ngrid;
+    a.grid_lo = fmt->cb->grid_lo;
+    a.grid_scale = fmt->cb->grid_scale;
     a.pifrag = fmt->rot->d_pifrag;
     a.sfrag = fmt->rot->d_sfrag;
     a.out = out;

@@ -18,8 +18,13 @@
 //   * z:  S = S0 + S1, r = R0 + R1 (16 bits each); S0 R0 + S0 R1 + S1 R0 leaves
 //         an error near 2^-16 of |z| per term, far inside the resolution at
 //         which a sign can legitimately flip.
-// All sums accumulate in fp32 inside the MFMA; ||k|| and ||r|| are summed in
-// fp64 from the fp32 values.
+// All sums accumulate in fp32 inside the MFMA.  ||k|| is summed in fp64 from
+// the exact fp32 squares (each wave takes a quarter of the k-steps); ||r||
+// in fp32 per lane and fp64 across lanes.
+//
+// Codes: idx = #{t_i < y}.  Up to 2 bits the boundaries sit in registers; from
+// 3 bits a uniform grid over [t_0, t_{L-2}] gives a lower bound of the count
+// that is at most two below it, and two exact comparisons finish it.
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -73,20 +78,23 @@ __device__ __forceinline__ void split_terms(const float (&x)[8], uint4 (&t)[NT])
     }
 }
 
-// eight consecutive channels of one key as B-operand terms, plus their sum of squares
-__device__ __forceinline__ void key_frag(const bf16_t *p, bool valid, uint4 (&t)[1], double &ss)
+// eight consecutive channels of one key as B-operand terms; with `norm`, their
+// sum of squares is added to ss (each wave sums a quarter of the k-steps)
+__device__ __forceinline__ void key_frag(const bf16_t *p, bool valid, uint4 (&t)[1], double &ss, bool norm)
 {
     t[0] = valid ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
+    if (norm) {
+        const uint32_t w[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = bf16_to_f32(w[i] & 0xffffu), hi = bf16_to_f32(w[i] >> 16);
-        ss += static_cast<double>(lo * lo) + static_cast<double>(hi * hi);   // squares exact in fp32
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_to_f32(w[i] & 0xffffu), hi = bf16_to_f32(w[i] >> 16);
+            ss += static_cast<double>(lo * lo) + static_cast<double>(hi * hi);   // squares exact in fp32
+        }
     }
 }
 
 template <typename TIn, int NT>
-__device__ __forceinline__ void key_frag(const TIn *p, bool valid, uint4 (&t)[NT], double &ss)
+__device__ __forceinline__ void key_frag(const TIn *p, bool valid, uint4 (&t)[NT], double &ss, bool norm)
 {
     float x[8];
     if (valid) {
@@ -95,9 +103,19 @@ __device__ __forceinline__ void key_frag(const TIn *p, bool valid, uint4 (&t)[NT
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.0f;
     }
+    if (norm) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);
+        for (int e = 0; e < 8; ++e) ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);
+    }
     split_terms<NT>(x, t);
+}
+
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16x2(float x0, float x1)
+{
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 struct KeySmem {
@@ -105,46 +123,53 @@ struct KeySmem {
     uint32_t *cw;       // [kKeys][D * bits / 32]  code words
     uint32_t *sw;       // [kKeys][D / 32]         sign words
     double *rho2;       // [4 waves][kKeys]
-    float *knorm;       // [kKeys]
+    double *nrm2;       // [4 waves][kKeys]
     float *cent;        // [256]
-    float *bnd;         // [256]
+    float *bnd;         // [256] (+inf after the last boundary)
+    uint8_t *grid;      // [kMaxGrid]
 };
 
-template <int D>
+template <int D, int BITS>
 constexpr size_t key_smem_bytes()
 {
-    return sizeof(uint4) * kKT * (D / 32) * 2 * 64 + sizeof(uint32_t) * kKeys * (D / 4 + D / 32)
-           + sizeof(double) * 4 * kKeys + sizeof(float) * (kKeys + 512);
+    return sizeof(uint4) * kKT * (D / 32) * 2 * 64 + sizeof(uint32_t) * kKeys * (D * BITS / 32 + D / 32)
+           + sizeof(double) * 8 * kKeys + sizeof(float) * 512 + (BITS >= 3 ? kMaxGrid : 0);
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, int BITS>
 __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
     constexpr int NK = KeyTerms<TIn>::n;
+    constexpr int L = 1 << BITS;
+    constexpr int CW = D * BITS / 32, SWN = D / 32;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     KeySmem s;
     {
         unsigned char *p = smem_raw;
         s.rfrag = reinterpret_cast<uint4 *>(p);   p += sizeof(uint4) * kKT * KS * 2 * 64;
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
-        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * (D / 4);
-        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * (D / 32);
-        s.knorm = reinterpret_cast<float *>(p);   p += sizeof(float) * kKeys;
+        s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
+        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
+        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWN;
         s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
-        s.bnd = reinterpret_cast<float *>(p);
+        s.bnd = reinterpret_cast<float *>(p);     p += sizeof(float) * 256;
+        s.grid = p;
     }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, kb = lane >> 4;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kKeys;
-    const int bits = a.bits, L = 1 << bits;
-    const int CW = D * bits / 32, SWN = D / 32;
 
     for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
-    for (int i = tid; i < L; i += kThreads) s.cent[i] = a.centroids[i];
-    for (int i = tid; i < L - 1; i += kThreads) s.bnd[i] = a.boundaries[i];
+    for (int i = tid; i < L; i += kThreads) {
+        s.cent[i] = a.centroids[i];
+        s.bnd[i] = a.boundaries[i];      // entry L - 1 is +inf
+    }
+    if constexpr (BITS >= 3)
+        for (int i = tid; i < a.ngrid; i += kThreads) s.grid[i] = a.grid[i];
 
     // rows of this lane's four keys
     const TIn *kp[kKT];
@@ -169,11 +194,12 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     double ss[kKT] = {0.0, 0.0, 0.0, 0.0};
     const int npp = a.hadamard ? 1 : 3;
+    const int bits = BITS;
 #pragma unroll 2
     for (int ks = 0; ks < KS; ++ks) {
         uint4 kf[kKT][NK];
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) key_frag(kp[kt] + 32 * ks, valid[kt], kf[kt], ss[kt]);
+        for (int kt = 0; kt < kKT; ++kt) key_frag(kp[kt] + 32 * ks, valid[kt], kf[kt], ss[kt], (ks & 3) == wave);
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
             const int rt = wave * RTW + j;
@@ -189,40 +215,62 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         }
     }
 
-    // ---- 2. ||k|| (fp64 over the four lanes that hold one key)
-    float inv_n[kKT];
+    // ---- 2. ||k||: fp64 partial sums of this wave's k-steps, over the four lanes
+    // that hold one key, then across the waves
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
         double t = ss[kt];
         t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
-        const double n = sqrt(t);
-        inv_n[kt] = (n > 0.0) ? static_cast<float>((a.hadamard ? 1.0 / sqrt(double(D)) : 1.0) / n) : 0.0f;
-        if (wave == 0 && kb == 0) s.knorm[16 * kt + col] = static_cast<float>(n);
+        if (kb == 0) s.nrm2[wave * kKeys + 16 * kt + col] = t;
     }
-    __syncthreads();   // cleared words, codebook tables
+    __syncthreads();   // partial norms, cleared words, codebook tables
+    float inv_n[kKT];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+        const int key = 16 * kt + col;
+        const double n = sqrt(s.nrm2[key] + s.nrm2[kKeys + key] + s.nrm2[2 * kKeys + key] + s.nrm2[3 * kKeys + key]);
+        inv_n[kt] = (n > 0.0) ? static_cast<float>((a.hadamard ? 1.0 / sqrt(double(D)) : 1.0) / n) : 0.0f;
+    }
+    float tb[BITS <= 2 ? L - 1 : 1];             // boundaries in registers (1-2 bits)
+    if constexpr (BITS <= 2) {
+#pragma unroll
+        for (int i = 0; i < L - 1; ++i) tb[i] = s.bnd[i];
+    }
 
     // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
-        double rr = 0.0;
+        float rr = 0.0f;
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
             const int rt = wave * RTW + j;
-            uint32_t chunk = 0, rh[4], rl[4];
+            uint32_t chunk = 0;
+            float res[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float y = acc[j][kt][r] * inv_n[kt];
-                int pos = 0;
-                for (int step = L >> 1; step > 0; step >>= 1)
-                    if (s.bnd[pos + step - 1] < y) pos += step;
-                const float res = y - s.cent[pos];
-                rr = fma(static_cast<double>(res), static_cast<double>(res), rr);
+                int pos;
+                if constexpr (BITS <= 2) {
+                    pos = 0;
+#pragma unroll
+                    for (int i = 0; i < L - 1; ++i) pos += (y > tb[i]) ? 1 : 0;
+                } else {
+                    int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
+                    c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
+                    pos = s.grid[c];
+                    pos += (y > s.bnd[pos]) ? 1 : 0;
+                    pos += (y > s.bnd[pos]) ? 1 : 0;
+                }
+                res[r] = y - s.cent[pos];
+                rr = fmaf(res[r], res[r], rr);
                 chunk |= static_cast<uint32_t>(pos) << (bits * r);
-                rh[r] = bf16_rne_bits(res);
-                rl[r] = bf16_rne_bits(res - bf16_bits_f32(rh[r]));
             }
+            // residual as two bf16 terms (hardware round to nearest even)
+            const uint32_t h01 = bf16x2(res[0], res[1]), h23 = bf16x2(res[2], res[3]);
+            const uint32_t l01 = bf16x2(res[0] - __uint_as_float(h01 << 16), res[1] - __uint_as_float(h01 & 0xffff0000u));
+            const uint32_t l23 = bf16x2(res[2] - __uint_as_float(h23 << 16), res[3] - __uint_as_float(h23 & 0xffff0000u));
             // 4 codes of `bits` bits at bit offset bits (16 rt + 4 kb) of the key's stream
             const int off = bits * (16 * rt + 4 * kb), w = off >> 5, sh = off & 31;
             atomicOr(&s.cw[key * CW + w], chunk << sh);
@@ -231,12 +279,13 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
             uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 0) * 64 + lane]);
             uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 1) * 64 + lane]);
             const int hw = 2 * (rt & 1);
-            *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(rh[0] | (rh[1] << 16), rh[2] | (rh[3] << 16));
-            *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(rl[0] | (rl[1] << 16), rl[2] | (rl[3] << 16));
+            *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(l01, l23);
         }
-        rr += __shfl_xor(rr, 16);
-        rr += __shfl_xor(rr, 32);
-        if (kb == 0) s.rho2[wave * kKeys + key] = rr;
+        double rd = static_cast<double>(rr);
+        rd += __shfl_xor(rd, 16);
+        rd += __shfl_xor(rd, 32);
+        if (kb == 0) s.rho2[wave * kKeys + key] = rd;
     }
     __syncthreads();
 
@@ -288,18 +337,19 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
     for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
     if (tid < nk) {
-        a.out.knorm[n0 + tid] = s.knorm[tid];
+        const double n2 = s.nrm2[tid] + s.nrm2[kKeys + tid] + s.nrm2[2 * kKeys + tid] + s.nrm2[3 * kKeys + tid];
+        a.out.knorm[n0 + tid] = static_cast<float>(sqrt(n2));
         const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
         a.out.rnorm[n0 + tid] = static_cast<float>(sqrt(r2));
     }
 }
 
-template <int D, typename TIn>
+template <int D, typename TIn, int BITS>
 hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
 {
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
-    constexpr size_t smem = key_smem_bytes<D>();
-    auto kern = k_compress_keys<D, TIn>;
+    constexpr size_t smem = key_smem_bytes<D, BITS>();
+    auto kern = k_compress_keys<D, TIn, BITS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -311,13 +361,28 @@ hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int D, typename TIn>
+hipError_t launch_keys_b(const KeyLaunch &a, hipStream_t stream)
+{
+    switch (a.bits) {
+    case 1: return launch_keys_t<D, TIn, 1>(a, stream);
+    case 2: return launch_keys_t<D, TIn, 2>(a, stream);
+    case 3: return launch_keys_t<D, TIn, 3>(a, stream);
+    case 4: return launch_keys_t<D, TIn, 4>(a, stream);
+    case 5: return launch_keys_t<D, TIn, 5>(a, stream);
+    case 6: return launch_keys_t<D, TIn, 6>(a, stream);
+    case 7: return launch_keys_t<D, TIn, 7>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <typename TIn>
 hipError_t launch_keys_d(const KeyLaunch &a, hipStream_t stream)
 {
     switch (a.d) {
-    case 64: return launch_keys_t<64, TIn>(a, stream);
-    case 128: return launch_keys_t<128, TIn>(a, stream);
-    case 256: return launch_keys_t<256, TIn>(a, stream);
+    case 64: return launch_keys_b<64, TIn>(a, stream);
+    case 128: return launch_keys_b<128, TIn>(a, stream);
+    case 256: return launch_keys_b<256, TIn>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -12,7 +12,12 @@ struct tq_codebook {
     int d = 0, bits = 0;
     std::vector<double> centroids, boundaries;   // fp64 host tables
     float *d_centroids = nullptr;                // device fp32 [2^bits]
-    float *d_boundaries = nullptr;               // device fp32 [2^bits - 1]
+    float *d_boundaries = nullptr;               // device fp32 [2^bits - 1], then +inf
+    // uniform grid over [first, last boundary] for codes of 3+ bits: grid[c] is a
+    // lower bound of #{t_i < y} for every y of cell c, at most two below it
+    uint8_t *d_grid = nullptr;
+    int ngrid = 0;
+    float grid_lo = 0.0f, grid_scale = 0.0f;
     int device = 0;
 };
 
@@ -60,10 +65,14 @@ struct KeyLaunch {
     int d, bits, m;
     bool hadamard;
     const float *piT, *sT, *dsign, *centroids, *boundaries;
+    const uint8_t *grid;
+    int ngrid;
+    float grid_lo, grid_scale;
     const uint16_t *pifrag, *sfrag;
     tq_kcache out;
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
+constexpr int kMaxGrid = 4096;     // cells of the code grid (bytes of LDS)
 
 struct ValueLaunch {
     const void *v;
