@@ -171,17 +171,27 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     if constexpr (BITS >= 3)
         for (int i = tid; i < a.ngrid; i += kThreads) s.grid[i] = a.grid[i];
 
-    // rows of this lane's four keys
+    // rows of this lane's four keys: one divide per workgroup (wave-uniform),
+    // then each lane steps from (b0, h0, t0) across sequence / head boundaries
     const TIn *kp[kKT];
     bool valid[kKT];
+    {
+        const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
+        const int64_t b0 = bh0 / a.H, h0 = bh0 - b0 * a.H;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-        const int64_t n = n0 + 16 * kt + col;
-        valid[kt] = n < n_total;
-        const int64_t nn = valid[kt] ? n : 0;
-        const int64_t t = nn % a.T, bh = nn / a.T;
-        const int64_t b = bh / a.H, h = bh % a.H;
-        kp[kt] = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st + 8 * kb;
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int64_t n = n0 + 16 * kt + col;
+            valid[kt] = n < n_total;
+            int64_t t = t0 + (valid[kt] ? 16 * kt + col : 0), b = b0, h = h0;
+            while (t >= a.T) {          // at most 64 / T + 1 steps
+                t -= a.T;
+                if (++h == a.H) {
+                    h = 0;
+                    ++b;
+                }
+            }
+            kp[kt] = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st + 8 * kb;
+        }
     }
 
     // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r

@@ -33,13 +33,26 @@ __device__ __forceinline__ uint32_t value_code(float v, float zero, float scale,
 template <typename TIn, int G, int BITS>
 __global__ __launch_bounds__(kThreads) void k_compress_values(ValueLaunch a, int64_t n_groups)
 {
-    const int64_t gi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kThreads;   // workgroup-uniform
+    const int64_t gi = g0 + threadIdx.x;
     if (gi >= n_groups) return;
-    const int ng = a.d / G;
-    const int64_t n = gi / ng;
-    const int grp = static_cast<int>(gi % ng);
-    const int64_t t = n % a.T, bh = n / a.T;
-    const int64_t b = bh / a.H, h = bh % a.H;
+    // groups per vector is a power of two dividing the workgroup size: one
+    // divide per workgroup, then each thread steps from (b0, h0, t0)
+    const int lg = __builtin_ctz(a.d / G);
+    const int64_t nfirst = g0 >> lg;
+    const int off = static_cast<int>(threadIdx.x) >> lg;
+    const int grp = static_cast<int>(threadIdx.x) & ((1 << lg) - 1);
+    const int64_t n = nfirst + off;
+    const int64_t bh0 = nfirst / a.T;
+    int64_t t = nfirst - bh0 * a.T + off;
+    int64_t b = bh0 / a.H, h = bh0 - b * a.H;
+    while (t >= a.T) {                  // at most kThreads / T + 1 steps
+        t -= a.T;
+        if (++h == a.H) {
+            h = 0;
+            ++b;
+        }
+    }
     const TIn *src = static_cast<const TIn *>(a.v) + b * a.sb + h * a.sh + t * a.st + grp * G;
 
     float x[G];
