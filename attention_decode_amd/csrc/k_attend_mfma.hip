@@ -429,9 +429,15 @@ struct ScoreBits {
         }
     }
 
+    __device__ void scores(const KeyWords<BITS, D> &kw, float kappa, float (&sc)[2][MT]) const
+    {
+        score_tile(kw, 0, kappa, sc[0]);
+        score_tile(kw, 1, kappa, sc[1]);
+    }
+
     // B bytes are raw key bits at weight 2^k (mask without shift; the digit
     // rows carry the 2^-k); returns n (sum q_rot c + kappa rho sum Sq (2s - 1)) per slot
-    __device__ void scores(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[MT]) const
+    __device__ void score_tile(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[MT]) const
     {
         v4i accc[MT], accs[MT];
 #pragma unroll
@@ -483,7 +489,7 @@ struct ScoreLut {
     static constexpr int NTAB = PAIR ? 2 : 1;
     // copies of the code tables, interleaved entry-major so that lane l reads
     // copy l % COPIES: with 64 copies every lane owns its bank (no conflicts)
-    static constexpr int COPIES_RAW = 32768 / (NENT * 4 * NTAB);
+    static constexpr int COPIES_RAW = 8192 / (NENT * 4 * NTAB);
     static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 4 ? 4 : 1));
     static constexpr int TAB1 = NENT * 4 * COPIES;                     // bytes of one code table
     // the lo table starts 16 bytes past a multiple of 256 so that a hi and a lo
@@ -492,11 +498,12 @@ struct ScoreLut {
     static constexpr int LO_OFF = TAB1 + 16;
     static constexpr int CODE_TAB = PAIR ? LO_OFF + TAB1 : TAB1;
     static constexpr int SIGN_TAB = 256 * 16;
-    static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB;
-    v8h acode[KS], asign[KS];
+    static constexpr int AOP_BYTES = 2 * KS * 64 * 16;                // the unit's A operands, [2][KS][64 lanes]
+    static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     float scc[2], scs[2];
     const unsigned char *tab;
     int copy;                  // this lane's table copy
+    int lane_;
 
     __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
 
@@ -534,12 +541,12 @@ struct ScoreLut {
             const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
             ts[i] = lo | (hi << 16);
         }
+        // the unit's A operands go to LDS (shared by the four waves; loaded per
+        // k-step rather than held in registers)
         const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * 2 * KS * 64;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            acode[ks] = __builtin_bit_cast(v8h, src[ks * 64 + lane]);
-            asign[ks] = __builtin_bit_cast(v8h, src[(KS + ks) * 64 + lane]);
-        }
+        v4i *adst = reinterpret_cast<v4i *>(lds + CODE_TAB + SIGN_TAB);
+        for (int i = tid; i < 2 * KS * 64; i += kThreads) adst[i] = src[i];
+        lane_ = lane;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             const int g = 2 * kb + qq;
@@ -560,40 +567,50 @@ struct ScoreLut {
         return __builtin_amdgcn_alignbit(w[i + 1], w[i], s) & mask;
     }
 
-    __device__ void scores(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[2]) const
+    __device__ void scores(const KeyWords<BITS, D> &kw, float kappa, float (&sc)[2][2]) const
     {
         const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
         const uint32_t *tl = reinterpret_cast<const uint32_t *>(tab + LO_OFF);
         const v4i *ts = reinterpret_cast<const v4i *>(tab + CODE_TAB);
-        v4f accc = {0.0f, 0.0f, 0.0f, 0.0f}, accs = {0.0f, 0.0f, 0.0f, 0.0f};
+        const v4i *aop = reinterpret_cast<const v4i *>(tab + CODE_TAB + SIGN_TAB);
+        v4f accc[2], accs[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) accc[c] = accs[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            v4i bhi, blo;
+            const v8h acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
+            const v8h asign = __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                if (PAIR) {
-                    const uint32_t e = field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS) * COPIES + copy;
-                    bhi[p] = static_cast<int>(t1[e]);
-                    blo[p] = static_cast<int>(tl[e]);
-                } else {
-                    const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS) * COPIES + copy];
-                    const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS) * COPIES + copy];
-                    bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
-                    blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
+            for (int c = 0; c < 2; ++c) {
+                v4i bhi, blo;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    if (PAIR) {
+                        const uint32_t e = field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS) * COPIES + copy;
+                        bhi[p] = static_cast<int>(t1[e]);
+                        blo[p] = static_cast<int>(tl[e]);
+                    } else {
+                        const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS) * COPIES + copy];
+                        const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS) * COPIES + copy];
+                        bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
+                        blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
+                    }
                 }
+                accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, bhi), accc[c], 0, 0, 0);
+                accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, blo), accc[c], 0, 0, 0);
+                const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
+                accs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accs[c], 0, 0, 0);
             }
-            accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode[ks], __builtin_bit_cast(v8h, bhi), accc, 0, 0, 0);
-            accc = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode[ks], __builtin_bit_cast(v8h, blo), accc, 0, 0, 0);
-            const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
-            accs = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign[ks], __builtin_bit_cast(v8h, ts[sb]), accs, 0, 0, 0);
         }
         // rows 4 kb + r: (query 2 kb + r / 2, part r % 2)
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const float dcode = (accc[2 * qq] + accc[2 * qq + 1]) * scc[qq];
-            const float dsign = (accs[2 * qq] + accs[2 * qq + 1]) * scs[qq];
-            sc[qq] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
-        }
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const float dcode = (accc[c][2 * qq] + accc[c][2 * qq + 1]) * scc[qq];
+                const float dsign = (accs[c][2 * qq] + accs[c][2 * qq + 1]) * scs[qq];
+                sc[c][qq] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
+            }
     }
 };
 
@@ -604,8 +621,8 @@ struct ScoreLut {
 // before the current one is computed (two register buffers in turn).  The
 // four waves are merged in LDS at the end; with one split the workgroup
 // writes the normalised output, else its partial (max, sum, weighted values).
-template <class SCORE, int BITS, int D, int VBITS>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
+template <class SCORE, int BITS, int D, int VBITS, bool TWO>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 : 2)) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NQ = SCORE::NQ;
     constexpr int TK = 32;                       // keys per wave tile
@@ -614,7 +631,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
     constexpr int NCB = VB / 16;                 // 16-byte column blocks of a value row
     constexpr int NF = 8 / VBITS;                // code fields per byte
     constexpr int NTILE = NCB * NF;              // 16-channel tiles of the value product
-    constexpr bool kTwoGroups = NF * 16 > 32;    // a tile can span two value groups (group >= 32)
+    constexpr bool kTwoGroups = TWO;             // a 16-channel tile spans two value groups (2-bit values, group 32)
     constexpr int VCL = TK * VB / 16 / 64;       // 16-byte value chunks per lane per tile
     constexpr int NGM = D / 32;                  // most value groups per row (group >= 32)
     constexpr int PD = TK * NGM / 64;            // (scale, zero) dwords per lane per tile
@@ -748,14 +765,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
 
         // ---- scores of keys j and 16 + j for this lane's queries
         float lamv[NQ][2];
+        {
+            float sc[2][NQ];
+            score.scores(cur.kw, kappa, sc);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            float sc[NQ];
-            score.scores(cur.kw, c, kappa, sc);
-            const bool valid = 16 * c + j < nv;
+            for (int c = 0; c < 2; ++c) {
+                const bool valid = 16 * c + j < nv;
 #pragma unroll
-            for (int sl = 0; sl < NQ; ++sl)
-                lamv[sl][c] = (valid && SCORE::query(sl, kb) < GC) ? a.scale * sc[sl] : -INFINITY;
+                for (int sl = 0; sl < NQ; ++sl)
+                    lamv[sl][c] = (valid && SCORE::query(sl, kb) < GC) ? a.scale * sc[c][sl] : -INFINITY;
+            }
         }
 
         // ---- online softmax (per query, over the 16 lanes of its row block)
@@ -831,7 +850,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
             const int g_lo = (NF * 16 * cb) >> (__builtin_ctz(a.group));
             const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + g_lo * 256 + ard));
             v8h af1 = af0;
-            if (kTwoGroups && NF * 16 > a.group)
+            if constexpr (kTwoGroups)
                 af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + (g_lo + 1) * 256 + ard));
             const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(tr_base + 16 * cb));
             const uint32_t x0 = static_cast<uint32_t>(raw.x), x1 = static_cast<uint32_t>(raw.y);
@@ -845,21 +864,19 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
                 const v8h bv = __builtin_bit_cast(v8h, bop);
                 const int nt = cb * NF + f;
                 acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af0, bv, acc0[nt], 0, 0, 0);
-                if constexpr (kTwoGroups) {
-                    if (NF * 16 > a.group) acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bv, acc1[nt], 0, 0, 0);
-                }
+                if constexpr (kTwoGroups) acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af1, bv, acc1[nt], 0, 0, 0);
             }
         }
     };
 
     // Register ring of prefetched tiles: the loads of each tile are issued
     // DEPTH - 1 tiles ahead of its use, so that a wave keeps that many tiles
-    // of HBM reads in flight behind its compute (d 256 keeps two buffers:
-    // its registers are the limit there).  Tiles left after the unrolled trips
+    // of HBM reads in flight behind its compute (d 256 and the table scores
+    // keep two buffers: registers and occupancy are the limit there).  Tiles left after the unrolled trips
     // are computed from the buffers that already hold them.
     constexpr int STEP = 4 * TK;
     if (first < t_end) {
-        if constexpr (D == 256) {
+        if constexpr (D == 256 || SCORE::TAB_BYTES > 0) {
             Prefetch pa, pb;
             fetch(first, pa);
             int64_t t = first;
@@ -913,7 +930,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void k_attend(DecodeLau
         v4f acc = acc0[nt];
         if constexpr (kTwoGroups) {
             const v4f alt = acc1[nt];
-            if (NF * 16 > a.group && ch / a.group != g_lo) acc = alt;
+            if (ch / a.group != g_lo) acc = alt;
         }
         const float sc = 16777216.0f / static_cast<float>(1 << (VBITS * f));
 #pragma unroll
@@ -1003,7 +1020,11 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
     const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(a.mf.units));
     void *tok;
     prof_begin("tq_attend_splitk", stream, &tok);
-    hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    // 2-bit values in groups of 32: a 16-byte column block spans two groups
+    if (VBITS == 2 && a.group == 32)
+        hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, VBITS == 2>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    else
+        hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, false>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
     prof_end(tok, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
