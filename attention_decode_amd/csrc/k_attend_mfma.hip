@@ -90,25 +90,40 @@ __device__ __forceinline__ float load1(const f16_t *p) { return f16_bits_to_f32(
 // and of (S Pi)^T for every query (each matrix row is one coalesced read
 // shared by all queries); the eight row groups of a column block are
 // adjacent lanes, summed with DPP.  Leaves qv[g] = [q_rot | Sq].
-template <typename TIn>
+template <typename TIn, int GQ>
 __device__ void rotate_unit_queries(const DecodeLaunch &a, int GC, int64_t row0, float (*qs)[256], float (*qv)[512])
 {
     const int tid = threadIdx.x;
     const int D = a.d, M = a.m;
-    for (int i = tid; i < GC * D; i += kThreads)
-        qs[i / D][i % D] = load1(static_cast<const TIn *>(a.q) + (row0 + i / D) * D + i % D);
+    // the unit's queries, eight elements per thread in one load (absent
+    // queries read as zero, so the products below need no per-query guard)
+    {
+        const int i = 8 * tid, g = i / D, c = i % D;       // kMaxG * 256 = 8 * kThreads elements
+        float v[8];
+        if (g < GC && c < D) {
+            load8_as_f32(static_cast<const TIn *>(a.q) + (row0 + g) * D + c, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+        if (g < kMaxG) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qs[g][c + e] = v[e];
+        }
+    }
     __syncthreads();
     const int rg = tid % 8;
     for (int c4 = tid / 8; c4 < D / 4; c4 += kThreads / 8) {
-        float acc[2][4][kMaxG];
+        float acc[2][4][GQ];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int g = 0; g < kMaxG; ++g) acc[m][e][g] = 0.0f;
+                for (int g = 0; g < GQ; ++g) acc[m][e][g] = 0.0f;
         const float4 *p1 = reinterpret_cast<const float4 *>(a.piT) + c4;
         const float4 *p2 = reinterpret_cast<const float4 *>(a.spiT) + c4;
+#pragma unroll 4
         for (int j0 = 0; j0 < D; j0 += 64) {
             float4 u[8], v[8];
 #pragma unroll
@@ -121,18 +136,16 @@ __device__ void rotate_unit_queries(const DecodeLaunch &a, int GC, int64_t row0,
             for (int i = 0; i < 8; ++i) {
                 const int jj = j0 + rg + 8 * i;
 #pragma unroll
-                for (int g = 0; g < kMaxG; ++g) {
-                    if (g < GC) {
-                        const float qj = qs[g][jj];
-                        acc[0][0][g] = fmaf(u[i].x, qj, acc[0][0][g]);
-                        acc[0][1][g] = fmaf(u[i].y, qj, acc[0][1][g]);
-                        acc[0][2][g] = fmaf(u[i].z, qj, acc[0][2][g]);
-                        acc[0][3][g] = fmaf(u[i].w, qj, acc[0][3][g]);
-                        acc[1][0][g] = fmaf(v[i].x, qj, acc[1][0][g]);
-                        acc[1][1][g] = fmaf(v[i].y, qj, acc[1][1][g]);
-                        acc[1][2][g] = fmaf(v[i].z, qj, acc[1][2][g]);
-                        acc[1][3][g] = fmaf(v[i].w, qj, acc[1][3][g]);
-                    }
+                for (int g = 0; g < GQ; ++g) {
+                    const float qj = qs[g][jj];
+                    acc[0][0][g] = fmaf(u[i].x, qj, acc[0][0][g]);
+                    acc[0][1][g] = fmaf(u[i].y, qj, acc[0][1][g]);
+                    acc[0][2][g] = fmaf(u[i].z, qj, acc[0][2][g]);
+                    acc[0][3][g] = fmaf(u[i].w, qj, acc[0][3][g]);
+                    acc[1][0][g] = fmaf(v[i].x, qj, acc[1][0][g]);
+                    acc[1][1][g] = fmaf(v[i].y, qj, acc[1][1][g]);
+                    acc[1][2][g] = fmaf(v[i].z, qj, acc[1][2][g]);
+                    acc[1][3][g] = fmaf(v[i].w, qj, acc[1][3][g]);
                 }
             }
         }
@@ -141,14 +154,12 @@ __device__ void rotate_unit_queries(const DecodeLaunch &a, int GC, int64_t row0,
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int g = 0; g < kMaxG; ++g) {
-                    if (g < GC) {
-                        float x = acc[m][e][g];
-                        x += dpp<0xB1>(x);          // xor 1
-                        x += dpp<0x4E>(x);          // xor 2
-                        x += dpp<0x141>(x);         // half-row mirror: lane i <-> 7 - i
-                        if (rg == 0) qv[g][m * D + 4 * c4 + e] = x;
-                    }
+                for (int g = 0; g < GQ; ++g) {
+                    float x = acc[m][e][g];
+                    x += dpp<0xB1>(x);          // xor 1
+                    x += dpp<0x4E>(x);          // xor 2
+                    x += dpp<0x141>(x);         // half-row mirror: lane i <-> 7 - i
+                    if (rg == 0) qv[g][m * D + 4 * c4 + e] = x;
                 }
     }
     __syncthreads();
@@ -164,7 +175,7 @@ __device__ __forceinline__ int64_t unit_row0(const DecodeLaunch &a, int unit)
 
 // Bit-plane score operands (keys with 1 or 2 bits): per query the fixed-point
 // scales and constant terms, and the int8 digit rows of the score products.
-template <typename TIn>
+template <typename TIn, int GQ>
 __global__ __launch_bounds__(kThreads) void k_qprep_bits(DecodeLaunch a)
 {
     __shared__ float qs[kMaxG][256];
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_qprep_bits(DecodeLaunch a)
         s_acoef[0] = a.centroids[1] - a.centroids[0];
         s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
     }
-    rotate_unit_queries<TIn>(a, GC, row0, qs, qv);
+    rotate_unit_queries<TIn, GQ>(a, GC, row0, qs, qv);
     // per-query maxima and sums, one wave per query
     for (int g = wave; g < GC; g += 4) {
         float mc = 0.0f, sc = 0.0f, ms = 0.0f, ss = 0.0f;
@@ -270,7 +281,7 @@ constexpr int kCodeExp = 10;       // centroid tables hold c * 2^kCodeExp
 
 __device__ __forceinline__ uint32_t f16_rn_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 
-template <typename TIn>
+template <typename TIn, int GQ>
 __global__ __launch_bounds__(kThreads) void k_qprep_lut(DecodeLaunch a)
 {
     __shared__ float qs[kMaxG][256];
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_qprep_lut(DecodeLaunch a)
     const int GC = a.mf.gc;
     const int unit = blockIdx.x;
     const int64_t row0 = unit_row0(a, unit);
-    rotate_unit_queries<TIn>(a, GC, row0, qs, qv);
+    rotate_unit_queries<TIn, GQ>(a, GC, row0, qs, qv);
     for (int g = wave; g < GC; g += 4) {
         float mc = 0.0f, ms = 0.0f;
         for (int j = lane; j < D; j += 64) mc = fmaxf(mc, fabsf(qv[g][j]));
@@ -1001,6 +1012,13 @@ __global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
         const int n = S - s0 < kThreads ? S - s0 : kThreads;
         if (tid < D) {
             int k = 0;
+            for (; k + 32 <= n; k += 32) {          // 32 loads in flight
+                float v[32];
+#pragma unroll
+                for (int u = 0; u < 32; ++u) v[u] = pa[static_cast<int64_t>(s0 + k + u) * D + tid];
+#pragma unroll
+                for (int u = 0; u < 32; ++u) o = fmaf(wts[k + u], v[u], o);
+            }
             for (; k + 8 <= n; k += 8) {
                 float v[8];
 #pragma unroll
@@ -1069,12 +1087,23 @@ hipError_t launch_attend_d(const DecodeLaunch &a, hipStream_t s, float kappa, in
     return hipErrorInvalidValue;
 }
 
+template <typename TIn, int GQ>
+void launch_qprep_g(const DecodeLaunch &a, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(a.mf.units));
+    if (a.bits <= 2) hipLaunchKernelGGL((k_qprep_bits<TIn, GQ>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_qprep_lut<TIn, GQ>), grid, dim3(kThreads), 0, stream, a);
+}
+
 template <typename TIn>
 void launch_qprep_t(const DecodeLaunch &a, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(a.mf.units));
-    if (a.bits <= 2) hipLaunchKernelGGL(k_qprep_bits<TIn>, grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(k_qprep_lut<TIn>, grid, dim3(kThreads), 0, stream, a);
+    switch (a.mf.gc) {
+    case 1: launch_qprep_g<TIn, 1>(a, stream); break;
+    case 2: launch_qprep_g<TIn, 2>(a, stream); break;
+    case 4: launch_qprep_g<TIn, 4>(a, stream); break;
+    default: launch_qprep_g<TIn, 8>(a, stream); break;
+    }
 }
 
 }  // namespace
