@@ -2,6 +2,7 @@
 // the launch of the HIP kernels.  Nothing here computes on the data path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -282,7 +283,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
     std::vector<double> pi(dd), s(dd);
     tq_status st = tq_rotation_host(seed, d, kind, pi.data(), s.data());
     if (st != TQ_OK) return st;
-    std::vector<float> host(5 * dd + d);
+    std::vector<float> host(5 * dd + 3 * d);
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
             host[i * d + j] = static_cast<float>(pi[i * d + j]);            // Pi
@@ -290,13 +291,26 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
             host[2 * dd + i * d + j] = static_cast<float>(s[i * d + j]);    // S
             host[3 * dd + j * d + i] = static_cast<float>(s[i * d + j]);    // S^T
         }
-    // (S Pi)^T in fp64, rounded once: Sq = S (Pi q) = (S Pi) q
-    for (int i = 0; i < d; ++i)
+    // (S Pi)^T in fp64, rounded once: Sq = S (Pi q) = (S Pi) q; with the
+    // column sums of Pi and S Pi and the largest row norm of S Pi
+    std::vector<double> pisum(d, 0.0), spisum(d, 0.0);
+    double rmax = 0.0;
+    for (int i = 0; i < d; ++i) {
+        double r2 = 0.0;
         for (int j = 0; j < d; ++j) {
             double acc = 0.0;
             for (int k = 0; k < d; ++k) acc += s[static_cast<size_t>(i) * d + k] * pi[static_cast<size_t>(k) * d + j];
             host[4 * dd + static_cast<size_t>(j) * d + i] = static_cast<float>(acc);
+            spisum[j] += acc;
+            pisum[j] += pi[static_cast<size_t>(i) * d + j];
+            r2 += acc * acc;
         }
+        rmax = std::max(rmax, std::sqrt(r2));
+    }
+    for (int j = 0; j < d; ++j) {
+        host[5 * dd + d + j] = static_cast<float>(pisum[j]);
+        host[5 * dd + 2 * d + j] = static_cast<float>(spisum[j]);
+    }
     if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 5 * dd);
     else for (int j = 0; j < d; ++j) host[5 * dd + j] = 1.0f;
     auto *rot = new (std::nothrow) tq_rotation;
@@ -356,6 +370,9 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
     rot->d_sT = base + 3 * dd;
     rot->d_spiT = base + 4 * dd;
     rot->d_dsign = base + 5 * dd;
+    rot->d_pisum = base + 5 * dd + d;
+    rot->d_spisum = base + 5 * dd + 2 * d;
+    rot->sq_bound = static_cast<float>(rmax * (1.0 + 1e-6));
     *out = rot;
     return TQ_OK;
 }
@@ -688,6 +705,9 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     a.piT = kfmt->rot->d_piT;
     a.sT = kfmt->rot->d_sT;
     a.spiT = kfmt->rot->d_spiT;
+    a.pisum = kfmt->rot->d_pisum;
+    a.spisum = kfmt->rot->d_spisum;
+    a.sq_bound = kfmt->rot->sq_bound;
     a.centroids = kfmt->cb->d_centroids;
     a.kc = kc;
     a.vbits = vfmt->bits;

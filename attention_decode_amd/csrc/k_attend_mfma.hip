@@ -83,88 +83,6 @@ __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(p->bits); }
 __device__ __forceinline__ float load1(const f16_t *p) { return f16_bits_to_f32(p->bits); }
 
-// ---------------------------------------------------------------- q-prep
-// One workgroup per unit (sequence, KV head, query chunk).  q_rot = Pi q and
-// Sq = (S Pi) q for the unit's GC queries: thread (column block c4, row group
-// rg = tid % 8) sums rows rg, rg + 8, ... of four adjacent columns of Pi^T
-// and of (S Pi)^T for every query (each matrix row is one coalesced read
-// shared by all queries); the eight row groups of a column block are
-// adjacent lanes, summed with DPP.  Leaves qv[g] = [q_rot | Sq].
-template <typename TIn, int GQ>
-__device__ void rotate_unit_queries(const DecodeLaunch &a, int GC, int64_t row0, float (*qs)[256], float (*qv)[512])
-{
-    const int tid = threadIdx.x;
-    const int D = a.d, M = a.m;
-    // the unit's queries, eight elements per thread in one load (absent
-    // queries read as zero, so the products below need no per-query guard)
-    {
-        const int i = 8 * tid, g = i / D, c = i % D;       // kMaxG * 256 = 8 * kThreads elements
-        float v[8];
-        if (g < GC && c < D) {
-            load8_as_f32(static_cast<const TIn *>(a.q) + (row0 + g) * D + c, v);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-        }
-        if (g < kMaxG) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qs[g][c + e] = v[e];
-        }
-    }
-    __syncthreads();
-    const int rg = tid % 8;
-    for (int c4 = tid / 8; c4 < D / 4; c4 += kThreads / 8) {
-        float acc[2][4][GQ];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int g = 0; g < GQ; ++g) acc[m][e][g] = 0.0f;
-        const float4 *p1 = reinterpret_cast<const float4 *>(a.piT) + c4;
-        const float4 *p2 = reinterpret_cast<const float4 *>(a.spiT) + c4;
-#pragma unroll 4
-        for (int j0 = 0; j0 < D; j0 += 64) {
-            float4 u[8], v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int jj = j0 + rg + 8 * i;
-                u[i] = p1[static_cast<int64_t>(jj) * (D / 4)];
-                v[i] = p2[static_cast<int64_t>(jj) * (M / 4)];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int jj = j0 + rg + 8 * i;
-#pragma unroll
-                for (int g = 0; g < GQ; ++g) {
-                    const float qj = qs[g][jj];
-                    acc[0][0][g] = fmaf(u[i].x, qj, acc[0][0][g]);
-                    acc[0][1][g] = fmaf(u[i].y, qj, acc[0][1][g]);
-                    acc[0][2][g] = fmaf(u[i].z, qj, acc[0][2][g]);
-                    acc[0][3][g] = fmaf(u[i].w, qj, acc[0][3][g]);
-                    acc[1][0][g] = fmaf(v[i].x, qj, acc[1][0][g]);
-                    acc[1][1][g] = fmaf(v[i].y, qj, acc[1][1][g]);
-                    acc[1][2][g] = fmaf(v[i].z, qj, acc[1][2][g]);
-                    acc[1][3][g] = fmaf(v[i].w, qj, acc[1][3][g]);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int g = 0; g < GQ; ++g) {
-                    float x = acc[m][e][g];
-                    x += dpp<0xB1>(x);          // xor 1
-                    x += dpp<0x4E>(x);          // xor 2
-                    x += dpp<0x141>(x);         // half-row mirror: lane i <-> 7 - i
-                    if (rg == 0) qv[g][m * D + 4 * c4 + e] = x;
-                }
-    }
-    __syncthreads();
-}
-
 // unit index -> first query row
 __device__ __forceinline__ int64_t unit_row0(const DecodeLaunch &a, int unit)
 {
@@ -173,168 +91,190 @@ __device__ __forceinline__ int64_t unit_row0(const DecodeLaunch &a, int unit)
     return static_cast<int64_t>(b) * a.Hq + hkv * (a.Hq / a.Hkv) + qc * a.mf.gc;
 }
 
-// Bit-plane score operands (keys with 1 or 2 bits): per query the fixed-point
-// scales and constant terms, and the int8 digit rows of the score products.
-template <typename TIn, int GQ>
-__global__ __launch_bounds__(kThreads) void k_qprep_bits(DecodeLaunch a)
-{
-    __shared__ float qs[kMaxG][256];
-    __shared__ float qv[kMaxG][512];           // [q_rot (D) | Sq (M)] per query
-    __shared__ int s_f[kMaxG][2];              // fixed-point exponents (code rows, sign rows)
-    __shared__ float s_acoef[2];
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int D = a.d, M = a.m;
-    const int GC = a.mf.gc, MT = a.mf.mt;
-    const int unit = blockIdx.x;
-    const int64_t row0 = unit_row0(a, unit);
-    if (tid == 0) {
-        // bit-affine form of the codebook (exact for symmetric codebooks)
-        s_acoef[0] = a.centroids[1] - a.centroids[0];
-        s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
-    }
-    rotate_unit_queries<TIn, GQ>(a, GC, row0, qs, qv);
-    // per-query maxima and sums, one wave per query
-    for (int g = wave; g < GC; g += 4) {
-        float mc = 0.0f, sc = 0.0f, ms = 0.0f, ss = 0.0f;
-        for (int j = lane; j < D; j += 64) {
-            mc = fmaxf(mc, fabsf(qv[g][j]));
-            sc += qv[g][j];
-        }
-        for (int i = lane; i < M; i += 64) {
-            ms = fmaxf(ms, fabsf(qv[g][D + i]));
-            ss += qv[g][D + i];
-        }
-        mc = wave_max(mc);
-        sc = wave_sum(sc);
-        ms = wave_max(ms);
-        ss = wave_sum(ss);
-        if (lane == 0) {
-            const float mw = mc * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1]));
-            int ec = 0, es = 0;
-            frexpf(mw, &ec);          // mw < 2^ec
-            frexpf(ms, &es);
-            const int fc = (mw > 0.0f) ? 26 - ec : 0;
-            const int fs = (ms > 0.0f) ? 26 - es : 0;
-            s_f[g][0] = fc;
-            s_f[g][1] = fs;
-            float *sc4 = a.mf.qscal + (row0 + g) * 4;
-            sc4[0] = ldexpf(1.0f, -fc);
-            sc4[1] = a.centroids[0] * sc;
-            sc4[2] = ldexpf(1.0f, -fs);
-            sc4[3] = ss;
-        }
-    }
-    __syncthreads();
-    // digit rows: query g uses lanes 16 kb + 4 (g % 4) + digit of row tile g / 4;
-    // dword r of a lane holds elements 4r..4r+3 of its 16-element k-block
-    const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
-    const int S = 2 * nc + 2 * ns;
-    uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
-    // one work item per (query, step, k-block, dword): four weights, each split
-    // into its four balanced digits, give the item's dword in all four limb rows
-    for (int w = tid; w < MT * 4 * S * 16; w += kThreads) {
-        const int r = w % 4, kb = (w / 4) % 4, s = (w / 16) % S, g = w / (16 * S);
-        uint32_t dw[4] = {0u, 0u, 0u, 0u};
-        if (g < GC) {
-#pragma unroll
-            for (int K = 0; K < 4; ++K) {
-                float wv;
-                int f;
-                if (s < 2 * nc) {
-                    const int u = s / 2, h = s % 2;
-                    const int bit = 32 * (kb * nc + u) + 8 * K + 4 * h + r;
-                    wv = qv[g][bit >> (a.bits - 1)] * s_acoef[bit & (a.bits - 1)];   // bits is 1 or 2
-                    f = s_f[g][0];
-                } else {
-                    const int s2 = s - 2 * nc, u = s2 / 2, h = s2 % 2;
-                    const int bit = 32 * (kb * ns + u) + 8 * K + 4 * h + r;
-                    wv = qv[g][D + bit];
-                    f = s_f[g][1];
-                }
-                // the key bit arrives as byte 2^sh (masked in place, not shifted):
-                // weight w 2^-sh, negated for sh = 7 where the byte reads as -128
-                const int sh = 4 * (s % 2) + r;
-                int x = static_cast<int>(rintf(ldexpf(wv, f - sh)));
-                if (sh == 7) x = -x;
-#pragma unroll
-                for (int limb = 0; limb < 3; ++limb) {
-                    const int d = ((x + 64) & 127) - 64;
-                    dw[limb] |= (static_cast<uint32_t>(d) & 0xffu) << (8 * K);
-                    x = (x - d) >> 7;
-                }
-                dw[3] |= (static_cast<uint32_t>(x) & 0xffu) << (8 * K);
-            }
-        }
-#pragma unroll
-        for (int limb = 0; limb < 4; ++limb) {
-            const int l = 16 * kb + 4 * (g % 4) + limb;
-            out[((g / 4) * S + s) * 256 + l * 4 + r] = dw[limb];
-        }
-    }
-}
-
-// Table score operands (keys with 3 to 8 bits): q_rot and Sq scaled by a power
-// of two to a largest magnitude below 2^10, as fp16 hi + lo rows (2 q, 2 q + 1)
-// of the A operands of v_mfma_f32_16x16x32_f16; k-block kb of step ks holds
-// coordinates kb d/4 + 8 ks + e.  Scales: qscal = {2^-(fq + kCodeExp), 2^-fs}.
+// ---------------------------------------------------------------- q-prep
+// Score operands of the unit's queries (unit = sequence, KV head, query
+// chunk): q_rot = Pi q and Sq = (S Pi) q ("turboquant-pytorch", section "What
+// it does": the query is rotated once and projected once per decode step),
+// converted to the A-operand layouts of the score products.  k-block kb of
+// every score step reads coordinates [kb D/4, (kb + 1) D/4) of one of the two
+// vectors, so workgroup (unit, part, kb) computes just that quarter of q_rot
+// (part 0) or Sq (part 1): eight workgroups per unit, each with a short
+// dependency chain.  The fixed-point exponents come from bounds that every
+// workgroup evaluates alike, with no exchange between them: |q_rot_j| <= |q|
+// (Pi is orthogonal) and |Sq_i| <= |q| max_i |(S Pi)_i|.  The constant terms
+// use column sums of Pi and S Pi fixed at rotation set-up:
+// sum_j q_rot_j = (1^T Pi) q and sum_i Sq_i = (1^T S Pi) q.
 constexpr int kCodeExp = 10;       // centroid tables hold c * 2^kCodeExp
 
 __device__ __forceinline__ uint32_t f16_rn_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 
-template <typename TIn, int GQ>
-__global__ __launch_bounds__(kThreads) void k_qprep_lut(DecodeLaunch a)
+template <typename TIn, int D, int GQ>
+__global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
 {
-    __shared__ float qs[kMaxG][256];
-    __shared__ float qv[kMaxG][512];
-    __shared__ int s_f[kMaxG][2];
+    constexpr int CB = D / 4;                  // coordinates of the quarter
+    constexpr int R = kThreads / CB;           // row parts of each product
+    constexpr int NR = D / R;                  // matrix rows per thread
+    __shared__ float qs[GQ][D];
+    __shared__ float red[R][GQ][CB];
+    __shared__ float xv[GQ][CB];
+    __shared__ int s_f[GQ][2];
+    __shared__ float s_acoef[2];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-    const int D = a.d, M = a.m;
-    const int GC = a.mf.gc;
-    const int unit = blockIdx.x;
+    const int unit = blockIdx.x, part = blockIdx.y / 4, kb = blockIdx.y % 4;
+    const bool bitplane = a.bits <= 2;
     const int64_t row0 = unit_row0(a, unit);
-    rotate_unit_queries<TIn, GQ>(a, GC, row0, qs, qv);
-    for (int g = wave; g < GC; g += 4) {
-        float mc = 0.0f, ms = 0.0f;
-        for (int j = lane; j < D; j += 64) mc = fmaxf(mc, fabsf(qv[g][j]));
-        for (int i = lane; i < M; i += 64) ms = fmaxf(ms, fabsf(qv[g][D + i]));
-        mc = wave_max(mc);
-        ms = wave_max(ms);
+    // this thread's rows of the matrix column: issued before the query load,
+    // which they do not depend on
+    const float *mtx = part ? a.spiT : a.piT;     // [D][D], row j = input coordinate
+    const int cl = tid % CB, jp = tid / CB;
+    float mv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) mv[i] = mtx[(jp * NR + i) * D + kb * CB + cl];
+    {
+        const int i = 8 * tid, g = i / D, c = i % D;
+        if (g < GQ) {
+            float v[8];
+            load8_as_f32(static_cast<const TIn *>(a.q) + (row0 + g) * D + c, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qs[g][c + e] = v[e];
+        }
+    }
+    if (tid == 0) {
+        // bit-affine form of a symmetric 1- or 2-bit codebook
+        s_acoef[0] = bitplane ? a.centroids[1] - a.centroids[0] : 0.0f;
+        s_acoef[1] = (a.bits == 2) ? a.centroids[2] - a.centroids[0] : 0.0f;
+    }
+    __syncthreads();
+    {
+        float acc[GQ];
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) acc[g] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int g = 0; g < GQ; ++g) acc[g] = fmaf(mv[i], qs[g][jp * NR + i], acc[g]);
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) red[jp][g][cl] = acc[g];
+    }
+    // per query: |q| bound, exponents; the (part 0, quarter 0) workgroup also
+    // writes the scales and constant terms
+    const bool head = blockIdx.y == 0;
+    for (int g = wave; g < GQ; g += 4) {
+        float s2 = 0.0f, sc = 0.0f, ss = 0.0f;
+        for (int j = lane; j < D; j += 64) {
+            const float x = qs[g][j];
+            s2 = fmaf(x, x, s2);
+            if (head && bitplane) {
+                sc = fmaf(a.pisum[j], x, sc);
+                ss = fmaf(a.spisum[j], x, ss);
+            }
+        }
+        s2 = wave_sum(s2);
+        if (head && bitplane) {
+            sc = wave_sum(sc);
+            ss = wave_sum(ss);
+        }
         if (lane == 0) {
+            const float qn = sqrtf(s2) * (1.0f + 0x1p-16f);      // >= max_j |q_rot_j|, rounding included
+            const float mc = bitplane ? qn * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1])) : qn;
+            const float ms = qn * a.sq_bound;
+            const int top = bitplane ? 26 : 10;                   // |scaled value| < 2^top
             int ec = 0, es = 0;
             frexpf(mc, &ec);
             frexpf(ms, &es);
-            const int fq = (mc > 0.0f) ? 10 - ec : 0;
-            const int fs = (ms > 0.0f) ? 10 - es : 0;
-            s_f[g][0] = fq;
+            const int fc = (mc > 0.0f) ? top - ec : 0;
+            const int fs = (ms > 0.0f) ? top - es : 0;
+            s_f[g][0] = fc;
             s_f[g][1] = fs;
-            float *sc4 = a.mf.qscal + (row0 + g) * 4;
-            sc4[0] = ldexpf(1.0f, -(fq + kCodeExp));
-            sc4[1] = ldexpf(1.0f, -fs);
-            sc4[2] = 0.0f;
-            sc4[3] = 0.0f;
+            if (head) {
+                float *sc4 = a.mf.qscal + (row0 + g) * 4;
+                if (bitplane) {
+                    sc4[0] = ldexpf(1.0f, -fc);
+                    sc4[1] = a.centroids[0] * sc;
+                    sc4[2] = ldexpf(1.0f, -fs);
+                    sc4[3] = ss;
+                } else {
+                    sc4[0] = ldexpf(1.0f, -(fc + kCodeExp));
+                    sc4[1] = ldexpf(1.0f, -fs);
+                    sc4[2] = 0.0f;
+                    sc4[3] = 0.0f;
+                }
+            }
         }
     }
     __syncthreads();
-    // aops[unit][part (code, sign)][ks][lane][4 dwords]
-    const int KS = D / 32;
-    uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * 2 * KS * 256;
-    for (int w = tid; w < 2 * KS * 256; w += kThreads) {
-        const int r = w % 4, l = (w / 4) % 64, ks = (w / 256) % KS, part = w / (256 * KS);
-        const int row = l % 16, kb = l / 16, g = row / 2, lo = row % 2;
-        uint32_t dw = 0u;
-        if (g < GC) {
+    for (int o = tid; o < GQ * CB; o += kThreads) {
+        const int g = o / CB, c = o % CB;
+        float x = 0.0f;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int coord = kb * (D / 4) + 8 * ks + 2 * r + h;
-                const float x = ldexpf(qv[g][part * D + coord], s_f[g][part]);
-                const _Float16 xh = static_cast<_Float16>(x);
-                const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
-                dw |= bits << (16 * h);
+        for (int r = 0; r < R; ++r) x += red[r][g][c];
+        xv[g][c] = x;
+    }
+    __syncthreads();
+    if (bitplane) {
+        // int8 digit rows: query g uses lanes 16 kb + 4 (g % 4) + digit of row
+        // tile g / 4; dword r of a lane holds elements 4r..4r+3 of its k-block.
+        // Code step s = 2u + h reads word u of the quarter (bit 32 u + 8 K + 4 h + r,
+        // coordinate bit / bits); sign step 2 nc + 2u + h reads coordinate
+        // 32 u + 8 K + 4 h + r of Sq.
+        const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
+        const int S = 2 * nc + 2 * ns, MT = a.mf.mt;
+        const int s_lo = part ? 2 * nc : 0, s_n = part ? 2 * ns : 2 * nc;
+        uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
+        for (int w = tid; w < MT * 4 * s_n * 4; w += kThreads) {
+            const int r = w % 4, sl = (w / 4) % s_n, g = w / (4 * s_n);
+            const int u = sl / 2, h = sl % 2;
+            uint32_t dw[4] = {0u, 0u, 0u, 0u};
+            if (g < GQ) {
+                const int f = s_f[g][part];
+#pragma unroll
+                for (int K = 0; K < 4; ++K) {
+                    const int bit = 32 * u + 8 * K + 4 * h + r;
+                    const float wv = part ? xv[g][bit] : xv[g][bit >> (a.bits - 1)] * s_acoef[bit & (a.bits - 1)];
+                    // the key bit arrives as byte 2^sh (masked in place, not shifted):
+                    // weight w 2^-sh, negated for sh = 7 where the byte reads as -128
+                    const int sh = 4 * h + r;
+                    int x = static_cast<int>(rintf(ldexpf(wv, f - sh)));
+                    if (sh == 7) x = -x;
+#pragma unroll
+                    for (int limb = 0; limb < 3; ++limb) {
+                        const int d = ((x + 64) & 127) - 64;
+                        dw[limb] |= (static_cast<uint32_t>(d) & 0xffu) << (8 * K);
+                        x = (x - d) >> 7;
+                    }
+                    dw[3] |= (static_cast<uint32_t>(x) & 0xffu) << (8 * K);
+                }
+            }
+#pragma unroll
+            for (int limb = 0; limb < 4; ++limb) {
+                const int l = 16 * kb + 4 * (g % 4) + limb;
+                out[((g / 4) * S + s_lo + sl) * 256 + l * 4 + r] = dw[limb];
             }
         }
-        out[w] = dw;
+    } else {
+        // fp16 hi + lo rows (2 g, 2 g + 1) of the A operands of
+        // v_mfma_f32_16x16x32_f16: aops[unit][part][ks][lane][4 dwords], k-block
+        // kb of step ks holding coordinates kb D/4 + 8 ks + e
+        constexpr int KS = D / 32;
+        uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * 2 * KS * 256;
+        for (int w = tid; w < KS * 64; w += kThreads) {
+            const int r = w % 4, row = (w / 4) % 16, ks = w / 64;
+            const int g = row / 2, lo = row % 2;
+            uint32_t dw = 0u;
+            if (g < GQ) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float x = ldexpf(xv[g][8 * ks + 2 * r + h], s_f[g][part]);
+                    const _Float16 xh = static_cast<_Float16>(x);
+                    const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
+                    dw |= bits << (16 * h);
+                }
+            }
+            out[((part * KS + ks) * 64 + 16 * kb + row) * 4 + r] = dw;
+        }
     }
 }
+
 
 // ------------------------------------------------------------ attention
 // 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
@@ -1087,23 +1027,23 @@ hipError_t launch_attend_d(const DecodeLaunch &a, hipStream_t s, float kappa, in
     return hipErrorInvalidValue;
 }
 
-template <typename TIn, int GQ>
-void launch_qprep_g(const DecodeLaunch &a, hipStream_t stream)
+template <typename TIn, int D>
+void launch_qprep_d(const DecodeLaunch &a, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(a.mf.units));
-    if (a.bits <= 2) hipLaunchKernelGGL((k_qprep_bits<TIn, GQ>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((k_qprep_lut<TIn, GQ>), grid, dim3(kThreads), 0, stream, a);
+    const dim3 grid(static_cast<unsigned>(a.mf.units), 8);
+    switch (a.mf.gc) {
+    case 1: hipLaunchKernelGGL((k_qprep<TIn, D, 1>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_qprep<TIn, D, 2>), grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_qprep<TIn, D, 4>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_qprep<TIn, D, 8>), grid, dim3(kThreads), 0, stream, a); break;
+    }
 }
 
 template <typename TIn>
 void launch_qprep_t(const DecodeLaunch &a, hipStream_t stream)
 {
-    switch (a.mf.gc) {
-    case 1: launch_qprep_g<TIn, 1>(a, stream); break;
-    case 2: launch_qprep_g<TIn, 2>(a, stream); break;
-    case 4: launch_qprep_g<TIn, 4>(a, stream); break;
-    default: launch_qprep_g<TIn, 8>(a, stream); break;
-    }
+    if (a.d == 128) launch_qprep_d<TIn, 128>(a, stream);
+    else launch_qprep_d<TIn, 256>(a, stream);
 }
 
 }  // namespace

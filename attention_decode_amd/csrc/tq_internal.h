@@ -32,6 +32,9 @@ struct tq_rotation {
     float *d_sT = nullptr;      // [d][m]  transpose of S
     float *d_dsign = nullptr;   // [d]     Hadamard signs (+-1), dense: unused
     float *d_spiT = nullptr;    // [d][m]  transpose of S Pi (Sq = S Pi q in one product)
+    float *d_pisum = nullptr;   // [d]     column sums of Pi: sum_j (Pi q)_j = pisum . q
+    float *d_spisum = nullptr;  // [d]     column sums of S Pi
+    float sq_bound = 0.0f;      // max row norm of S Pi (rounded up): |(S Pi q)_i| <= sq_bound |q|
     // bf16 operand fragments of the matrix-core key compressor, in lane order
     // (16x16x32 MFMA A operand: lane = row % 16 + 16 * k-block, 8 elements):
     //   pifrag [d/16 row tiles][d/32 k-steps][3 parts][64][8]: Pi = hi + mid + lo
@@ -102,6 +105,8 @@ struct DecodeLaunch {
     int d, bits, m;
     const float *piT, *sT, *centroids;
     const float *spiT;          // (S Pi)^T, [d][m]
+    const float *pisum, *spisum;    // column sums of Pi and S Pi
+    float sq_bound;             // max row norm of S Pi
     tq_kcache kc;
     // attention only
     int vbits, group;
