@@ -503,7 +503,12 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits) : 0;
     const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;
     const int64_t tiles = (T + tile - 1) / tile;
-    int64_t want = (1024 + p.units - 1) / p.units;      // about four workgroups per CU
+    // workgroups per launch: about eight per CU for the d = 128 matrix-core
+    // kernels (short enough splits that the last round is cheap), two for
+    // d = 256 (one workgroup per CU at a time, and a longer set-up), four for
+    // the scalar kernels
+    const int64_t target = p.mfma ? (fmt->d >= 256 ? 512 : 2048) : 1024;
+    int64_t want = (target + p.units - 1) / p.units;
     if (want > tiles) want = tiles;
     if (want > 1024) want = 1024;
     p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);

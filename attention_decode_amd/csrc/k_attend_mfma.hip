@@ -277,13 +277,26 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
 
 
 // ------------------------------------------------------------ attention
+// Softmax runs in base 2: scores leave the score stage multiplied by
+// scale log2(e), so every weight is one v_exp_f32 (2^x; -inf gives 0).  The
+// split maxima handed to the merge are in the same units.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
+// The maximum runs as four v_max_f32 with a DPP operand, each in place (every
+// lane of a row reads its source before any lane writes); the s_nop covers the
+// wait states between a VALU write and a DPP read of the same register.  The
+// operands are finite scores or -inf, never NaN, so the IEEE quieting that
+// fmaxf would add around a DPP move is not needed.
 __device__ __forceinline__ float row16_max(float x)
 {
-    x = fmaxf(x, dpp<0xB1>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    return fmaxf(x, dpp<0x140>(x));
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+        : "+v"(x));
+    return x;
 }
 
 __device__ __forceinline__ float row16_sum(float x)
@@ -361,7 +374,7 @@ struct ScoreBits {
         return r;
     }
 
-    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, unsigned char *)
+    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, float kappa, unsigned char *)
     {
         const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * MT * S * 64;
 #pragma unroll
@@ -373,22 +386,26 @@ struct ScoreBits {
             const int g = 4 * mt + kb;
             const bool ok = g < GC;
             const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
-            fc[mt] = ok ? sc[0] : 0.0f;
-            cc[mt] = ok ? sc[1] : 0.0f;
-            fs[mt] = ok ? sc[2] : 0.0f;
-            ssq[mt] = ok ? sc[3] : 0.0f;
+            // scores leave in log2 units of the softmax: scale log2(e) and the
+            // QJL factor kappa are folded into the per-query terms
+            const float f = a.scale * kLog2e, fk = f * kappa;
+            fc[mt] = ok ? sc[0] * f : 0.0f;
+            cc[mt] = ok ? sc[1] * f : 0.0f;
+            fs[mt] = ok ? 2.0f * sc[2] * fk : 0.0f;
+            ssq[mt] = ok ? sc[3] * fk : 0.0f;
         }
     }
 
-    __device__ void scores(const KeyWords<BITS, D> &kw, float kappa, float (&sc)[2][MT]) const
+    __device__ void scores(const KeyWords<BITS, D> &kw, float (&sc)[2][MT]) const
     {
-        score_tile(kw, 0, kappa, sc[0]);
-        score_tile(kw, 1, kappa, sc[1]);
+        score_tile(kw, 0, sc[0]);
+        score_tile(kw, 1, sc[1]);
     }
 
     // B bytes are raw key bits at weight 2^k (mask without shift; the digit
-    // rows carry the 2^-k); returns n (sum q_rot c + kappa rho sum Sq (2s - 1)) per slot
-    __device__ void score_tile(const KeyWords<BITS, D> &kw, int c, float kappa, float (&sc)[MT]) const
+    // rows carry the 2^-k); returns n (sum q_rot c + kappa rho sum Sq (2s - 1))
+    // per slot, times scale log2(e)
+    __device__ void score_tile(const KeyWords<BITS, D> &kw, int c, float (&sc)[MT]) const
     {
         v4i accc[MT], accs[MT];
 #pragma unroll
@@ -416,8 +433,8 @@ struct ScoreBits {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
-            const float dsign = fmaf(2.0f * limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
-            sc[mt] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
+            const float dsign = fmaf(limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
+            sc[mt] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
         }
     }
 };
@@ -453,7 +470,7 @@ struct ScoreLut {
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     float scc[2], scs[2];
     const unsigned char *tab;
-    int copy;                  // this lane's table copy
+    uint32_t copy4;            // byte offset of this lane's table copy within an entry
     int lane_;
 
     __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
@@ -462,10 +479,10 @@ struct ScoreLut {
     __device__ static float for_query(const float (&v)[2], int q, int) { return v[q % 2]; }
 
     // builds the tables (all threads; the caller synchronises) and loads the operands
-    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, unsigned char *lds)
+    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, float kappa, unsigned char *lds)
     {
         tab = lds;
-        copy = lane % COPIES;
+        copy4 = 4u * static_cast<uint32_t>(lane % COPIES);
         const int tid = threadIdx.x;
         constexpr int L = 1 << BITS;
         if (PAIR) {
@@ -503,22 +520,30 @@ struct ScoreLut {
             const int g = 2 * kb + qq;
             const bool ok = g < GC;
             const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
-            scc[qq] = ok ? sc[0] : 0.0f;
-            scs[qq] = ok ? sc[1] : 0.0f;
+            // scores leave in log2 units of the softmax (scale log2(e) folded in)
+            const float f = a.scale * kLog2e;
+            scc[qq] = ok ? sc[0] * f : 0.0f;
+            scs[qq] = ok ? sc[1] * f * kappa : 0.0f;
         }
     }
 
-    // field of `width` bits at bit offset o of a lane's word array (o, width constant)
-    template <int NW>
-    __device__ static uint32_t field(const uint32_t (&w)[NW], int o, int width)
+    // byte offset of the table entry for the W-bit field at bit offset o of a
+    // lane's word array (o constant after unrolling): the field lands at bit
+    // ESH = log2(entry stride) by one shift, so with the copy bits or-ed in the
+    // offset costs a shift and an and-or
+    static constexpr int ESH = __builtin_ctz(4 * COPIES);
+    template <int W, int NW>
+    __device__ uint32_t entry(const uint32_t (&w)[NW], int o) const
     {
         const int i = o / 32, s = o % 32;
-        const uint32_t mask = (1u << width) - 1u;
-        if (s + width <= 32 || i + 1 >= NW) return (w[i] >> s) & mask;
-        return __builtin_amdgcn_alignbit(w[i + 1], w[i], s) & mask;
+        constexpr uint32_t mask = ((1u << W) - 1u) << ESH;
+        uint32_t x;
+        if (s + W <= 32 || i + 1 >= NW) x = s >= ESH ? (w[i] >> (s - ESH)) : (w[i] << (ESH - s));
+        else x = __builtin_amdgcn_alignbit(w[i + 1], w[i], s) << ESH;
+        return (x & mask) | copy4;
     }
 
-    __device__ void scores(const KeyWords<BITS, D> &kw, float kappa, float (&sc)[2][2]) const
+    __device__ void scores(const KeyWords<BITS, D> &kw, float (&sc)[2][2]) const
     {
         const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
         const uint32_t *tl = reinterpret_cast<const uint32_t *>(tab + LO_OFF);
@@ -537,12 +562,12 @@ struct ScoreLut {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     if (PAIR) {
-                        const uint32_t e = field(kw.cw[c], 8 * BITS * ks + 2 * BITS * p, 2 * BITS) * COPIES + copy;
-                        bhi[p] = static_cast<int>(t1[e]);
-                        blo[p] = static_cast<int>(tl[e]);
+                        const uint32_t e = entry<2 * BITS>(kw.cw[c], 8 * BITS * ks + 2 * BITS * p);
+                        bhi[p] = static_cast<int>(*at_bytes(t1, e));
+                        blo[p] = static_cast<int>(*at_bytes(tl, e));
                     } else {
-                        const uint32_t e0 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p), BITS) * COPIES + copy];
-                        const uint32_t e1 = t1[field(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1), BITS) * COPIES + copy];
+                        const uint32_t e0 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p)));
+                        const uint32_t e1 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1)));
                         bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
                         blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
                     }
@@ -560,7 +585,7 @@ struct ScoreLut {
             for (int qq = 0; qq < 2; ++qq) {
                 const float dcode = (accc[c][2 * qq] + accc[c][2 * qq + 1]) * scc[qq];
                 const float dsign = (accs[c][2 * qq] + accs[c][2 * qq + 1]) * scs[qq];
-                sc[c][qq] = kw.nrm[c] * fmaf(kappa * kw.rho[c], dsign, dcode);
+                sc[c][qq] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
             }
     }
 };
@@ -615,7 +640,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     uint32_t *pst = reinterpret_cast<uint32_t *>(vt + VT_BYTES + AF_BYTES);   // [TK][NGM]
 
     SCORE score;
-    score.init(a, unit, row0, lane, kb, GC, stab);
+    score.init(a, unit, row0, lane, kb, GC, kappa, stab);
     // value-product A rows of absent queries stay zero
     for (int i = lane; i < NGM * 64 * 4; i += 64) afr[i] = 0u;
     if (SCORE::TAB_BYTES > 0) __syncthreads();   // score tables built by all threads
@@ -718,13 +743,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
         float lamv[NQ][2];
         {
             float sc[2][NQ];
-            score.scores(cur.kw, kappa, sc);
+            score.scores(cur.kw, sc);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const bool valid = 16 * c + j < nv;
 #pragma unroll
                 for (int sl = 0; sl < NQ; ++sl)
-                    lamv[sl][c] = (valid && SCORE::query(sl, kb) < GC) ? a.scale * sc[c][sl] : -INFINITY;
+                    lamv[sl][c] = (valid && SCORE::query(sl, kb) < GC) ? sc[c][sl] : -INFINITY;
             }
         }
 
@@ -741,7 +766,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
             float alpha[NQ];
 #pragma unroll
             for (int sl = 0; sl < NQ; ++sl) {
-                alpha[sl] = (m_new[sl] > m_run[sl]) ? __expf(m_run[sl] - m_new[sl]) : 1.0f;
+                alpha[sl] = (m_new[sl] > m_run[sl]) ? exp2_fast(m_run[sl] - m_new[sl]) : 1.0f;
                 l_run[sl] *= alpha[sl];
 #pragma unroll
                 for (int gg = 0; gg < NGM; ++gg) zacc[sl][gg] *= alpha[sl];
@@ -761,8 +786,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
 #pragma unroll
         for (int sl = 0; sl < NQ; ++sl) {
             const float mref = m_run[sl] == -INFINITY ? 0.0f : m_run[sl];
-            p[sl][0] = __expf(lamv[sl][0] - mref);
-            p[sl][1] = __expf(lamv[sl][1] - mref);
+            p[sl][0] = exp2_fast(lamv[sl][0] - mref);
+            p[sl][1] = exp2_fast(lamv[sl][1] - mref);
             l_run[sl] += p[sl][0] + p[sl][1];
         }
 
@@ -899,7 +924,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
         float l = 0.0f, o = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float e = (s_wm[w][g] == -INFINITY) ? 0.0f : __expf(s_wm[w][g] - mx);
+            const float e = (s_wm[w][g] == -INFINITY) ? 0.0f : exp2_fast(s_wm[w][g] - mx);
             l = fmaf(e, s_wl[w][g], l);
             o = fmaf(e, wo[(w * kMaxG + g) * D + ch] + s_wz[w][g][grp], o);
         }
@@ -916,60 +941,83 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
 }
 
 // ------------------------------------------------------------ split merge
-// One workgroup per query row: out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
-// (M the largest split maximum), split weights staged through LDS 256 at a time.
+// One workgroup per (query row, block of CH channels): out = sum_s 2^(m_s - M)
+// acc_s / sum_s 2^(m_s - M) l_s with M the largest split maximum (maxima in
+// log2 units).  Thread (channel c, phase ph) takes splits ph, ph + P, ...
+// (P = 256 / CH) in batches of NB, every load of a batch unconditional
+// (indices clamped, weights zeroed), and the first batch is issued before the
+// maxima are reduced.  CH and NB follow the split count, so that few splits
+// spread over more channels per workgroup and no load is wasted on clamping.
+
+__device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l2)
+{
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;                 // both empty
+    l = l * exp2_fast(m - mn) + l2 * exp2_fast(m2 - mn);
+    m = mn;
+}
+
+template <int CH, int NB>
 __global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
 {
-    __shared__ float red[kThreads / 64];
-    __shared__ float wts[kThreads];
+    constexpr int P = kThreads / CH;
+    __shared__ float red[2][kThreads / 64];
+    __shared__ float part[kThreads];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int64_t row = blockIdx.x;
     const int S = a.splits, D = a.d;
-    const float *ml = a.part_ml + row * S * 2;
-    float mx = -INFINITY;
-    for (int s = tid; s < S; s += kThreads)
-        if (ml[2 * s + 1] > 0.0f) mx = fmaxf(mx, ml[2 * s]);
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    float l = 0.0f;
-    for (int s = tid; s < S; s += kThreads)
-        if (ml[2 * s + 1] > 0.0f) l = fmaf(ml[2 * s + 1], __expf(ml[2 * s] - mx), l);
-    l = wave_sum(l);
-    if (lane == 0) red[wave] = l;
-    __syncthreads();
-    l = red[0] + red[1] + red[2] + red[3];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int c = blockIdx.y * CH + tid % CH, ph = tid / CH;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml + row * S * 2);
     const float *pa = a.part_acc + row * S * D;
-    float o = 0.0f;
-    for (int s0 = 0; s0 < S; s0 += kThreads) {
-        __syncthreads();
-        const int s = s0 + tid;
-        wts[tid] = (s < S && ml[2 * s + 1] > 0.0f) ? __expf(ml[2 * s] - mx) * inv : 0.0f;
-        __syncthreads();
-        const int n = S - s0 < kThreads ? S - s0 : kThreads;
-        if (tid < D) {
-            int k = 0;
-            for (; k + 32 <= n; k += 32) {          // 32 loads in flight
-                float v[32];
+    float v[NB];
+    float2 mv[NB];
+    auto load_batch = [&](int s0) {
 #pragma unroll
-                for (int u = 0; u < 32; ++u) v[u] = pa[static_cast<int64_t>(s0 + k + u) * D + tid];
-#pragma unroll
-                for (int u = 0; u < 32; ++u) o = fmaf(wts[k + u], v[u], o);
-            }
-            for (; k + 8 <= n; k += 8) {
-                float v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = pa[static_cast<int64_t>(s0 + k + u) * D + tid];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) o = fmaf(wts[k + u], v[u], o);
-            }
-            for (; k < n; ++k) o = fmaf(wts[k], pa[static_cast<int64_t>(s0 + k) * D + tid], o);
+        for (int u = 0; u < NB; ++u) {
+            const int s = min(s0 + ph + P * u, S - 1);
+            v[u] = pa[static_cast<int64_t>(s) * D + c];
+            mv[u] = ml[s];
         }
+    };
+    load_batch(0);
+    // (M, L) over all splits: per-thread online pairs, then wave and block
+    float m = -INFINITY, l = 0.0f;
+    for (int s = tid; s < S; s += kThreads) {
+        const float2 x = ml[s];
+        if (x.y > 0.0f) ml_combine(m, l, x.x, x.y);
     }
-    if (tid < D) a.out[row * D + tid] = o;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+        ml_combine(m, l, m2, l2);
+    }
+    if (lane == 0) {
+        red[0][wave] = m;
+        red[1][wave] = l;
+    }
+    __syncthreads();
+    m = red[0][0];
+    l = red[1][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) ml_combine(m, l, red[0][w], red[1][w]);
+    float o = 0.0f;
+    for (int s0 = 0;;) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const bool ok = s0 + ph + P * u < S && mv[u].y > 0.0f;
+            o = fmaf(ok ? exp2_fast(mv[u].x - m) : 0.0f, v[u], o);
+        }
+        s0 += P * NB;
+        if (s0 >= S) break;
+        load_batch(s0);
+    }
+    part[tid] = o;
+    __syncthreads();
+    if (tid < CH) {
+#pragma unroll
+        for (int p = 1; p < P; ++p) o += part[p * CH + tid];
+        a.out[row * D + c] = l > 0.0f ? o / l : 0.0f;
+    }
 }
 
 template <class SCORE, int BITS, int D, int VBITS>
@@ -987,8 +1035,15 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     prof_begin("tq_merge_splits", stream, &tok);
-    hipLaunchKernelGGL(k_merge_splits, dim3(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq)), dim3(kThreads), 0,
-                       stream, a);
+    const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq);
+    const int S = a.splits;
+    if (S <= 2) hipLaunchKernelGGL((k_merge_splits<128, 1>), dim3(rows, a.d / 128), dim3(kThreads), 0, stream, a);
+    else if (S <= 4) hipLaunchKernelGGL((k_merge_splits<64, 1>), dim3(rows, a.d / 64), dim3(kThreads), 0, stream, a);
+    else if (S <= 8) hipLaunchKernelGGL((k_merge_splits<32, 1>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 16) hipLaunchKernelGGL((k_merge_splits<32, 2>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 32) hipLaunchKernelGGL((k_merge_splits<32, 4>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 64) hipLaunchKernelGGL((k_merge_splits<32, 8>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_merge_splits<32, 16>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     prof_end(tok, stream);
     return hipGetLastError();
 }
