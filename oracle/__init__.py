@@ -84,6 +84,8 @@ def _l():
     lib.orc_dequant_values.argtypes = [i32, i32, i32, _u8p, _u16p, i64, _f64p]
     lib.orc_scores.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _f64p, i32,
                                _u8p, _u8p, _f32p, _f32p, i64, _f64p, vp, vp]
+    lib.orc_dequant_keys.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _u8p, _u8p, _f32p, _f32p,
+                                     i64, _f64p]
     lib.orc_attend.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _f64p, i32,
                                _u8p, _u8p, _f32p, _f32p, i64, i32, i32, _u8p, _u16p,
                                ctypes.c_double, _f64p]
@@ -156,6 +158,7 @@ class Rotation:
 
 
 def rotation(seed: int, d: int, kind: str = "dense", m: int | None = None) -> Rotation:
+    """Pi and S of a seed; m = 0 gives the key format without the QJL stage."""
     m = d if m is None else m
     pi = rotation_dense(seed, d) if kind == "dense" else rotation_hadamard(seed, d)
     return Rotation(seed, d, kind, pi, qjl_matrix(seed, m, d))
@@ -292,6 +295,22 @@ def scores(q: np.ndarray, kc: KeyCache, bits: int, rot: Rotation, terms: bool = 
                     np.ascontiguousarray(kc.knorm), np.ascontiguousarray(kc.rnorm), T, out,
                     _ptr(t1), _ptr(t2))
     return (out, t1, t2) if terms else out
+
+
+def dequant_keys(kc: KeyCache, bits: int, rot: Rotation) -> np.ndarray:
+    """Explicit key estimates k_hat [N, d] (fp64) of one packed key plane set:
+    the vectors whose inner products with a query are the asymmetric scores;
+    a rotation with m = 0 rows of S gives the first (MSE) stage alone."""
+    d = rot.d
+    m = rot.s.shape[0]
+    n = kc.codes.shape[0]
+    c, _ = codebook(d, bits)
+    out = np.zeros((n, d))
+    signs = kc.signs if m > 0 else np.zeros((n, 1), np.uint8)
+    _l().orc_dequant_keys(d, bits, m, np.ascontiguousarray(rot.pi), np.ascontiguousarray(rot.s), c,
+                          np.ascontiguousarray(kc.codes), np.ascontiguousarray(signs),
+                          np.ascontiguousarray(kc.knorm), np.ascontiguousarray(kc.rnorm), n, out)
+    return out
 
 
 def attend(q: np.ndarray, kc: KeyCache, bits: int, rot: Rotation, vc: ValueCache,

@@ -592,8 +592,9 @@ void orc_scores(int d, int bits, int m, const double *pi, const double *s,
 {
     int64_t code_bytes = ((int64_t)d * bits + 7) / 8, sign_bytes = ((int64_t)m + 7) / 8;
     double *qrot = (double *)malloc(sizeof(double) * d * nq);
-    double *sq = (double *)malloc(sizeof(double) * m * nq);
-    double kappa = sqrt(M_PI / 2.0) / m;
+    double *sq = (double *)malloc(sizeof(double) * (m > 0 ? m : 1) * nq);
+    /* m = 0: the first (MSE) stage alone, no QJL term */
+    double kappa = m > 0 ? sqrt(M_PI / 2.0) / m : 0.0;
     for (int h = 0; h < nq; h++) {
         for (int i = 0; i < d; i++) {
             double acc = 0.0;
@@ -609,7 +610,7 @@ void orc_scores(int d, int bits, int m, const double *pi, const double *s,
 #pragma omp parallel
     {
         unsigned *idx = (unsigned *)malloc(sizeof(unsigned) * d);
-        double *sgn = (double *)malloc(sizeof(double) * m);
+        double *sgn = (double *)malloc(sizeof(double) * (m > 0 ? m : 1));
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < T; t++) {
             const uint8_t *cr = codes + t * code_bytes, *sr = signs + t * sign_bytes;
@@ -631,6 +632,46 @@ void orc_scores(int d, int bits, int m, const double *pi, const double *s,
     }
     free(qrot);
     free(sq);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Explicit estimate of packed keys (dequantisation):                        */
+/*   k_hat = n Pi^T ( c[idx] + sqrt(pi/2)/m * rho * S^T (2 s - 1) ),          */
+/* the vector whose inner product with any query equals the asymmetric      */
+/* score above; with m = 0 (first stage alone) k_hat = n Pi^T c[idx].        */
+/* ------------------------------------------------------------------------ */
+void orc_dequant_keys(int d, int bits, int m, const double *pi, const double *s,
+                      const double *centroids, const uint8_t *codes, const uint8_t *signs,
+                      const float *knorm, const float *rnorm, int64_t n_vec, double *out)
+{
+    int64_t code_bytes = ((int64_t)d * bits + 7) / 8, sign_bytes = ((int64_t)m + 7) / 8;
+    double kappa = m > 0 ? sqrt(M_PI / 2.0) / m : 0.0;
+#pragma omp parallel
+    {
+        double *yh = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n_vec; t++) {
+            const uint8_t *cr = codes + t * code_bytes;
+            for (int j = 0; j < d; j++) yh[j] = centroids[orc_get_bits(cr, j, bits)];
+            if (m > 0) {
+                const uint8_t *sr = signs + t * sign_bytes;
+                double f = kappa * (double)rnorm[t];
+                for (int j = 0; j < d; j++) {
+                    double acc = 0.0;
+                    for (int i = 0; i < m; i++)
+                        acc += s[(size_t)i * d + j] * (orc_get_bits(sr, i, 1) ? 1.0 : -1.0);
+                    yh[j] += f * acc;
+                }
+            }
+            double n = (double)knorm[t];
+            for (int c = 0; c < d; c++) {
+                double acc = 0.0;
+                for (int j = 0; j < d; j++) acc += pi[(size_t)j * d + c] * yh[j];
+                out[t * d + c] = n * acc;
+            }
+        }
+        free(yh);
+    }
 }
 
 /* ------------------------------------------------------------------------ */
