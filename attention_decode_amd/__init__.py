@@ -115,13 +115,13 @@ class ValueFormat:
 @dataclass
 class KeyCache:
     codes: "torch.Tensor"   # noqa: F821  [B, H, T, d*b/8] uint8
-    signs: "torch.Tensor"   # noqa: F821  [B, H, T, m/8] uint8
+    signs: "torch.Tensor"   # noqa: F821  [B, H, T, m/8] uint8 (None without QJL rows)
     knorm: "torch.Tensor"   # noqa: F821  [B, H, T] float32
-    rnorm: "torch.Tensor"   # noqa: F821  [B, H, T] float32
+    rnorm: "torch.Tensor"   # noqa: F821  [B, H, T] float32 (None without QJL rows)
 
     def c(self) -> L.KCache:
-        return L.KCache(self.codes.data_ptr(), self.signs.data_ptr(), self.knorm.data_ptr(),
-                        self.rnorm.data_ptr())
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return L.KCache(self.codes.data_ptr(), ptr(self.signs), self.knorm.data_ptr(), ptr(self.rnorm))
 
 
 @dataclass
@@ -134,13 +134,16 @@ class ValueCache:
 
 
 def alloc_key_cache(fmt: KeyFormat, B: int, H: int, T: int, device="cuda") -> KeyCache:
+    """Planes of a key cache; the first-stage format (qjl_m = 0) has no signs
+    and no rnorm plane."""
     import torch
     kf = fmt.c()
     row = lambda p: lib().tq_key_plane_bytes(ctypes.byref(kf), 1, p)
+    qjl = kf.qjl_m > 0
     return KeyCache(torch.empty((B, H, T, row(0)), dtype=torch.uint8, device=device),
-                    torch.empty((B, H, T, row(1)), dtype=torch.uint8, device=device),
+                    torch.empty((B, H, T, row(1)), dtype=torch.uint8, device=device) if qjl else None,
                     torch.empty((B, H, T), dtype=torch.float32, device=device),
-                    torch.empty((B, H, T), dtype=torch.float32, device=device))
+                    torch.empty((B, H, T), dtype=torch.float32, device=device) if qjl else None)
 
 
 def alloc_value_cache(fmt: ValueFormat, B: int, H: int, T: int, device="cuda") -> ValueCache:
@@ -200,6 +203,17 @@ def tq_scores(fmt: KeyFormat, q, kc: KeyCache, Hkv: int, T: int, out=None, ws=No
     kf = fmt.c()
     check(lib().tq_scores(ctypes.byref(kf), q.data_ptr(), _dtype_code(q), B, Hq, Hkv, T, kc.c(),
                           out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)), "tq_scores")
+    return out
+
+
+def tq_dequantize_keys(fmt: KeyFormat, kc: KeyCache, B: int, Hkv: int, T: int, out=None, stream=None):
+    """Explicit key estimates of a packed cache -> [B, Hkv, T, d] fp32."""
+    import torch
+    if out is None:
+        out = torch.empty((B, Hkv, T, fmt.d), dtype=torch.float32, device=kc.codes.device)
+    kf = fmt.c()
+    check(lib().tq_dequantize_keys(ctypes.byref(kf), B, Hkv, T, kc.c(), out.data_ptr(), _stream(stream)),
+          "tq_dequantize_keys")
     return out
 
 

@@ -58,6 +58,7 @@ SIGNATURES = {
     "tq_attend_workspace_bytes": (_sz, [_c.POINTER(KeyFmt), _i, _i, _i, _i64, _i]),
     "tq_attend_decode": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64,
                               KCache, VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
+    "tq_dequantize_keys": (_i, [_c.POINTER(KeyFmt), _i, _i, _i64, KCache, _vp, _vp]),
     "tq_last_error": (_c.c_char_p, []),
     "tq_profile_enable": (_i, [_i]),
     "tq_profile_read": (_i, [_c.c_char_p, _dp, _c.POINTER(_i64)]),

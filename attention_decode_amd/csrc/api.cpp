@@ -394,7 +394,7 @@ size_t tq_key_plane_bytes(const tq_key_fmt *fmt, int64_t n_vec, int plane)
     case 0: return n * ((static_cast<size_t>(fmt->d) * fmt->mse_bits + 7) / 8);
     case 1: return n * ((static_cast<size_t>(fmt->qjl_m) + 7) / 8);
     case 2: return n * sizeof(float);
-    case 3: return n * sizeof(float);
+    case 3: return fmt->qjl_m > 0 ? n * sizeof(float) : 0;
     }
     return 0;
 }
@@ -422,11 +422,12 @@ tq_status check_key_fmt(const tq_key_fmt *f, const char *who)
     if (!supported_d(f->d)) return fail(TQ_EUNSUPPORTED, "%s: d=%d not in {64, 128, 256}", who, f->d);
     if (f->mse_bits < 1 || f->mse_bits > 7)
         return fail(TQ_EUNSUPPORTED, "%s: mse_bits=%d not in [1, 7]", who, f->mse_bits);
-    if (f->qjl_m != f->d) return fail(TQ_EUNSUPPORTED, "%s: qjl_m=%d must equal d=%d", who, f->qjl_m, f->d);
+    if (f->qjl_m != f->d && f->qjl_m != 0)
+        return fail(TQ_EUNSUPPORTED, "%s: qjl_m=%d must be d=%d or 0", who, f->qjl_m, f->d);
     if (f->cb->d != f->d || f->cb->bits != f->mse_bits)
         return fail(TQ_EINVAL, "%s: codebook is for (d=%d, bits=%d), format wants (%d, %d)", who,
                     f->cb->d, f->cb->bits, f->d, f->mse_bits);
-    if (f->rot->d != f->d || f->rot->m != f->qjl_m)
+    if (f->rot->d != f->d || (f->qjl_m > 0 && f->rot->m != f->qjl_m))
         return fail(TQ_EINVAL, "%s: rotation is for d=%d, format wants %d", who, f->rot->d, f->d);
     return TQ_OK;
 }
@@ -463,10 +464,12 @@ tq_status check_input(const void *x, tq_dtype dt, int B, int H, int64_t T, int64
     return TQ_OK;
 }
 
-tq_status check_kcache(const tq_kcache &kc, const char *who)
+// the signs and rnorm planes exist only with QJL rows (m > 0)
+tq_status check_kcache(const tq_kcache &kc, int m, const char *who)
 {
-    if (!kc.codes || !kc.signs || !kc.knorm || !kc.rnorm) return fail(TQ_EINVAL, "%s: NULL key plane", who);
-    if (!aligned16(kc.codes) || !aligned16(kc.signs) || !aligned16(kc.knorm) || !aligned16(kc.rnorm))
+    if (!kc.codes || !kc.knorm || (m > 0 && (!kc.signs || !kc.rnorm)))
+        return fail(TQ_EINVAL, "%s: NULL key plane", who);
+    if (!aligned16(kc.codes) || !aligned16(kc.knorm) || (m > 0 && (!aligned16(kc.signs) || !aligned16(kc.rnorm))))
         return fail(TQ_EALIGN, "%s: key planes must be 16-byte aligned", who);
     return TQ_OK;
 }
@@ -500,7 +503,7 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     p.nqc = G / p.gc;
     p.mt = p.mfma ? tq::mfma_row_tiles(fmt->mse_bits, p.gc) : (p.gc + 3) / 4;
     p.units = B * Hkv * p.nqc;
-    p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits) : 0;
+    p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits, fmt->qjl_m) : 0;
     const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;
     const int64_t tiles = (T + tile - 1) / tile;
     // workgroups per launch: about eight per CU for the d = 128 matrix-core
@@ -551,7 +554,7 @@ tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype,
     TQ_TRY(check_dtype(dtype, who));
     TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
     if (T == 0) return TQ_OK;
-    TQ_TRY(check_kcache(out, who));
+    TQ_TRY(check_kcache(out, fmt->qjl_m, who));
     tq::KeyLaunch a{};
     a.k = k;
     a.dtype = dtype;
@@ -617,7 +620,7 @@ static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, tq_dt
     if (!q) return fail(TQ_EINVAL, "%s: NULL query", who);
     if (!aligned16(q)) return fail(TQ_EALIGN, "%s: query must be 16-byte aligned", who);
     if (static_cast<int64_t>(B) * Hkv * T > (int64_t(1) << 40)) return fail(TQ_EINVAL, "%s: too many keys", who);
-    if (T > 0) TQ_TRY(check_kcache(kc, who));
+    if (T > 0) TQ_TRY(check_kcache(kc, fmt->qjl_m, who));
     return TQ_OK;
 }
 
@@ -656,6 +659,35 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = tq::launch_qprep(a, s);
     if (e == hipSuccess) e = tq::launch_scores(a, s);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+tq_status tq_dequantize_keys(const tq_key_fmt *fmt, int B, int Hkv, int64_t T, tq_kcache kc, float *out,
+                             void *stream)
+{
+    const char *who = "tq_dequantize_keys";
+    TQ_TRY(check_key_fmt(fmt, who));
+    if (B < 1 || Hkv < 1 || T < 0) return fail(TQ_EINVAL, "%s: bad shape B=%d Hkv=%d T=%lld", who, B, Hkv, (long long)T);
+    if (static_cast<int64_t>(B) * Hkv * T > (int64_t(1) << 40)) return fail(TQ_EINVAL, "%s: too many keys", who);
+    if (T == 0) return TQ_OK;
+    TQ_TRY(check_kcache(kc, fmt->qjl_m, who));
+    if (!out) return fail(TQ_EINVAL, "%s: NULL output", who);
+    if (!aligned16(out)) return fail(TQ_EALIGN, "%s: output must be 16-byte aligned", who);
+    tq::DequantLaunch a{};
+    a.N = static_cast<int64_t>(B) * Hkv * T;
+    a.d = fmt->d;
+    a.bits = fmt->mse_bits;
+    a.m = fmt->qjl_m;
+    a.kappa = a.m > 0 ? static_cast<float>(std::sqrt(M_PI / 2.0) / a.m) : 0.0f;
+    a.pi = fmt->rot->d_pi;
+    a.s = fmt->rot->d_s;
+    a.centroids = fmt->cb->d_centroids;
+    a.codes = kc.codes;
+    a.signs = kc.signs;
+    a.knorm = kc.knorm;
+    a.rnorm = kc.rnorm;
+    a.out = out;
+    const hipError_t e = tq::launch_dequant_keys(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
 

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
         // Code step s = 2u + h reads word u of the quarter (bit 32 u + 8 K + 4 h + r,
         // coordinate bit / bits); sign step 2 nc + 2u + h reads coordinate
         // 32 u + 8 K + 4 h + r of Sq.
-        const int nc = code_dwords(D, a.bits), ns = sign_dwords(D);
+        const int nc = code_dwords(D, a.bits), ns = a.m > 0 ? sign_dwords(D) : 0;
         const int S = 2 * nc + 2 * ns, MT = a.mf.mt;
         const int s_lo = part ? 2 * nc : 0, s_n = part ? 2 * ns : 2 * nc;
         uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * MT * S * 256;
@@ -331,30 +331,36 @@ __device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off)
 }
 
 // Key words of the two keys (columns j and 16 + j of a wave tile) that lane
-// (j, kb) reads: the kb-th quarter of the code row and of the sign row.
-template <int BITS, int D>
+// (j, kb) reads: the kb-th quarter of the code row and of the sign row.  The
+// first-stage format (QJL false) has no sign row and no residual norm.
+template <int BITS, int D, bool QJL>
 struct KeyWords {
-    static constexpr int NC = D * BITS / 128, NS = D / 128;
-    uint32_t cw[2][NC], sw[2][NS];
+    static constexpr int NC = D * BITS / 128, NS = QJL ? D / 128 : 0;
+    uint32_t cw[2][NC], sw[2][NS > 0 ? NS : 1];
     float nrm[2], rho[2];
     __device__ void load(const uint32_t *crow, const uint32_t *srow, const float *np, const float *rp, int c)
     {
 #pragma unroll
         for (int u = 0; u < NC; ++u) cw[c][u] = crow[u];
-#pragma unroll
-        for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
         nrm[c] = *np;
-        rho[c] = *rp;
+        if constexpr (QJL) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
+            rho[c] = *rp;
+        } else {
+            rho[c] = 0.0f;
+        }
     }
 };
 
 // Bit-plane scores (1-2 bit keys).  Rows of the int8 products are (query,
 // digit), four queries per 16-row tile: lane (j, kb) scores query 4 slot + kb.
-template <int BITS, int D, int MT>
+template <int BITS, int D, int MT, bool QJL>
 struct ScoreBits {
+    using KW = KeyWords<BITS, D, QJL>;
     static constexpr int NQ = MT;
     static constexpr int TAB_BYTES = 0;
-    static constexpr int NC = D * BITS / 128, NS = D / 128;
+    static constexpr int NC = D * BITS / 128, NS = QJL ? D / 128 : 0;
     static constexpr int SC = 2 * NC, SS = 2 * NS, S = SC + SS;
     v4i aop[MT][S];
     float fc[MT], cc[MT], fs[MT], ssq[MT];
@@ -396,7 +402,7 @@ struct ScoreBits {
         }
     }
 
-    __device__ void scores(const KeyWords<BITS, D> &kw, float (&sc)[2][MT]) const
+    __device__ void scores(const KW &kw, float (&sc)[2][MT]) const
     {
         score_tile(kw, 0, sc[0]);
         score_tile(kw, 1, sc[1]);
@@ -405,7 +411,7 @@ struct ScoreBits {
     // B bytes are raw key bits at weight 2^k (mask without shift; the digit
     // rows carry the 2^-k); returns n (sum q_rot c + kappa rho sum Sq (2s - 1))
     // per slot, times scale log2(e)
-    __device__ void score_tile(const KeyWords<BITS, D> &kw, int c, float (&sc)[MT]) const
+    __device__ void score_tile(const KW &kw, int c, float (&sc)[MT]) const
     {
         v4i accc[MT], accs[MT];
 #pragma unroll
@@ -433,8 +439,12 @@ struct ScoreBits {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const float dcode = fmaf(limbs_to_float(accc[mt]), fc[mt], cc[mt]);
-            const float dsign = fmaf(limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
-            sc[mt] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
+            if constexpr (QJL) {
+                const float dsign = fmaf(limbs_to_float(accs[mt]), fs[mt], -ssq[mt]);
+                sc[mt] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
+            } else {
+                sc[mt] = kw.nrm[c] * dcode;
+            }
         }
     }
 };
@@ -445,8 +455,9 @@ struct ScoreBits {
 // its sign bytes as eight fp16 +-1; the products run on
 // v_mfma_f32_16x16x32_f16 with rows (query, hi/lo): lane (j, kb) scores
 // queries 2 kb and 2 kb + 1.
-template <int BITS, int D>
+template <int BITS, int D, bool QJL>
 struct ScoreLut {
+    using KW = KeyWords<BITS, D, QJL>;
     static constexpr int NQ = 2;
     static constexpr int KS = D / 32;
     static constexpr bool PAIR = BITS <= 5;
@@ -465,8 +476,8 @@ struct ScoreLut {
     // in adjacent registers and cost moves into the two operand quads)
     static constexpr int LO_OFF = TAB1 + 16;
     static constexpr int CODE_TAB = PAIR ? LO_OFF + TAB1 : TAB1;
-    static constexpr int SIGN_TAB = 256 * 16;
-    static constexpr int AOP_BYTES = 2 * KS * 64 * 16;                // the unit's A operands, [2][KS][64 lanes]
+    static constexpr int SIGN_TAB = QJL ? 256 * 16 : 0;
+    static constexpr int AOP_BYTES = (QJL ? 2 : 1) * KS * 64 * 16;    // the unit's A operands, [part][KS][64 lanes]
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     float scc[2], scs[2];
     const unsigned char *tab;
@@ -503,7 +514,7 @@ struct ScoreLut {
             }
         }
         uint32_t *ts = reinterpret_cast<uint32_t *>(lds + CODE_TAB);
-        for (int i = tid; i < 256 * 4; i += kThreads) {
+        for (int i = tid; i < (QJL ? 256 * 4 : 0); i += kThreads) {
             const int e = i / 4, r = i % 4;
             const uint32_t lo = ((e >> (2 * r)) & 1) ? 0x3C00u : 0xBC00u;
             const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
@@ -513,7 +524,7 @@ struct ScoreLut {
         // k-step rather than held in registers)
         const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * 2 * KS * 64;
         v4i *adst = reinterpret_cast<v4i *>(lds + CODE_TAB + SIGN_TAB);
-        for (int i = tid; i < 2 * KS * 64; i += kThreads) adst[i] = src[i];
+        for (int i = tid; i < (QJL ? 2 : 1) * KS * 64; i += kThreads) adst[i] = src[i];
         lane_ = lane;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
@@ -543,7 +554,7 @@ struct ScoreLut {
         return (x & mask) | copy4;
     }
 
-    __device__ void scores(const KeyWords<BITS, D> &kw, float (&sc)[2][2]) const
+    __device__ void scores(const KW &kw, float (&sc)[2][2]) const
     {
         const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
         const uint32_t *tl = reinterpret_cast<const uint32_t *>(tab + LO_OFF);
@@ -555,7 +566,7 @@ struct ScoreLut {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const v8h acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
-            const v8h asign = __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]);
+            const v8h asign = QJL ? __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]) : acode;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 v4i bhi, blo;
@@ -574,8 +585,10 @@ struct ScoreLut {
                 }
                 accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, bhi), accc[c], 0, 0, 0);
                 accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, blo), accc[c], 0, 0, 0);
-                const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
-                accs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accs[c], 0, 0, 0);
+                if constexpr (QJL) {
+                    const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
+                    accs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accs[c], 0, 0, 0);
+                }
             }
         }
         // rows 4 kb + r: (query 2 kb + r / 2, part r % 2)
@@ -584,8 +597,12 @@ struct ScoreLut {
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
                 const float dcode = (accc[c][2 * qq] + accc[c][2 * qq + 1]) * scc[qq];
-                const float dsign = (accs[c][2 * qq] + accs[c][2 * qq + 1]) * scs[qq];
-                sc[c][qq] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
+                if constexpr (QJL) {
+                    const float dsign = (accs[c][2 * qq] + accs[c][2 * qq + 1]) * scs[qq];
+                    sc[c][qq] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
+                } else {
+                    sc[c][qq] = kw.nrm[c] * dcode;
+                }
             }
     }
 };
@@ -683,7 +700,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     const unsigned char *tr_base = vt + slot_token(8 * kb + e_of_r) * VSTR + 8 * (j % 2);
 
     struct Prefetch {
-        KeyWords<BITS, D> kw;
+        typename SCORE::KW kw;
         v4i vcode[VCL];
         uint32_t par[PD];
     };
@@ -703,8 +720,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const uint32_t t = static_cast<uint32_t>(16 * c + j < nv ? 16 * c + j : nv - 1);
-            pf.kw.load(at_bytes(cbase, 4u * (t * (D * BITS / 32) + kb * KeyWords<BITS, D>::NC)),
-                       at_bytes(sbase, 4u * (t * (D / 32) + kb * KeyWords<BITS, D>::NS)),
+            pf.kw.load(at_bytes(cbase, 4u * (t * (D * BITS / 32) + kb * SCORE::KW::NC)),
+                       at_bytes(sbase, 4u * (t * (D / 32) + kb * SCORE::KW::NS)),
                        at_bytes(nbase, 4u * t), at_bytes(rbase, 4u * t), c);
         }
         const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
@@ -1055,29 +1072,28 @@ hipError_t launch_attend_v(const DecodeLaunch &a, hipStream_t s, float kappa, in
                         : launch_attend_t<SCORE, BITS, D, 4>(a, s, kappa, chunk);
 }
 
-template <int BITS, int D>
+template <int BITS, int D, bool QJL>
 hipError_t launch_attend_b(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
     if constexpr (BITS <= 2) {
-        return a.mf.mt == 1 ? launch_attend_v<ScoreBits<BITS, D, 1>, BITS, D>(a, s, kappa, chunk)
-                            : launch_attend_v<ScoreBits<BITS, D, 2>, BITS, D>(a, s, kappa, chunk);
+        return a.mf.mt == 1 ? launch_attend_v<ScoreBits<BITS, D, 1, QJL>, BITS, D>(a, s, kappa, chunk)
+                            : launch_attend_v<ScoreBits<BITS, D, 2, QJL>, BITS, D>(a, s, kappa, chunk);
     } else {
-        return launch_attend_v<ScoreLut<BITS, D>, BITS, D>(a, s, kappa, chunk);
+        return launch_attend_v<ScoreLut<BITS, D, QJL>, BITS, D>(a, s, kappa, chunk);
     }
 }
 
-template <int D>
+template <int D, bool QJL>
 hipError_t launch_attend_d(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
     switch (a.bits) {
-    case 1: return launch_attend_b<1, D>(a, s, kappa, chunk);
-    case 2: return launch_attend_b<2, D>(a, s, kappa, chunk);
-    case 3: return launch_attend_b<3, D>(a, s, kappa, chunk);
-    case 4: return launch_attend_b<4, D>(a, s, kappa, chunk);
-    case 5: return launch_attend_b<5, D>(a, s, kappa, chunk);
-    case 6: return launch_attend_b<6, D>(a, s, kappa, chunk);
-    case 7: return launch_attend_b<7, D>(a, s, kappa, chunk);
-    case 8: return launch_attend_b<8, D>(a, s, kappa, chunk);
+    case 1: return launch_attend_b<1, D, QJL>(a, s, kappa, chunk);
+    case 2: return launch_attend_b<2, D, QJL>(a, s, kappa, chunk);
+    case 3: return launch_attend_b<3, D, QJL>(a, s, kappa, chunk);
+    case 4: return launch_attend_b<4, D, QJL>(a, s, kappa, chunk);
+    case 5: return launch_attend_b<5, D, QJL>(a, s, kappa, chunk);
+    case 6: return launch_attend_b<6, D, QJL>(a, s, kappa, chunk);
+    case 7: return launch_attend_b<7, D, QJL>(a, s, kappa, chunk);
     }
     return hipErrorInvalidValue;
 }
@@ -1085,7 +1101,8 @@ hipError_t launch_attend_d(const DecodeLaunch &a, hipStream_t s, float kappa, in
 template <typename TIn, int D>
 void launch_qprep_d(const DecodeLaunch &a, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(a.mf.units), 8);
+    // (part, quarter): q_rot and, with QJL rows, Sq
+    const dim3 grid(static_cast<unsigned>(a.mf.units), a.m > 0 ? 8 : 4);
     switch (a.mf.gc) {
     case 1: hipLaunchKernelGGL((k_qprep<TIn, D, 1>), grid, dim3(kThreads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((k_qprep<TIn, D, 2>), grid, dim3(kThreads), 0, stream, a); break;
@@ -1107,7 +1124,7 @@ bool mfma_decode_supported(int d, int bits, int G, int vbits, int group)
 {
     (void)group;
     const int gc = mfma_query_chunk(G);
-    return (d == 128 || d == 256) && bits >= 1 && bits <= 8 && gc >= 1 && (vbits == 2 || vbits == 4);
+    return (d == 128 || d == 256) && bits >= 1 && bits <= 7 && gc >= 1 && (vbits == 2 || vbits == 4);
 }
 
 int mfma_query_chunk(int G)
@@ -1119,7 +1136,10 @@ int mfma_query_chunk(int G)
 
 int mfma_row_tiles(int bits, int gc) { return bits <= 2 ? (gc + 3) / 4 : 1; }
 
-int mfma_score_steps(int d, int bits) { return bits <= 2 ? 2 * code_dwords(d, bits) + 2 * sign_dwords(d) : 2 * (d / 32); }
+int mfma_score_steps(int d, int bits, int m)
+{
+    return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0) : 2 * (d / 32);
+}
 
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
 {
@@ -1133,10 +1153,14 @@ hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
     prof_end(tok, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const float kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / a.m);
+    const float kappa = a.m > 0 ? static_cast<float>(std::sqrt(M_PI / 2.0) / a.m) : 0.0f;
     const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
     const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kMfmaTile;
-    return a.d == 128 ? launch_attend_d<128>(a, stream, kappa, chunk) : launch_attend_d<256>(a, stream, kappa, chunk);
+    if (a.m > 0)
+        return a.d == 128 ? launch_attend_d<128, true>(a, stream, kappa, chunk)
+                          : launch_attend_d<256, true>(a, stream, kappa, chunk);
+    return a.d == 128 ? launch_attend_d<128, false>(a, stream, kappa, chunk)
+                      : launch_attend_d<256, false>(a, stream, kappa, chunk);
 }
 
 }  // namespace tq

@@ -62,10 +62,11 @@ __device__ __forceinline__ float signed_by_bit(float x, uint32_t w, int e)
     return __uint_as_float(__float_as_uint(x) ^ (((~w >> e) & 1u) << 31));
 }
 
-// the two inner sums of the score for one key row and GC queries
+// the two inner sums of the score for one key row and GC queries (the sign
+// sum only with QJL rows; qjl is uniform over the launch)
 template <int BITS, int GC>
 __device__ __forceinline__ void key_dots(const uint32_t *__restrict__ crow,
-                                         const uint32_t *__restrict__ srow, int D,
+                                         const uint32_t *__restrict__ srow, int D, bool qjl,
                                          const float *qr_s, const float *sq_s, const float *cent_s,
                                          float (&dc)[GC], float (&ds)[GC])
 {
@@ -95,6 +96,7 @@ __device__ __forceinline__ void key_dots(const uint32_t *__restrict__ crow,
                 dc[g] = fmaf(q4.w, cv[4 * e4 + 3], dc[g]);
             }
         }
+        if (!qjl) continue;
         const uint32_t sw = srow[c0 / 32];
 #pragma unroll
         for (int e4 = 0; e4 < 8; ++e4) {
@@ -134,7 +136,7 @@ __device__ __forceinline__ void stage_queries(const DecodeLaunch &a, const UnitC
         const int g = i / D, j = i % D;
         const float *row = a.qprep + (static_cast<size_t>(u.b) * a.Hq + u.hq0 + g) * (D + M);
         qr_s[i] = row[j];
-        sq_s[i] = row[D + j];
+        sq_s[i] = M > 0 ? row[D + j] : 0.0f;
     }
     for (int i = tid; i < (1 << a.bits); i += kThreads) cent_s[i] = a.centroids[i];
 }
@@ -154,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void k_scores(DecodeLaunch a, int nqc, fl
     const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (a.d * BITS / 32);
     const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (a.m / 32);
     float dc[GC], ds[GC];
-    key_dots<BITS, GC>(crow, srow, a.d, qr_s, sq_s, cent_s, dc, ds);
-    const float nrm = a.kc.knorm[n], rho = a.kc.rnorm[n];
+    key_dots<BITS, GC>(crow, srow, a.d, a.m > 0, qr_s, sq_s, cent_s, dc, ds);
+    const float nrm = a.kc.knorm[n], rho = a.m > 0 ? a.kc.rnorm[n] : 0.0f;
 #pragma unroll
     for (int g = 0; g < GC; ++g)
         a.scores[(static_cast<int64_t>(u.b) * a.Hq + u.hq0 + g) * a.T + t] =
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeLaunch a, int nqc, fl
                 const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32);
                 const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (a.m / 32);
                 float dc[GC], ds[GC];
-                key_dots<BITS, GC>(crow, srow, D, s.qr, s.sq, s.cent, dc, ds);
-                const float nrm = a.kc.knorm[n], rho = a.kc.rnorm[n];
+                key_dots<BITS, GC>(crow, srow, D, a.m > 0, s.qr, s.sq, s.cent, dc, ds);
+                const float nrm = a.kc.knorm[n], rho = a.m > 0 ? a.kc.rnorm[n] : 0.0f;
 #pragma unroll
                 for (int g = 0; g < GC; ++g) lam[g] = a.scale * (nrm * fmaf(kappa * rho, ds[g], dc[g]));
             } else {
@@ -404,7 +406,8 @@ hipError_t dispatch_attend(const DecodeLaunch &a, hipStream_t stream, int gc, in
     }
 }
 
-float qjl_kappa(int m) { return static_cast<float>(std::sqrt(M_PI / 2.0) / m); }
+// sqrt(pi/2) / m; 0 for the first-stage format (no QJL rows)
+float qjl_kappa(int m) { return m > 0 ? static_cast<float>(std::sqrt(M_PI / 2.0) / m) : 0.0f; }
 
 }  // namespace
 

@@ -299,7 +299,10 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     }
     __syncthreads();
 
-    // ---- 4. z = S r on this wave's rows; signs [z >= 0]
+    // ---- 4. z = S r on this wave's rows; signs [z >= 0] (skipped for the
+    // first-stage format, m = 0; the condition is uniform over the launch)
+    const bool qjl = a.m > 0;
+    if (qjl) {
     f32x4 zacc[RTW][kKT];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
@@ -339,18 +342,23 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         }
     }
     __syncthreads();
+    }
 
     // ---- 5. store the WG's keys (contiguous rows of every plane)
     const int nk = static_cast<int>(n_total - n0 < kKeys ? n_total - n0 : kKeys);
     uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
     for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
-    uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
-    for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+    if (qjl) {
+        uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
+        for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+    }
     if (tid < nk) {
         const double n2 = s.nrm2[tid] + s.nrm2[kKeys + tid] + s.nrm2[2 * kKeys + tid] + s.nrm2[3 * kKeys + tid];
         a.out.knorm[n0 + tid] = static_cast<float>(sqrt(n2));
-        const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
-        a.out.rnorm[n0 + tid] = static_cast<float>(sqrt(r2));
+        if (qjl) {
+            const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
+            a.out.rnorm[n0 + tid] = static_cast<float>(sqrt(r2));
+        }
     }
 }
 

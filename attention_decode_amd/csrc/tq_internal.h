@@ -87,6 +87,18 @@ struct ValueLaunch {
 };
 hipError_t launch_compress_values(const ValueLaunch &a, hipStream_t stream);
 
+// explicit key estimates (k_dequant.hip)
+struct DequantLaunch {
+    int64_t N;                  // keys (B * Hkv * T), rows of every plane
+    int d, bits, m;
+    float kappa;                // sqrt(pi/2) / m, 0 without QJL rows
+    const float *pi, *s, *centroids;    // Pi [d][d] and S [m][d] row-major
+    const uint8_t *codes, *signs;
+    const float *knorm, *rnorm;
+    float *out;                 // [N][d]
+};
+hipError_t launch_dequant_keys(const DequantLaunch &a, hipStream_t stream);
+
 // extra state of the matrix-core decode path
 struct MfmaArgs {
     int gc = 0;                 // query heads per unit (<= 8)
@@ -133,7 +145,7 @@ constexpr int kDecodeTile = 256;   // keys per decode tile
 constexpr int kMfmaTile = 128;     // keys per workgroup step (four waves x 32)
 bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
 int mfma_query_chunk(int G);
-int mfma_score_steps(int d, int bits);
+int mfma_score_steps(int d, int bits, int m);
 int mfma_row_tiles(int bits, int gc);
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream);
 

@@ -58,8 +58,11 @@ typedef struct tq_codebook tq_codebook;   /* opaque, immutable */
 typedef struct tq_rotation tq_rotation;   /* opaque, immutable */
 
 /* Key format: d channels, mse_bits Lloyd-Max bits per coordinate, qjl_m sign
-   rows (this build: qjl_m == d), the codebook for (d, mse_bits) and the
-   rotation (Pi and S) for d. */
+   rows, the codebook for (d, mse_bits) and the rotation (Pi and S) for d.
+   qjl_m is d (both stages of the two-stage quantiser, "turboquant-pytorch",
+   section "What it does") or 0: the first stage alone, no sign or residual
+   norm planes, score n sum_j (Pi q)_j c[idx_j] (a biased estimate of <q, k>
+   that reads fewer bytes per key). */
 typedef struct {
     int d;
     int mse_bits;
@@ -77,7 +80,8 @@ typedef struct {
 } tq_val_fmt;
 
 /* Packed key cache planes (device, caller-owned), per vector:
-   codes d*mse_bits/8 B, signs qjl_m/8 B, knorm fp32 ||k||, rnorm fp32 ||r||. */
+   codes d*mse_bits/8 B, signs qjl_m/8 B, knorm fp32 ||k||, rnorm fp32 ||r||.
+   With qjl_m = 0 the signs and rnorm planes are empty (may be NULL). */
 typedef struct {
     uint8_t *codes;
     uint8_t *signs;
@@ -125,7 +129,8 @@ void tq_rotation_free(tq_rotation *rot);
 tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, double *s);
 
 /* Bytes of one plane for n_vec vectors.  Key planes: 0 codes, 1 signs,
-   2 knorm, 3 rnorm.  Value planes: 0 codes, 1 params.  0 on a bad argument. */
+   2 knorm, 3 rnorm (signs and rnorm are 0 bytes when qjl_m = 0).  Value
+   planes: 0 codes, 1 params.  0 on a bad argument. */
 size_t tq_key_plane_bytes(const tq_key_fmt *fmt, int64_t n_vec, int plane);
 size_t tq_val_plane_bytes(const tq_val_fmt *fmt, int64_t n_vec, int plane);
 
@@ -178,6 +183,16 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
                            tq_dtype dtype, int B, int Hq, int Hkv, int64_t T, tq_kcache kc,
                            tq_vcache vc, float softmax_scale, int n_splits, void *ws,
                            size_t ws_bytes, float *out, void *stream);
+
+/* Explicit key estimates of a packed cache (dequantisation), fp32
+   out[B, Hkv, T, d] (contiguous, device):
+     k_hat = ||k|| Pi^T ( c[idx] + sqrt(pi/2)/m ||r|| S^T (2 s - 1) ),
+   the vector whose inner product with any query equals the score above
+   ("turboquant-pytorch", section "What it does": the inverse of the
+   two-stage encoding); with qjl_m = 0, k_hat = ||k|| Pi^T c[idx].  Not on the
+   decode path, which never forms k_hat.  T = 0 is a no-op. */
+tq_status tq_dequantize_keys(const tq_key_fmt *fmt, int B, int Hkv, int64_t T, tq_kcache kc,
+                             float *out, void *stream);
 
 /* ------------------------------------------------------------- utilities */
 

@@ -333,8 +333,9 @@ def attend(q: np.ndarray, kc: KeyCache, bits: int, rot: Rotation, vc: ValueCache
 
 # ------------------------------------------------------------ size accounting
 def key_bytes_per_vector(d: int, bits: int, m: int) -> int:
-    """codes + signs + fp32 ||k|| + fp32 ||r||"""
-    return (d * bits + 7) // 8 + (m + 7) // 8 + 4 + 4
+    """codes + signs + fp32 ||k|| + fp32 ||r||; the first-stage format (m = 0)
+    stores neither signs nor ||r||, which its score does not use"""
+    return (d * bits + 7) // 8 + (m + 7) // 8 + 4 + (4 if m > 0 else 0)
 
 
 def value_bytes_per_vector(d: int, bits: int, group: int) -> int:

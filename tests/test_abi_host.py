@@ -116,6 +116,23 @@ def test_plane_sizes():
         assert vbb == O.value_bytes_per_vector(d, vb, g)
 
 
+def test_first_stage_format_sizes_and_checks():
+    """qjl_m = 0: no signs and no rnorm plane; qjl_m other than 0 or d is refused."""
+    lib = L.lib()
+    for d, b in [(64, 3), (128, 2), (256, 7)]:
+        kf = _kf(d=d, mse_bits=b, qjl_m=0)
+        sizes = [lib.tq_key_plane_bytes(ctypes.byref(kf), 5, p) for p in range(4)]
+        assert sizes == [5 * d * b // 8, 0, 20, 0]
+        assert sum(sizes) == 5 * O.key_bytes_per_vector(d, b, 0)
+    kc = L.KCache()
+    kf = _kf(qjl_m=64)
+    assert lib.tq_compress_keys(ctypes.byref(kf), None, 1, 1, 1, 8, 0, 0, 128, kc, None) == L.TQ_EINVAL
+    # the format check runs first: no codebook handle
+    assert lib.tq_dequantize_keys(ctypes.byref(_kf(qjl_m=0)), 1, 1, 8, kc, None, None) == L.TQ_EINVAL
+    assert b"codebook" in lib.tq_last_error()
+    assert lib.tq_dequantize_keys(None, 1, 1, 8, kc, None, None) == L.TQ_EINVAL
+
+
 def test_split_policy_and_workspace():
     lib = L.lib()
     kf = _kf()
