@@ -48,6 +48,7 @@ class Workload:
     keys: str           # "iid" | "channel_lognormal" | "scaled"
     kv_ratio: float     # target mean ||k|| / mean ||v|| (0: unscaled)
     seed: int
+    qjl: bool = True    # False: the first-stage key format (codes and ||k|| only)
 
     @property
     def G(self) -> int:
@@ -58,8 +59,13 @@ class Workload:
                        layers=self.layers if layers is None else layers)
 
     def key_bytes(self) -> int:
-        """packed bytes per key vector: codes + signs + fp32 ||k|| + fp32 ||r||"""
-        return self.d * self.k_bits // 8 + self.d // 8 + 8
+        """packed bytes per key vector: codes + signs + fp32 ||k|| + fp32 ||r||
+        (codes + fp32 ||k|| for the first-stage format)"""
+        return self.d * self.k_bits // 8 + (self.d // 8 + 4 if self.qjl else 0) + 4
+
+    @property
+    def qjl_m(self) -> int:
+        return self.d if self.qjl else 0
 
     def value_bytes(self) -> int:
         """packed bytes per value vector: codes + fp16 (scale, zero) per group"""

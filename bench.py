@@ -14,7 +14,8 @@ the launch stream, in a separate pass after the timed region) against the
 8 TB/s HBM peak.  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import replace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -36,6 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen25-3b-8k")
+    ap.add_argument("--key-format", choices=["full", "first-stage"], default="full",
+                    help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
+                         "||k|| only (qjl_m = 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -66,7 +71,7 @@ class Layer:
     def __init__(self, w, layer, tq, W, torch):
         self.cb = tq.tq_build_codebook(w.d, w.k_bits)
         self.rot = tq.tq_make_rotation(w.rotation_seed(layer), w.d, w.rot)
-        self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot)
+        self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot, qjl_m=w.qjl_m)
         self.vf = tq.ValueFormat(w.d, w.v_bits, w.group)
         self.k = W.make_keys(w, layer, device="cuda")
         self.v = W.make_values(w, layer, device="cuda")
@@ -112,7 +117,7 @@ def cpu_baseline(w, seconds: float):
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     small = w.with_T(min(w.T, 8192), B=1, layers=1)
-    rot = O.rotation(w.rotation_seed(0), w.d, w.rot)
+    rot = O.rotation(w.rotation_seed(0), w.d, w.rot, m=w.qjl_m)
     O.codebook(w.d, w.k_bits)
     k = W.make_keys(small, 0).double().numpy()[0]
     v = W.make_values(small, 0).double().numpy()[0]
@@ -170,6 +175,8 @@ def main():
         calib_copy(torch)
         return
     w = W.WORKLOADS[args.workload]
+    if args.key_format == "first-stage":
+        w = replace(w, name=w.name + "-first-stage", qjl=False)
     print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
           file=sys.stderr, flush=True)
     layers = [Layer(w, l, tq, W, torch) for l in range(w.layers)]
@@ -251,7 +258,8 @@ def main():
         "data": "synthetic (seeded; shapes and statistics of the workload, no model weights)",
         "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "kv_heads": w.Hkv,
                    "q_heads": w.Hq, "tokens": w.T, "head_dim": w.d, "input_dtype": w.dtype,
-                   "k_bits": f"{w.k_bits}+1 (Lloyd-Max + QJL sign)", "rotation": w.rot,
+                   "k_bits": (f"{w.k_bits}+1 (Lloyd-Max + QJL sign)" if w.qjl
+                              else f"{w.k_bits} (Lloyd-Max only, first-stage format)"), "rotation": w.rot,
                    "v_bits": w.v_bits, "v_group": w.group, "attn_splits": splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_ms_per_step": round(d_ms, 4),
