@@ -22,7 +22,9 @@ __all__ = [
     "tq_scores", "tq_attend_decode", "tq_codebook_host", "tq_rotation_host",
     "KeyFormat", "ValueFormat", "KeyCache", "ValueCache", "alloc_key_cache", "alloc_value_cache",
     "tq_attend_splits", "tq_attend_workspace_bytes", "tq_scores_workspace_bytes",
-    "tq_profile_enable", "tq_profile_read", "TQError",
+    "tq_profile_enable", "tq_profile_read", "TQError", "tq_dequantize_keys",
+    "CacheLayout", "alloc_layout_key_cache", "alloc_layout_value_cache", "tq_append_keys", "tq_append_values",
+    "tq_attend_paged_workspace_bytes", "tq_attend_decode_paged",
 ]
 
 _ROT_KIND = {"dense": TQ_ROT_DENSE, "hadamard": TQ_ROT_HADAMARD}
@@ -242,6 +244,94 @@ def tq_attend_decode(kfmt: KeyFormat, vfmt: ValueFormat, q, kc: KeyCache, vc: Va
     check(lib().tq_attend_decode(ctypes.byref(kf), ctypes.byref(vf), q.data_ptr(), _dtype_code(q), B, Hq,
                                  Hkv, T, kc.c(), vc.c(), softmax_scale, n_splits, ws.data_ptr(),
                                  ws.numel(), out.data_ptr(), _stream(stream)), "tq_attend_decode")
+    return out
+
+
+# ------------------------------------------------------------ serving caches
+@dataclass
+class CacheLayout:
+    """A preallocated cache that grows per decode step (tq_cache_layout).
+    seq_lens: int32 [B] device tensor.  block_table: None (contiguous planes
+    [B, Hkv, capacity, row]) or int32 [B, max_blocks] device tensor into a pool
+    of num_blocks blocks of block_size tokens (planes [num_blocks, Hkv,
+    block_size, row])."""
+    capacity: int
+    seq_lens: "torch.Tensor"        # noqa: F821
+    block_table: "torch.Tensor" = None  # noqa: F821
+    block_size: int = 0
+    num_blocks: int = 0
+
+    def c(self) -> L.CacheLayout:
+        bt = self.block_table
+        return L.CacheLayout(self.capacity, None if self.seq_lens is None else self.seq_lens.data_ptr(),
+                             None if bt is None else bt.data_ptr(), self.block_size,
+                             0 if bt is None else bt.shape[1], self.num_blocks)
+
+
+def paged_rows(layout: CacheLayout, B: int, Hkv: int) -> int:
+    """Rows each plane of a layout cache holds."""
+    if layout.block_table is None:
+        return B * Hkv * layout.capacity
+    return layout.num_blocks * Hkv * layout.block_size
+
+
+def alloc_layout_key_cache(fmt: KeyFormat, layout: CacheLayout, B: int, Hkv: int, device="cuda") -> KeyCache:
+    """Key planes of a layout cache, flattened to rows."""
+    import torch
+    kf = fmt.c()
+    n = paged_rows(layout, B, Hkv)
+    row = lambda p: lib().tq_key_plane_bytes(ctypes.byref(kf), 1, p)
+    qjl = kf.qjl_m > 0
+    return KeyCache(torch.zeros((n, row(0)), dtype=torch.uint8, device=device),
+                    torch.zeros((n, row(1)), dtype=torch.uint8, device=device) if qjl else None,
+                    torch.zeros((n,), dtype=torch.float32, device=device),
+                    torch.zeros((n,), dtype=torch.float32, device=device) if qjl else None)
+
+
+def alloc_layout_value_cache(fmt: ValueFormat, layout: CacheLayout, B: int, Hkv: int, device="cuda") -> ValueCache:
+    import torch
+    n = paged_rows(layout, B, Hkv)
+    return ValueCache(torch.zeros((n, fmt.d * fmt.bits // 8), dtype=torch.uint8, device=device),
+                      torch.zeros((n, fmt.d // fmt.group, 2), dtype=torch.int16, device=device))
+
+
+def tq_append_keys(fmt: KeyFormat, k, layout: CacheLayout, pos, cache: KeyCache, stream=None) -> None:
+    """k [B, Hkv, n_new, d] -> positions pos[b] .. pos[b] + n_new - 1 of each sequence."""
+    B, H, T, sb, sh, st = _bhtd(k)
+    kf, lay = fmt.c(), layout.c()
+    check(lib().tq_append_keys(ctypes.byref(kf), k.data_ptr(), _dtype_code(k), B, H, T, sb, sh, st,
+                               ctypes.byref(lay), pos.data_ptr(), cache.c(), _stream(stream)), "tq_append_keys")
+
+
+def tq_append_values(fmt: ValueFormat, v, layout: CacheLayout, pos, cache: ValueCache, stream=None) -> None:
+    B, H, T, sb, sh, st = _bhtd(v)
+    vf, lay = fmt.c(), layout.c()
+    check(lib().tq_append_values(ctypes.byref(vf), v.data_ptr(), _dtype_code(v), B, H, T, sb, sh, st,
+                                 ctypes.byref(lay), pos.data_ptr(), cache.c(), _stream(stream)), "tq_append_values")
+
+
+def tq_attend_paged_workspace_bytes(fmt: KeyFormat, B: int, Hq: int, Hkv: int, layout: CacheLayout,
+                                    n_splits: int = 0) -> int:
+    kf, lay = fmt.c(), layout.c()
+    return int(lib().tq_attend_paged_workspace_bytes(ctypes.byref(kf), B, Hq, Hkv, ctypes.byref(lay), n_splits))
+
+
+def tq_attend_decode_paged(kfmt: KeyFormat, vfmt: ValueFormat, q, kc: KeyCache, vc: ValueCache, Hkv: int,
+                           layout: CacheLayout, out=None, ws=None, n_splits: int = 0, softmax_scale: float = 0.0,
+                           stream=None):
+    """q [B, Hq, d] contiguous over a layout cache -> [B, Hq, d] fp32."""
+    import torch
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        need = tq_attend_paged_workspace_bytes(kfmt, B, Hq, Hkv, layout, n_splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    kf, vf, lay = kfmt.c(), vfmt.c(), layout.c()
+    check(lib().tq_attend_decode_paged(ctypes.byref(kf), ctypes.byref(vf), q.data_ptr(), _dtype_code(q), B, Hq,
+                                       Hkv, ctypes.byref(lay), kc.c(), vc.c(), softmax_scale, n_splits,
+                                       ws.data_ptr(), ws.numel(), out.data_ptr(), _stream(stream)),
+          "tq_attend_decode_paged")
     return out
 
 

@@ -36,6 +36,11 @@ class VCache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
 
 
+class CacheLayout(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int64), ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("block_size", ctypes.c_int), ("max_blocks", ctypes.c_int), ("num_blocks", ctypes.c_int64)]
+
+
 # name -> (restype, argtypes); every entry point of include/tq.h
 _c = ctypes
 _vp, _i, _i64, _u64, _sz = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_uint64, _c.c_size_t
@@ -59,6 +64,13 @@ SIGNATURES = {
     "tq_attend_decode": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64,
                               KCache, VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
     "tq_dequantize_keys": (_i, [_c.POINTER(KeyFmt), _i, _i, _i64, KCache, _vp, _vp]),
+    "tq_append_keys": (_i, [_c.POINTER(KeyFmt), _vp, _i, _i, _i, _i, _i64, _i64, _i64, _c.POINTER(CacheLayout),
+                            _vp, KCache, _vp]),
+    "tq_append_values": (_i, [_c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64, _i64, _i64, _c.POINTER(CacheLayout),
+                              _vp, VCache, _vp]),
+    "tq_attend_paged_workspace_bytes": (_sz, [_c.POINTER(KeyFmt), _i, _i, _i, _c.POINTER(CacheLayout), _i]),
+    "tq_attend_decode_paged": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i,
+                                    _c.POINTER(CacheLayout), KCache, VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
     "tq_last_error": (_c.c_char_p, []),
     "tq_profile_enable": (_i, [_i]),
     "tq_profile_read": (_i, [_c.c_char_p, _dp, _c.POINTER(_i64)]),

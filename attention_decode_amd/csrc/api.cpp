@@ -542,14 +542,44 @@ AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePla
     return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
-                           int64_t T, int64_t sb, int64_t sh, int64_t st, tq_kcache out, void *stream)
+// A layout cache (tq_cache_layout) as the kernels' row map; seq_lens are
+// required for decode, pos for appends.
+tq_status layout_map(const tq_cache_layout *lay, const int32_t *pos, bool decode, const char *who, tq::CacheMap &m)
 {
-    const char *who = "tq_compress_keys";
+    if (!lay) return fail(TQ_EINVAL, "%s: NULL cache layout", who);
+    if (lay->capacity < 1 || lay->capacity > (int64_t(1) << 31))
+        return fail(TQ_EINVAL, "%s: capacity %lld outside [1, 2^31]", who, (long long)lay->capacity);
+    auto al4 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (decode && (!lay->seq_lens || !al4(lay->seq_lens)))
+        return fail(TQ_EINVAL, "%s: seq_lens must be a 4-byte aligned device array", who);
+    if (!decode && (!pos || !al4(pos))) return fail(TQ_EINVAL, "%s: pos must be a 4-byte aligned device array", who);
+    m = tq::CacheMap{};
+    m.cap = lay->capacity;
+    m.seq_lens = lay->seq_lens;
+    m.pos = pos;
+    if (lay->block_table) {
+        if (!al4(lay->block_table)) return fail(TQ_EINVAL, "%s: block_table must be 4-byte aligned", who);
+        if (lay->block_size < 32 || lay->block_size % 32)
+            return fail(TQ_EUNSUPPORTED, "%s: block_size=%d is not a positive multiple of 32", who, lay->block_size);
+        if (lay->max_blocks < 1 || lay->num_blocks < 1)
+            return fail(TQ_EINVAL, "%s: max_blocks=%d, num_blocks=%lld", who, lay->max_blocks, (long long)lay->num_blocks);
+        if (static_cast<int64_t>(lay->max_blocks) * lay->block_size != lay->capacity)
+            return fail(TQ_EINVAL, "%s: capacity %lld != max_blocks * block_size", who, (long long)lay->capacity);
+        m.mode = tq::CacheMap::kPaged;
+        m.bt = lay->block_table;
+        m.bs = lay->block_size;
+        m.maxb = lay->max_blocks;
+        m.nblocks = lay->num_blocks;
+    } else {
+        m.mode = tq::CacheMap::kContig;
+    }
+    return TQ_OK;
+}
+
+tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv, int64_t T,
+                             int64_t sb, int64_t sh, int64_t st, tq_kcache out, const tq::CacheMap &map,
+                             void *stream, const char *who)
+{
     TQ_TRY(check_key_fmt(fmt, who));
     TQ_TRY(check_dtype(dtype, who));
     TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
@@ -580,14 +610,15 @@ tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype,
     a.pifrag = fmt->rot->d_pifrag;
     a.sfrag = fmt->rot->d_sfrag;
     a.out = out;
+    a.map = map;
     const hipError_t e = tq::launch_compress_keys(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
 
-tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv,
-                             int64_t T, int64_t sb, int64_t sh, int64_t st, tq_vcache out, void *stream)
+tq_status compress_values_impl(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv, int64_t T,
+                               int64_t sb, int64_t sh, int64_t st, tq_vcache out, const tq::CacheMap &map,
+                               void *stream, const char *who)
 {
-    const char *who = "tq_compress_values";
     TQ_TRY(check_val_fmt(fmt, who));
     TQ_TRY(check_dtype(dtype, who));
     TQ_TRY(check_input(v, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
@@ -606,8 +637,46 @@ tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtyp
     a.bits = fmt->bits;
     a.group = fmt->group;
     a.out = out;
+    a.map = map;
     const hipError_t e = tq::launch_compress_values(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
+                           int64_t T, int64_t sb, int64_t sh, int64_t st, tq_kcache out, void *stream)
+{
+    return compress_keys_impl(fmt, k, dtype, B, Hkv, T, sb, sh, st, out, tq::CacheMap{}, stream, "tq_compress_keys");
+}
+
+tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv,
+                             int64_t T, int64_t sb, int64_t sh, int64_t st, tq_vcache out, void *stream)
+{
+    return compress_values_impl(fmt, v, dtype, B, Hkv, T, sb, sh, st, out, tq::CacheMap{}, stream,
+                                "tq_compress_values");
+}
+
+tq_status tq_append_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv, int n_new,
+                         int64_t sb, int64_t sh, int64_t st, const tq_cache_layout *lay, const int32_t *pos,
+                         tq_kcache cache, void *stream)
+{
+    const char *who = "tq_append_keys";
+    tq::CacheMap m;
+    TQ_TRY(layout_map(lay, pos, false, who, m));
+    return compress_keys_impl(fmt, k, dtype, B, Hkv, n_new, sb, sh, st, cache, m, stream, who);
+}
+
+tq_status tq_append_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv, int n_new,
+                           int64_t sb, int64_t sh, int64_t st, const tq_cache_layout *lay, const int32_t *pos,
+                           tq_vcache cache, void *stream)
+{
+    const char *who = "tq_append_values";
+    tq::CacheMap m;
+    TQ_TRY(layout_map(lay, pos, false, who, m));
+    return compress_values_impl(fmt, v, dtype, B, Hkv, n_new, sb, sh, st, cache, m, stream, who);
 }
 
 static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq,
@@ -704,11 +773,20 @@ size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, 
     return attend_layout(fmt, B, Hq, p).total;
 }
 
-tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
-                           int B, int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
-                           int n_splits, void *ws, size_t ws_bytes, float *out, void *stream)
+size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, const tq_cache_layout *lay,
+                                       int n_splits)
 {
-    const char *who = "tq_attend_decode";
+    if (!lay || lay->capacity < 1) return 0;
+    return tq_attend_workspace_bytes(fmt, B, Hq, Hkv, lay->capacity, n_splits);
+}
+
+// decode attention over T tokens per sequence (flat map) or over a layout
+// cache with T = its capacity
+static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype, int B,
+                             int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
+                             int n_splits, void *ws, size_t ws_bytes, float *out, const tq::CacheMap &map,
+                             void *stream, const char *who)
+{
     TQ_TRY(check_decode_common(kfmt, q, dtype, B, Hq, Hkv, T, kc, who));
     TQ_TRY(check_val_fmt(vfmt, who));
     if (vfmt->d != kfmt->d) return fail(TQ_EINVAL, "%s: key d=%d and value d=%d differ", who, kfmt->d, vfmt->d);
@@ -762,6 +840,7 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
     a.mf.units = plan.units;
     a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
+    a.map = map;
     hipError_t e;
     if (plan.mfma) {
         e = tq::launch_decode_mfma(a, s);
@@ -770,6 +849,26 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
         if (e == hipSuccess) e = tq::launch_attend(a, s);
     }
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
+                           int B, int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
+                           int n_splits, void *ws, size_t ws_bytes, float *out, void *stream)
+{
+    return attend_impl(kfmt, vfmt, q, dtype, B, Hq, Hkv, T, kc, vc, softmax_scale, n_splits, ws, ws_bytes, out,
+                       tq::CacheMap{}, stream, "tq_attend_decode");
+}
+
+tq_status tq_attend_decode_paged(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
+                                 int B, int Hq, int Hkv, const tq_cache_layout *lay, tq_kcache kc, tq_vcache vc,
+                                 float softmax_scale, int n_splits, void *ws, size_t ws_bytes, float *out,
+                                 void *stream)
+{
+    const char *who = "tq_attend_decode_paged";
+    tq::CacheMap m;
+    TQ_TRY(layout_map(lay, nullptr, true, who, m));
+    return attend_impl(kfmt, vfmt, q, dtype, B, Hq, Hkv, lay->capacity, kc, vc, softmax_scale, n_splits, ws,
+                       ws_bytes, out, m, stream, who);
 }
 
 }  // extern "C"

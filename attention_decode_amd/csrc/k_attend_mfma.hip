@@ -647,9 +647,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     const int lg_ng = __builtin_ctz(NG);
     const int unit = blockIdx.y, split = blockIdx.x;
     const int64_t bh = unit / nqc;
+    const int64_t seq = bh / a.Hkv, kvh = bh - seq * a.Hkv;
     const int64_t row0 = unit_row0(a, unit);
     const int64_t t_begin = static_cast<int64_t>(split) * chunk;
-    const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
+    const int64_t len = seq_len_of(a.map, a.T, seq);        // T, or the sequence's length
+    const int64_t t_end = t_begin + chunk < len ? t_begin + chunk : len;
     const int j = lane % 16, kb = lane / 16;
 
     unsigned char *vt = smem + wave * WAVE_BYTES;
@@ -700,6 +702,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     const unsigned char *tr_base = vt + slot_token(8 * kb + e_of_r) * VSTR + 8 * (j % 2);
 
     struct Prefetch {
+        int nvalid;             // keys of the tile (0: a block id outside the pool)
         typename SCORE::KW kw;
         v4i vcode[VCL];
         uint32_t par[PD];
@@ -711,7 +714,15 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     auto fetch = [&](int64_t tile0, Prefetch &pf) {
         const int64_t tc = tile0 < t_end ? tile0 : first;
         const int nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
-        const int64_t n0 = bh * a.T + tc;            // wave-uniform row of the tile
+        // wave-uniform row of the tile: a tile never straddles a block (tiles
+        // start at multiples of 32 tokens, blocks hold a multiple of 32)
+        int64_t n0 = bh * a.T + tc;
+        pf.nvalid = nv;
+        if (a.map.mode == CacheMap::kPaged) {
+            const int64_t r = layout_row(a.map, a.Hkv, seq, kvh, tc);
+            n0 = r < 0 ? 0 : r;
+            if (r < 0) pf.nvalid = 0;
+        }
         const uint32_t *cbase = reinterpret_cast<const uint32_t *>(a.kc.codes) + n0 * (D * BITS / 32);
         const uint32_t *sbase = reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32);
         const float *nbase = a.kc.knorm + n0, *rbase = a.kc.rnorm + n0;
@@ -741,7 +752,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     };
 
     auto compute = [&](int64_t tile0, const Prefetch &cur) {
-        const int nv = static_cast<int>(t_end - tile0 < TK ? t_end - tile0 : TK);
+        (void)tile0;
+        const int nv = cur.nvalid;
         wave_sync();        // the previous tile's LDS reads come before these writes
         // ---- value codes and (scale, zero) words of the tile into this wave's LDS
 #pragma unroll

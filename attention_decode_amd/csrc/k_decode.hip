@@ -199,8 +199,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeLaunch a, int nqc, fl
         s.m[tid] = -INFINITY;
         s.l[tid] = 0.0f;
     }
+    __shared__ int64_t s_rows[kTile];           // plane row of each token of the tile (-1: none)
     const int64_t t_begin = static_cast<int64_t>(split) * chunk;
-    const int64_t t_end = t_begin + chunk < a.T ? t_begin + chunk : a.T;
+    const int64_t len = seq_len_of(a.map, a.T, u.b);
+    const int64_t t_end = t_begin + chunk < len ? t_begin + chunk : len;
     const int P = kThreads / D, part = tid / D, c = tid % D;
     const int span = kTile / P, grp = c / a.group;
     const uint32_t vmask = (1u << a.vbits) - 1u;
@@ -215,8 +217,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeLaunch a, int nqc, fl
         // A. scaled scores of this thread's key
         {
             float lam[GC];
-            if (tid < ntile) {
-                const int64_t n = u.bh * a.T + tile0 + tid;
+            int64_t n = -1;
+            if (tid < ntile)
+                n = a.map.mode == CacheMap::kPaged ? layout_row(a.map, a.Hkv, u.b, u.hkv, tile0 + tid)
+                                                   : u.bh * a.T + tile0 + tid;
+            s_rows[tid] = n;
+            if (n >= 0) {
                 const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.kc.codes) + n * (D * BITS / 32);
                 const uint32_t *srow = reinterpret_cast<const uint32_t *>(a.kc.signs) + n * (a.m / 32);
                 float dc[GC], ds[GC];
@@ -231,17 +237,23 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeLaunch a, int nqc, fl
 #pragma unroll
             for (int g = 0; g < GC; ++g) s.p[g * kTile + tid] = lam[g];
         }
-        // stage the value tile: raw code rows and (scale, zero) as fp32
+        __syncthreads();        // token rows
+        // stage the value tile: raw code rows and (scale, zero) as fp32 (tokens
+        // without a row read as zero codes and zero parameters)
         {
-            const int64_t n0 = u.bh * a.T + tile0;
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.vc.codes + n0 * VB);
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.vc.codes);
             uint4 *dst = reinterpret_cast<uint4 *>(s.vcode);
-            for (int i = tid; i < ntile * VB / 16; i += kThreads) dst[i] = src[i];
-            const uint32_t *par = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
+            const int cpr = VB / 16;                // 16-byte chunks per row
+            for (int i = tid; i < ntile * cpr; i += kThreads) {
+                const int64_t r = s_rows[i / cpr];
+                dst[i] = r >= 0 ? src[r * cpr + i % cpr] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const uint32_t *par = reinterpret_cast<const uint32_t *>(a.vc.params);
             for (int i = tid; i < kTile * NG; i += kThreads) {
                 float sc = 0.0f, ze = 0.0f;
-                if (i < ntile * NG) {
-                    const uint32_t w = par[i];
+                const int64_t r = i < ntile * NG ? s_rows[i / NG] : -1;
+                if (r >= 0) {
+                    const uint32_t w = par[r * NG + i % NG];
                     sc = f16_bits_to_f32(w & 0xffffu);
                     ze = f16_bits_to_f32(w >> 16);
                 }

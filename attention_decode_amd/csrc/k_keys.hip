@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     constexpr int L = 1 << BITS;
     constexpr int CW = D * BITS / 32, SWN = D / 32;
     extern __shared__ __align__(16) unsigned char smem_raw[];
+    __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup
     KeySmem s;
     {
         unsigned char *p = smem_raw;
@@ -344,20 +345,40 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     __syncthreads();
     }
 
-    // ---- 5. store the WG's keys (contiguous rows of every plane)
+    // ---- 5. store the WG's keys: contiguous rows of every plane, or (when
+    // appending to a layout cache) each key at its own row
     const int nk = static_cast<int>(n_total - n0 < kKeys ? n_total - n0 : kKeys);
-    uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
-    for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
-    if (qjl) {
-        uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
-        for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+    if (a.map.mode == CacheMap::kFlat) {
+        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
+        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
+        if (qjl) {
+            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
+            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+        }
+        if (tid < nk) s_row[tid] = n0 + tid;
+    } else {
+        if (tid < nk) s_row[tid] = out_row(a.map, a.H, a.T, n0 + tid);
+        __syncthreads();
+        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes);
+        for (int i = tid; i < nk * CW; i += kThreads) {
+            const int64_t r = s_row[i / CW];
+            if (r >= 0) codes[r * CW + i % CW] = s.cw[i];
+        }
+        if (qjl) {
+            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs);
+            for (int i = tid; i < nk * SWN; i += kThreads) {
+                const int64_t r = s_row[i / SWN];
+                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[i];
+            }
+        }
     }
-    if (tid < nk) {
+    if (tid < nk && s_row[tid] >= 0) {
+        const int64_t r = s_row[tid];
         const double n2 = s.nrm2[tid] + s.nrm2[kKeys + tid] + s.nrm2[2 * kKeys + tid] + s.nrm2[3 * kKeys + tid];
-        a.out.knorm[n0 + tid] = static_cast<float>(sqrt(n2));
+        a.out.knorm[r] = static_cast<float>(sqrt(n2));
         if (qjl) {
             const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
-            a.out.rnorm[n0 + tid] = static_cast<float>(sqrt(r2));
+            a.out.rnorm[r] = static_cast<float>(sqrt(r2));
         }
     }
 }

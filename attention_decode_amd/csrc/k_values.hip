@@ -75,7 +75,9 @@ __global__ __launch_bounds__(kThreads) void k_compress_values(ValueLaunch a, int
     const float sc = f16_bits_to_f32(sh), ze = f16_bits_to_f32(zh);
 
     constexpr int per_word = 32 / BITS, words = G * BITS / 32;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.out.codes) + n * (a.d * BITS / 32) + grp * words;
+    const int64_t row = out_row(a.map, a.H, a.T, n);      // n itself unless appending
+    if (row < 0) return;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(a.out.codes) + row * (a.d * BITS / 32) + grp * words;
 #pragma unroll
     for (int w = 0; w < words; ++w) {
         uint32_t word = 0;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_values(ValueLaunch a, int
             word |= value_code(x[w * per_word + e], ze, sc, levels) << (BITS * e);
         dst[w] = word;
     }
-    reinterpret_cast<uint32_t *>(a.out.params)[gi] = sh | (zh << 16);
+    reinterpret_cast<uint32_t *>(a.out.params)[row * (a.d / G) + grp] = sh | (zh << 16);
 }
 
 template <typename TIn, int G, int BITS>

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "tq_internal.h"
+
 #include <cstdint>
 
 namespace tq {
@@ -81,6 +83,36 @@ __device__ __forceinline__ uint32_t f64_to_f16_rne(double x)
     if (rem > half || (rem == half && (q & 1))) ++q;
     if (e < -14) return sign | static_cast<uint32_t>(q);          // subnormal (q = 1024 -> min normal)
     return sign | (static_cast<uint32_t>(e + 15) << 10) + static_cast<uint32_t>(q) - 1024u;
+}
+
+// ---- layout caches (CacheMap): every index is checked, so that no access
+// leaves the planes whatever the device tables hold
+
+// row of token t of (b, h) in a layout cache, -1 outside it
+__device__ __forceinline__ int64_t layout_row(const CacheMap &m, int H, int64_t b, int64_t h, int64_t t)
+{
+    if (t < 0 || t >= m.cap) return -1;
+    if (m.mode == CacheMap::kContig) return (b * H + h) * m.cap + t;
+    const int64_t blk = m.bt[b * m.maxb + t / m.bs];
+    if (blk < 0 || blk >= m.nblocks) return -1;
+    return (blk * H + h) * m.bs + t % m.bs;
+}
+
+// plane row of row n of a compress call over [B, H, T] inputs, -1 to skip
+__device__ __forceinline__ int64_t out_row(const CacheMap &m, int H, int64_t T, int64_t n)
+{
+    if (m.mode == CacheMap::kFlat) return n;
+    const int64_t t = n % T, bh = n / T;
+    const int64_t b = bh / H, h = bh - b * H;
+    return layout_row(m, H, b, h, static_cast<int64_t>(m.pos[b]) + t);
+}
+
+// tokens sequence b attends (T for a flat call)
+__device__ __forceinline__ int64_t seq_len_of(const CacheMap &m, int64_t T, int64_t b)
+{
+    if (m.mode == CacheMap::kFlat) return T;
+    const int64_t l = m.seq_lens[b];
+    return l < 0 ? 0 : (l > m.cap ? m.cap : l);
 }
 
 }  // namespace tq

@@ -49,6 +49,22 @@ struct tq_rotation {
 
 namespace tq {
 
+// Where the packed rows of a call live.  Flat: row n of the [B, H, T] call is
+// row n of the planes.  Layout (contiguous or paged, tq_cache_layout): token t
+// of (b, h) sits at layout_row(); a compress call in layout mode appends its
+// token t of (b, h) at position pos[b] + t; a decode call in layout mode reads
+// seq_lens[b] tokens of sequence b.
+struct CacheMap {
+    enum Mode { kFlat = 0, kContig = 1, kPaged = 2 };
+    int mode = kFlat;
+    int64_t cap = 0;                    // tokens a sequence can hold
+    const int32_t *seq_lens = nullptr;  // decode: [B]
+    const int32_t *pos = nullptr;       // append: [B]
+    const int32_t *bt = nullptr;        // paged: [B][maxb]
+    int bs = 0, maxb = 0;
+    int64_t nblocks = 0;
+};
+
 // ---- host math (host_math.cpp)
 uint64_t rng_draw(uint64_t seed, int stream, uint64_t k);
 double rng_normal(uint64_t seed, int stream, uint64_t n);
@@ -73,6 +89,7 @@ struct KeyLaunch {
     float grid_lo, grid_scale;
     const uint16_t *pifrag, *sfrag;
     tq_kcache out;
+    CacheMap map;               // flat, or appending into a layout cache
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
 constexpr int kMaxGrid = 4096;     // cells of the code grid (bytes of LDS)
@@ -84,6 +101,7 @@ struct ValueLaunch {
     int64_t T, sb, sh, st;
     int d, bits, group;
     tq_vcache out;
+    CacheMap map;
 };
 hipError_t launch_compress_values(const ValueLaunch &a, hipStream_t stream);
 
@@ -131,6 +149,7 @@ struct DecodeLaunch {
     float *part_acc;            // [B, Hq, splits, d]
     float *scores;              // tq_scores output [B, Hq, T]
     float *out;                 // [B, Hq, d]
+    CacheMap map;               // flat (T tokens each) or a layout cache (T = capacity)
     MfmaArgs mf;
 };
 hipError_t launch_qprep(const DecodeLaunch &a, hipStream_t stream);

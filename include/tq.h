@@ -184,6 +184,59 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
                            tq_vcache vc, float softmax_scale, int n_splits, void *ws,
                            size_t ws_bytes, float *out, void *stream);
 
+/* ------------------------------------------------- serving-style caches */
+
+/* Layout of a preallocated cache that grows by a few tokens per decode step,
+   with sequences of different lengths: the serving integration the pages
+   describe (discosf.com article, section on known limitations: new K/V of
+   each layer are captured into a paged cache; tproger.ru article, section
+   "Implementations": TurboQuant as a KV-cache option of a serving engine).
+     seq_lens     device int32 [B]: valid tokens of each sequence.
+     block_table  NULL: contiguous planes [B, Hkv, capacity, row]; token t of
+                  sequence b, KV head h is row (b * Hkv + h) * capacity + t.
+                  Otherwise a device int32 [B, max_blocks] table into a pool of
+                  num_blocks blocks of block_size tokens, planes
+                  [num_blocks, Hkv, block_size, row]; token t lives in block
+                  blk = block_table[b * max_blocks + t / block_size], row
+                  (blk * Hkv + h) * block_size + t % block_size.
+     capacity     tokens a sequence can hold (max_blocks * block_size when
+                  paged).
+   block_size is a multiple of 32.  The kernels read seq_lens and block_table
+   on the device: a length is clamped to [0, capacity], and a token whose
+   block id is outside [0, num_blocks) is skipped (not read, not written), so
+   no access leaves the planes whatever the tables hold. */
+typedef struct {
+    int64_t capacity;
+    const int32_t *seq_lens;
+    const int32_t *block_table;
+    int block_size;
+    int max_blocks;
+    int64_t num_blocks;
+} tq_cache_layout;
+
+/* Compress n_new new tokens per sequence, k[B, Hkv, n_new, d] (strides as in
+   tq_compress_keys), into positions pos[b] .. pos[b] + n_new - 1 of sequence
+   b of a layout cache (pos: device int32 [B], typically the lengths before
+   the step; the layout's seq_lens are not read).  Positions outside
+   [0, capacity) are skipped.  Each key is encoded exactly as by
+   tq_compress_keys. */
+tq_status tq_append_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
+                         int n_new, int64_t sb, int64_t sh, int64_t st, const tq_cache_layout *lay,
+                         const int32_t *pos, tq_kcache cache, void *stream);
+tq_status tq_append_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv,
+                           int n_new, int64_t sb, int64_t sh, int64_t st, const tq_cache_layout *lay,
+                           const int32_t *pos, tq_vcache cache, void *stream);
+
+/* tq_attend_decode over a layout cache: sequence b attends its seq_lens[b]
+   tokens (a sequence of length 0 gives zeros).  Split planning uses the
+   capacity; ws: at least tq_attend_paged_workspace_bytes() bytes. */
+size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv,
+                                       const tq_cache_layout *lay, int n_splits);
+tq_status tq_attend_decode_paged(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q,
+                                 tq_dtype dtype, int B, int Hq, int Hkv, const tq_cache_layout *lay,
+                                 tq_kcache kc, tq_vcache vc, float softmax_scale, int n_splits,
+                                 void *ws, size_t ws_bytes, float *out, void *stream);
+
 /* Explicit key estimates of a packed cache (dequantisation), fp32
    out[B, Hkv, T, d] (contiguous, device):
      k_hat = ||k|| Pi^T ( c[idx] + sqrt(pi/2)/m ||r|| S^T (2 s - 1) ),
