@@ -494,7 +494,9 @@ struct DecodePlan {
     int gc = 0, nqc = 0, mt = 0, units = 0, splits = 0, steps = 0;
 };
 
-DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits)
+// paged_bs > 0: a paged cache with that block size, whose splits must each
+// span at most kStageBlocks blocks (their ids are staged in LDS)
+DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits, int paged_bs = 0)
 {
     DecodePlan p;
     const int G = Hq / Hkv;
@@ -515,6 +517,11 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     if (want > tiles) want = tiles;
     if (want > 1024) want = 1024;
     p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);
+    if (paged_bs > 0 && p.mfma) {
+        const int64_t max_tiles = static_cast<int64_t>(tq::kStageBlocks - 1) * paged_bs / tile;
+        const int64_t need = (tiles + max_tiles - 1) / max_tiles;
+        if (p.splits < need) p.splits = static_cast<int>(need);
+    }
     return p;
 }
 
@@ -559,8 +566,8 @@ tq_status layout_map(const tq_cache_layout *lay, const int32_t *pos, bool decode
     m.pos = pos;
     if (lay->block_table) {
         if (!al4(lay->block_table)) return fail(TQ_EINVAL, "%s: block_table must be 4-byte aligned", who);
-        if (lay->block_size < 32 || lay->block_size % 32)
-            return fail(TQ_EUNSUPPORTED, "%s: block_size=%d is not a positive multiple of 32", who, lay->block_size);
+        if (lay->block_size < 32 || (lay->block_size & (lay->block_size - 1)))
+            return fail(TQ_EUNSUPPORTED, "%s: block_size=%d is not a power of two >= 32", who, lay->block_size);
         if (lay->max_blocks < 1 || lay->num_blocks < 1)
             return fail(TQ_EINVAL, "%s: max_blocks=%d, num_blocks=%lld", who, lay->max_blocks, (long long)lay->num_blocks);
         if (static_cast<int64_t>(lay->max_blocks) * lay->block_size != lay->capacity)
@@ -776,8 +783,9 @@ size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, 
 size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, const tq_cache_layout *lay,
                                        int n_splits)
 {
-    if (!lay || lay->capacity < 1) return 0;
-    return tq_attend_workspace_bytes(fmt, B, Hq, Hkv, lay->capacity, n_splits);
+    if (!fmt || !lay || lay->capacity < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return 0;
+    const DecodePlan p = decode_plan(fmt, B, Hq, Hkv, lay->capacity, n_splits, lay->block_table ? lay->block_size : 0);
+    return attend_layout(fmt, B, Hq, p).total;
 }
 
 // decode attention over T tokens per sequence (flat map) or over a layout
@@ -814,7 +822,8 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     TQ_TRY(check_vcache(vc, who));
     if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
     if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
-    const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits);
+    const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits,
+                                        map.mode == tq::CacheMap::kPaged ? map.bs : 0);
     const AttendLayout L = attend_layout(kfmt, B, Hq, plan);
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;

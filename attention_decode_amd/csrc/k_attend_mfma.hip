@@ -639,6 +639,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     __shared__ __align__(16) unsigned char stab[SCORE::TAB_BYTES > 0 ? SCORE::TAB_BYTES : 16];
     __shared__ float s_wm[4][kMaxG], s_wl[4][kMaxG];
     __shared__ float s_wz[4][kMaxG][kMaxNG];
+    __shared__ int32_t s_blk[kStageBlocks];       // block ids of this split (paged caches)
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // wave-uniform: tile bases stay scalar
@@ -662,7 +663,27 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
     score.init(a, unit, row0, lane, kb, GC, kappa, stab);
     // value-product A rows of absent queries stay zero
     for (int i = lane; i < NGM * 64 * 4; i += 64) afr[i] = 0u;
-    if (SCORE::TAB_BYTES > 0) __syncthreads();   // score tables built by all threads
+    // Rows of the split's tiles, one formula for every cache: token t of the
+    // unit lives at row (blk * Hkv + kvh) * rstride + (t & rmask) with blk =
+    // s_blk[(t >> rshift) - blk0].  Flat and contiguous caches: one "block" per
+    // sequence (blk = seq, rstride = T).  Paged: the split's block ids, staged
+    // in LDS once (the host keeps a split within kStageBlocks blocks), ids
+    // outside the pool as -1.  A tile's row costs an LDS read, no branch.
+    const bool paged = a.map.mode == CacheMap::kPaged;
+    const int rshift = paged ? __builtin_ctz(a.map.bs) : 31;       // t < 2^31
+    const uint32_t rmask = paged ? static_cast<uint32_t>(a.map.bs - 1) : 0x7fffffffu;
+    const int64_t rstride = paged ? a.map.bs : a.T;
+    const int blk0 = static_cast<int>(t_begin >> rshift);
+    if (paged) {
+        const int nblk = t_end > t_begin ? static_cast<int>((t_end - 1) >> rshift) - blk0 + 1 : 0;
+        for (int i = tid; i < nblk && i < kStageBlocks; i += kThreads) {
+            const int32_t id = a.map.bt[seq * a.map.maxb + blk0 + i];
+            s_blk[i] = (id >= 0 && id < a.map.nblocks) ? id : -1;
+        }
+    } else if (tid == 0) {
+        s_blk[0] = static_cast<int32_t>(seq);
+    }
+    __syncthreads();        // block ids (and score tables), written by all threads
 
     float m_run[NQ], l_run[NQ];
     float zacc[NQ][NGM];
@@ -716,13 +737,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
         const int nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
         // wave-uniform row of the tile: a tile never straddles a block (tiles
         // start at multiples of 32 tokens, blocks hold a multiple of 32)
-        int64_t n0 = bh * a.T + tc;
-        pf.nvalid = nv;
-        if (a.map.mode == CacheMap::kPaged) {
-            const int64_t r = layout_row(a.map, a.Hkv, seq, kvh, tc);
-            n0 = r < 0 ? 0 : r;
-            if (r < 0) pf.nvalid = 0;
-        }
+        // (the clamp only guards LDS: the host keeps every split within kStageBlocks blocks)
+        const int bi = min(static_cast<int>(tc >> rshift) - blk0, kStageBlocks - 1);
+        const int blk = __builtin_amdgcn_readfirstlane(s_blk[bi]);
+        const int64_t n0 = blk >= 0 ? (static_cast<int64_t>(blk) * a.Hkv + kvh) * rstride
+                                          + (static_cast<uint32_t>(tc) & rmask) : 0;
+        pf.nvalid = blk >= 0 ? nv : 0;
         const uint32_t *cbase = reinterpret_cast<const uint32_t *>(a.kc.codes) + n0 * (D * BITS / 32);
         const uint32_t *sbase = reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32);
         const float *nbase = a.kc.knorm + n0, *rbase = a.kc.rnorm + n0;

@@ -162,6 +162,7 @@ constexpr int kDecodeTile = 256;   // keys per decode tile
 
 // matrix-core decode path (k_attend_mfma.hip): d 128/256, any key bits
 constexpr int kMfmaTile = 128;     // keys per workgroup step (four waves x 32)
+constexpr int kStageBlocks = 512;  // paged caches: block ids of one split staged in LDS
 bool mfma_decode_supported(int d, int bits, int G, int vbits, int group);
 int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits, int m);

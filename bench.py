@@ -15,6 +15,7 @@ the launch stream, in a separate pass after the timed region) against the
 fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage]
+                    [--layout flat|paged] [--block-size N]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -41,6 +42,11 @@ def parse():
     ap.add_argument("--key-format", choices=["full", "first-stage"], default="full",
                     help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
                          "||k|| only (qjl_m = 0)")
+    ap.add_argument("--layout", choices=["flat", "paged"], default="flat",
+                    help="flat: one contiguous cache per call (the default); paged: the same tokens in a "
+                         "block pool behind a shuffled block table, written with tq_append_* and read with "
+                         "tq_attend_decode_paged")
+    ap.add_argument("--block-size", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -66,9 +72,10 @@ def calib_copy(torch):
 
 
 class Layer:
-    """Inputs, formats and packed planes of one layer."""
+    """Inputs, formats and packed planes of one layer (flat, or a block pool
+    behind a seeded shuffled block table)."""
 
-    def __init__(self, w, layer, tq, W, torch):
+    def __init__(self, w, layer, tq, W, torch, paged_block=0):
         self.cb = tq.tq_build_codebook(w.d, w.k_bits)
         self.rot = tq.tq_make_rotation(w.rotation_seed(layer), w.d, w.rot)
         self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot, qjl_m=w.qjl_m)
@@ -76,12 +83,46 @@ class Layer:
         self.k = W.make_keys(w, layer, device="cuda")
         self.v = W.make_values(w, layer, device="cuda")
         self.q = W.make_queries(w, layer, device="cuda")
-        self.kc = tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T)
-        self.vc = tq.alloc_value_cache(self.vf, w.B, w.Hkv, w.T)
-        self.splits = tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, w.T)
-        n = tq.tq_attend_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, w.T, self.splits)
-        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+        self.lay = None
+        if paged_block:
+            import numpy as np
+            maxb = (w.T + paged_block - 1) // paged_block
+            perm = np.random.default_rng(w.seed * 7 + layer).permutation(w.B * maxb).astype(np.int32)
+            self.lay = tq.CacheLayout(maxb * paged_block, torch.full((w.B,), w.T, dtype=torch.int32, device="cuda"),
+                                      torch.from_numpy(perm.reshape(w.B, maxb)).cuda(), paged_block, w.B * maxb)
+            self.pos0 = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+            self.kc = tq.alloc_layout_key_cache(self.kf, self.lay, w.B, w.Hkv)
+            self.vc = tq.alloc_layout_value_cache(self.vf, self.lay, w.B, w.Hkv)
+            cap = self.lay.capacity
+        else:
+            self.kc = tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T)
+            self.vc = tq.alloc_value_cache(self.vf, w.B, w.Hkv, w.T)
+            cap = w.T
+        self.splits = tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, cap)
+        n = (tq.tq_attend_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, cap, self.splits) if self.lay is None
+             else tq.tq_attend_paged_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, self.lay, self.splits))
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def compress_keys(self, tq):
+        if self.lay is None:
+            tq.tq_compress_keys(self.kf, self.k, self.kc)
+        else:
+            tq.tq_append_keys(self.kf, self.k, self.lay, self.pos0, self.kc)
+
+    def compress_values(self, tq):
+        if self.lay is None:
+            tq.tq_compress_values(self.vf, self.v, self.vc)
+        else:
+            tq.tq_append_values(self.vf, self.v, self.lay, self.pos0, self.vc)
+
+    def decode(self, tq, w):
+        if self.lay is None:
+            tq.tq_attend_decode(self.kf, self.vf, self.q, self.kc, self.vc, w.Hkv, w.T, out=self.out, ws=self.ws,
+                                n_splits=self.splits)
+        else:
+            tq.tq_attend_decode_paged(self.kf, self.vf, self.q, self.kc, self.vc, w.Hkv, self.lay, out=self.out,
+                                      ws=self.ws, n_splits=self.splits)
 
 
 def measured_traffic(w):
@@ -179,7 +220,10 @@ def main():
         w = replace(w, name=w.name + "-first-stage", qjl=False)
     print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
           file=sys.stderr, flush=True)
-    layers = [Layer(w, l, tq, W, torch) for l in range(w.layers)]
+    paged = args.block_size if args.layout == "paged" else 0
+    if paged and (paged % 32 or paged < 32):
+        sys.exit("--block-size must be a positive multiple of 32")
+    layers = [Layer(w, l, tq, W, torch, paged) for l in range(w.layers)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -187,16 +231,15 @@ def main():
         if ev:
             ev[0].record(stream)
         for L in layers:
-            tq.tq_compress_keys(L.kf, L.k, L.kc)
+            L.compress_keys(tq)
         if ev:
             ev[1].record(stream)
         for L in layers:
-            tq.tq_compress_values(L.vf, L.v, L.vc)
+            L.compress_values(tq)
         if ev:
             ev[2].record(stream)
         for L in layers:
-            tq.tq_attend_decode(L.kf, L.vf, L.q, L.kc, L.vc, w.Hkv, w.T, out=L.out, ws=L.ws,
-                                n_splits=L.splits)
+            L.decode(tq, w)
         if ev:
             ev[3].record(stream)
 
@@ -256,7 +299,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and statistics of the workload, no model weights)",
-        "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "kv_heads": w.Hkv,
+        "config": {"workload": w.name + ("" if not paged else f"-paged{paged}"), "layers": w.layers,
+                   "batch": w.B, "kv_heads": w.Hkv,
                    "q_heads": w.Hq, "tokens": w.T, "head_dim": w.d, "input_dtype": w.dtype,
                    "k_bits": (f"{w.k_bits}+1 (Lloyd-Max + QJL sign)" if w.qjl
                               else f"{w.k_bits} (Lloyd-Max only, first-stage format)"), "rotation": w.rot,
@@ -278,6 +322,24 @@ def main():
                           "tq_attend_splitk": round(attn_avg_s * 1e6, 3),
                           "tq_merge_splits": round(mg_ms * 1e3 / max(mg_n, 1), 3) if mg_n else None},
     }
+    if paged:
+        # one decode step's append: one new token per sequence into every layer's pool
+        pos = torch.full((w.B,), w.T - 1, dtype=torch.int32, device="cuda")
+        ones = [(L.k[:, :, -1:].contiguous(), L.v[:, :, -1:].contiguous()) for L in layers]
+        torch.cuda.synchronize()
+        tq.tq_profile_enable(True)
+        tq.tq_profile_read("")
+        for _ in range(10):
+            for L, (k1, v1) in zip(layers, ones):
+                tq.tq_append_keys(L.kf, k1, L.lay, pos, L.kc)
+                tq.tq_append_values(L.vf, v1, L.lay, pos, L.vc)
+        torch.cuda.synchronize()
+        tq.tq_profile_enable(False)
+        ak_ms, ak_n = tq.tq_profile_read("tq_compress_keys")
+        av_ms, av_n = tq.tq_profile_read("tq_compress_values")
+        result["append_one_token_us"] = {"keys_per_layer": round(ak_ms * 1e3 / max(ak_n, 1), 3),
+                                         "values_per_layer": round(av_ms * 1e3 / max(av_n, 1), 3),
+                                         "tokens_per_call": w.B * w.Hkv}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -201,7 +201,7 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
                   (blk * Hkv + h) * block_size + t % block_size.
      capacity     tokens a sequence can hold (max_blocks * block_size when
                   paged).
-   block_size is a multiple of 32.  The kernels read seq_lens and block_table
+   block_size is a power of two, at least 32.  The kernels read seq_lens and block_table
    on the device: a length is clamped to [0, capacity], and a token whose
    block id is outside [0, num_blocks) is skipped (not read, not written), so
    no access leaves the planes whatever the tables hold. */
@@ -229,7 +229,9 @@ tq_status tq_append_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype,
 
 /* tq_attend_decode over a layout cache: sequence b attends its seq_lens[b]
    tokens (a sequence of length 0 gives zeros).  Split planning uses the
-   capacity; ws: at least tq_attend_paged_workspace_bytes() bytes. */
+   capacity, and raises n_splits where needed so that a split spans at most
+   511 blocks; ws: at least tq_attend_paged_workspace_bytes() bytes (same
+   n_splits). */
 size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv,
                                        const tq_cache_layout *lay, int n_splits);
 tq_status tq_attend_decode_paged(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q,
