@@ -221,8 +221,10 @@ def main():
     print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
           file=sys.stderr, flush=True)
     paged = args.block_size if args.layout == "paged" else 0
-    if paged and (paged % 32 or paged < 32):
-        sys.exit("--block-size must be a positive multiple of 32")
+    if paged and (paged < 32 or paged & (paged - 1)):
+        sys.exit("--block-size must be a power of two, at least 32")
+    if paged:
+        w = replace(w, name=f"{w.name}-paged{paged}")
     layers = [Layer(w, l, tq, W, torch, paged) for l in range(w.layers)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -299,8 +301,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and statistics of the workload, no model weights)",
-        "config": {"workload": w.name + ("" if not paged else f"-paged{paged}"), "layers": w.layers,
-                   "batch": w.B, "kv_heads": w.Hkv,
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "kv_heads": w.Hkv,
                    "q_heads": w.Hq, "tokens": w.T, "head_dim": w.d, "input_dtype": w.dtype,
                    "k_bits": (f"{w.k_bits}+1 (Lloyd-Max + QJL sign)" if w.qjl
                               else f"{w.k_bits} (Lloyd-Max only, first-stage format)"), "rotation": w.rot,
