@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
+SPIN_CYCLES = 40_000_000     # ~20 ms: covers the host enqueue time of the profiled steps
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,9 +261,19 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # per-kernel launch durations: a separate pass with libtq's per-launch events
-    tq.tq_profile_enable(True)
+    # per-kernel launch durations: a separate pass with libtq's per-launch events.
+    # The pass is queued behind one short spin kernel (torch.cuda._sleep), so
+    # that the host runs ahead of the GPU and each launch's event pair brackets
+    # the kernel rather than the host's launch latency (which matters for the
+    # microsecond kernels of the per-layer decode).
+    # One unrecorded step follows the spin, so that the recorded ones run at
+    # the clocks of a busy GPU.
+    spin = getattr(torch.cuda, "_sleep", None)
     tq.tq_profile_read("")
+    if spin is not None:
+        spin(SPIN_CYCLES)
+    step()
+    tq.tq_profile_enable(True)
     for _ in range(max(1, min(args.steps, 5))):
         step()
     torch.cuda.synchronize()
