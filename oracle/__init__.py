@@ -86,6 +86,11 @@ def _l():
                                _u8p, _u8p, _f32p, _f32p, i64, _f64p, vp, vp]
     lib.orc_dequant_keys.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _u8p, _u8p, _f32p, _f32p,
                                      i64, _f64p]
+    lib.orc_compress_keys_block.argtypes = [i32, i32, _f64p, _f64p, i64, _u8p, _u16p, vp, vp]
+    lib.orc_scores_block.argtypes = [i32, i32, _f64p, _f64p, i32, _u8p, _u16p, i64, _f64p]
+    lib.orc_dequant_keys_block.argtypes = [i32, i32, _f64p, _u8p, _u16p, i64, _f64p]
+    lib.orc_attend_block.argtypes = [i32, i32, _f64p, _f64p, i32, _u8p, _u16p, i64, i32, i32, _u8p, _u16p,
+                                     ctypes.c_double, _f64p]
     lib.orc_attend.argtypes = [i32, i32, i32, _f64p, _f64p, _f64p, _f64p, i32,
                                _u8p, _u8p, _f32p, _f32p, i64, i32, i32, _u8p, _u16p,
                                ctypes.c_double, _f64p]
@@ -328,6 +333,59 @@ def attend(q: np.ndarray, kc: KeyCache, bits: int, rot: Rotation, vc: ValueCache
                     np.ascontiguousarray(kc.knorm), np.ascontiguousarray(kc.rnorm), T,
                     vbits, group, np.ascontiguousarray(vc.codes), np.ascontiguousarray(vc.params),
                     float(scale), out)
+    return out
+
+
+# ------------------------------------------------- rotated block formats
+@dataclass
+class BlockKeyCache:
+    codes: np.ndarray    # [N, d*bits/8] u8: int8 codes (8 bits) or q + 8 nibbles (4 bits)
+    scales: np.ndarray   # [N, d/32] u16 fp16 bit patterns
+    x: np.ndarray | None = None      # [N, d] rotated key (fp64)
+    quot: np.ndarray | None = None   # [N, d] x / scale before rounding
+
+
+def compress_keys_block(k: np.ndarray, bits: int, pi: np.ndarray, keep_aux: bool = False) -> BlockKeyCache:
+    """Rotated Q8_0 (bits 8) / Q4_0 (bits 4) keys: x = pi @ k, 32-value blocks."""
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    n, d = k.shape
+    codes = np.zeros((n, d * bits // 8), np.uint8)
+    scales = np.zeros((n, d // 32), np.uint16)
+    x = np.zeros((n, d)) if keep_aux else None
+    quot = np.zeros((n, d)) if keep_aux else None
+    _l().orc_compress_keys_block(d, bits, np.ascontiguousarray(pi), k, n, codes, scales, _ptr(x), _ptr(quot))
+    return BlockKeyCache(codes, scales, x, quot)
+
+
+def scores_block(q: np.ndarray, kc: BlockKeyCache, bits: int, pi: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    nq, d = q.shape
+    T = kc.codes.shape[0]
+    out = np.zeros((nq, T))
+    _l().orc_scores_block(d, bits, np.ascontiguousarray(pi), q, nq, np.ascontiguousarray(kc.codes),
+                          np.ascontiguousarray(kc.scales), T, out)
+    return out
+
+
+def dequant_keys_block(kc: BlockKeyCache, bits: int, pi: np.ndarray) -> np.ndarray:
+    n = kc.codes.shape[0]
+    d = pi.shape[0]
+    out = np.zeros((n, d))
+    _l().orc_dequant_keys_block(d, bits, np.ascontiguousarray(pi), np.ascontiguousarray(kc.codes),
+                                np.ascontiguousarray(kc.scales), n, out)
+    return out
+
+
+def attend_block(q: np.ndarray, kc: BlockKeyCache, bits: int, pi: np.ndarray, vc: ValueCache,
+                 vbits: int, group: int, scale: float | None = None) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    nq, d = q.shape
+    T = kc.codes.shape[0]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out = np.zeros((nq, d))
+    _l().orc_attend_block(d, bits, np.ascontiguousarray(pi), q, nq, np.ascontiguousarray(kc.codes),
+                          np.ascontiguousarray(kc.scales), T, vbits, group, np.ascontiguousarray(vc.codes),
+                          np.ascontiguousarray(vc.params), float(scale), out)
     return out
 
 

@@ -678,7 +678,13 @@ void orc_dequant_keys(int d, int bits, int m, const double *pi, const double *s,
 /* Decode attention of nq query heads over one KV head's T packed tokens:   */
 /*   lambda_t = scale * score_t, p = softmax(lambda), out = sum_t p_t v_hat_t */
 /* with the max subtracted before exponentiation.  T = 0 gives zeros.        */
+/* orc_softmax_values takes the scores [nq][T] (overwritten) and does the    */
+/* rest; orc_attend and orc_attend_block differ only in the scores.          */
 /* ------------------------------------------------------------------------ */
+static void orc_softmax_values(int d, int nq, int64_t T, double *sc, int vbits, int group,
+                               const uint8_t *vcodes, const uint16_t *vparams, double scale,
+                               double *out);
+
 void orc_attend(int d, int bits, int m, const double *pi, const double *s,
                 const double *centroids, const double *q, int nq,
                 const uint8_t *codes, const uint8_t *signs, const float *knorm,
@@ -690,6 +696,14 @@ void orc_attend(int d, int bits, int m, const double *pi, const double *s,
     if (T <= 0) return;
     double *sc = (double *)malloc(sizeof(double) * nq * T);
     orc_scores(d, bits, m, pi, s, centroids, q, nq, codes, signs, knorm, rnorm, T, sc, NULL, NULL);
+    orc_softmax_values(d, nq, T, sc, vbits, group, vcodes, vparams, scale, out);
+    free(sc);
+}
+
+static void orc_softmax_values(int d, int nq, int64_t T, double *sc, int vbits, int group,
+                               const uint8_t *vcodes, const uint16_t *vparams, double scale,
+                               double *out)
+{
     int64_t vbytes = ((int64_t)d * vbits + 7) / 8;
     int ng = d / group;
     /* softmax weights per query head (max subtracted) */
@@ -718,5 +732,135 @@ void orc_attend(int d, int bits, int m, const double *pi, const double *s,
             for (int h = 0; h < nq; h++) out[(int64_t)h * d + j] += sc[(int64_t)h * T + t] * vh;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rotated scalar block formats, the comparison the tproger.ru article      */
+/* reports (section "First benchmarks": Q8_0 and Q4_0 with and without      */
+/* rotation).  The key is rotated, x = Pi k (no normalisation), and each    */
+/* block of 32 consecutive rotated coordinates keeps one fp16 scale and one */
+/* signed integer per coordinate:                                           */
+/*   scale = fp16_rne(amax / qmax), qmax = 127 (8 bits) or 7 (4 bits),      */
+/*   q_j = clamp(round_half_even(x_j / scale), -qmax, qmax), 0 if scale = 0,  */
+/* stored as an int8 byte (8 bits) or as q + 8 in 4 bits (LSB-first).       */
+/* x_hat_j = scale * q_j, and the score of q is sum_j (Pi q)_j x_hat_j =     */
+/* <q, Pi^T x_hat>.  x_out and quot_out (optional) receive x and x / scale    */
+/* for tie accounting.                                                      */
+/* ------------------------------------------------------------------------ */
+static int orc_block_qmax(int bits) { return bits == 8 ? 127 : 7; }
+
+void orc_compress_keys_block(int d, int bits, const double *pi, const double *k, int64_t n_vec,
+                             uint8_t *codes, uint16_t *scales, double *x_out, double *quot_out)
+{
+    const int qmax = orc_block_qmax(bits), nb = d / 32;
+    const int64_t code_bytes = (int64_t)d * bits / 8;
+    memset(codes, 0, (size_t)(code_bytes * n_vec));
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n_vec; t++) {
+            for (int i = 0; i < d; i++) {
+                double acc = 0.0;
+                for (int j = 0; j < d; j++) acc += pi[(size_t)i * d + j] * k[t * d + j];
+                x[i] = acc;
+                if (x_out) x_out[t * d + i] = acc;
+            }
+            for (int b = 0; b < nb; b++) {
+                double amax = 0.0;
+                for (int j = 0; j < 32; j++)
+                    if (fabs(x[32 * b + j]) > amax) amax = fabs(x[32 * b + j]);
+                uint16_t sh = orc_f64_to_f16(amax / qmax);
+                double sc = orc_f16_to_f64(sh);
+                scales[t * nb + b] = sh;
+                for (int j = 0; j < 32; j++) {
+                    int c = 32 * b + j;
+                    int qv = 0;
+                    double qt = 0.0;
+                    if (sc > 0.0) {
+                        qt = x[c] / sc;
+                        double r = nearbyint(qt);
+                        if (r > qmax) r = qmax;
+                        if (r < -qmax) r = -qmax;
+                        qv = (int)r;
+                    }
+                    if (quot_out) quot_out[t * d + c] = qt;
+                    if (bits == 8) codes[t * code_bytes + c] = (uint8_t)(int8_t)qv;
+                    else orc_put_bits(codes + t * code_bytes, c, 4, (unsigned)(qv + 8));
+                }
+            }
+        }
+        free(x);
+    }
+}
+
+/* x_hat of one packed block-format row */
+static void orc_block_row(int d, int bits, const uint8_t *row, const uint16_t *sc, double *xh)
+{
+    for (int c = 0; c < d; c++) {
+        int qv = bits == 8 ? (int)(int8_t)row[c] : (int)orc_get_bits(row, c, 4) - 8;
+        xh[c] = orc_f16_to_f64(sc[c / 32]) * qv;
+    }
+}
+
+void orc_scores_block(int d, int bits, const double *pi, const double *q, int nq,
+                      const uint8_t *codes, const uint16_t *scales, int64_t T, double *scores)
+{
+    const int64_t code_bytes = (int64_t)d * bits / 8;
+    double *qrot = (double *)malloc(sizeof(double) * d * nq);
+    for (int h = 0; h < nq; h++)
+        for (int i = 0; i < d; i++) {
+            double acc = 0.0;
+            for (int j = 0; j < d; j++) acc += pi[(size_t)i * d + j] * q[h * d + j];
+            qrot[h * d + i] = acc;
+        }
+#pragma omp parallel
+    {
+        double *xh = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; t++) {
+            orc_block_row(d, bits, codes + t * code_bytes, scales + t * (d / 32), xh);
+            for (int h = 0; h < nq; h++) {
+                double a = 0.0;
+                for (int c = 0; c < d; c++) a += qrot[h * d + c] * xh[c];
+                scores[(int64_t)h * T + t] = a;
+            }
+        }
+        free(xh);
+    }
+    free(qrot);
+}
+
+/* k_hat = Pi^T x_hat */
+void orc_dequant_keys_block(int d, int bits, const double *pi, const uint8_t *codes,
+                            const uint16_t *scales, int64_t n_vec, double *out)
+{
+    const int64_t code_bytes = (int64_t)d * bits / 8;
+#pragma omp parallel
+    {
+        double *xh = (double *)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n_vec; t++) {
+            orc_block_row(d, bits, codes + t * code_bytes, scales + t * (d / 32), xh);
+            for (int c = 0; c < d; c++) {
+                double acc = 0.0;
+                for (int j = 0; j < d; j++) acc += pi[(size_t)j * d + c] * xh[j];
+                out[t * d + c] = acc;
+            }
+        }
+        free(xh);
+    }
+}
+
+void orc_attend_block(int d, int bits, const double *pi, const double *q, int nq,
+                      const uint8_t *codes, const uint16_t *scales, int64_t T,
+                      int vbits, int group, const uint8_t *vcodes, const uint16_t *vparams,
+                      double scale, double *out)
+{
+    memset(out, 0, sizeof(double) * d * nq);
+    if (T <= 0) return;
+    double *sc = (double *)malloc(sizeof(double) * nq * T);
+    orc_scores_block(d, bits, pi, q, nq, codes, scales, T, sc);
+    orc_softmax_values(d, nq, T, sc, vbits, group, vcodes, vparams, scale, out);
     free(sc);
 }
