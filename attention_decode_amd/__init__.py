@@ -25,6 +25,8 @@ __all__ = [
     "tq_profile_enable", "tq_profile_read", "TQError", "tq_dequantize_keys",
     "CacheLayout", "alloc_layout_key_cache", "alloc_layout_value_cache", "tq_append_keys", "tq_append_values",
     "tq_attend_paged_workspace_bytes", "tq_attend_decode_paged",
+    "BlockFormat", "BlockCache", "alloc_block_cache", "tq_compress_keys_block", "tq_attend_decode_block",
+    "tq_attend_block_workspace_bytes",
 ]
 
 _ROT_KIND = {"dense": TQ_ROT_DENSE, "hadamard": TQ_ROT_HADAMARD}
@@ -332,6 +334,62 @@ def tq_attend_decode_paged(kfmt: KeyFormat, vfmt: ValueFormat, q, kc: KeyCache, 
                                        Hkv, ctypes.byref(lay), kc.c(), vc.c(), softmax_scale, n_splits,
                                        ws.data_ptr(), ws.numel(), out.data_ptr(), _stream(stream)),
           "tq_attend_decode_paged")
+    return out
+
+
+# ------------------------------------------------- rotated block key formats
+@dataclass
+class BlockFormat:
+    """Rotated 8-bit or 4-bit block key format (tq_block_fmt)."""
+    d: int
+    bits: int
+    rot: Rotation
+
+    def c(self) -> L.BlockFmt:
+        return L.BlockFmt(self.d, self.bits, self.rot.handle)
+
+
+@dataclass
+class BlockCache:
+    codes: "torch.Tensor"   # noqa: F821  [B, H, T, d*bits/8] uint8
+    scales: "torch.Tensor"  # noqa: F821  [B, H, T, d/32] int16 (fp16 bit patterns)
+
+    def c(self) -> L.BCache:
+        return L.BCache(self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def alloc_block_cache(fmt: BlockFormat, B: int, H: int, T: int, device="cuda") -> BlockCache:
+    import torch
+    return BlockCache(torch.empty((B, H, T, fmt.d * fmt.bits // 8), dtype=torch.uint8, device=device),
+                      torch.empty((B, H, T, fmt.d // 32), dtype=torch.int16, device=device))
+
+
+def tq_compress_keys_block(fmt: BlockFormat, k, out: BlockCache, stream=None) -> None:
+    B, H, T, sb, sh, st = _bhtd(k)
+    bf = fmt.c()
+    check(lib().tq_compress_keys_block(ctypes.byref(bf), k.data_ptr(), _dtype_code(k), B, H, T, sb, sh, st,
+                                       out.c(), _stream(stream)), "tq_compress_keys_block")
+
+
+def tq_attend_block_workspace_bytes(fmt: BlockFormat, B: int, Hq: int, Hkv: int, T: int, n_splits: int = 0) -> int:
+    bf = fmt.c()
+    return int(lib().tq_attend_block_workspace_bytes(ctypes.byref(bf), B, Hq, Hkv, T, n_splits))
+
+
+def tq_attend_decode_block(kfmt: BlockFormat, vfmt: ValueFormat, q, kc: BlockCache, vc: ValueCache, Hkv: int,
+                           T: int, out=None, ws=None, n_splits: int = 0, softmax_scale: float = 0.0, stream=None):
+    """q [B, Hq, d] contiguous over block-format keys -> [B, Hq, d] fp32."""
+    import torch
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        need = tq_attend_block_workspace_bytes(kfmt, B, Hq, Hkv, T, n_splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    bf, vf = kfmt.c(), vfmt.c()
+    check(lib().tq_attend_decode_block(ctypes.byref(bf), ctypes.byref(vf), q.data_ptr(), _dtype_code(q), B, Hq,
+                                       Hkv, T, kc.c(), vc.c(), softmax_scale, n_splits, ws.data_ptr(), ws.numel(),
+                                       out.data_ptr(), _stream(stream)), "tq_attend_decode_block")
     return out
 
 

@@ -36,6 +36,14 @@ class VCache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
 
 
+class BlockFmt(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("bits", ctypes.c_int), ("rot", ctypes.c_void_p)]
+
+
+class BCache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
 class CacheLayout(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int64), ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("block_size", ctypes.c_int), ("max_blocks", ctypes.c_int), ("num_blocks", ctypes.c_int64)]
@@ -71,6 +79,11 @@ SIGNATURES = {
     "tq_attend_paged_workspace_bytes": (_sz, [_c.POINTER(KeyFmt), _i, _i, _i, _c.POINTER(CacheLayout), _i]),
     "tq_attend_decode_paged": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i,
                                     _c.POINTER(CacheLayout), KCache, VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
+    "tq_block_plane_bytes": (_sz, [_c.POINTER(BlockFmt), _i64, _i]),
+    "tq_compress_keys_block": (_i, [_c.POINTER(BlockFmt), _vp, _i, _i, _i, _i64, _i64, _i64, _i64, BCache, _vp]),
+    "tq_attend_block_workspace_bytes": (_sz, [_c.POINTER(BlockFmt), _i, _i, _i, _i64, _i]),
+    "tq_attend_decode_block": (_i, [_c.POINTER(BlockFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64, BCache,
+                                    VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
     "tq_last_error": (_c.c_char_p, []),
     "tq_profile_enable": (_i, [_i]),
     "tq_profile_read": (_i, [_c.c_char_p, _dp, _c.POINTER(_i64)]),

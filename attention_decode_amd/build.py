@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["api.cpp", "host_math.cpp", "k_keys.hip", "k_values.hip", "k_decode.hip", "k_attend_mfma.hip",
-           "k_dequant.hip"]
+           "k_dequant.hip", "k_block.hip"]
 ARCH = "gfx950"
 
 

@@ -361,6 +361,19 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
         delete rot;
         return hip_fail(e, "tq_make_rotation: fragment upload");
     }
+    // fp64 Pi^T for the block-format compressor
+    std::vector<double> pi64T(dd);
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) pi64T[static_cast<size_t>(j) * d + i] = pi[static_cast<size_t>(i) * d + j];
+    e = hipMalloc(&rot->d_pi64T, sizeof(double) * dd);
+    if (e == hipSuccess) e = hipMemcpy(rot->d_pi64T, pi64T.data(), sizeof(double) * dd, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (rot->d_pi64T) hipFree(rot->d_pi64T);
+        hipFree(rot->d_frag_block);
+        hipFree(rot->d_block);
+        delete rot;
+        return hip_fail(e, "tq_make_rotation: fp64 upload");
+    }
     rot->d_pifrag = static_cast<uint16_t *>(rot->d_frag_block);
     rot->d_sfrag = rot->d_pifrag + static_cast<size_t>(rt_n) * ks_n * 3 * 512;
     float *base = static_cast<float *>(rot->d_block);
@@ -382,6 +395,7 @@ void tq_rotation_free(tq_rotation *rot)
     if (!rot) return;
     if (rot->d_block) hipFree(rot->d_block);
     if (rot->d_frag_block) hipFree(rot->d_frag_block);
+    if (rot->d_pi64T) hipFree(rot->d_pi64T);
     delete rot;
 }
 
@@ -526,14 +540,14 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
 }
 
 struct AttendLayout {
-    size_t qprep, aops, qscal, ml, acc, total;
+    size_t qprep, aops, qscal, qaux, ml, acc, total;
 };
 
-AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePlan &p)
+// d channels, m QJL rows (0 for the block formats)
+AttendLayout attend_layout(int d, int m, int B, int Hq, const DecodePlan &p)
 {
     AttendLayout L;
     const size_t rows = static_cast<size_t>(B) * Hq;
-    const int d = fmt->d, m = fmt->qjl_m;
     size_t off = 0;
     L.qprep = off;
     off += align256(rows * (d + m) * sizeof(float));
@@ -541,6 +555,8 @@ AttendLayout attend_layout(const tq_key_fmt *fmt, int B, int Hq, const DecodePla
     off += align256(static_cast<size_t>(p.units) * p.mt * p.steps * 64 * 16);
     L.qscal = off;
     off += align256(rows * 4 * sizeof(float));
+    L.qaux = off;
+    off += align256(rows * (d / 32) * sizeof(float));
     L.ml = off;
     off += align256(rows * p.splits * 2 * sizeof(float));
     L.acc = off;
@@ -738,6 +754,160 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
 
+}  // extern "C"
+
+namespace {
+
+tq_status check_block_fmt(const tq_block_fmt *f, const char *who)
+{
+    if (!f) return fail(TQ_EINVAL, "%s: NULL block format", who);
+    if (!f->rot) return fail(TQ_EINVAL, "%s: block format without rotation", who);
+    if (f->d != 128 && f->d != 256) return fail(TQ_EUNSUPPORTED, "%s: d=%d not in {128, 256}", who, f->d);
+    if (f->bits != 8 && f->bits != 4) return fail(TQ_EUNSUPPORTED, "%s: bits=%d not in {4, 8}", who, f->bits);
+    if (f->rot->d != f->d) return fail(TQ_EINVAL, "%s: rotation is for d=%d, format wants %d", who, f->rot->d, f->d);
+    return TQ_OK;
+}
+
+tq_status check_bcache(const tq_bcache &c, const char *who)
+{
+    if (!c.codes || !c.scales) return fail(TQ_EINVAL, "%s: NULL block plane", who);
+    if (!aligned16(c.codes) || !aligned16(c.scales)) return fail(TQ_EALIGN, "%s: block planes must be 16-byte aligned", who);
+    return TQ_OK;
+}
+
+DecodePlan block_plan(int d, int B, int Hq, int Hkv, int64_t T, int n_splits)
+{
+    DecodePlan p;
+    const int G = Hq / Hkv;
+    p.mfma = true;
+    p.gc = tq::mfma_query_chunk(G);
+    p.nqc = G / p.gc;
+    p.mt = (p.gc + 3) / 4;
+    p.units = B * Hkv * p.nqc;
+    p.steps = d / 64;                      // 16-byte operand slots per row tile (two blocks each)
+    const int64_t tiles = (T + tq::kMfmaTile - 1) / tq::kMfmaTile;
+    const int64_t target = d >= 256 ? 512 : 2048;
+    int64_t want = (target + p.units - 1) / p.units;
+    if (want > tiles) want = tiles;
+    if (want > 1024) want = 1024;
+    p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_block_plane_bytes(const tq_block_fmt *fmt, int64_t n_vec, int plane)
+{
+    if (!fmt || n_vec < 0 || fmt->d <= 0 || fmt->d % 32 || (fmt->bits != 8 && fmt->bits != 4)) return 0;
+    const size_t n = static_cast<size_t>(n_vec);
+    switch (plane) {
+    case 0: return n * (static_cast<size_t>(fmt->d) * fmt->bits / 8);
+    case 1: return n * (static_cast<size_t>(fmt->d) / 32) * sizeof(uint16_t);
+    }
+    return 0;
+}
+
+tq_status tq_compress_keys_block(const tq_block_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv, int64_t T,
+                                 int64_t sb, int64_t sh, int64_t st, tq_bcache out, void *stream)
+{
+    const char *who = "tq_compress_keys_block";
+    TQ_TRY(check_block_fmt(fmt, who));
+    TQ_TRY(check_dtype(dtype, who));
+    TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
+    if (T == 0) return TQ_OK;
+    TQ_TRY(check_bcache(out, who));
+    tq::BlockLaunch a{};
+    a.k = k;
+    a.dtype = dtype;
+    a.B = B;
+    a.H = Hkv;
+    a.T = T;
+    a.sb = sb;
+    a.sh = sh;
+    a.st = st;
+    a.d = fmt->d;
+    a.bits = fmt->bits;
+    a.pi64T = fmt->rot->d_pi64T;
+    a.out = out;
+    const hipError_t e = tq::launch_compress_keys_block(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
+size_t tq_attend_block_workspace_bytes(const tq_block_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits)
+{
+    if (!fmt || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < 0) return 0;
+    return attend_layout(fmt->d, 0, B, Hq, block_plan(fmt->d, B, Hq, Hkv, T, n_splits)).total;
+}
+
+tq_status tq_attend_decode_block(const tq_block_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
+                                 int B, int Hq, int Hkv, int64_t T, tq_bcache kc, tq_vcache vc, float softmax_scale,
+                                 int n_splits, void *ws, size_t ws_bytes, float *out, void *stream)
+{
+    const char *who = "tq_attend_decode_block";
+    TQ_TRY(check_block_fmt(kfmt, who));
+    TQ_TRY(check_dtype(dtype, who));
+    TQ_TRY(check_val_fmt(vfmt, who));
+    if (B < 1 || Hq < 1 || Hkv < 1 || T < 0) return fail(TQ_EINVAL, "%s: bad shape", who);
+    if (Hq % Hkv) return fail(TQ_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
+    if (static_cast<int64_t>(B) * Hkv * T > (int64_t(1) << 40)) return fail(TQ_EINVAL, "%s: too many keys", who);
+    if (vfmt->d != kfmt->d) return fail(TQ_EINVAL, "%s: key d=%d and value d=%d differ", who, kfmt->d, vfmt->d);
+    if (!q || !out) return fail(TQ_EINVAL, "%s: NULL query or output", who);
+    if (!aligned16(q) || !aligned16(out)) return fail(TQ_EALIGN, "%s: query and output must be 16-byte aligned", who);
+    if (n_splits < 0 || n_splits > 65535) return fail(TQ_EINVAL, "%s: n_splits=%d outside [0, 65535]", who, n_splits);
+    if (!(softmax_scale >= 0.0f) || !std::isfinite(softmax_scale))
+        return fail(TQ_EINVAL, "%s: softmax_scale must be finite and >= 0", who);
+    tq::DecodeLaunch a{};
+    a.q = q;
+    a.dtype = dtype;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.d = kfmt->d;
+    a.bits = kfmt->bits;
+    a.m = 0;
+    a.out = out;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        const hipError_t e = tq::launch_attend(a, s);
+        return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+    }
+    TQ_TRY(check_bcache(kc, who));
+    TQ_TRY(check_vcache(vc, who));
+    if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
+    if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
+    const DecodePlan plan = block_plan(kfmt->d, B, Hq, Hkv, T, n_splits);
+    const AttendLayout L = attend_layout(kfmt->d, 0, B, Hq, plan);
+    if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
+    a.piT = kfmt->rot->d_piT;
+    a.spiT = kfmt->rot->d_spiT;
+    a.pisum = kfmt->rot->d_pisum;
+    a.spisum = kfmt->rot->d_spisum;
+    a.sq_bound = kfmt->rot->sq_bound;
+    a.kfmt_block = true;
+    a.kq = kc;
+    a.vbits = vfmt->bits;
+    a.group = vfmt->group;
+    a.vc = vc;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : static_cast<float>(1.0 / std::sqrt(double(kfmt->d)));
+    a.splits = plan.splits;
+    char *base = static_cast<char *>(ws);
+    a.qprep = reinterpret_cast<float *>(base + L.qprep);
+    a.part_ml = reinterpret_cast<float *>(base + L.ml);
+    a.part_acc = reinterpret_cast<float *>(base + L.acc);
+    a.mf.gc = plan.gc;
+    a.mf.nqc = plan.nqc;
+    a.mf.mt = plan.mt;
+    a.mf.units = plan.units;
+    a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
+    a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
+    a.qaux = reinterpret_cast<float *>(base + L.qaux);
+    const hipError_t e = tq::launch_decode_block(a, s);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+}
+
 tq_status tq_dequantize_keys(const tq_key_fmt *fmt, int B, int Hkv, int64_t T, tq_kcache kc, float *out,
                              void *stream)
 {
@@ -777,7 +947,7 @@ size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, 
 {
     if (!fmt || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < 0) return 0;
     const DecodePlan p = decode_plan(fmt, B, Hq, Hkv, T, n_splits);
-    return attend_layout(fmt, B, Hq, p).total;
+    return attend_layout(fmt->d, fmt->qjl_m, B, Hq, p).total;
 }
 
 size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, const tq_cache_layout *lay,
@@ -785,7 +955,7 @@ size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int
 {
     if (!fmt || !lay || lay->capacity < 1 || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return 0;
     const DecodePlan p = decode_plan(fmt, B, Hq, Hkv, lay->capacity, n_splits, lay->block_table ? lay->block_size : 0);
-    return attend_layout(fmt, B, Hq, p).total;
+    return attend_layout(fmt->d, fmt->qjl_m, B, Hq, p).total;
 }
 
 // decode attention over T tokens per sequence (flat map) or over a layout
@@ -824,7 +994,7 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
     const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits,
                                         map.mode == tq::CacheMap::kPaged ? map.bs : 0);
-    const AttendLayout L = attend_layout(kfmt, B, Hq, plan);
+    const AttendLayout L = attend_layout(kfmt->d, kfmt->qjl_m, B, Hq, plan);
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;
     a.sT = kfmt->rot->d_sT;
@@ -849,6 +1019,7 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     a.mf.units = plan.units;
     a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
+    a.qaux = reinterpret_cast<float *>(base + L.qaux);
     a.map = map;
     hipError_t e;
     if (plan.mfma) {

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
     __shared__ float s_acoef[2];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int unit = blockIdx.x, part = blockIdx.y / 4, kb = blockIdx.y % 4;
-    const bool bitplane = a.bits <= 2;
+    const bool bitplane = a.bits <= 2 && !a.kfmt_block;
     const int64_t row0 = unit_row0(a, unit);
     // this thread's rows of the matrix column: issued before the query load,
     // which they do not depend on
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
             const float qn = sqrtf(s2) * (1.0f + 0x1p-16f);      // >= max_j |q_rot_j|, rounding included
             const float mc = bitplane ? qn * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1])) : qn;
             const float ms = qn * a.sq_bound;
-            const int top = bitplane ? 26 : 10;                   // |scaled value| < 2^top
+            const int top = (bitplane || a.kfmt_block) ? 26 : 10; // |scaled value| < 2^top
             int ec = 0, es = 0;
             frexpf(mc, &ec);
             frexpf(ms, &es);
@@ -188,7 +188,10 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
             s_f[g][1] = fs;
             if (head) {
                 float *sc4 = a.mf.qscal + (row0 + g) * 4;
-                if (bitplane) {
+                if (a.kfmt_block) {
+                    sc4[0] = ldexpf(1.0f, -fc);
+                    sc4[1] = sc4[2] = sc4[3] = 0.0f;
+                } else if (bitplane) {
                     sc4[0] = ldexpf(1.0f, -fc);
                     sc4[1] = a.centroids[0] * sc;
                     sc4[2] = ldexpf(1.0f, -fs);
@@ -211,7 +214,40 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
         xv[g][c] = x;
     }
     __syncthreads();
-    if (bitplane) {
+    if (a.kfmt_block) {
+        // Block key formats: int8 digit rows of the 16x16x32 int8 product, one
+        // 8-byte A slot per (row tile, block, lane) in aops[unit][MT][D/32][64];
+        // lane (row 4 q + digit, k-block kk) holds coordinates 32 b + 8 kk + o(e)
+        // of query 4 mt + q, with o(e) = e for 8-bit codes and the nibble order
+        // {0, 2, 4, 6, 1, 3, 5, 7} (low nibbles, then high ones) for 4-bit codes.
+        // With 4-bit codes stored as q + 8, qaux[row][b] = 8 sum_b x (in the
+        // units of the integer block sums) removes the offset.
+        constexpr int NB = D / 32, NBQ = CB / 32;
+        const int MT = a.mf.mt;
+        uint64_t *out = reinterpret_cast<uint64_t *>(a.mf.aops) + static_cast<int64_t>(unit) * MT * NB * 64;
+        for (int w = tid; w < MT * NBQ * 64; w += kThreads) {
+            const int ln = w % 64, bq = (w / 64) % NBQ, mt = w / (64 * NBQ);
+            const int row = ln % 16, kk = ln / 16, g = 4 * mt + row / 4, digit = row % 4;
+            uint64_t v = 0;
+            if (g < GQ) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int o = a.bits == 8 ? e : (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+                    int x = static_cast<int>(rintf(ldexpf(xv[g][32 * bq + 8 * kk + o], s_f[g][0])));
+                    for (int r = 0; r < digit; ++r) x = (x - (((x + 64) & 127) - 64)) >> 7;
+                    const int dg = digit < 3 ? ((x + 64) & 127) - 64 : x;
+                    v |= static_cast<uint64_t>(static_cast<uint32_t>(dg) & 0xffu) << (8 * e);
+                }
+            }
+            out[(mt * NB + kb * NBQ + bq) * 64 + ln] = v;
+        }
+        for (int w = tid; w < GQ * NBQ; w += kThreads) {
+            const int g = w / NBQ, bq = w % NBQ;
+            double sum = 0.0;
+            for (int e = 0; e < 32; ++e) sum += rintf(ldexpf(xv[g][32 * bq + e], s_f[g][0]));
+            a.qaux[(row0 + g) * NB + kb * NBQ + bq] = a.bits == 4 ? static_cast<float>(8.0 * sum) : 0.0f;
+        }
+    } else if (bitplane) {
         // int8 digit rows: query g uses lanes 16 kb + 4 (g % 4) + digit of row
         // tile g / 4; dword r of a lane holds elements 4r..4r+3 of its k-block.
         // Code step s = 2u + h reads word u of the quarter (bit 32 u + 8 K + 4 h + r,
@@ -333,20 +369,34 @@ __device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off)
 // Key words of the two keys (columns j and 16 + j of a wave tile) that lane
 // (j, kb) reads: the kb-th quarter of the code row and of the sign row.  The
 // first-stage format (QJL false) has no sign row and no residual norm.
+// Loads go through wave-uniform plane bases of the tile (scalar registers)
+// plus 32-bit lane offsets.
 template <int BITS, int D, bool QJL>
 struct KeyWords {
     static constexpr int NC = D * BITS / 128, NS = QJL ? D / 128 : 0;
     uint32_t cw[2][NC], sw[2][NS > 0 ? NS : 1];
     float nrm[2], rho[2];
-    __device__ void load(const uint32_t *crow, const uint32_t *srow, const float *np, const float *rp, int c)
+    struct Bases {
+        const uint32_t *c, *s;
+        const float *n, *r;
+    };
+    __device__ static Bases bases(const DecodeLaunch &a, int64_t n0)
     {
+        return {reinterpret_cast<const uint32_t *>(a.kc.codes) + n0 * (D * BITS / 32),
+                reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32), a.kc.knorm + n0, a.kc.rnorm + n0};
+    }
+    // key t of the tile (column c of this lane: key j or 16 + j), k-block kb
+    __device__ void load(const Bases &b, uint32_t t, int kb, int c)
+    {
+        const uint32_t *crow = at_bytes(b.c, 4u * (t * (D * BITS / 32) + kb * NC));
 #pragma unroll
         for (int u = 0; u < NC; ++u) cw[c][u] = crow[u];
-        nrm[c] = *np;
+        nrm[c] = *at_bytes(b.n, 4u * t);
         if constexpr (QJL) {
+            const uint32_t *srow = at_bytes(b.s, 4u * (t * (D / 32) + kb * NS));
 #pragma unroll
             for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
-            rho[c] = *rp;
+            rho[c] = *at_bytes(b.r, 4u * t);
         } else {
             rho[c] = 0.0f;
         }
@@ -614,6 +664,118 @@ struct ScoreLut {
 // before the current one is computed (two register buffers in turn).  The
 // four waves are merged in LDS at the end; with one split the workgroup
 // writes the normalised output, else its partial (max, sum, weighted values).
+// Rotated block key formats (8-bit or 4-bit codes, one fp16 scale per 32
+// rotated coordinates).  Lane (j, kb) holds, for each block, the 8 codes at
+// coordinates 32 b + 8 kb .. + 7 of keys j and 16 + j (two dwords of bytes,
+// or one dword of nibbles) and the keys' block scales.
+template <int QB, int D>
+struct KeyWordsQ {
+    static constexpr int NB = D / 32;
+    static constexpr int WB = QB == 8 ? 2 : 1;     // code dwords per block and lane
+    static constexpr int PB = QB;                  // code dwords per block (32 codes)
+    static constexpr int ROWW = D * QB / 32;       // code dwords per key
+    static constexpr int SW = D / 64;              // scale dwords per key (fp16 pairs)
+    static constexpr int NC = 0, NS = 0;
+    uint32_t cw[2][NB * WB];
+    uint32_t sc[2][SW];
+    struct Bases {
+        const uint32_t *c, *s;
+    };
+    __device__ static Bases bases(const DecodeLaunch &a, int64_t n0)
+    {
+        return {reinterpret_cast<const uint32_t *>(a.kq.codes) + n0 * ROWW,
+                reinterpret_cast<const uint32_t *>(a.kq.scales) + n0 * SW};
+    }
+    __device__ void load(const Bases &b, uint32_t t, int kb, int c)
+    {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+            for (int w = 0; w < WB; ++w) cw[c][blk * WB + w] = *at_bytes(b.c, 4u * (t * ROWW + blk * PB + kb * WB + w));
+#pragma unroll
+        for (int w = 0; w < SW; ++w) sc[c][w] = *at_bytes(b.s, 4u * (t * SW + w));
+    }
+};
+
+// Block-format scores: per block one v_mfma_i32_16x16x32_i8 with rows
+// (query, digit) as in the bit-plane scores (the query as four balanced 7-bit
+// digits of a fixed-point value) and the raw codes as B: 8-bit codes as they
+// are, 4-bit codes as their low and high nibbles (q + 8, the offset removed
+// with a per-query block constant).  Each block's exact integer sum is scaled
+// by the key's block scale.
+template <int QB, int D, int MT>
+struct ScoreQ {
+    using KW = KeyWordsQ<QB, D>;
+    static constexpr int NQ = MT;
+    static constexpr int TAB_BYTES = 0;
+    static constexpr int NB = D / 32;
+    int64_t aop[MT][NB];
+    float fq[MT];              // 2^-f * softmax scale * log2(e)
+    float kq[MT][NB];          // 4-bit codes: 8 sum_block x (integer units of the block sums)
+
+    __device__ static int query(int slot, int kb) { return 4 * slot + kb; }
+
+    __device__ static float for_query(const float (&v)[MT], int q, int j)
+    {
+        float r = 1.0f;
+#pragma unroll
+        for (int s = 0; s < MT; ++s) {
+            const float t = __shfl(v[s], 16 * (q % 4) + j);
+            if (q / 4 == s) r = t;
+        }
+        return r;
+    }
+
+    __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, float, unsigned char *)
+    {
+        const int64_t *src = reinterpret_cast<const int64_t *>(a.mf.aops) + static_cast<int64_t>(unit) * MT * NB * 64;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) aop[mt][b] = src[(mt * NB + b) * 64 + lane];
+        const float f = a.scale * kLog2e;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int g = 4 * mt + kb;
+            const bool ok = g < GC;
+            const int64_t r = row0 + (ok ? g : 0);
+            fq[mt] = ok ? a.mf.qscal[r * 4] * f : 0.0f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) kq[mt][b] = (ok && QB == 4) ? a.qaux[r * NB + b] : 0.0f;
+        }
+    }
+
+    __device__ void scores(const KW &kw, float (&sc)[2][MT]) const
+    {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float s[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) s[mt] = 0.0f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                int64_t bop;
+                if constexpr (QB == 8) {
+                    bop = static_cast<int64_t>(kw.cw[c][2 * b]) | (static_cast<int64_t>(kw.cw[c][2 * b + 1]) << 32);
+                } else {
+                    const uint32_t x = kw.cw[c][b];
+                    bop = static_cast<int64_t>(x & 0x0F0F0F0Fu) | (static_cast<int64_t>((x >> 4) & 0x0F0F0F0Fu) << 32);
+                }
+                const float scl = f16_bits_to_f32((kw.sc[c][b / 2] >> (16 * (b % 2))) & 0xffffu);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[mt][b], bop, v4i{0, 0, 0, 0}, 0, 0, 0);
+                    float val = limbs_to_float(acc);
+                    if constexpr (QB == 4) val -= kq[mt][b];
+                    s[mt] = fmaf(scl, val, s[mt]);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) sc[c][mt] = s[mt] * fq[mt];
+        }
+    }
+};
+
 template <class SCORE, int BITS, int D, int VBITS, bool TWO>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 : 2)) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
@@ -743,17 +905,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
         const int64_t n0 = blk >= 0 ? (static_cast<int64_t>(blk) * a.Hkv + kvh) * rstride
                                           + (static_cast<uint32_t>(tc) & rmask) : 0;
         pf.nvalid = blk >= 0 ? nv : 0;
-        const uint32_t *cbase = reinterpret_cast<const uint32_t *>(a.kc.codes) + n0 * (D * BITS / 32);
-        const uint32_t *sbase = reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32);
-        const float *nbase = a.kc.knorm + n0, *rbase = a.kc.rnorm + n0;
-        // lane offsets are 32-bit unsigned so that the loads take the uniform base
-        // from scalar registers
+        const auto kbase = SCORE::KW::bases(a, n0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const uint32_t t = static_cast<uint32_t>(16 * c + j < nv ? 16 * c + j : nv - 1);
-            pf.kw.load(at_bytes(cbase, 4u * (t * (D * BITS / 32) + kb * SCORE::KW::NC)),
-                       at_bytes(sbase, 4u * (t * (D / 32) + kb * SCORE::KW::NS)),
-                       at_bytes(nbase, 4u * t), at_bytes(rbase, 4u * t), c);
+            pf.kw.load(kbase, t, kb, c);
         }
         const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
@@ -1134,7 +1290,7 @@ template <typename TIn, int D>
 void launch_qprep_d(const DecodeLaunch &a, hipStream_t stream)
 {
     // (part, quarter): q_rot and, with QJL rows, Sq
-    const dim3 grid(static_cast<unsigned>(a.mf.units), a.m > 0 ? 8 : 4);
+    const dim3 grid(static_cast<unsigned>(a.mf.units), (a.m > 0 && !a.kfmt_block) ? 8 : 4);
     switch (a.mf.gc) {
     case 1: hipLaunchKernelGGL((k_qprep<TIn, D, 1>), grid, dim3(kThreads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((k_qprep<TIn, D, 2>), grid, dim3(kThreads), 0, stream, a); break;
@@ -1171,6 +1327,31 @@ int mfma_row_tiles(int bits, int gc) { return bits <= 2 ? (gc + 3) / 4 : 1; }
 int mfma_score_steps(int d, int bits, int m)
 {
     return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0) : 2 * (d / 32);
+}
+
+template <int QB, int D>
+hipError_t launch_attend_q(const DecodeLaunch &a, hipStream_t s, int64_t chunk)
+{
+    return a.mf.mt == 1 ? launch_attend_v<ScoreQ<QB, D, 1>, QB, D>(a, s, 0.0f, chunk)
+                        : launch_attend_v<ScoreQ<QB, D, 2>, QB, D>(a, s, 0.0f, chunk);
+}
+
+hipError_t launch_decode_block(const DecodeLaunch &a, hipStream_t stream)
+{
+    void *tok;
+    prof_begin("tq_qprep", stream, &tok);
+    switch (a.dtype) {
+    case TQ_F32: launch_qprep_t<float>(a, stream); break;
+    case TQ_BF16: launch_qprep_t<bf16_t>(a, stream); break;
+    case TQ_F16: launch_qprep_t<f16_t>(a, stream); break;
+    }
+    prof_end(tok, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
+    const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kMfmaTile;
+    if (a.bits == 8) return a.d == 128 ? launch_attend_q<8, 128>(a, stream, chunk) : launch_attend_q<8, 256>(a, stream, chunk);
+    return a.d == 128 ? launch_attend_q<4, 128>(a, stream, chunk) : launch_attend_q<4, 256>(a, stream, chunk);
 }
 
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)

@@ -35,6 +35,7 @@ struct tq_rotation {
     float *d_pisum = nullptr;   // [d]     column sums of Pi: sum_j (Pi q)_j = pisum . q
     float *d_spisum = nullptr;  // [d]     column sums of S Pi
     float sq_bound = 0.0f;      // max row norm of S Pi (rounded up): |(S Pi q)_i| <= sq_bound |q|
+    double *d_pi64T = nullptr;  // [d][d]  fp64 transpose of Pi (block-format compressor)
     // bf16 operand fragments of the matrix-core key compressor, in lane order
     // (16x16x32 MFMA A operand: lane = row % 16 + 16 * k-block, 8 elements):
     //   pifrag [d/16 row tiles][d/32 k-steps][3 parts][64][8]: Pi = hi + mid + lo
@@ -105,6 +106,18 @@ struct ValueLaunch {
 };
 hipError_t launch_compress_values(const ValueLaunch &a, hipStream_t stream);
 
+// rotated block key formats (k_block.hip)
+struct BlockLaunch {
+    const void *k;
+    tq_dtype dtype;
+    int B, H;
+    int64_t T, sb, sh, st;
+    int d, bits;                // bits 8 or 4
+    const double *pi64T;        // [d][d], row j = input coordinate
+    tq_bcache out;
+};
+hipError_t launch_compress_keys_block(const BlockLaunch &a, hipStream_t stream);
+
 // explicit key estimates (k_dequant.hip)
 struct DequantLaunch {
     int64_t N;                  // keys (B * Hkv * T), rows of every plane
@@ -150,6 +163,10 @@ struct DecodeLaunch {
     float *scores;              // tq_scores output [B, Hq, T]
     float *out;                 // [B, Hq, d]
     CacheMap map;               // flat (T tokens each) or a layout cache (T = capacity)
+    // rotated block key formats (kfmt_block): planes and per-(query, block) offsets
+    bool kfmt_block = false;
+    tq_bcache kq;
+    float *qaux;                // [B, Hq, d / 32]
     MfmaArgs mf;
 };
 hipError_t launch_qprep(const DecodeLaunch &a, hipStream_t stream);
@@ -168,6 +185,7 @@ int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits, int m);
 int mfma_row_tiles(int bits, int gc);
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream);
+hipError_t launch_decode_block(const DecodeLaunch &a, hipStream_t stream);
 
 // ---- profiling hooks (api.cpp)
 void prof_begin(const char *name, hipStream_t stream, void **token);

@@ -239,6 +239,47 @@ tq_status tq_attend_decode_paged(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt,
                                  tq_kcache kc, tq_vcache vc, float softmax_scale, int n_splits,
                                  void *ws, size_t ws_bytes, float *out, void *stream);
 
+/* ------------------------------------- rotated block formats (comparison) */
+
+/* Rotated scalar block key formats, the comparison the tproger.ru article
+   reports (section "First benchmarks": Q8_0 and Q4_0 with rotation against
+   the same formats without it).  The key is rotated, x = Pi k (the rotation
+   handle's Pi, no normalisation), and every block of 32 consecutive rotated
+   coordinates keeps one fp16 scale = fp16_rne(amax / qmax) (qmax 127 for
+   bits = 8, 7 for bits = 4) and the signed codes
+   q = clamp(round_half_even(x / scale), -qmax, qmax) (0 where scale = 0):
+   one int8 byte each (bits 8) or q + 8 in 4 bits, LSB-first (bits 4).
+   The score of a query is sum_j (Pi q)_j scale q_j.  d in {128, 256}. */
+typedef struct {
+    int d;
+    int bits;                   /* 8 or 4 */
+    const tq_rotation *rot;
+} tq_block_fmt;
+
+/* Planes (device, caller-owned), per vector: codes d*bits/8 B, scales d/32
+   fp16 bit patterns. */
+typedef struct {
+    uint8_t *codes;
+    uint16_t *scales;
+} tq_bcache;
+
+/* Bytes of one plane (0 codes, 1 scales) for n_vec vectors; 0 on a bad argument. */
+size_t tq_block_plane_bytes(const tq_block_fmt *fmt, int64_t n_vec, int plane);
+/* Compress keys k[B, Hkv, T, d] (strides as in tq_compress_keys).  The
+   rotation is accumulated in fp64, so the codes are those of the exact
+   rotated key but for ties. */
+tq_status tq_compress_keys_block(const tq_block_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
+                                 int64_t T, int64_t sb, int64_t sh, int64_t st, tq_bcache out,
+                                 void *stream);
+/* Decode attention over block-format keys and the usual packed values, as
+   tq_attend_decode. */
+size_t tq_attend_block_workspace_bytes(const tq_block_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
+                                       int n_splits);
+tq_status tq_attend_decode_block(const tq_block_fmt *kfmt, const tq_val_fmt *vfmt, const void *q,
+                                 tq_dtype dtype, int B, int Hq, int Hkv, int64_t T, tq_bcache kc,
+                                 tq_vcache vc, float softmax_scale, int n_splits, void *ws,
+                                 size_t ws_bytes, float *out, void *stream);
+
 /* Explicit key estimates of a packed cache (dequantisation), fp32
    out[B, Hkv, T, d] (contiguous, device):
      k_hat = ||k|| Pi^T ( c[idx] + sqrt(pi/2)/m ||r|| S^T (2 s - 1) ),
