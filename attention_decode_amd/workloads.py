@@ -49,6 +49,7 @@ class Workload:
     kv_ratio: float     # target mean ||k|| / mean ||v|| (0: unscaled)
     seed: int
     qjl: bool = True    # False: the first-stage key format (codes and ||k|| only)
+    block_bits: int = 0  # 8 or 4: rotated block key format instead of TurboQuant keys
 
     @property
     def G(self) -> int:
@@ -60,7 +61,10 @@ class Workload:
 
     def key_bytes(self) -> int:
         """packed bytes per key vector: codes + signs + fp32 ||k|| + fp32 ||r||
-        (codes + fp32 ||k|| for the first-stage format)"""
+        (codes + fp32 ||k|| for the first-stage format; codes + an fp16 scale
+        per 32 coordinates for a block format)"""
+        if self.block_bits:
+            return self.d * self.block_bits // 8 + 2 * (self.d // 32)
         return self.d * self.k_bits // 8 + (self.d // 8 + 4 if self.qjl else 0) + 4
 
     @property

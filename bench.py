@@ -14,7 +14,7 @@ the launch stream, in a separate pass after the timed region) against the
 8 TB/s HBM peak.  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage|q8_0|q4_0]
                     [--layout flat|paged] [--block-size N]
                     [--no-cpu-baseline]
 """
@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen25-3b-8k")
-    ap.add_argument("--key-format", choices=["full", "first-stage"], default="full",
+    ap.add_argument("--key-format", choices=["full", "first-stage", "q8_0", "q4_0"], default="full",
                     help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
-                         "||k|| only (qjl_m = 0)")
+                         "||k|| only (qjl_m = 0); q8_0 / q4_0: the rotated 8-bit / 4-bit block formats "
+                         "(comparison workload)")
     ap.add_argument("--layout", choices=["flat", "paged"], default="flat",
                     help="flat: one contiguous cache per call (the default); paged: the same tokens in a "
                          "block pool behind a shuffled block table, written with tq_append_* and read with "
@@ -82,6 +83,7 @@ class Layer:
         self.cb = tq.tq_build_codebook(w.d, w.k_bits)
         self.rot = tq.tq_make_rotation(w.rotation_seed(layer), w.d, w.rot)
         self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot, qjl_m=w.qjl_m)
+        self.bf = tq.BlockFormat(w.d, w.block_bits, self.rot) if w.block_bits else None
         self.vf = tq.ValueFormat(w.d, w.v_bits, w.group)
         self.k = W.make_keys(w, layer, device="cuda")
         self.v = W.make_values(w, layer, device="cuda")
@@ -99,16 +101,22 @@ class Layer:
             self.vc = tq.alloc_layout_value_cache(self.vf, self.lay, w.B, w.Hkv)
             cap = self.lay.capacity
         else:
-            self.kc = tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T)
+            self.kc = (tq.alloc_block_cache(self.bf, w.B, w.Hkv, w.T) if self.bf
+                       else tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T))
             self.vc = tq.alloc_value_cache(self.vf, w.B, w.Hkv, w.T)
             cap = w.T
         self.splits = tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, cap)
-        n = (tq.tq_attend_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, cap, self.splits) if self.lay is None
-             else tq.tq_attend_paged_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, self.lay, self.splits))
+        if self.bf:     # same split plan as the TurboQuant keys of this shape
+            n = tq.tq_attend_block_workspace_bytes(self.bf, w.B, w.Hq, w.Hkv, cap, self.splits)
+        else:
+            n = (tq.tq_attend_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, cap, self.splits) if self.lay is None
+                 else tq.tq_attend_paged_workspace_bytes(self.kf, w.B, w.Hq, w.Hkv, self.lay, self.splits))
         self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
 
     def compress_keys(self, tq):
-        if self.lay is None:
+        if self.bf:
+            tq.tq_compress_keys_block(self.bf, self.k, self.kc)
+        elif self.lay is None:
             tq.tq_compress_keys(self.kf, self.k, self.kc)
         else:
             tq.tq_append_keys(self.kf, self.k, self.lay, self.pos0, self.kc)
@@ -120,7 +128,10 @@ class Layer:
             tq.tq_append_values(self.vf, self.v, self.lay, self.pos0, self.vc)
 
     def decode(self, tq, w):
-        if self.lay is None:
+        if self.bf:
+            tq.tq_attend_decode_block(self.bf, self.vf, self.q, self.kc, self.vc, w.Hkv, w.T, out=self.out,
+                                      ws=self.ws, n_splits=self.splits)
+        elif self.lay is None:
             tq.tq_attend_decode(self.kf, self.vf, self.q, self.kc, self.vc, w.Hkv, w.T, out=self.out, ws=self.ws,
                                 n_splits=self.splits)
         else:
@@ -221,6 +232,10 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.key_format == "first-stage":
         w = replace(w, name=w.name + "-first-stage", qjl=False)
+    elif args.key_format in ("q8_0", "q4_0"):
+        w = replace(w, name=f"{w.name}-{args.key_format}", block_bits=8 if args.key_format == "q8_0" else 4)
+    if w.block_bits and args.layout != "flat":
+        sys.exit("the block key formats run on the flat layout only")
     print(f"[bench] setting up {w.name}: layers={w.layers} B={w.B} Hkv={w.Hkv} Hq={w.Hq} T={w.T} d={w.d}",
           file=sys.stderr, flush=True)
     paged = args.block_size if args.layout == "paged" else 0
@@ -316,7 +331,8 @@ def main():
         "data": "synthetic (seeded; shapes and statistics of the workload, no model weights)",
         "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "kv_heads": w.Hkv,
                    "q_heads": w.Hq, "tokens": w.T, "head_dim": w.d, "input_dtype": w.dtype,
-                   "k_bits": (f"{w.k_bits}+1 (Lloyd-Max + QJL sign)" if w.qjl
+                   "k_bits": (f"{w.block_bits} (rotated block format, fp16 scale per 32)" if w.block_bits
+                              else f"{w.k_bits}+1 (Lloyd-Max + QJL sign)" if w.qjl
                               else f"{w.k_bits} (Lloyd-Max only, first-stage format)"), "rotation": w.rot,
                    "v_bits": w.v_bits, "v_group": w.group, "attn_splits": splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
