@@ -29,7 +29,7 @@ __all__ = [
     "tq_attend_block_workspace_bytes",
 ]
 
-_ROT_KIND = {"dense": TQ_ROT_DENSE, "hadamard": TQ_ROT_HADAMARD}
+_ROT_KIND = {"dense": TQ_ROT_DENSE, "hadamard": TQ_ROT_HADAMARD, "hadamard2": L.TQ_ROT_HADAMARD2}
 
 
 def _dptr(a: np.ndarray):

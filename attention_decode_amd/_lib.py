@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_ENOMEM, TQ_EHIP, TQ_ENOTCONV = range(7)
 STATUS_NAMES = ["TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EALIGN", "TQ_ENOMEM", "TQ_EHIP",
                 "TQ_ENOTCONV"]
-TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
+TQ_ROT_DENSE, TQ_ROT_HADAMARD, TQ_ROT_HADAMARD2 = 0, 1, 2
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 
 

@@ -263,12 +263,14 @@ tq_status tq_codebook_tables(const tq_codebook *cb, double *centroids, double *b
 tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, double *s)
 {
     if (d < 2 || d > 4096) return fail(TQ_EINVAL, "rotation: d=%d outside [2, 4096]", d);
-    if (kind != TQ_ROT_DENSE && kind != TQ_ROT_HADAMARD) return fail(TQ_EINVAL, "rotation: bad kind %d", kind);
-    if (kind == TQ_ROT_HADAMARD && (d & (d - 1)) != 0)
+    if (kind != TQ_ROT_DENSE && kind != TQ_ROT_HADAMARD && kind != TQ_ROT_HADAMARD2)
+        return fail(TQ_EINVAL, "rotation: bad kind %d", kind);
+    if (kind != TQ_ROT_DENSE && (d & (d - 1)) != 0)
         return fail(TQ_EUNSUPPORTED, "rotation: Hadamard needs a power-of-two d, got %d", d);
     if (pi) {
         if (kind == TQ_ROT_DENSE) tq::dense_rotation(seed, d, pi);
-        else tq::hadamard_rotation(seed, d, pi);
+        else if (kind == TQ_ROT_HADAMARD) tq::hadamard_rotation(seed, d, pi);
+        else tq::hadamard2_rotation(seed, d, pi);
     }
     if (s) tq::qjl_projection(seed, d, d, s);
     return TQ_OK;
@@ -343,6 +345,11 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
                     if (kind == TQ_ROT_HADAMARD) {
                         // the +-1 sign matrix H D, exact in one part; 1/sqrt(d) is applied in fp32
                         parts[0] = bf16_rne(pv > 0.0 ? 1.0 : -1.0);
+                        parts[1] = parts[2] = 0;
+                    } else if (kind == TQ_ROT_HADAMARD2) {
+                        // H D2 H D1 has integer entries in [-d, d], exact in one bf16 part
+                        // (|entry| <= 256); 1/d is applied in fp32
+                        parts[0] = bf16_rne(std::nearbyint(pv * d));
                         parts[1] = parts[2] = 0;
                     } else {
                         bf16_split(pv, 3, parts);
@@ -620,7 +627,9 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, tq_dtype dtyp
     a.d = fmt->d;
     a.bits = fmt->mse_bits;
     a.m = fmt->qjl_m;
-    a.hadamard = fmt->rot->kind == TQ_ROT_HADAMARD;
+    a.hadamard = fmt->rot->kind != TQ_ROT_DENSE;
+    a.rot_scale = fmt->rot->kind == TQ_ROT_HADAMARD2 ? 1.0f / fmt->d
+                : fmt->rot->kind == TQ_ROT_HADAMARD ? static_cast<float>(1.0 / std::sqrt(double(fmt->d))) : 1.0f;
     a.piT = fmt->rot->d_piT;
     a.sT = fmt->rot->d_sT;
     a.dsign = fmt->rot->d_dsign;

@@ -239,20 +239,34 @@ void dense_rotation(uint64_t seed, int d, double *pi)
         for (int j = 0; j < d; ++j) pi[static_cast<size_t>(i) * d + j] = q[static_cast<size_t>(j) * d + i];
 }
 
-void hadamard_signs(uint64_t seed, int d, float *signs)
+void hadamard_signs(uint64_t seed, int d, float *signs, int stream)
 {
-    for (int j = 0; j < d; ++j) signs[j] = (rng_draw(seed, 1, j) & 1ULL) ? -1.0f : 1.0f;
+    for (int j = 0; j < d; ++j) signs[j] = (rng_draw(seed, stream, j) & 1ULL) ? -1.0f : 1.0f;
 }
 
-void hadamard_rotation(uint64_t seed, int d, double *pi)
+void hadamard_rotation(uint64_t seed, int d, double *pi, int stream)
 {
     std::vector<float> sg(d);
-    hadamard_signs(seed, d, sg.data());
+    hadamard_signs(seed, d, sg.data(), stream);
     const double inv = 1.0 / std::sqrt(static_cast<double>(d));
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
             const bool odd = __builtin_parity(static_cast<unsigned>(i & j));
             pi[static_cast<size_t>(i) * d + j] = (odd ? -inv : inv) * sg[j];
+        }
+}
+
+// two rounds: (H D2 / sqrt(d)) (H D1 / sqrt(d)), D1 from stream 1, D2 from stream 3
+void hadamard2_rotation(uint64_t seed, int d, double *pi)
+{
+    std::vector<double> a1(static_cast<size_t>(d) * d), a2(static_cast<size_t>(d) * d);
+    hadamard_rotation(seed, d, a1.data(), 1);
+    hadamard_rotation(seed, d, a2.data(), 3);
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += a2[static_cast<size_t>(i) * d + k] * a1[static_cast<size_t>(k) * d + j];
+            pi[static_cast<size_t>(i) * d + j] = acc;
         }
 }
 

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
         const double n = sqrt(s.nrm2[key] + s.nrm2[kKeys + key] + s.nrm2[2 * kKeys + key] + s.nrm2[3 * kKeys + key]);
-        inv_n[kt] = (n > 0.0) ? static_cast<float>((a.hadamard ? 1.0 / sqrt(double(D)) : 1.0) / n) : 0.0f;
+        inv_n[kt] = (n > 0.0) ? static_cast<float>(static_cast<double>(a.rot_scale) / n) : 0.0f;
     }
     float tb[BITS <= 2 ? L - 1 : 1];             // boundaries in registers (1-2 bits)
     if constexpr (BITS <= 2) {

@@ -72,8 +72,9 @@ double rng_normal(uint64_t seed, int stream, uint64_t n);
 tq_status lloyd_max_codebook(int d, int bits, double *centroids, double *boundaries,
                              double *residual_out);
 void dense_rotation(uint64_t seed, int d, double *pi);
-void hadamard_signs(uint64_t seed, int d, float *signs);
-void hadamard_rotation(uint64_t seed, int d, double *pi);
+void hadamard_signs(uint64_t seed, int d, float *signs, int stream = 1);
+void hadamard_rotation(uint64_t seed, int d, double *pi, int stream = 1);
+void hadamard2_rotation(uint64_t seed, int d, double *pi);
 void qjl_projection(uint64_t seed, int m, int d, double *s);
 
 // ---- kernel launchers.  All return hipSuccess or the launch error.
@@ -83,7 +84,8 @@ struct KeyLaunch {
     int B, H;
     int64_t T, sb, sh, st;      // element strides
     int d, bits, m;
-    bool hadamard;
+    bool hadamard;              // Pi = integer matrix * rot_scale, exact in one bf16 term
+    float rot_scale;            // 1/sqrt(d) (one Hadamard round), 1/d (two rounds)
     const float *piT, *sT, *dsign, *centroids, *boundaries;
     const uint8_t *grid;
     int ngrid;

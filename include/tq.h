@@ -51,7 +51,7 @@ typedef enum {
     TQ_ENOTCONV = 6       /* the codebook iteration did not converge          */
 } tq_status;
 
-typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot_kind;
+typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1, TQ_ROT_HADAMARD2 = 2 } tq_rot_kind;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 typedef struct tq_codebook tq_codebook;   /* opaque, immutable */
@@ -118,8 +118,12 @@ tq_status tq_codebook_host(int d, int bits, double *centroids, double *boundarie
    of a Gaussian matrix with a positive-diagonal R.  TQ_ROT_HADAMARD:
    H D / sqrt(d), H the Sylvester Walsh-Hadamard matrix and D random signs (the
    O(d log d) rotation the tproger.ru article, section "Implementations",
-   names); d must be a power of two.  Random numbers: SplitMix64 counter
-   generator, stream 0 = Gaussian matrix for Pi, 1 = signs of D, 2 = S;
+   names); d must be a power of two.  TQ_ROT_HADAMARD2: two such rounds,
+   Pi = (H D2 / sqrt(d)) (H D1 / sqrt(d)) = H D2 H D1 / d, the multi-round
+   form that mixes more like a dense rotation at the same O(d log d) cost
+   (D1 as in one round, D2 from its own stream).  Random numbers: SplitMix64
+   counter generator, stream 0 = Gaussian matrix for Pi, 1 = signs of D (D1),
+   2 = S, 3 = signs of D2;
    Box-Muller, row-major fill.  d in {64, 128, 256}.  Allocates device
    copies on the current device. */
 tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation **out);

@@ -66,6 +66,7 @@ def _l():
     lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.orc_rotation_dense.argtypes = [u64, i32, _f64p]
     lib.orc_rotation_hadamard.argtypes = [u64, i32, _f64p]
+    lib.orc_rotation_hadamard2.argtypes = [u64, i32, _f64p]
     lib.orc_hadamard_signs.argtypes = [u64, i32, _f64p]
     lib.orc_qjl_matrix.argtypes = [u64, i32, i32, _f64p]
     lib.orc_density.restype = ctypes.c_double
@@ -141,6 +142,12 @@ def rotation_hadamard(seed: int, d: int) -> np.ndarray:
     return pi
 
 
+def rotation_hadamard2(seed: int, d: int) -> np.ndarray:
+    pi = np.zeros((d, d))
+    _l().orc_rotation_hadamard2(seed, d, pi)
+    return pi
+
+
 def hadamard_signs(seed: int, d: int) -> np.ndarray:
     s = np.zeros(d)
     _l().orc_hadamard_signs(seed, d, s)
@@ -157,7 +164,7 @@ def qjl_matrix(seed: int, m: int, d: int) -> np.ndarray:
 class Rotation:
     seed: int
     d: int
-    kind: str          # "dense" | "hadamard"
+    kind: str          # "dense" | "hadamard" | "hadamard2"
     pi: np.ndarray     # d x d, y = pi @ u
     s: np.ndarray      # m x d QJL projection
 
@@ -165,7 +172,7 @@ class Rotation:
 def rotation(seed: int, d: int, kind: str = "dense", m: int | None = None) -> Rotation:
     """Pi and S of a seed; m = 0 gives the key format without the QJL stage."""
     m = d if m is None else m
-    pi = rotation_dense(seed, d) if kind == "dense" else rotation_hadamard(seed, d)
+    pi = {"dense": rotation_dense, "hadamard": rotation_hadamard, "hadamard2": rotation_hadamard2}[kind](seed, d)
     return Rotation(seed, d, kind, pi, qjl_matrix(seed, m, d))
 
 

@@ -180,6 +180,32 @@ void orc_hadamard_signs(uint64_t seed, int d, double *dsign)
         dsign[j] = (orc_splitmix_draw(seed, 1, (uint64_t)j) & 1ULL) ? -1.0 : 1.0;
 }
 
+/* Two Hadamard rounds: Pi = (H D2 / sqrt(d)) (H D1 / sqrt(d)), D1 the signs of
+   stream 1 (as one round), D2 those of stream 3.  Written as the product of
+   the two explicit round matrices. */
+void orc_rotation_hadamard2(uint64_t seed, int d, double *pi)
+{
+    double *a1 = (double *)malloc(sizeof(double) * d * d);
+    double *a2 = (double *)malloc(sizeof(double) * d * d);
+    double s = 1.0 / sqrt((double)d);
+    for (int i = 0; i < d; i++)
+        for (int j = 0; j < d; j++) {
+            double h = (orc_popcount((unsigned)(i & j)) & 1) ? -1.0 : 1.0;
+            double d1 = (orc_splitmix_draw(seed, 1, (uint64_t)j) & 1ULL) ? -1.0 : 1.0;
+            double d2 = (orc_splitmix_draw(seed, 3, (uint64_t)j) & 1ULL) ? -1.0 : 1.0;
+            a1[i * d + j] = h * d1 * s;
+            a2[i * d + j] = h * d2 * s;
+        }
+    for (int i = 0; i < d; i++)
+        for (int j = 0; j < d; j++) {
+            double acc = 0.0;
+            for (int k = 0; k < d; k++) acc += a2[i * d + k] * a1[k * d + j];
+            pi[i * d + j] = acc;
+        }
+    free(a1);
+    free(a2);
+}
+
 void orc_rotation_hadamard(uint64_t seed, int d, double *pi)
 {
     double *dsign = (double *)malloc(sizeof(double) * d);

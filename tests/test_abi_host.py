@@ -41,7 +41,8 @@ def test_host_codebook_matches_oracle(d, bits):
 
 
 @pytest.mark.parametrize("d,kind", [(64, "dense"), (128, "dense"), (256, "dense"),
-                                    (128, "hadamard"), (256, "hadamard")])
+                                    (128, "hadamard"), (256, "hadamard"), (128, "hadamard2"),
+                                    (256, "hadamard2")])
 def test_host_rotation_matches_oracle(d, kind):
     seed = 4242 + d
     pi, s = tq.tq_rotation_host(seed, d, kind)

@@ -73,6 +73,27 @@ def test_hadamard_rotation(d):
         assert dsg[j] == (-1.0 if O.splitmix_draw(seed, 1, j) & 1 else 1.0)
 
 
+@pytest.mark.parametrize("d", [4, 64, 256])
+def test_two_round_hadamard_rotation(d):
+    """Pi = (H D2 / sqrt(d)) (H D1 / sqrt(d)): scipy's Hadamard with the sign
+    vectors drawn from streams 1 and 3; orthogonal, d Pi integral, and the
+    first round is the one-round rotation."""
+    seed = 11
+    pi = O.rotation_hadamard2(seed, d)
+    h = linalg.hadamard(d).astype(np.float64)
+    d1 = np.array([-1.0 if O.splitmix_draw(seed, 1, j) & 1 else 1.0 for j in range(d)])
+    d2 = np.array([-1.0 if O.splitmix_draw(seed, 3, j) & 1 else 1.0 for j in range(d)])
+    want = (h * d2[None, :]) @ (h * d1[None, :]) / d
+    assert np.abs(pi - want).max() < 1e-14
+    assert np.abs(pi.T @ pi - np.eye(d)).max() < 1e-12
+    assert np.abs(pi * d - np.rint(pi * d)).max() < 1e-9
+    assert np.abs(pi - (h * d2[None, :] / math.sqrt(d)) @ O.rotation_hadamard(seed, d)).max() < 1e-14
+    # at the head dims in use the product is dense-looking (many entry sizes),
+    # unlike one round's +-1/sqrt(d) (at d = 4 the two sign draws may cancel)
+    if d >= 64:
+        assert len(np.unique(np.abs(np.rint(pi * d)))) > 2
+
+
 def test_qjl_matrix_statistics():
     s = O.qjl_matrix(3, 128, 128)
     assert stats.kstest(s.ravel(), "norm").pvalue > 1e-3
