@@ -15,7 +15,7 @@ the launch stream, in a separate pass after the timed region) against the
 fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage|q8_0|q4_0]
-                    [--layout flat|paged] [--block-size N]
+                    [--rotation dense|hadamard|hadamard2] [--layout flat|paged] [--block-size N]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -46,6 +46,8 @@ def parse():
                     help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
                          "||k|| only (qjl_m = 0); q8_0 / q4_0: the rotated 8-bit / 4-bit block formats "
                          "(comparison workload)")
+    ap.add_argument("--rotation", choices=["dense", "hadamard", "hadamard2"], default=None,
+                    help="override the workload's rotation (hadamard2: two Walsh-Hadamard rounds)")
     ap.add_argument("--layout", choices=["flat", "paged"], default="flat",
                     help="flat: one contiguous cache per call (the default); paged: the same tokens in a "
                          "block pool behind a shuffled block table, written with tq_append_* and read with "
@@ -230,6 +232,8 @@ def main():
         calib_copy(torch)
         return
     w = W.WORKLOADS[args.workload]
+    if args.rotation and args.rotation != w.rot:
+        w = replace(w, name=f"{w.name}-{args.rotation}", rot=args.rotation)
     if args.key_format == "first-stage":
         w = replace(w, name=w.name + "-first-stage", qjl=False)
     elif args.key_format in ("q8_0", "q4_0"):
