@@ -22,9 +22,10 @@
 // the exact fp32 squares (each wave takes a quarter of the k-steps); ||r||
 // in fp32 per lane and fp64 across lanes.
 //
-// Codes: idx = #{t_i < y}.  Up to 2 bits the boundaries sit in registers; from
-// 3 bits a uniform grid over [t_0, t_{L-2}] gives a lower bound of the count
-// that is at most two below it, and two exact comparisons finish it.
+// Codes: idx = #{t_i < y}.  Up to 3 bits the boundaries sit in registers (at
+// most seven comparisons, no dependent LDS reads); from 4 bits a uniform grid
+// over [t_0, t_{L-2}] gives a lower bound of the count that is at most two
+// below it, and two exact comparisons finish it.
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -133,7 +134,7 @@ template <int D, int BITS>
 constexpr size_t key_smem_bytes()
 {
     return sizeof(uint4) * kKT * (D / 32) * 2 * 64 + sizeof(uint32_t) * kKeys * (D * BITS / 32 + D / 32)
-           + sizeof(double) * 8 * kKeys + sizeof(float) * 512 + (BITS >= 3 ? kMaxGrid : 0);
+           + sizeof(double) * 8 * kKeys + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
 }
 
 template <int D, typename TIn, int BITS>
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         s.cent[i] = a.centroids[i];
         s.bnd[i] = a.boundaries[i];      // entry L - 1 is +inf
     }
-    if constexpr (BITS >= 3)
+    if constexpr (BITS >= 4)
         for (int i = tid; i < a.ngrid; i += kThreads) s.grid[i] = a.grid[i];
 
     // rows of this lane's four keys: one divide per workgroup (wave-uniform),
@@ -240,11 +241,13 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
-        const double n = sqrt(s.nrm2[key] + s.nrm2[kKeys + key] + s.nrm2[2 * kKeys + key] + s.nrm2[3 * kKeys + key]);
-        inv_n[kt] = (n > 0.0) ? static_cast<float>(static_cast<double>(a.rot_scale) / n) : 0.0f;
+        // 1/||k|| only scales y: fp32 rsqrt (about 1 ulp) moves y by ~1e-7 at most,
+        // far inside the 1e-5 boundary band; the stored ||k|| is rounded from fp64
+        const float n2 = static_cast<float>(s.nrm2[key] + s.nrm2[kKeys + key] + s.nrm2[2 * kKeys + key] + s.nrm2[3 * kKeys + key]);
+        inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
     }
-    float tb[BITS <= 2 ? L - 1 : 1];             // boundaries in registers (1-2 bits)
-    if constexpr (BITS <= 2) {
+    float tb[BITS <= 3 ? L - 1 : 1];             // boundaries in registers (1-3 bits)
+    if constexpr (BITS <= 3) {
 #pragma unroll
         for (int i = 0; i < L - 1; ++i) tb[i] = s.bnd[i];
     }
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
             for (int r = 0; r < 4; ++r) {
                 const float y = acc[j][kt][r] * inv_n[kt];
                 int pos;
-                if constexpr (BITS <= 2) {
+                if constexpr (BITS <= 3) {
                     pos = 0;
 #pragma unroll
                     for (int i = 0; i < L - 1; ++i) pos += (y > tb[i]) ? 1 : 0;
