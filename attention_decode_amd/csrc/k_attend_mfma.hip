@@ -59,24 +59,27 @@ __device__ __forceinline__ float limbs_to_float(v4i c)
     return fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
 }
 
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// wavefront sum: DPP within each 16-lane row (quad swaps, half-row and row
+// mirrors), then the four row sums read from lanes 0, 16, 32, 48; the result
+// is wave-uniform
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    const int xi = __builtin_bit_cast(int, x);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float load1(const float *p) { return *p; }
@@ -130,6 +133,18 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
     float mv[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) mv[i] = mtx[(jp * NR + i) * D + kb * CB + cl];
+    // column sums for the constant terms (bit-plane scores, written by the
+    // (part 0, quarter 0) workgroup): coordinates lane + 64 i of this lane
+    const bool head = blockIdx.y == 0;
+    const bool sums = head && bitplane;
+    float psum[D / 64], pssum[D / 64];
+    if (sums) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            psum[i] = a.pisum[lane + 64 * i];
+            pssum[i] = a.spisum[lane + 64 * i];
+        }
+    }
     {
         const int i = 8 * tid, g = i / D, c = i % D;
         if (g < GQ) {
@@ -158,19 +173,19 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
     }
     // per query: |q| bound, exponents; the (part 0, quarter 0) workgroup also
     // writes the scales and constant terms
-    const bool head = blockIdx.y == 0;
     for (int g = wave; g < GQ; g += 4) {
         float s2 = 0.0f, sc = 0.0f, ss = 0.0f;
-        for (int j = lane; j < D; j += 64) {
-            const float x = qs[g][j];
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const float x = qs[g][lane + 64 * i];
             s2 = fmaf(x, x, s2);
-            if (head && bitplane) {
-                sc = fmaf(a.pisum[j], x, sc);
-                ss = fmaf(a.spisum[j], x, ss);
+            if (sums) {
+                sc = fmaf(psum[i], x, sc);
+                ss = fmaf(pssum[i], x, ss);
             }
         }
         s2 = wave_sum(s2);
-        if (head && bitplane) {
+        if (sums) {
             sc = wave_sum(sc);
             ss = wave_sum(ss);
         }
@@ -441,14 +456,16 @@ struct ScoreBits {
         for (int mt = 0; mt < MT; ++mt) {
             const int g = 4 * mt + kb;
             const bool ok = g < GC;
-            const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
+            // loaded unconditionally (row clamped): no wait on the operand
+            // loads in flight until the scores need them
+            const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + (row0 + (ok ? g : 0)) * 4);
             // scores leave in log2 units of the softmax: scale log2(e) and the
             // QJL factor kappa are folded into the per-query terms
             const float f = a.scale * kLog2e, fk = f * kappa;
-            fc[mt] = ok ? sc[0] * f : 0.0f;
-            cc[mt] = ok ? sc[1] * f : 0.0f;
-            fs[mt] = ok ? 2.0f * sc[2] * fk : 0.0f;
-            ssq[mt] = ok ? sc[3] * fk : 0.0f;
+            fc[mt] = ok ? sc.x * f : 0.0f;
+            cc[mt] = ok ? sc.y * f : 0.0f;
+            fs[mt] = ok ? 2.0f * sc.z * fk : 0.0f;
+            ssq[mt] = ok ? sc.w * fk : 0.0f;
         }
     }
 
@@ -580,11 +597,11 @@ struct ScoreLut {
         for (int qq = 0; qq < 2; ++qq) {
             const int g = 2 * kb + qq;
             const bool ok = g < GC;
-            const float *sc = a.mf.qscal + (row0 + (ok ? g : 0)) * 4;
+            const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + (row0 + (ok ? g : 0)) * 4);
             // scores leave in log2 units of the softmax (scale log2(e) folded in)
             const float f = a.scale * kLog2e;
-            scc[qq] = ok ? sc[0] * f : 0.0f;
-            scs[qq] = ok ? sc[1] * f * kappa : 0.0f;
+            scc[qq] = ok ? sc.x * f : 0.0f;
+            scs[qq] = ok ? sc.y * f * kappa : 0.0f;
         }
     }
 
@@ -739,9 +756,18 @@ struct ScoreQ {
             const int g = 4 * mt + kb;
             const bool ok = g < GC;
             const int64_t r = row0 + (ok ? g : 0);
-            fq[mt] = ok ? a.mf.qscal[r * 4] * f : 0.0f;
+            const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + r * 4);
+            fq[mt] = ok ? sc.x * f : 0.0f;
+            if constexpr (QB == 4) {
+                float kv[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) kq[mt][b] = (ok && QB == 4) ? a.qaux[r * NB + b] : 0.0f;
+                for (int b = 0; b < NB; ++b) kv[b] = a.qaux[r * NB + b];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) kq[mt][b] = ok ? kv[b] : 0.0f;
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) kq[mt][b] = 0.0f;
+            }
         }
     }
 
@@ -1146,13 +1172,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
 }
 
 // ------------------------------------------------------------ split merge
-// One workgroup per (query row, block of CH channels): out = sum_s 2^(m_s - M)
-// acc_s / sum_s 2^(m_s - M) l_s with M the largest split maximum (maxima in
-// log2 units).  Thread (channel c, phase ph) takes splits ph, ph + P, ...
-// (P = 256 / CH) in batches of NB, every load of a batch unconditional
-// (indices clamped, weights zeroed), and the first batch is issued before the
-// maxima are reduced.  CH and NB follow the split count, so that few splits
-// spread over more channels per workgroup and no load is wasted on clamping.
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M the largest
+// split maximum (maxima in log2 units).  Beyond 16 splits: one workgroup per
+// (query row, block of CH channels); thread (channel c, phase ph) takes splits
+// ph, ph + P, ... (P = 256 / CH) in batches of NB, every load of a batch
+// unconditional (indices clamped, weights zeroed), and the first batch is
+// issued before the maxima are reduced.
 
 __device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l2)
 {
@@ -1160,6 +1185,39 @@ __device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l
     if (mn == -INFINITY) return;                 // both empty
     l = l * exp2_fast(m - mn) + l2 * exp2_fast(m2 - mn);
     m = mn;
+}
+
+// Up to NS <= 16 splits: one workgroup of D threads per query row, thread c
+// loads channel c of every split's partial and every (m, l) pair at once
+// (indices clamped, weights zeroed past S) and combines them with no
+// barrier: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <int D, int NS>
+__global__ __launch_bounds__(D) void k_merge_rows(DecodeLaunch a)
+{
+    const int64_t row = blockIdx.x;
+    const int S = a.splits, c = threadIdx.x;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml + row * S * 2);
+    const float *pa = a.part_acc + row * S * D + c;
+    float2 m2[NS];
+    float v[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int sc = s < S ? s : S - 1;
+        m2[s] = ml[sc];
+        v[s] = pa[static_cast<int64_t>(sc) * D];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < S && m2[s].y > 0.0f) M = fmaxf(M, m2[s].x);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const float e = (s < S && m2[s].y > 0.0f) ? exp2_fast(m2[s].x - M) : 0.0f;
+        L = fmaf(e, m2[s].y, L);
+        o = fmaf(e, v[s], o);
+    }
+    a.out[row * D + c] = L > 0.0f ? o / L : 0.0f;
 }
 
 template <int CH, int NB>
@@ -1242,10 +1300,10 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
     prof_begin("tq_merge_splits", stream, &tok);
     const unsigned rows = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hq);
     const int S = a.splits;
-    if (S <= 2) hipLaunchKernelGGL((k_merge_splits<128, 1>), dim3(rows, a.d / 128), dim3(kThreads), 0, stream, a);
-    else if (S <= 4) hipLaunchKernelGGL((k_merge_splits<64, 1>), dim3(rows, a.d / 64), dim3(kThreads), 0, stream, a);
-    else if (S <= 8) hipLaunchKernelGGL((k_merge_splits<32, 1>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
-    else if (S <= 16) hipLaunchKernelGGL((k_merge_splits<32, 2>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    if (S <= 2) hipLaunchKernelGGL((k_merge_rows<D, 2>), dim3(rows), dim3(D), 0, stream, a);
+    else if (S <= 4) hipLaunchKernelGGL((k_merge_rows<D, 4>), dim3(rows), dim3(D), 0, stream, a);
+    else if (S <= 8) hipLaunchKernelGGL((k_merge_rows<D, 8>), dim3(rows), dim3(D), 0, stream, a);
+    else if (S <= 16) hipLaunchKernelGGL((k_merge_rows<D, 16>), dim3(rows), dim3(D), 0, stream, a);
     else if (S <= 32) hipLaunchKernelGGL((k_merge_splits<32, 4>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     else if (S <= 64) hipLaunchKernelGGL((k_merge_splits<32, 8>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((k_merge_splits<32, 16>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);

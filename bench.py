@@ -3,7 +3,8 @@
 One step = the whole path over one batch of seeded synthetic input already in
 HBM: compress every layer's keys and values into the packed planes, then run
 one decode-attention step (query prep, split-K attention, combine) per layer
-straight from the packed cache.
+straight from the packed cache.  The decode launches of all layers are
+replayed from one captured HIP graph (--eager-decode launches them one by one).
 
 Prints ONE JSON line.  `value` is decode-attention throughput in GB/s of
 packed KV read (packed K + V bytes of all layers / decode time of the step);
@@ -16,7 +17,7 @@ fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage|q8_0|q4_0]
                     [--rotation dense|hadamard|hadamard2] [--layout flat|paged] [--block-size N]
-                    [--no-cpu-baseline]
+                    [--eager-decode] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -53,6 +54,9 @@ def parse():
                          "block pool behind a shuffled block table, written with tq_append_* and read with "
                          "tq_attend_decode_paged")
     ap.add_argument("--block-size", type=int, default=64)
+    ap.add_argument("--eager-decode", action="store_true",
+                    help="launch the per-layer decode kernels one by one from the host instead of replaying "
+                         "them from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -251,7 +255,7 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, eager=False):
         if ev:
             ev[0].record(stream)
         for L in layers:
@@ -262,17 +266,48 @@ def main():
             L.compress_values(tq)
         if ev:
             ev[2].record(stream)
-        for L in layers:
-            L.decode(tq, w)
+        if decode_graph is not None and not eager:
+            decode_graph.replay()
+        else:
+            for L in layers:
+                L.decode(tq, w)
         if ev:
             ev[3].record(stream)
 
+    decode_graph = None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The per-layer decode launches (q-prep, split-K attention, merge for every
+    # layer) are captured once into a HIP graph and replayed each step: at the
+    # microsecond kernels of a small cache the host's launch path, not the GPU,
+    # would otherwise set the pace.  The first replay must reproduce the eager
+    # outputs bit for bit.
+    if not args.eager_decode:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for L in layers:
+                L.decode(tq, w)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        eager_out = [L.out.clone() for L in layers]
+        decode_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(decode_graph):
+            for L in layers:
+                L.decode(tq, w)
+        for L in layers:
+            L.out.zero_()
+        decode_graph.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(L.out, o) for L, o in zip(layers, eager_out)):
+            sys.exit("graph replay of the decode launches differs from the eager launches")
+        del eager_out
+
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    # timed region: plain launches, phase boundaries marked by stream events only
+    # timed region: the compress launches, then the decode graph (or the eager
+    # decode launches); phase boundaries marked by stream events only
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -291,10 +326,10 @@ def main():
     tq.tq_profile_read("")
     if spin is not None:
         spin(SPIN_CYCLES)
-    step()
+    step(eager=True)
     tq.tq_profile_enable(True)
     for _ in range(max(1, min(args.steps, 5))):
-        step()
+        step(eager=True)
     torch.cuda.synchronize()
     tq.tq_profile_enable(False)
     attn_ms, attn_n = tq.tq_profile_read("tq_attend_splitk")
@@ -340,6 +375,7 @@ def main():
                               else f"{w.k_bits} (Lloyd-Max only, first-stage format)"), "rotation": w.rot,
                    "v_bits": w.v_bits, "v_group": w.group, "attn_splits": splits},
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "decode_launch": "eager" if decode_graph is None else "hip-graph",
         "decode_ms_per_step": round(d_ms, 4),
         "compress_keys_ms_per_step": round(k_ms, 4),
         "compress_values_ms_per_step": round(v_ms, 4),

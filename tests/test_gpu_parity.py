@@ -73,7 +73,7 @@ def test_decode_on_oracle_cache(torch_cuda, name):
     print(f"[parity] {name}: score err {r:.3g} x bound, attention max abs err {e:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 33, 64, 100])
 def test_split_count_invariance(torch_cuda, splits):
     torch = torch_cuda
     w = _reduced("long-1m")
