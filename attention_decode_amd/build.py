@@ -33,6 +33,15 @@ def compile_cmd(src: str, obj: str) -> list[str]:
             "-I", os.path.join(PKG, "..", "include"), "-c", src, "-o", obj]
 
 
+CALIB = os.path.join(PKG, "calib_read")
+
+
+def calib_cmd(out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            os.path.join(PKG, "calib_read.hip"), "-o", out]
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -64,6 +73,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # streaming-read calibration program (bench.py --calib-read)
+    subprocess.check_call(calib_cmd(CALIB + ".tmp"))
+    os.replace(CALIB + ".tmp", CALIB)
     return LIB
 
 

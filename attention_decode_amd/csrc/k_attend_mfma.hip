@@ -425,6 +425,7 @@ struct ScoreBits {
     using KW = KeyWords<BITS, D, QJL>;
     static constexpr int NQ = MT;
     static constexpr int TAB_BYTES = 0;
+    static constexpr bool OCC3 = false;     // three workgroups measured no faster
     static constexpr int NC = D * BITS / 128, NS = QJL ? D / 128 : 0;
     static constexpr int SC = 2 * NC, SS = 2 * NS, S = SC + SS;
     v4i aop[MT][S];
@@ -526,6 +527,7 @@ template <int BITS, int D, bool QJL>
 struct ScoreLut {
     using KW = KeyWords<BITS, D, QJL>;
     static constexpr int NQ = 2;
+    static constexpr bool OCC3 = true;
     static constexpr int KS = D / 32;
     static constexpr bool PAIR = BITS <= 5;
     // pair mode: a hi table and a lo table of packed (coordinate 2p, 2p + 1)
@@ -725,6 +727,7 @@ struct ScoreQ {
     using KW = KeyWordsQ<QB, D>;
     static constexpr int NQ = MT;
     static constexpr int TAB_BYTES = 0;
+    static constexpr bool OCC3 = false;     // three workgroups measured no faster
     static constexpr int NB = D / 32;
     int64_t aop[MT][NB];
     float fq[MT];              // 2^-f * softmax scale * log2(e)
@@ -802,8 +805,17 @@ struct ScoreQ {
     }
 };
 
+// Workgroups per CU the register budget is fitted to: one at d = 256; three
+// for the table scores (OCC3), with a two-deep prefetch ring; otherwise two,
+// with a three-deep ring.  Per SIMD the tiles in flight stay at six either way.
+template <class SCORE, int D, bool TWO>
+constexpr int attend_occupancy()
+{
+    return D == 256 ? 1 : SCORE::OCC3 ? 3 : 2;
+}
+
 template <class SCORE, int BITS, int D, int VBITS, bool TWO>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 : 2)) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
+__global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NQ = SCORE::NQ;
     constexpr int TK = 32;                       // keys per wave tile
@@ -1078,12 +1090,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : (SCORE::TAB_BYTES > 0 ? 3 
 
     // Register ring of prefetched tiles: the loads of each tile are issued
     // DEPTH - 1 tiles ahead of its use, so that a wave keeps that many tiles
-    // of HBM reads in flight behind its compute (d 256 and the table scores
-    // keep two buffers: registers and occupancy are the limit there).  Tiles left after the unrolled trips
+    // of HBM reads in flight behind its compute (two buffers at one or three
+    // workgroups per CU, three at two).  Tiles left after the unrolled trips
     // are computed from the buffers that already hold them.
     constexpr int STEP = 4 * TK;
+    constexpr bool kRing2 = attend_occupancy<SCORE, D, TWO>() != 2;
     if (first < t_end) {
-        if constexpr (D == 256 || SCORE::TAB_BYTES > 0) {
+        if constexpr (kRing2) {
             Prefetch pa, pb;
             fetch(first, pa);
             int64_t t = first;

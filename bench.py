@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (to calibrate HBM byte counters)")
+    ap.add_argument("--calib-read", action="store_true",
+                    help="run only the streaming-read calibration program (the practical HBM read ceiling)")
     return ap.parse_args()
 
 
@@ -227,6 +229,12 @@ def main():
               "(the path shards by sequence / KV head with no exchange, see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.calib_read:
+        import subprocess
+        prog = os.path.join(ROOT, "attention_decode_amd", "calib_read")
+        if not os.path.exists(prog):
+            sys.exit("calib_read is not built (python -m attention_decode_amd.build)")
+        sys.exit(subprocess.call([prog]))
     import torch
     import attention_decode_amd as tq
     from attention_decode_amd import workloads as W
