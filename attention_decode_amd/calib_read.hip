@@ -1,9 +1,9 @@
 // Streaming-read ceiling of the GPU: the HBM bandwidth a plain read kernel
 // reaches (each thread sums 16-byte loads over a grid-stride loop with U
-// independent loads in flight).  Prints one JSON line with the best of a small
-// sweep of grid sizes and U.  A calibration aid for the decode roofline: the
-// decode kernels are read streams, so this is the practical ceiling their HBM
-// fraction is set against.
+// independent loads in flight).  Prints one JSON line with the best of a sweep
+// of grid sizes (1024..32768 workgroups of 256) and U (4, 8, 16).  A
+// calibration aid for the decode roofline: the decode kernels are read
+// streams, so this is the practical ceiling their HBM fraction is set against.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -63,7 +63,7 @@ int main()
 {
     const size_t bytes = static_cast<size_t>(2) << 30;
     const size_t n = bytes / 16;
-    constexpr int kMaxBlocks = 8192;
+    constexpr int kMaxBlocks = 32768;
     float4 *d = nullptr;
     float *out = nullptr;
     CK(hipMalloc(&d, bytes));
@@ -72,10 +72,16 @@ int main()
     double best = 0.0;
     int best_blocks = 0, best_u = 0;
     for (int blocks = 1024; blocks <= kMaxBlocks; blocks *= 2) {
-        double g4 = 0.0, g8 = 0.0;
-        if (time_read<4>(d, n, out, blocks, g4) || time_read<8>(d, n, out, blocks, g8)) return 1;
-        if (g4 > best) { best = g4; best_blocks = blocks; best_u = 4; }
-        if (g8 > best) { best = g8; best_blocks = blocks; best_u = 8; }
+        double g[3] = {0.0, 0.0, 0.0};
+        if (time_read<4>(d, n, out, blocks, g[0]) || time_read<8>(d, n, out, blocks, g[1]) ||
+            time_read<16>(d, n, out, blocks, g[2]))
+            return 1;
+        for (int k = 0; k < 3; ++k)
+            if (g[k] > best) {
+                best = g[k];
+                best_blocks = blocks;
+                best_u = 4 << k;
+            }
     }
     std::printf("{\"read_GBps\": %.1f, \"bytes\": %zu, \"blocks\": %d, \"threads\": 256, \"loads_in_flight\": %d}\n",
                 best, bytes, best_blocks, best_u);
