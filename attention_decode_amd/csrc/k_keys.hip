@@ -79,36 +79,56 @@ __device__ __forceinline__ void split_terms(const float (&x)[8], uint4 (&t)[NT])
     }
 }
 
-// eight consecutive channels of one key as B-operand terms; with `norm`, their
-// sum of squares is added to ss (each wave sums a quarter of the k-steps)
-__device__ __forceinline__ void key_frag(const bf16_t *p, bool valid, uint4 (&t)[1], double &ss, bool norm)
+// elements of 16-byte chunk c of a staged key row as fp32 (eight 16-bit
+// elements, or four fp32 ones in x[0..3])
+template <typename TIn, int N>
+__device__ __forceinline__ void chunk_as_f32(const uint4 (&v)[N], int c, float (&x)[8])
 {
-    t[0] = valid ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
-    if (norm) {
-        const uint32_t w[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
+    const uint32_t u[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+    if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(u[i]);
+#pragma unroll
+        for (int i = 4; i < 8; ++i) x[i] = 0.0f;
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_to_f32(w[i] & 0xffffu), hi = bf16_to_f32(w[i] >> 16);
-            ss += static_cast<double>(lo * lo) + static_cast<double>(hi * hi);   // squares exact in fp32
+            if constexpr (sizeof(TIn) == 2 && __is_same(TIn, bf16_t)) {
+                x[2 * i] = bf16_to_f32(u[i] & 0xffffu);
+                x[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+            } else {
+                x[2 * i] = f16_bits_to_f32(u[i] & 0xffffu);
+                x[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
+            }
         }
     }
 }
 
+// eight consecutive channels of one staged key (LDS) as NT bf16 B-operand
+// terms: a bf16 key is its own single term
 template <typename TIn, int NT>
-__device__ __forceinline__ void key_frag(const TIn *p, bool valid, uint4 (&t)[NT], double &ss, bool norm)
+__device__ __forceinline__ void key_frag_lds(const unsigned char *p, uint4 (&t)[NT])
 {
-    float x[8];
-    if (valid) {
-        load8_as_f32(p, x);
+    if constexpr (__is_same(TIn, bf16_t)) {
+        t[0] = *reinterpret_cast<const uint4 *>(p);
     } else {
+        float x[8];
+        if constexpr (sizeof(TIn) == 4) {
+            const float4 a = reinterpret_cast<const float4 *>(p)[0];
+            const float4 b = reinterpret_cast<const float4 *>(p)[1];
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+            const uint4 w = *reinterpret_cast<const uint4 *>(p);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = f16_bits_to_f32(u[i] & 0xffffu);
+                x[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
+            }
+        }
+        split_terms<NT>(x, t);
     }
-    if (norm) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);
-    }
-    split_terms<NT>(x, t);
 }
 
 // fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -130,10 +150,25 @@ struct KeySmem {
     uint8_t *grid;      // [kMaxGrid]
 };
 
-template <int D, int BITS>
+// LDS row stride of a staged key: the row plus 16 bytes, so that the 16 keys
+// one B-fragment read touches start in 16 different 4-bank groups
+template <int D, typename TIn>
+constexpr int key_stage_stride() { return D * static_cast<int>(sizeof(TIn)) + 16; }
+
+// the workgroup's raw keys (step 0-1) and the residual operands (steps 3-4)
+// share one region: the keys are dead before the first residual is written
+template <int D, typename TIn>
+constexpr size_t key_union_bytes()
+{
+    const size_t rfrag = sizeof(uint4) * kKT * (D / 32) * 2 * 64;
+    const size_t stage = static_cast<size_t>(kKeys) * key_stage_stride<D, TIn>();
+    return rfrag > stage ? rfrag : stage;
+}
+
+template <int D, typename TIn, int BITS>
 constexpr size_t key_smem_bytes()
 {
-    return sizeof(uint4) * kKT * (D / 32) * 2 * 64 + sizeof(uint32_t) * kKeys * (D * BITS / 32 + D / 32)
+    return key_union_bytes<D, TIn>() + sizeof(uint32_t) * kKeys * (D * BITS / 32 + D / 32)
            + sizeof(double) * 8 * kKeys + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
 }
 
@@ -150,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     KeySmem s;
     {
         unsigned char *p = smem_raw;
-        s.rfrag = reinterpret_cast<uint4 *>(p);   p += sizeof(uint4) * kKT * KS * 2 * 64;
+        s.rfrag = reinterpret_cast<uint4 *>(p);   p += key_union_bytes<D, TIn>();
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
         s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
         s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
@@ -164,37 +199,69 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     const int col = lane & 15, kb = lane >> 4;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kKeys;
 
+    // codebook tables (L <= 128 entries, a grid of at most 4096 bytes in
+    // 16-byte pieces): loads issued unconditionally (indices clamped) ahead of
+    // the keys, stored to LDS after them, so both share one round trip
+    const int ti = tid < L ? tid : L - 1;
+    const float cent_v = a.centroids[ti];
+    const float bnd_v = a.boundaries[ti];      // entry L - 1 is +inf
+    uint4 grid_v = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BITS >= 4) {
+        const int ng16 = a.ngrid / 16;
+        grid_v = reinterpret_cast<const uint4 *>(a.grid)[tid < ng16 ? tid : ng16 - 1];
+    }
     for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
-    for (int i = tid; i < L; i += kThreads) {
-        s.cent[i] = a.centroids[i];
-        s.bnd[i] = a.boundaries[i];      // entry L - 1 is +inf
+
+    // ---- 0. the workgroup's 64 keys into LDS, one HBM round trip: thread
+    // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (rows
+    // found with one divide per workgroup, then stepping across sequence /
+    // head boundaries) and adds the exact squares of its elements in fp64:
+    // partial q of ||k||^2.  Slots past the last key reload that key (loads
+    // stay unconditional); their results are never stored.
+    constexpr int RSTR = key_stage_stride<D, TIn>();
+    constexpr int CH16 = D * static_cast<int>(sizeof(TIn)) / 16;     // 16-byte chunks per row
+    constexpr int TPK = kThreads / kKeys;                              // threads per key
+    constexpr int CPT = CH16 / TPK;                                    // chunks per thread
+    unsigned char *kst = reinterpret_cast<unsigned char *>(s.rfrag);
+    {
+        const int kk = tid / TPK, q = tid % TPK;
+        const int last = static_cast<int>(n_total - 1 - n0 < kKeys - 1 ? n_total - 1 - n0 : kKeys - 1);
+        const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
+        int64_t t = t0 + (kk < last ? kk : last), h = bh0 % a.H, b = bh0 / a.H;
+        while (t >= a.T) {          // at most 64 / T + 1 steps
+            t -= a.T;
+            if (++h == a.H) {
+                h = 0;
+                ++b;
+            }
+        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st)
+                           + q * CPT;
+        uint4 v[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) v[c] = src[c];
+        uint4 *dst = reinterpret_cast<uint4 *>(kst + kk * RSTR) + q * CPT;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) dst[c] = v[c];
+        double ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            float x[8];
+            chunk_as_f32<TIn>(v, c, x);
+#pragma unroll
+            for (int e = 0; e < 16 / static_cast<int>(sizeof(TIn)); ++e)
+                ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);    // exact squares
+        }
+        s.nrm2[q * kKeys + kk] = ss;
+    }
+    if (tid < L) {
+        s.cent[tid] = cent_v;
+        s.bnd[tid] = bnd_v;
     }
     if constexpr (BITS >= 4)
-        for (int i = tid; i < a.ngrid; i += kThreads) s.grid[i] = a.grid[i];
-
-    // rows of this lane's four keys: one divide per workgroup (wave-uniform),
-    // then each lane steps from (b0, h0, t0) across sequence / head boundaries
-    const TIn *kp[kKT];
-    bool valid[kKT];
-    {
-        const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
-        const int64_t b0 = bh0 / a.H, h0 = bh0 - b0 * a.H;
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
-            const int64_t n = n0 + 16 * kt + col;
-            valid[kt] = n < n_total;
-            int64_t t = t0 + (valid[kt] ? 16 * kt + col : 0), b = b0, h = h0;
-            while (t >= a.T) {          // at most 64 / T + 1 steps
-                t -= a.T;
-                if (++h == a.H) {
-                    h = 0;
-                    ++b;
-                }
-            }
-            kp[kt] = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st + 8 * kb;
-        }
-    }
+        if (tid < a.ngrid / 16) reinterpret_cast<uint4 *>(s.grid)[tid] = grid_v;
+    __syncthreads();   // staged keys, cleared words, codebook tables
 
     // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r
     const uint4 *pif = reinterpret_cast<const uint4 *>(a.pifrag);
@@ -204,39 +271,40 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     for (int j = 0; j < RTW; ++j)
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    double ss[kKT] = {0.0, 0.0, 0.0, 0.0};
-    const int npp = a.hadamard ? 1 : 3;
+    const bool three = !a.hadamard;
     const int bits = BITS;
 #pragma unroll 2
     for (int ks = 0; ks < KS; ++ks) {
-        uint4 kf[kKT][NK];
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) key_frag(kp[kt] + 32 * ks, valid[kt], kf[kt], ss[kt], (ks & 3) == wave);
+        // A fragments of this k-step (the Hadamard sign matrix is one exact term)
+        uint4 af[RTW][3];
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
             const int rt = wave * RTW + j;
-            for (int pp = 0; pp < npp; ++pp) {
-                const uint4 af = pif[((rt * KS + ks) * 3 + pp) * 64 + lane];
+            af[j][0] = pif[((rt * KS + ks) * 3 + 0) * 64 + lane];
+            if (three) {
+                af[j][1] = pif[((rt * KS + ks) * 3 + 1) * 64 + lane];
+                af[j][2] = pif[((rt * KS + ks) * 3 + 2) * 64 + lane];
+            }
+        }
+        uint4 kf[kKT][NK];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+            key_frag_lds<TIn, NK>(kst + (16 * kt + col) * RSTR + (32 * ks + 8 * kb) * static_cast<int>(sizeof(TIn)), kf[kt]);
+#pragma unroll
+        for (int j = 0; j < RTW; ++j) {
+#pragma unroll
+            for (int pp = 0; pp < 3; ++pp) {
+                if (pp > 0 && !three) continue;
 #pragma unroll
                 for (int kq = 0; kq < NK; ++kq) {
-                    if (!a.hadamard && pp + kq > 2) continue;
+                    if (three && pp + kq > 2) continue;
 #pragma unroll
-                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af, kf[kt][kq], acc[j][kt]);
+                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af[j][pp], kf[kt][kq], acc[j][kt]);
                 }
             }
         }
     }
-
-    // ---- 2. ||k||: fp64 partial sums of this wave's k-steps, over the four lanes
-    // that hold one key, then across the waves
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-        double t = ss[kt];
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        if (kb == 0) s.nrm2[wave * kKeys + 16 * kt + col] = t;
-    }
-    __syncthreads();   // partial norms, cleared words, codebook tables
+    __syncthreads();   // every wave is done with the staged keys (the region takes the residuals next)
     float inv_n[kKT];
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
@@ -390,7 +458,7 @@ template <int D, typename TIn, int BITS>
 hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
 {
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
-    constexpr size_t smem = key_smem_bytes<D, BITS>();
+    constexpr size_t smem = key_smem_bytes<D, TIn, BITS>();
     auto kern = k_compress_keys<D, TIn, BITS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
