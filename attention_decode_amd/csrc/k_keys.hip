@@ -4,10 +4,12 @@
 // steps 1-3 (y = Pi k/||k||, nearest-centroid codes, signs of S r with
 // r = y - c[idx]).
 //
-// One 256-thread workgroup encodes 64 keys (four 16-key tiles).  Both products
-// run as v_mfma_f32_16x16x32_bf16 with the keys / residuals as the B operand
+// One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 at d = 256)
+// and stages them in LDS first, in one round trip to HBM.  Both products run
+// as v_mfma_f32_16x16x32_bf16 with the keys / residuals as the B operand
 // (lane = key column) and the matrix as the A operand, so that every A
-// fragment read from L2 serves 64 keys; the four waves split the output rows.
+// fragment read from L2 serves all keys of the workgroup; the four waves split
+// the output rows.
 //
 // Accuracy: the bf16 operands are made exact or near-fp32 by splitting.
 //   * y:  Pi = P0 + P1 + P2 (three bf16 terms, about 24 significant bits); a
@@ -36,8 +38,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kKT = 4;              // 16-key tiles per workgroup
-constexpr int kKeys = 16 * kKT;     // keys per workgroup
+// 16-key tiles per workgroup: four (64 keys) up to d = 128; two at d = 256,
+// where the residual operands of 64 keys would leave room in LDS for a
+// single workgroup per CU
+template <int D> constexpr int key_tiles() { return D >= 256 ? 2 : 4; }
 
 // bf16 terms that represent one input element exactly
 template <typename TIn> struct KeyTerms;
@@ -140,11 +144,11 @@ __device__ __forceinline__ uint32_t bf16x2(float x0, float x1)
 }
 
 struct KeySmem {
-    uint4 *rfrag;       // [kKT][KS][2][64]  residual B operands (two bf16 terms)
-    uint32_t *cw;       // [kKeys][D * bits / 32]  code words
-    uint32_t *sw;       // [kKeys][D / 32]         sign words
-    double *rho2;       // [4 waves][kKeys]
-    double *nrm2;       // [4 waves][kKeys]
+    uint4 *rfrag;       // [KT][KS][2][64]  residual B operands (two bf16 terms)
+    uint32_t *cw;       // [KEYS][D * bits / 32]  code words
+    uint32_t *sw;       // [KEYS][D / 32]         sign words
+    double *rho2;       // [4 waves][KEYS]
+    double *nrm2;       // [256 / KEYS threads per key][KEYS]
     float *cent;        // [256]
     float *bnd;         // [256] (+inf after the last boundary)
     uint8_t *grid;      // [kMaxGrid]
@@ -160,26 +164,30 @@ constexpr int key_stage_stride() { return D * static_cast<int>(sizeof(TIn)) + 16
 template <int D, typename TIn>
 constexpr size_t key_union_bytes()
 {
-    const size_t rfrag = sizeof(uint4) * kKT * (D / 32) * 2 * 64;
-    const size_t stage = static_cast<size_t>(kKeys) * key_stage_stride<D, TIn>();
+    const size_t rfrag = sizeof(uint4) * key_tiles<D>() * (D / 32) * 2 * 64;
+    const size_t stage = static_cast<size_t>(16 * key_tiles<D>()) * key_stage_stride<D, TIn>();
     return rfrag > stage ? rfrag : stage;
 }
 
 template <int D, typename TIn, int BITS>
 constexpr size_t key_smem_bytes()
 {
-    return key_union_bytes<D, TIn>() + sizeof(uint32_t) * kKeys * (D * BITS / 32 + D / 32)
-           + sizeof(double) * 8 * kKeys + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
+    constexpr size_t keys = 16 * key_tiles<D>();
+    return key_union_bytes<D, TIn>() + sizeof(uint32_t) * keys * (D * BITS / 32 + D / 32)
+           + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
 }
 
 template <int D, typename TIn, int BITS>
-__global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t n_total)
+__global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
     constexpr int NK = KeyTerms<TIn>::n;
     constexpr int L = 1 << BITS;
     constexpr int CW = D * BITS / 32, SWN = D / 32;
+    constexpr int kKT = key_tiles<D>();  // 16-key tiles of the workgroup
+    constexpr int kKeys = 16 * kKT;      // keys of the workgroup
+    constexpr int TPK = kThreads / kKeys;                              // threads per staged key
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup
     KeySmem s;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         unsigned char *p = smem_raw;
         s.rfrag = reinterpret_cast<uint4 *>(p);   p += key_union_bytes<D, TIn>();
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
-        s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
+        s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kThreads;
         s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
         s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWN;
         s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
 
-    // ---- 0. the workgroup's 64 keys into LDS, one HBM round trip: thread
+    // ---- 0. the workgroup's keys into LDS, one HBM round trip: thread
     // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (rows
     // found with one divide per workgroup, then stepping across sequence /
     // head boundaries) and adds the exact squares of its elements in fp64:
@@ -221,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     // stay unconditional); their results are never stored.
     constexpr int RSTR = key_stage_stride<D, TIn>();
     constexpr int CH16 = D * static_cast<int>(sizeof(TIn)) / 16;     // 16-byte chunks per row
-    constexpr int TPK = kThreads / kKeys;                              // threads per key
     constexpr int CPT = CH16 / TPK;                                    // chunks per thread
     unsigned char *kst = reinterpret_cast<unsigned char *>(s.rfrag);
     {
@@ -311,7 +318,10 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
         const int key = 16 * kt + col;
         // 1/||k|| only scales y: fp32 rsqrt (about 1 ulp) moves y by ~1e-7 at most,
         // far inside the 1e-5 boundary band; the stored ||k|| is rounded from fp64
-        const float n2 = static_cast<float>(s.nrm2[key] + s.nrm2[kKeys + key] + s.nrm2[2 * kKeys + key] + s.nrm2[3 * kKeys + key]);
+        double n2d = 0.0;
+#pragma unroll
+        for (int q = 0; q < TPK; ++q) n2d += s.nrm2[q * kKeys + key];
+        const float n2 = static_cast<float>(n2d);
         inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
     }
     float tb[BITS <= 3 ? L - 1 : 1];             // boundaries in registers (1-3 bits)
@@ -445,7 +455,9 @@ __global__ __launch_bounds__(kThreads) void k_compress_keys(KeyLaunch a, int64_t
     }
     if (tid < nk && s_row[tid] >= 0) {
         const int64_t r = s_row[tid];
-        const double n2 = s.nrm2[tid] + s.nrm2[kKeys + tid] + s.nrm2[2 * kKeys + tid] + s.nrm2[3 * kKeys + tid];
+        double n2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < TPK; ++q) n2 += s.nrm2[q * kKeys + tid];
         a.out.knorm[r] = static_cast<float>(sqrt(n2));
         if (qjl) {
             const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
@@ -463,7 +475,8 @@ hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const int64_t blocks = (n + kKeys - 1) / kKeys;
+    constexpr int keys = 16 * key_tiles<D>();
+    const int64_t blocks = (n + keys - 1) / keys;
     void *tok;
     prof_begin("tq_compress_keys", stream, &tok);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, stream, a, n);
