@@ -24,10 +24,11 @@
 // the exact fp32 squares (each wave takes a quarter of the k-steps); ||r||
 // in fp32 per lane and fp64 across lanes.
 //
-// Codes: idx = #{t_i < y}.  Up to 3 bits the boundaries sit in registers (at
-// most seven comparisons, no dependent LDS reads); from 4 bits a uniform grid
-// over [t_0, t_{L-2}] gives a lower bound of the count that is at most two
-// below it, and two exact comparisons finish it.
+// Codes: idx = #{t_i < y}.  Up to 3 bits a binary search of |y| among the
+// positive boundaries of the symmetric codebook, in registers (at most two
+// comparisons, no LDS reads); from 4 bits a uniform grid over [t_0, t_{L-2}]
+// gives a lower bound of the count that is at most two below it, and two
+// exact comparisons finish it.
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -324,10 +325,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
         const float n2 = static_cast<float>(n2d);
         inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
     }
-    float tb[BITS <= 3 ? L - 1 : 1];             // boundaries in registers (1-3 bits)
+    // 1-3 bits: the codebook is exactly symmetric (c[L-1-i] = -c[i], and so
+    // the boundaries, with t[L/2-1] = 0), so |y| is placed among the H - 1
+    // positive boundaries by a binary search in registers and the centroid
+    // taken from the H positive ones; idx and y - c[idx] follow from the sign
+    // of y, bit for bit as the full count would give them (up to exact ties)
+    constexpr int H = L / 2;
+    float tp[H > 1 ? H - 1 : 1], cp[H];
     if constexpr (BITS <= 3) {
 #pragma unroll
-        for (int i = 0; i < L - 1; ++i) tb[i] = s.bnd[i];
+        for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
+#pragma unroll
+        for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
     }
 
     // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
@@ -345,17 +354,32 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
                 const float y = acc[j][kt][r] * inv_n[kt];
                 int pos;
                 if constexpr (BITS <= 3) {
-                    pos = 0;
-#pragma unroll
-                    for (int i = 0; i < L - 1; ++i) pos += (y > tb[i]) ? 1 : 0;
+                    const float ay = fabsf(y);
+                    int cnt = 0;          // positive boundaries below |y|
+                    float c = cp[0];
+                    if constexpr (BITS == 2) {
+                        const bool b0 = ay > tp[0];
+                        cnt = b0 ? 1 : 0;
+                        c = b0 ? cp[1] : cp[0];
+                    } else if constexpr (BITS == 3) {
+                        const bool b1 = ay > tp[1];
+                        const bool b0 = ay > (b1 ? tp[2] : tp[0]);
+                        cnt = (b1 ? 2 : 0) + (b0 ? 1 : 0);
+                        const float clo = b0 ? cp[1] : cp[0], chi = b0 ? cp[3] : cp[2];
+                        c = b1 ? chi : clo;
+                    }
+                    const bool up = y > 0.0f;
+                    pos = cnt ^ (up ? H : H - 1);     // H + cnt above zero, H - 1 - cnt below (cnt < H)
+                    const float dv = ay - c;
+                    res[r] = up ? dv : -dv;
                 } else {
                     int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
                     c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
                     pos = s.grid[c];
                     pos += (y > s.bnd[pos]) ? 1 : 0;
                     pos += (y > s.bnd[pos]) ? 1 : 0;
+                    res[r] = y - s.cent[pos];
                 }
-                res[r] = y - s.cent[pos];
                 rr = fmaf(res[r], res[r], rr);
                 chunk |= static_cast<uint32_t>(pos) << (bits * r);
             }
