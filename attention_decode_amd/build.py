@@ -74,7 +74,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     subprocess.check_call([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     # streaming-read calibration program (bench.py --calib-read)
-    subprocess.check_call(calib_cmd(CALIB + ".tmp"))
+    r = subprocess.run(calib_cmd(CALIB + ".tmp"), stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for calib_read.hip")
     os.replace(CALIB + ".tmp", CALIB)
     return LIB
 
