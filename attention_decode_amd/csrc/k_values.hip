@@ -12,12 +12,14 @@ namespace {
 constexpr int kThreads = 256;
 
 // round((v - zero) / scale) to nearest even, clamped to [0, levels].  The fp32
-// quotient is within 4e-6 of the exact one (|q| <= 16), so it decides every
-// case except those within 1e-4 of a half-integer, which are redone in fp64.
-__device__ __forceinline__ uint32_t value_code(float v, float zero, float scale, int levels)
+// quotient, (v - zero) times the group's rounded reciprocal of the scale, is
+// within 4e-6 of the exact one (three roundings of 2^-24 relative, |q| <= 16),
+// so it decides every case except those within 1e-4 of a half-integer, which
+// are redone in fp64.
+__device__ __forceinline__ uint32_t value_code(float v, float zero, float scale, float inv_scale, int levels)
 {
     if (scale == 0.0f) return 0;
-    float q = __fdiv_rn(v - zero, scale);
+    float q = (v - zero) * inv_scale;
     const float frac = q - floorf(q);
     float r;
     if (fabsf(frac - 0.5f) < 1e-4f) {
@@ -73,6 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_values(ValueLaunch a, int
     const uint32_t sh = f64_to_f16_rne((static_cast<double>(mx) - static_cast<double>(mn)) / levels);
     const uint32_t zh = f64_to_f16_rne(static_cast<double>(mn));
     const float sc = f16_bits_to_f32(sh), ze = f16_bits_to_f32(zh);
+    const float inv = sc != 0.0f ? 1.0f / sc : 0.0f;
 
     constexpr int per_word = 32 / BITS, words = G * BITS / 32;
     const int64_t row = out_row(a.map, a.H, a.T, n);      // n itself unless appending
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_compress_values(ValueLaunch a, int
         uint32_t word = 0;
 #pragma unroll
         for (int e = 0; e < per_word; ++e)
-            word |= value_code(x[w * per_word + e], ze, sc, levels) << (BITS * e);
+            word |= value_code(x[w * per_word + e], ze, sc, inv, levels) << (BITS * e);
         dst[w] = word;
     }
     reinterpret_cast<uint32_t *>(a.out.params)[row * (a.d / G) + grp] = sh | (zh << 16);
