@@ -41,7 +41,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3, and until 1.5 s of steps have run, so "
+                         "that the GPU's clocks have settled under load)")
     ap.add_argument("--workload", default="qwen25-3b-8k")
     ap.add_argument("--key-format", choices=["full", "first-stage", "q8_0", "q4_0"], default="full",
                     help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
@@ -283,8 +285,18 @@ def main():
             ev[3].record(stream)
 
     decode_graph = None
-    for _ in range(args.warmup):
+    # Warm-up: the GPU takes tens of milliseconds of sustained load to reach
+    # its steady clocks, far more than three steps of a small cache, so by
+    # default the warm-up runs for at least 1.5 s (and three steps).
+    n_warm = 0
+    t_warm = time.perf_counter()
+    while args.warmup is None or n_warm < args.warmup:
         step()
+        n_warm += 1
+        if args.warmup is None and n_warm >= 3:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_warm >= 1.5:
+                break
     torch.cuda.synchronize()
     # The per-layer decode launches (q-prep, split-K attention, merge for every
     # layer) are captured once into a HIP graph and replayed each step: at the
@@ -369,7 +381,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
