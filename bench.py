@@ -171,6 +171,18 @@ def measured_traffic(w):
         return None
 
 
+def read_ceiling():
+    """The streaming-read ceiling measured on this GPU model (GB/s), from the
+    committed calibration summary (bench.py --calib-read), or None."""
+    try:
+        for line in open(os.path.join(ROOT, "profiles", "hbm_read_ceiling.txt")):
+            if line.startswith("{"):
+                return float(json.loads(line)["read_GBps"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle (as is) on a bounded sample of the workload: one (sequence,
     KV head) unit's keys compressed, then decode attention of its G query heads
@@ -364,6 +376,7 @@ def main():
     d_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    ceiling = read_ceiling()
     packed = w.packed_bytes()
     vectors = w.vectors()
     value = packed / (d_ms * 1e-3) / 1e9
@@ -405,13 +418,37 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "tq_attend_splitk", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w), "bytes_per_launch": attn_bytes,
-                     "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n},
+                     "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n,
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
         "kernel_avg_us": {"tq_compress_keys": round(kq_ms * 1e3 / max(kq_n, 1), 3),
                           "tq_compress_values": round(vq_ms * 1e3 / max(vq_n, 1), 3),
                           "tq_qprep": round(qp_ms * 1e3 / max(qp_n, 1), 3),
                           "tq_attend_splitk": round(attn_avg_s * 1e6, 3),
                           "tq_merge_splits": round(mg_ms * 1e3 / max(mg_n, 1), 3) if mg_n else None},
     }
+    if packed < (256 << 20):
+        # The packed cache of all layers fits the 256 MB MALL, so the decode
+        # above reads it largely from there.  Cold figure: before each decode
+        # phase, a 512 MiB read evicts it; median over five phases.
+        flush = torch.ones((512 << 20) // 4, device="cuda")
+        cold = []
+        for _ in range(5):
+            flush.sum()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            if decode_graph is not None:
+                decode_graph.replay()
+            else:
+                for L in layers:
+                    L.decode(tq, w)
+            c1.record(stream)
+            cold.append((c0, c1))
+        torch.cuda.synchronize()
+        cold_ms = sorted(a.elapsed_time(b) for a, b in cold)[len(cold) // 2]
+        del flush
+        result["decode_cold"] = {"ms_per_step": round(cold_ms, 4), "GBps": round(packed / (cold_ms * 1e-3) / 1e9, 2),
+                                 "flush_bytes": 512 << 20}
     if paged:
         # one decode step's append: one new token per sequence into every layer's pool
         pos = torch.full((w.B,), w.T - 1, dtype=torch.int32, device="cuda")
