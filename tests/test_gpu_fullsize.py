@@ -76,7 +76,7 @@ def test_fullsize_decode_sampled_units(torch_cuda, name, peaked):
     if w.B * w.Hkv > 2:
         units.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
     G = w.G
-    worst = 0.0
+    worst = worst_rel = 0.0
     for b, h in sorted(units):
         okc = O.KeyCache(pc["codes"][b, h].cpu().numpy(), pc["signs"][b, h].cpu().numpy(),
                          pc["knorm"][b, h].cpu().numpy(), pc["rnorm"][b, h].cpu().numpy())
@@ -86,7 +86,9 @@ def test_fullsize_decode_sampled_units(torch_cuda, name, peaked):
         ref = O.attend(qq, okc, w.k_bits, fm.orot, ovc, w.v_bits, w.group)
         got = out[b, h * G:(h + 1) * G].double().cpu().numpy()
         worst = max(worst, P.check_attention(got, ref))
-    print(f"[full] {name} peaked={peaked}: units {sorted(units)} max abs err {worst:.3g}", flush=True)
+        worst_rel = max(worst_rel, P.attention_rel_err(got, ref))
+    print(f"[full] {name} peaked={peaked}: units {sorted(units)} max abs err {worst:.3g}, "
+          f"relative to the row's largest output {worst_rel:.3g}", flush=True)
     del pc, kc, vc
     torch.cuda.empty_cache()
 
