@@ -814,7 +814,13 @@ constexpr int attend_occupancy()
     return D == 256 ? 1 : SCORE::OCC3 ? 3 : 2;
 }
 
-template <class SCORE, int BITS, int D, int VBITS, bool TWO>
+// SP (table scores, at most two query heads per unit, at least four value
+// groups): the value-product A operand of the unit's queries is built with its
+// (query, group) pairs spread over the four lanes that share a token pair
+// (lane kb takes groups kb, kb + 4, ...), instead of each lane building all
+// groups for its own two query slots, three of whose four lanes would hold
+// only absent queries.
+template <class SCORE, int BITS, int D, int VBITS, bool TWO, bool SP = false>
 __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NQ = SCORE::NQ;
@@ -885,8 +891,13 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
     }
     __syncthreads();        // block ids (and score tables), written by all threads
 
+    static_assert(!SP || (SCORE::TAB_BYTES > 0 && NGM >= 4), "spread A operand: table scores, >= 4 value groups");
+    constexpr int NSP = SP ? NGM / 4 : 1;         // groups per lane in the spread A operand
     float m_run[NQ], l_run[NQ];
     float zacc[NQ][NGM];
+    float zsp[2][NSP];                            // spread mode: zero-point sums of queries 0, 1
+#pragma unroll
+    for (int i = 0; i < NSP; ++i) zsp[0][i] = zsp[1][i] = 0.0f;
 #pragma unroll
     for (int sl = 0; sl < NQ; ++sl) {
         m_run[sl] = -INFINITY;
@@ -915,6 +926,11 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
         for (int part = 0; part < 2; ++part)
             awr[sl][part] = aslot(2 * SCORE::query(sl, kb) + part + 16 * (j / 4)) * 4 + (j % 4);
     const int ard = aslot(lane) * 4;
+    int awq[2][2];                                // spread mode: slots of queries 0 and 1
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) awq[q][part] = aslot(2 * q + part + 16 * (j / 4)) * 4 + (j % 4);
     // tr-read row of this lane in every value block: k-slot 8 kb + e holds the
     // token of slot order; lanes 2r, 2r + 1 address read row r, and row r lands
     // in half e(r) of the operand with e = {0, 2, 1, 3, 4, 6, 5, 7}
@@ -1015,6 +1031,15 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
                 for (int gg = 0; gg < NGM; ++gg) zacc[sl][gg] *= alpha[sl];
                 m_run[sl] = m_new[sl];
             }
+            if constexpr (SP) {
+                // queries 0 and 1 live in slots 0 and 1 of lane (j, 0)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float aq = __shfl(alpha[q], j);
+#pragma unroll
+                    for (int i = 0; i < NSP; ++i) zsp[q][i] *= aq;
+                }
+            }
             // value rows of this lane: queries 2 kb and 2 kb + 1
             const float a0 = SCORE::for_query(alpha, 2 * kb, j), a1 = SCORE::for_query(alpha, 2 * kb + 1, j);
             const v4f av = {a0, a0, a1, a1};
@@ -1036,6 +1061,32 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
 
         // ---- value-product A operand: p * scale as fp16 hi + lo in rows 2 q and
         // 2 q + 1, tokens j and 16 + j packed in dword j % 4 of k-block j / 4
+        if constexpr (SP) {
+            float pq[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                pq[q][0] = __shfl(p[q][0], j);
+                pq[q][1] = __shfl(p[q][1], j);
+            }
+#pragma unroll
+            for (int i = 0; i < NSP; ++i) {
+                const int gg = 4 * i + kb;
+                if (gg < NG) {
+                    const uint32_t r0 = pst[j * NGM + gg], r1 = pst[(16 + j) * NGM + gg];
+                    const float s0 = f16_bits_to_f32(r0 & 0xffffu), s1 = f16_bits_to_f32(r1 & 0xffffu);
+                    const float z0 = f16_bits_to_f32(r0 >> 16), z1 = f16_bits_to_f32(r1 >> 16);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const float w0 = pq[q][0] * s0, w1 = pq[q][1] * s1;
+                        zsp[q][i] = fmaf(pq[q][0], z0, fmaf(pq[q][1], z1, zsp[q][i]));
+                        const auto hi = __builtin_amdgcn_cvt_pkrtz(w0, w1);
+                        const auto lo = __builtin_amdgcn_cvt_pkrtz(w0 - static_cast<float>(hi[0]), w1 - static_cast<float>(hi[1]));
+                        afr[gg * 256 + awq[q][0]] = __builtin_bit_cast(uint32_t, hi);
+                        afr[gg * 256 + awq[q][1]] = __builtin_bit_cast(uint32_t, lo);
+                    }
+                }
+            }
+        } else {
         uint32_t pr[2][NGM];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -1060,6 +1111,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
                     afr[gg * 256 + awr[sl][1]] = __builtin_bit_cast(uint32_t, lo);
                 }
             }
+        }
         }
 
         wave_sync();        // the A operand is read by other lanes below
@@ -1134,11 +1186,23 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
             s_wm[wave][g] = m_run[sl];
             s_wl[wave][g] = l;
         }
+        if constexpr (!SP) {
 #pragma unroll
-        for (int gg = 0; gg < NGM; ++gg) {
-            const float z = row16_sum(zacc[sl][gg]);
-            if (j == 0) s_wz[wave][g][gg] = z;
+            for (int gg = 0; gg < NGM; ++gg) {
+                const float z = row16_sum(zacc[sl][gg]);
+                if (j == 0) s_wz[wave][g][gg] = z;
+            }
         }
+    }
+    if constexpr (SP) {
+        // group 4 i + kb of queries 0 and 1 is summed over the 16 lanes of row kb
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < NSP; ++i) {
+                const float z = row16_sum(zsp[q][i]);
+                if (j == 0) s_wz[wave][q][4 * i + kb] = z;
+            }
     }
     __syncthreads();        // every wave is done with its tile buffers
     float *wo = reinterpret_cast<float *>(smem);      // [4 waves][kMaxG][D]
@@ -1296,18 +1360,24 @@ __global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
     }
 }
 
-template <class SCORE, int BITS, int D, int VBITS>
+template <class SCORE, int BITS, int D, int VBITS, bool SP = false>
 hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kappa, int64_t chunk)
 {
     const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(a.mf.units));
     void *tok;
     prof_begin("tq_attend_splitk", stream, &tok);
     // 2-bit values in groups of 32: a 16-byte column block spans two groups
-    if (VBITS == 2 && a.group == 32)
-        hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, VBITS == 2>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
-    else
-        hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, false>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    hipError_t bad = hipSuccess;
+    if (VBITS == 2 && a.group == 32) {
+        if constexpr (SP)
+            bad = hipErrorInvalidValue;         // not dispatched: the spread mode excludes two-group value tiles
+        else
+            hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, VBITS == 2>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    } else {
+        hipLaunchKernelGGL((k_attend<SCORE, BITS, D, VBITS, false, SP>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    }
     prof_end(tok, stream);
+    if (bad != hipSuccess) return bad;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     prof_begin("tq_merge_splits", stream, &tok);
@@ -1327,6 +1397,11 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
 template <class SCORE, int BITS, int D>
 hipError_t launch_attend_v(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
+    if constexpr (SCORE::TAB_BYTES > 0 && D == 256) {
+        if (a.mf.gc <= 2 && a.d / a.group >= 4 && !(a.vbits == 2 && a.group == 32))
+            return a.vbits == 2 ? launch_attend_t<SCORE, BITS, D, 2, true>(a, s, kappa, chunk)
+                                : launch_attend_t<SCORE, BITS, D, 4, true>(a, s, kappa, chunk);
+    }
     return a.vbits == 2 ? launch_attend_t<SCORE, BITS, D, 2>(a, s, kappa, chunk)
                         : launch_attend_t<SCORE, BITS, D, 4>(a, s, kappa, chunk);
 }

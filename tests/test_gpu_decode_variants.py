@@ -31,6 +31,8 @@ CASES = [
     (128, 6, "dense", 1, 2, 4, 32, 333, "iid", "float32"),         # 6-bit keys (single-code table)
     (256, 7, "dense", 2, 4, 4, 32, 260, "scaled", "bfloat16"),     # 7-bit keys (largest format), d 256
     (256, 3, "dense", 1, 8, 2, 32, 500, "iid", "bfloat16"),        # 3-bit keys, d 256, two-group value tiles
+    (256, 5, "dense", 2, 2, 4, 64, 300, "scaled", "bfloat16"),     # GQA 1 at d 256: value operand spread over lanes
+    (256, 4, "hadamard", 1, 2, 2, 64, 333, "iid", "bfloat16"),     # GQA 2, 2-bit values g64: spread, four groups
     (64, 2, "dense", 1, 4, 2, 32, 260, "iid", "float32"),          # d 64 (general kernel)
 ]
 
