@@ -546,9 +546,16 @@ struct ScoreLut {
     static constexpr int LO_OFF = TAB1 + 16;
     static constexpr int CODE_TAB = PAIR ? LO_OFF + TAB1 : TAB1;
     static constexpr int SIGN_TAB = QJL ? 256 * 16 : 0;
-    static constexpr int AOP_BYTES = (QJL ? 2 : 1) * KS * 64 * 16;    // the unit's A operands, [part][KS][64 lanes]
+    // the unit's A operands, [part][KS][64 lanes]: in registers for the
+    // first-stage format at d = 128 (one part, 16 VGPRs), else in LDS, shared
+    // by the four waves and read per k-step (registers for both parts cost a
+    // workgroup per CU, which measured slower)
+    static constexpr bool AREG = D == 128 && !QJL;
+    static constexpr int NPART = QJL ? 2 : 1;
+    static constexpr int AOP_BYTES = AREG ? 0 : NPART * KS * 64 * 16;
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     float scc[2], scs[2];
+    v4i areg[AREG ? NPART : 1][AREG ? KS : 1];
     const unsigned char *tab;
     uint32_t copy4;            // byte offset of this lane's table copy within an entry
     int lane_;
@@ -589,11 +596,16 @@ struct ScoreLut {
             const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
             ts[i] = lo | (hi << 16);
         }
-        // the unit's A operands go to LDS (shared by the four waves; loaded per
-        // k-step rather than held in registers)
         const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * 2 * KS * 64;
-        v4i *adst = reinterpret_cast<v4i *>(lds + CODE_TAB + SIGN_TAB);
-        for (int i = tid; i < (QJL ? 2 : 1) * KS * 64; i += kThreads) adst[i] = src[i];
+        if constexpr (AREG) {
+#pragma unroll
+            for (int pt = 0; pt < NPART; ++pt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) areg[pt][ks] = src[(pt * KS + ks) * 64 + lane];
+        } else {
+            v4i *adst = reinterpret_cast<v4i *>(lds + CODE_TAB + SIGN_TAB);
+            for (int i = tid; i < NPART * KS * 64; i += kThreads) adst[i] = src[i];
+        }
         lane_ = lane;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
@@ -634,8 +646,14 @@ struct ScoreLut {
         for (int c = 0; c < 2; ++c) accc[c] = accs[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const v8h acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
-            const v8h asign = QJL ? __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]) : acode;
+            v8h acode, asign;
+            if constexpr (AREG) {
+                acode = __builtin_bit_cast(v8h, areg[0][ks]);
+                asign = __builtin_bit_cast(v8h, areg[NPART - 1][ks]);
+            } else {
+                acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
+                asign = QJL ? __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]) : acode;
+            }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 v4i bhi, blo;
