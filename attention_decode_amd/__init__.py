@@ -51,9 +51,9 @@ class Codebook:
         check(lib().tq_codebook_tables(self.handle, _dptr(c), _dptr(t)), "tq_codebook_tables")
         return c, t
 
-    def __del__(self):
-        if getattr(self, "handle", None) and L._lib is not None:
-            L._lib.tq_codebook_free(self.handle)
+    def __del__(self, _L=L):    # the loader module, held past interpreter shutdown
+        if getattr(self, "handle", None) and _L._lib is not None:
+            _L._lib.tq_codebook_free(self.handle)
             self.handle = None
 
 
@@ -65,9 +65,9 @@ class Rotation:
         check(lib().tq_make_rotation(seed, d, _ROT_KIND[kind], ctypes.byref(h)), "tq_make_rotation")
         self.handle, self.seed, self.d, self.kind = h, seed, d, kind
 
-    def __del__(self):
-        if getattr(self, "handle", None) and L._lib is not None:
-            L._lib.tq_rotation_free(self.handle)
+    def __del__(self, _L=L):    # the loader module, held past interpreter shutdown
+        if getattr(self, "handle", None) and _L._lib is not None:
+            _L._lib.tq_rotation_free(self.handle)
             self.handle = None
 
 

@@ -510,6 +510,10 @@ tq_status check_vcache(const tq_vcache &vc, const char *who)
 
 // Decode path and split count for a shape: the matrix-core path when the key
 // format allows it, else the general kernel.
+// the matrix-core kernels run the softmax in base 2: scores leave the score
+// stage multiplied by scale log2(e)
+constexpr float kLog2e = 1.4426950408889634f;
+
 struct DecodePlan {
     bool mfma = false;
     int gc = 0, nqc = 0, mt = 0, units = 0, splits = 0, steps = 0;
@@ -728,7 +732,14 @@ static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, tq_dt
 size_t tq_scores_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq)
 {
     if (!fmt || B < 1 || Hq < 1) return 0;
-    return align256(static_cast<size_t>(B) * Hq * (fmt->d + fmt->qjl_m) * sizeof(float));
+    const size_t rows = static_cast<size_t>(B) * Hq;
+    // the scalar kernel: the prepared queries; the matrix-core kernel also the
+    // score operands of every unit (units * row tiles <= B * Hq for any GQA
+    // group) and the per-query scales
+    const size_t scalar = align256(rows * (fmt->d + fmt->qjl_m) * sizeof(float));
+    const int steps = tq::mfma_score_steps(fmt->d, fmt->mse_bits, fmt->qjl_m);
+    const size_t mfma = scalar + align256(rows * steps * 64 * 16) + align256(rows * 4 * sizeof(float));
+    return mfma > scalar ? mfma : scalar;
 }
 
 tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq, int Hkv,
@@ -753,11 +764,33 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
     a.m = fmt->qjl_m;
     a.piT = fmt->rot->d_piT;
     a.sT = fmt->rot->d_sT;
+    a.spiT = fmt->rot->d_spiT;
+    a.pisum = fmt->rot->d_pisum;
+    a.spisum = fmt->rot->d_spisum;
+    a.sq_bound = fmt->rot->sq_bound;
     a.centroids = fmt->cb->d_centroids;
     a.kc = kc;
-    a.qprep = static_cast<float *>(ws);
     a.scores = scores;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const DecodePlan plan = decode_plan(fmt, B, Hq, Hkv, T, 0);
+    if (plan.mfma) {
+        // the matrix-core decode kernel with its value and softmax stages
+        // compiled out: same tiles, same score products, raw scores out
+        const AttendLayout L = attend_layout(fmt->d, fmt->qjl_m, B, Hq, plan);
+        char *base = static_cast<char *>(ws);
+        a.qprep = reinterpret_cast<float *>(base + L.qprep);
+        a.splits = plan.splits;
+        a.mf.gc = plan.gc;
+        a.mf.nqc = plan.nqc;
+        a.mf.mt = plan.mt;
+        a.mf.units = plan.units;
+        a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
+        a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
+        a.mf.lscale = 1.0f;
+        const hipError_t e = tq::launch_scores_mfma(a, s);
+        return e == hipSuccess ? TQ_OK : hip_fail(e, who);
+    }
+    a.qprep = static_cast<float *>(ws);
     hipError_t e = tq::launch_qprep(a, s);
     if (e == hipSuccess) e = tq::launch_scores(a, s);
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
@@ -913,6 +946,7 @@ tq_status tq_attend_decode_block(const tq_block_fmt *kfmt, const tq_val_fmt *vfm
     a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
     a.qaux = reinterpret_cast<float *>(base + L.qaux);
+    a.mf.lscale = a.scale * kLog2e;
     const hipError_t e = tq::launch_decode_block(a, s);
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
@@ -1029,6 +1063,7 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
     a.qaux = reinterpret_cast<float *>(base + L.qaux);
+    a.mf.lscale = a.scale * kLog2e;
     a.map = map;
     hipError_t e;
     if (plan.mfma) {

@@ -329,9 +329,9 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
 
 // ------------------------------------------------------------ attention
 // Softmax runs in base 2: scores leave the score stage multiplied by
-// scale log2(e), so every weight is one v_exp_f32 (2^x; -inf gives 0).  The
-// split maxima handed to the merge are in the same units.
-constexpr float kLog2e = 1.4426950408889634f;
+// scale log2(e) (the host's factor a.mf.lscale), so every weight is one
+// v_exp_f32 (2^x; -inf gives 0).  The split maxima handed to the merge are in
+// the same units.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-lane (one DPP row) reductions: xor 1, xor 2, half-row mirror, row mirror
@@ -462,7 +462,7 @@ struct ScoreBits {
             const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + (row0 + (ok ? g : 0)) * 4);
             // scores leave in log2 units of the softmax: scale log2(e) and the
             // QJL factor kappa are folded into the per-query terms
-            const float f = a.scale * kLog2e, fk = f * kappa;
+            const float f = a.mf.lscale, fk = f * kappa;
             fc[mt] = ok ? sc.x * f : 0.0f;
             cc[mt] = ok ? sc.y * f : 0.0f;
             fs[mt] = ok ? 2.0f * sc.z * fk : 0.0f;
@@ -613,7 +613,7 @@ struct ScoreLut {
             const bool ok = g < GC;
             const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + (row0 + (ok ? g : 0)) * 4);
             // scores leave in log2 units of the softmax (scale log2(e) folded in)
-            const float f = a.scale * kLog2e;
+            const float f = a.mf.lscale;
             scc[qq] = ok ? sc.x * f : 0.0f;
             scs[qq] = ok ? sc.y * f * kappa : 0.0f;
         }
@@ -771,7 +771,7 @@ struct ScoreQ {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int b = 0; b < NB; ++b) aop[mt][b] = src[(mt * NB + b) * 64 + lane];
-        const float f = a.scale * kLog2e;
+        const float f = a.mf.lscale;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int g = 4 * mt + kb;
@@ -838,7 +838,9 @@ constexpr int attend_occupancy()
 // (lane kb takes groups kb, kb + 4, ...), instead of each lane building all
 // groups for its own two query slots, three of whose four lanes would hold
 // only absent queries.
-template <class SCORE, int BITS, int D, int VBITS, bool TWO, bool SP = false>
+// SO: scores only (tq_scores): the same tiles and score products, the raw
+// scores written to a.scores [B, Hq, T]; no value loads, softmax or merge.
+template <class SCORE, int BITS, int D, int VBITS, bool TWO, bool SP = false, bool SO = false>
 __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NQ = SCORE::NQ;
@@ -983,25 +985,40 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
             const uint32_t t = static_cast<uint32_t>(16 * c + j < nv ? 16 * c + j : nv - 1);
             pf.kw.load(kbase, t, kb, c);
         }
-        const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
+        if constexpr (!SO) {
+            const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
-        for (int v = 0; v < VCL; ++v) {
-            const uint32_t i = static_cast<uint32_t>(lane + 64 * v);
-            const uint32_t tok = i / (VB / 16);
-            pf.vcode[v] = *at_bytes(vsrc, 16u * ((tok < static_cast<uint32_t>(nv) ? tok : nv - 1) * (VB / 16) + i % (VB / 16)));
-        }
-        const uint32_t *psrc = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
-        const uint32_t plim = static_cast<uint32_t>(nv * NG - 1);
+            for (int v = 0; v < VCL; ++v) {
+                const uint32_t i = static_cast<uint32_t>(lane + 64 * v);
+                const uint32_t tok = i / (VB / 16);
+                pf.vcode[v] = *at_bytes(vsrc, 16u * ((tok < static_cast<uint32_t>(nv) ? tok : nv - 1) * (VB / 16) + i % (VB / 16)));
+            }
+            const uint32_t *psrc = reinterpret_cast<const uint32_t *>(a.vc.params) + n0 * NG;
+            const uint32_t plim = static_cast<uint32_t>(nv * NG - 1);
 #pragma unroll
-        for (int k = 0; k < PD; ++k) {
-            const uint32_t idx = static_cast<uint32_t>(lane + 64 * k);
-            pf.par[k] = *at_bytes(psrc, 4u * (idx < plim ? idx : plim));
+            for (int k = 0; k < PD; ++k) {
+                const uint32_t idx = static_cast<uint32_t>(lane + 64 * k);
+                pf.par[k] = *at_bytes(psrc, 4u * (idx < plim ? idx : plim));
+            }
         }
     };
 
     auto compute = [&](int64_t tile0, const Prefetch &cur) {
         (void)tile0;
         const int nv = cur.nvalid;
+        if constexpr (SO) {
+            // raw scores (the host sets the folded score factor to 1)
+            float sc[2][NQ];
+            score.scores(cur.kw, sc);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int sl = 0; sl < NQ; ++sl) {
+                    const int q = SCORE::query(sl, kb);
+                    if (16 * c + j < nv && q < GC) a.scores[(row0 + q) * a.T + tile0 + 16 * c + j] = sc[c][sl];
+                }
+            return;
+        }
         wave_sync();        // the previous tile's LDS reads come before these writes
         // ---- value codes and (scale, zero) words of the tile into this wave's LDS
 #pragma unroll
@@ -1195,6 +1212,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
         }
     }
 
+    if constexpr (SO) return;
     // ---- merge the four waves: m, l, zero-point sums and value sums per query
 #pragma unroll
     for (int sl = 0; sl < NQ; ++sl) {
@@ -1518,7 +1536,45 @@ hipError_t launch_decode_block(const DecodeLaunch &a, hipStream_t stream)
     return a.d == 128 ? launch_attend_q<4, 128>(a, stream, chunk) : launch_attend_q<4, 256>(a, stream, chunk);
 }
 
-hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
+template <class SCORE, int BITS, int D>
+hipError_t launch_scores_t(const DecodeLaunch &a, hipStream_t stream, float kappa, int64_t chunk)
+{
+    const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(a.mf.units));
+    void *tok;
+    prof_begin("tq_scores_mfma", stream, &tok);
+    hipLaunchKernelGGL((k_attend<SCORE, BITS, D, 4, false, false, true>), grid, dim3(kThreads), 0, stream, a, kappa, chunk);
+    prof_end(tok, stream);
+    return hipGetLastError();
+}
+
+template <int BITS, int D, bool QJL>
+hipError_t launch_scores_b(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
+{
+    if constexpr (BITS <= 2) {
+        return a.mf.mt == 1 ? launch_scores_t<ScoreBits<BITS, D, 1, QJL>, BITS, D>(a, s, kappa, chunk)
+                            : launch_scores_t<ScoreBits<BITS, D, 2, QJL>, BITS, D>(a, s, kappa, chunk);
+    } else {
+        return launch_scores_t<ScoreLut<BITS, D, QJL>, BITS, D>(a, s, kappa, chunk);
+    }
+}
+
+template <int D, bool QJL>
+hipError_t launch_scores_d(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
+{
+    switch (a.bits) {
+    case 1: return launch_scores_b<1, D, QJL>(a, s, kappa, chunk);
+    case 2: return launch_scores_b<2, D, QJL>(a, s, kappa, chunk);
+    case 3: return launch_scores_b<3, D, QJL>(a, s, kappa, chunk);
+    case 4: return launch_scores_b<4, D, QJL>(a, s, kappa, chunk);
+    case 5: return launch_scores_b<5, D, QJL>(a, s, kappa, chunk);
+    case 6: return launch_scores_b<6, D, QJL>(a, s, kappa, chunk);
+    case 7: return launch_scores_b<7, D, QJL>(a, s, kappa, chunk);
+    }
+    return hipErrorInvalidValue;
+}
+
+// q-prep of the matrix-core kernels (score operands and per-query scales)
+static hipError_t qprep_mfma(const DecodeLaunch &a, hipStream_t stream)
 {
     void *tok;
     prof_begin("tq_qprep", stream, &tok);
@@ -1528,7 +1584,12 @@ hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
     case TQ_F16: launch_qprep_t<f16_t>(a, stream); break;
     }
     prof_end(tok, stream);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
+{
+    const hipError_t e = qprep_mfma(a, stream);
     if (e != hipSuccess) return e;
     const float kappa = a.m > 0 ? static_cast<float>(std::sqrt(M_PI / 2.0) / a.m) : 0.0f;
     const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
@@ -1538,6 +1599,20 @@ hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream)
                           : launch_attend_d<256, true>(a, stream, kappa, chunk);
     return a.d == 128 ? launch_attend_d<128, false>(a, stream, kappa, chunk)
                       : launch_attend_d<256, false>(a, stream, kappa, chunk);
+}
+
+hipError_t launch_scores_mfma(const DecodeLaunch &a, hipStream_t stream)
+{
+    const hipError_t e = qprep_mfma(a, stream);
+    if (e != hipSuccess) return e;
+    const float kappa = a.m > 0 ? static_cast<float>(std::sqrt(M_PI / 2.0) / a.m) : 0.0f;
+    const int64_t tiles = (a.T + kMfmaTile - 1) / kMfmaTile;
+    const int64_t chunk = ((tiles + a.splits - 1) / a.splits) * kMfmaTile;
+    if (a.m > 0)
+        return a.d == 128 ? launch_scores_d<128, true>(a, stream, kappa, chunk)
+                          : launch_scores_d<256, true>(a, stream, kappa, chunk);
+    return a.d == 128 ? launch_scores_d<128, false>(a, stream, kappa, chunk)
+                      : launch_scores_d<256, false>(a, stream, kappa, chunk);
 }
 
 }  // namespace tq

@@ -140,6 +140,7 @@ struct MfmaArgs {
     int units = 0;              // B * Hkv * nqc
     uint32_t *aops = nullptr;   // [units][mt][steps][64 lanes][4 dwords] score digit operands
     float *qscal = nullptr;     // [B, Hq, 4] fixed-point scales, constant terms
+    float lscale = 0.0f;        // factor on the scores: softmax scale * log2(e), or 1 for raw scores
 };
 
 struct DecodeLaunch {
@@ -187,6 +188,7 @@ int mfma_query_chunk(int G);
 int mfma_score_steps(int d, int bits, int m);
 int mfma_row_tiles(int bits, int gc);
 hipError_t launch_decode_mfma(const DecodeLaunch &a, hipStream_t stream);
+hipError_t launch_scores_mfma(const DecodeLaunch &a, hipStream_t stream);   // raw scores, tq_scores
 hipError_t launch_decode_block(const DecodeLaunch &a, hipStream_t stream);
 
 // ---- profiling hooks (api.cpp)
