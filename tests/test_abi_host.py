@@ -151,3 +151,13 @@ def test_split_policy_and_workspace():
     assert lib.tq_attend_splits(ctypes.byref(kf), 1, 5, 2, 100) == 0      # Hq % Hkv != 0
     ws = lib.tq_attend_workspace_bytes(ctypes.byref(kf), 2, 8, 2, 1000, 3)
     assert ws >= 2 * 8 * ((128 + 128) + 3 * 2 + 3 * 128) * 4
+    # tq_scores: the prepared queries, plus (matrix-core path) the score
+    # operands of every unit and the per-query scales, independent of Hkv
+    rows = 2 * 8
+    steps2 = 2 * (128 * 2 // 128) + 2 * (128 // 128)     # 2-bit codes and signs, per k-block quarter
+    need2 = rows * (128 + 128) * 4 + rows * steps2 * 1024 + rows * 16
+    assert lib.tq_scores_workspace_bytes(ctypes.byref(kf), 2, 8) >= need2
+    need3 = rows * (128 + 128) * 4 + rows * 2 * (128 // 32) * 1024 + rows * 16
+    assert lib.tq_scores_workspace_bytes(ctypes.byref(kf3), 2, 8) >= need3
+    assert lib.tq_scores_workspace_bytes(None, 2, 8) == 0
+    assert lib.tq_scores_workspace_bytes(ctypes.byref(kf), 0, 8) == 0
