@@ -4,8 +4,9 @@
 // steps 1-3 (y = Pi k/||k||, nearest-centroid codes, signs of S r with
 // r = y - c[idx]).
 //
-// One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 at d = 256)
-// and stages them in LDS first, in one round trip to HBM.  Both products run
+// One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 at d = 256,
+// and in launches too small to give every CU two workgroups) and stages them
+// in LDS first, in one round trip to HBM.  Both products run
 // as v_mfma_f32_16x16x32_bf16 with the keys / residuals as the B operand
 // (lane = key column) and the matrix as the A operand, so that every A
 // fragment read from L2 serves all keys of the workgroup; the four waves split
@@ -162,23 +163,23 @@ constexpr int key_stage_stride() { return D * static_cast<int>(sizeof(TIn)) + 16
 
 // the workgroup's raw keys (step 0-1) and the residual operands (steps 3-4)
 // share one region: the keys are dead before the first residual is written
-template <int D, typename TIn>
+template <int D, typename TIn, int KT>
 constexpr size_t key_union_bytes()
 {
-    const size_t rfrag = sizeof(uint4) * key_tiles<D>() * (D / 32) * 2 * 64;
-    const size_t stage = static_cast<size_t>(16 * key_tiles<D>()) * key_stage_stride<D, TIn>();
+    const size_t rfrag = sizeof(uint4) * KT * (D / 32) * 2 * 64;
+    const size_t stage = static_cast<size_t>(16 * KT) * key_stage_stride<D, TIn>();
     return rfrag > stage ? rfrag : stage;
 }
 
-template <int D, typename TIn, int BITS>
+template <int D, typename TIn, int BITS, int KT>
 constexpr size_t key_smem_bytes()
 {
-    constexpr size_t keys = 16 * key_tiles<D>();
-    return key_union_bytes<D, TIn>() + sizeof(uint32_t) * keys * (D * BITS / 32 + D / 32)
+    constexpr size_t keys = 16 * KT;
+    return key_union_bytes<D, TIn, KT>() + sizeof(uint32_t) * keys * (D * BITS / 32 + D / 32)
            + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
 }
 
-template <int D, typename TIn, int BITS>
+template <int D, typename TIn, int BITS, int KT>
 __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
     constexpr int NK = KeyTerms<TIn>::n;
     constexpr int L = 1 << BITS;
     constexpr int CW = D * BITS / 32, SWN = D / 32;
-    constexpr int kKT = key_tiles<D>();  // 16-key tiles of the workgroup
+    constexpr int kKT = KT;              // 16-key tiles of the workgroup
     constexpr int kKeys = 16 * kKT;      // keys of the workgroup
     constexpr int TPK = kThreads / kKeys;                              // threads per staged key
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
     KeySmem s;
     {
         unsigned char *p = smem_raw;
-        s.rfrag = reinterpret_cast<uint4 *>(p);   p += key_union_bytes<D, TIn>();
+        s.rfrag = reinterpret_cast<uint4 *>(p);   p += key_union_bytes<D, TIn, KT>();
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
         s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kThreads;
         s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
@@ -490,22 +491,40 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
     }
 }
 
-template <int D, typename TIn, int BITS>
-hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
+template <int D, typename TIn, int BITS, int KT>
+hipError_t launch_keys_k(const KeyLaunch &a, hipStream_t stream)
 {
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
-    constexpr size_t smem = key_smem_bytes<D, TIn, BITS>();
-    auto kern = k_compress_keys<D, TIn, BITS>;
+    constexpr size_t smem = key_smem_bytes<D, TIn, BITS, KT>();
+    auto kern = k_compress_keys<D, TIn, BITS, KT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    constexpr int keys = 16 * key_tiles<D>();
+    constexpr int keys = 16 * KT;
     const int64_t blocks = (n + keys - 1) / keys;
     void *tok;
     prof_begin("tq_compress_keys", stream, &tok);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, stream, a, n);
     prof_end(tok, stream);
     return hipGetLastError();
+}
+
+// Small launches (a few thousand keys, as in one decode step's append or a
+// short cache): with 64 keys per workgroup the grid would not reach two
+// workgroups per CU and each workgroup's dependent chain (staging, two
+// products, the code and residual work on one wave per SIMD) sets the time;
+// 32 keys per workgroup halves the per-wave work and doubles the grid.
+constexpr int64_t kSmallKeyGrid = 512;
+
+template <int D, typename TIn, int BITS>
+hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
+{
+    constexpr int KT = key_tiles<D>();
+    if constexpr (KT > 2) {
+        const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
+        if ((n + 16 * KT - 1) / (16 * KT) < kSmallKeyGrid) return launch_keys_k<D, TIn, BITS, 2>(a, stream);
+    }
+    return launch_keys_k<D, TIn, BITS, KT>(a, stream);
 }
 
 template <int D, typename TIn>
