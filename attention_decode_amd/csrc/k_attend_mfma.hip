@@ -974,8 +974,9 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
         // wave-uniform row of the tile: a tile never straddles a block (tiles
         // start at multiples of 32 tokens, blocks hold a multiple of 32)
         // (the clamp only guards LDS: the host keeps every split within kStageBlocks blocks)
+        // (flat and contiguous caches skip the LDS read: their one block is the sequence)
         const int bi = min(static_cast<int>(tc >> rshift) - blk0, kStageBlocks - 1);
-        const int blk = __builtin_amdgcn_readfirstlane(s_blk[bi]);
+        const int blk = paged ? __builtin_amdgcn_readfirstlane(s_blk[bi]) : static_cast<int>(seq);
         const int64_t n0 = blk >= 0 ? (static_cast<int64_t>(blk) * a.Hkv + kvh) * rstride
                                           + (static_cast<uint32_t>(tc) & rmask) : 0;
         pf.nvalid = blk >= 0 ? nv : 0;
