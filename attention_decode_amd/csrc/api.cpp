@@ -527,12 +527,15 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     const int G = Hq / Hkv;
     p.mfma = tq::mfma_decode_supported(fmt->d, fmt->mse_bits, G, 2, 32);
     p.gc = p.mfma ? tq::mfma_query_chunk(G) : tq::query_chunk(G);
+    const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;
+    const int64_t tiles = (T + tile - 1) / tile;
+    // a grid too small to give every CU a workgroup even at one tile per split
+    // (short caches with few KV heads): smaller query chunks, more units
+    while (p.mfma && p.gc > 1 && static_cast<int64_t>(B) * Hkv * (G / p.gc) * tiles < 256) p.gc /= 2;
     p.nqc = G / p.gc;
     p.mt = p.mfma ? tq::mfma_row_tiles(fmt->mse_bits, p.gc) : (p.gc + 3) / 4;
     p.units = B * Hkv * p.nqc;
     p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits, fmt->qjl_m) : 0;
-    const int tile = p.mfma ? tq::kMfmaTile : tq::kDecodeTile;
-    const int64_t tiles = (T + tile - 1) / tile;
     // workgroups per launch: about eight per CU for the d = 128 matrix-core
     // kernels (short enough splits that the last round is cheap), two for
     // d = 256 (one workgroup per CU at a time, and a longer set-up), four for

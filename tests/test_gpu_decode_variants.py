@@ -23,8 +23,8 @@ CASES = [
     (128, 1, "dense", 2, 8, 4, 64, 333, "iid", "float32"),         # 1-bit keys
     (256, 2, "dense", 1, 4, 4, 32, 700, "iid", "bfloat16"),        # d 256
     (256, 1, "hadamard", 2, 2, 2, 64, 129, "iid", "bfloat16"),     # GQA 1
-    (128, 2, "hadamard", 1, 6, 4, 128, 517, "iid", "bfloat16"),    # GQA 6 -> chunks of 2
-    (128, 2, "dense", 1, 16, 2, 128, 300, "scaled", "bfloat16"),   # GQA 16 -> two chunks of 8, one-hot regime
+    (128, 2, "hadamard", 1, 6, 4, 128, 517, "iid", "bfloat16"),    # GQA 6
+    (128, 2, "dense", 1, 16, 2, 128, 300, "scaled", "bfloat16"),   # GQA 16, one-hot regime
     (128, 3, "dense", 1, 8, 2, 64, 400, "iid", "bfloat16"),        # 3-bit keys (pair table)
     (128, 4, "dense", 2, 8, 4, 32, 450, "iid", "bfloat16"),        # 4-bit keys (pair table)
     (128, 5, "hadamard", 1, 4, 2, 64, 290, "iid", "bfloat16"),     # 5-bit keys (largest pair table)
@@ -34,6 +34,11 @@ CASES = [
     (256, 5, "dense", 2, 2, 4, 64, 300, "scaled", "bfloat16"),     # GQA 1 at d 256: value operand spread over lanes
     (256, 4, "hadamard", 1, 2, 2, 64, 333, "iid", "bfloat16"),     # GQA 2, 2-bit values g64: spread, four groups
     (64, 2, "dense", 1, 4, 2, 32, 260, "iid", "float32"),          # d 64 (general kernel)
+    # the decode plan splits a GQA group into smaller query chunks while the
+    # grid has fewer than 256 (unit, tile) pairs, so the short cases above run
+    # with small chunks; these two keep chunks of 8 (2 x 8 heads x 17 tiles)
+    (128, 2, "dense", 8, 64, 2, 32, 2100, "iid", "bfloat16"),      # bit-plane scores, two row tiles
+    (128, 3, "dense", 8, 64, 2, 64, 2100, "iid", "bfloat16"),      # table scores, eight queries per unit
 ]
 
 
