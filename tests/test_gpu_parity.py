@@ -108,6 +108,22 @@ def test_edge_cases(torch_cuda):
     out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc1, vc1, 1, 1)
     torch.cuda.synchronize()
     assert torch.all(out.cpu() == 0.75)
+    # scores of the three edge keys on the oracle's packed cache (the zero key
+    # scores exactly 0), and of a one-key cache (the same key, the same score)
+    ok = O.compress_keys(P.f64(k).reshape(-1, 128), w.k_bits, fm.orot)
+    ov = O.compress_values(P.f64(v).reshape(-1, 128), w.v_bits, w.group)
+    kco, _ = P.to_device_cache(ok, ov, (1, 1, 3), "cuda")
+    qn = P.f64(q.cpu())
+    osc, _ = P.oracle_units(fm, qn, ok, ov, (1, 1, 3), want_attn=False)
+    sc = tq.tq_scores(fm.kf, q, kco, 1, 3)
+    torch.cuda.synchronize()
+    P.check_scores(sc.double().cpu().numpy(), osc, qn, ok.knorm.reshape(1, 1, 3), 1)
+    assert torch.all(sc[:, :, 0] == 0)
+    kco1 = tq.KeyCache(kco.codes[:, :, 2:3].clone(), kco.signs[:, :, 2:3].clone(),
+                       kco.knorm[:, :, 2:3].clone(), kco.rnorm[:, :, 2:3].clone())
+    sc1 = tq.tq_scores(fm.kf, q, kco1, 1, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1[:, :, 0], sc[:, :, 2])
     # T = 0: zeros, and compression is a no-op
     out0 = torch.full((1, 4, 128), 7.0, device="cuda")
     tq.tq_attend_decode(fm.kf, fm.vf, q, kc1, vc1, 1, 0, out=out0)
