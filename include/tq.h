@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     TQ_OK = 0,
     TQ_EINVAL = 1,        /* an argument is out of range or inconsistent   */
-    TQ_EUNSUPPORTED = 2,  /* a valid combination this build does not serve  */
+    TQ_EUNSUPPORTED = 2,  /* a valid combination the library does not serve */
     TQ_EALIGN = 3,        /* a device pointer or stride is not 16-B aligned  */
     TQ_ENOMEM = 4,        /* handle allocation failed, or workspace too small*/
     TQ_EHIP = 5,          /* the HIP runtime reported an error                */
