@@ -1334,6 +1334,63 @@ __global__ __launch_bounds__(D) void k_merge_rows(DecodeLaunch a)
     a.out[row * D + c] = L > 0.0f ? o / L : 0.0f;
 }
 
+// Up to P * NB splits (P = kThreads / CH phases, NB splits each): one
+// workgroup per (query row, CH channels) holds every partial after one round
+// of loads.  The maximum needs no exchange of (m, l) pairs: each thread takes
+// the maximum of its own splits, the two phases of a wave meet in one lane
+// swap and the four waves in LDS; then each thread weights its own splits,
+// and the phases' sums of weighted values and of weights meet in LDS.
+template <int CH, int NB>
+__global__ __launch_bounds__(kThreads) void k_merge_batch(DecodeLaunch a)
+{
+    constexpr int P = kThreads / CH;
+    static_assert(P == 8 && CH == 32, "two phases per wave, four waves");
+    __shared__ float s_m[kThreads / 64];
+    __shared__ float s_o[P][CH];
+    __shared__ float s_l[P];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int64_t row = blockIdx.x;
+    const int S = a.splits, D = a.d;
+    const int ch = tid % CH, c = blockIdx.y * CH + ch, ph = tid / CH;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml + row * S * 2);
+    const float *pa = a.part_acc + row * S * D;
+    float v[NB];
+    float2 mv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int s = min(ph + P * u, S - 1);
+        v[u] = pa[static_cast<int64_t>(s) * D + c];
+        mv[u] = ml[s];
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+        if (ph + P * u < S && mv[u].y > 0.0f) m = fmaxf(m, mv[u].x);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane == 0) s_m[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const float e = (ph + P * u < S && mv[u].y > 0.0f) ? exp2_fast(mv[u].x - m) : 0.0f;
+        o = fmaf(e, v[u], o);
+        l = fmaf(e, mv[u].y, l);
+    }
+    s_o[ph][ch] = o;
+    if (ch == 0) s_l[ph] = l;
+    __syncthreads();
+    if (tid < CH) {
+        float O = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            O += s_o[q][tid];
+            L += s_l[q];
+        }
+        a.out[row * D + c] = L > 0.0f ? O / L : 0.0f;
+    }
+}
+
 template <int CH, int NB>
 __global__ __launch_bounds__(kThreads) void k_merge_splits(DecodeLaunch a)
 {
@@ -1424,8 +1481,8 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
     else if (S <= 4) hipLaunchKernelGGL((k_merge_rows<D, 4>), dim3(rows), dim3(D), 0, stream, a);
     else if (S <= 8) hipLaunchKernelGGL((k_merge_rows<D, 8>), dim3(rows), dim3(D), 0, stream, a);
     else if (S <= 16) hipLaunchKernelGGL((k_merge_rows<D, 16>), dim3(rows), dim3(D), 0, stream, a);
-    else if (S <= 32) hipLaunchKernelGGL((k_merge_splits<32, 4>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
-    else if (S <= 64) hipLaunchKernelGGL((k_merge_splits<32, 8>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 32) hipLaunchKernelGGL((k_merge_batch<32, 4>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 64) hipLaunchKernelGGL((k_merge_batch<32, 8>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((k_merge_splits<32, 16>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     prof_end(tok, stream);
     return hipGetLastError();
