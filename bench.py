@@ -17,7 +17,7 @@ fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage|q8_0|q4_0]
                     [--rotation dense|hadamard|hadamard2] [--layout flat|paged] [--block-size N]
-                    [--eager-decode] [--no-cpu-baseline]
+                    [--eager-decode] [--no-cpu-baseline] [--scores] [--calib-read]
 """
 from __future__ import annotations
 
@@ -65,6 +65,9 @@ def parse():
                     help="run only a plain 1 GiB device copy (to calibrate HBM byte counters)")
     ap.add_argument("--calib-read", action="store_true",
                     help="run only the streaming-read calibration program (the practical HBM read ceiling)")
+    ap.add_argument("--scores", action="store_true",
+                    help="time only tq_scores (query prep + raw scores [B, Hq, T]) over every layer's packed "
+                         "keys and print its own JSON line")
     return ap.parse_args()
 
 
@@ -147,6 +150,37 @@ class Layer:
         else:
             tq.tq_attend_decode_paged(self.kf, self.vf, self.q, self.kc, self.vc, w.Hkv, self.lay, out=self.out,
                                       ws=self.ws, n_splits=self.splits)
+
+
+def scores_only(w, layers, tq, torch, steps):
+    """tq_scores over every layer's packed keys: key planes read plus fp32
+    scores written, per second (HIP events around the timed layer passes)."""
+    for L in layers:
+        L.compress_keys(tq)
+    out = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(tq.tq_scores_workspace_bytes(layers[0].kf, w.B, w.Hq), 16), dtype=torch.uint8,
+                     device="cuda")
+
+    def one_pass():
+        for L in layers:
+            tq.tq_scores(L.kf, L.q, L.kc, w.Hkv, w.T, out=out, ws=ws)
+
+    for _ in range(3):
+        one_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    key_bytes = w.layers * w.B * w.Hkv * w.T * w.key_bytes()
+    score_bytes = w.layers * w.B * w.Hq * w.T * 4
+    return {"mode": "scores", "workload": w.name, "layers": w.layers, "steps": steps,
+            "tq_scores_ms_per_step": round(ms, 4), "key_bytes": key_bytes, "score_bytes": score_bytes,
+            "GBps": round((key_bytes + score_bytes) / (ms * 1e-3) / 1e9, 1),
+            "hbm_fraction": round((key_bytes + score_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def measured_traffic(w):
@@ -273,8 +307,13 @@ def main():
         sys.exit("--block-size must be a power of two, at least 32")
     if paged:
         w = replace(w, name=f"{w.name}-paged{paged}")
+    if args.scores and (w.block_bits or paged):
+        sys.exit("--scores times tq_scores on the flat TurboQuant key planes only")
     layers = [Layer(w, l, tq, W, torch, paged) for l in range(w.layers)]
     torch.cuda.synchronize()
+    if args.scores:
+        print(json.dumps(scores_only(w, layers, tq, torch, args.steps)), flush=True)
+        return
     stream = torch.cuda.current_stream()
 
     def step(ev=None, eager=False):
