@@ -1,7 +1,7 @@
 """Decode launches replayed from a captured HIP graph give the eager results.
 
-The per-layer decode (q-prep, split-K attention, split merge) is captured once
-for several layers and replayed three times; before each replay the queries
+The per-layer decode (q-prep, split-K attention, split merge), or tq_scores,
+is captured once for several layers and replayed three times; before each replay the queries
 are rewritten in place and the eager launches run on the same inputs, so each
 replay must reproduce the eager outputs bit for bit (same kernels, same launch
 configuration, no state kept between calls)."""
@@ -49,7 +49,12 @@ def _layers(torch, kind):
             cb = tq.tq_build_codebook(w.d, w.k_bits)
             kf = tq.KeyFormat(w.d, w.k_bits, cb, rot)
             kc = tq.KeyCache(pc["codes"], pc["signs"], pc["knorm"], pc["rnorm"])
-            if kind == "flat":
+            if kind == "scores":
+                o = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device="cuda")
+                ws = torch.empty(tq.tq_scores_workspace_bytes(kf, w.B, w.Hq), dtype=torch.uint8, device="cuda")
+                call = (lambda kf=kf, q=q, kc=kc, o=o, ws=ws:
+                        tq.tq_scores(kf, q, kc, w.Hkv, w.T, out=o, ws=ws))
+            elif kind == "flat":
                 ws = torch.empty(tq.tq_attend_workspace_bytes(kf, w.B, w.Hq, w.Hkv, w.T), dtype=torch.uint8,
                                  device="cuda")
                 call = (lambda kf=kf, vf=vf, q=q, kc=kc, vc=vc, o=o, ws=ws:
@@ -69,7 +74,7 @@ def _layers(torch, kind):
     return w, out
 
 
-@pytest.mark.parametrize("kind", ["flat", "layout", "q8_0"])
+@pytest.mark.parametrize("kind", ["flat", "layout", "q8_0", "scores"])
 def test_graph_replay_matches_eager(torch_cuda, kind):
     torch = torch_cuda
     w, layers = _layers(torch, kind)
