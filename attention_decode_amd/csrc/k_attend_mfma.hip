@@ -304,24 +304,35 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
         }
     } else {
         // fp16 hi + lo rows (2 g, 2 g + 1) of the A operands of
-        // v_mfma_f32_16x16x32_f16: aops[unit][part][ks][lane][4 dwords], k-block
-        // kb of step ks holding coordinates kb D/4 + 8 ks + e
+        // v_mfma_f32_16x16x32_f16, aops[unit][step][lane][4 dwords] with the
+        // code steps first, then the sign steps.  Sign step ks (and the code
+        // step of single-code tables): k-block kb holds coordinates
+        // kb D/4 + 8 ks + e.  Pair tables (up to 5 bits) take two code steps
+        // per ks, m = 0, 1, over coordinates kb D/4 + 8 ks + 4 m + i, each
+        // slot pair repeated for the hi and lo halves of the centroid pair
+        // that the B operand holds: slots (x0, x1, x0, x1, x2, x3, x2, x3).
         constexpr int KS = D / 32;
-        uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * 2 * KS * 256;
-        for (int w = tid; w < KS * 64; w += kThreads) {
-            const int r = w % 4, row = (w / 4) % 16, ks = w / 64;
+        const bool pair = a.bits <= 5;
+        const int code_steps = pair ? 2 * KS : KS;
+        const int nsteps = (part ? KS : code_steps);
+        const int step0 = part ? code_steps : 0;
+        uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * (code_steps + KS) * 256;
+        for (int w = tid; w < nsteps * 64; w += kThreads) {
+            const int r = w % 4, row = (w / 4) % 16, st = w / 64;
             const int g = row / 2, lo = row % 2;
+            // first coordinate of this dword's slot pair
+            const int c0 = (part || !pair) ? 8 * st + 2 * r : 8 * (st / 2) + 4 * (st % 2) + 2 * (r / 2);
             uint32_t dw = 0u;
             if (g < GQ) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float x = ldexpf(xv[g][8 * ks + 2 * r + h], s_f[g][part]);
+                    const float x = ldexpf(xv[g][c0 + h], s_f[g][part]);
                     const _Float16 xh = static_cast<_Float16>(x);
                     const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
                     dw |= bits << (16 * h);
                 }
             }
-            out[((part * KS + ks) * 64 + 16 * kb + row) * 4 + r] = dw;
+            out[((step0 + st) * 64 + 16 * kb + row) * 4 + r] = dw;
         }
     }
 }
@@ -517,47 +528,46 @@ struct ScoreBits {
     }
 };
 
-// Table scores (3-8 bit keys).  The key's centroids are looked up in LDS as
-// fp16 hi + lo (c * 2^kCodeExp; two coordinates per lookup up to 5 bits, so
-// each lookup yields one packed dword of the hi and one of the lo operand),
-// its sign bytes as eight fp16 +-1; the products run on
-// v_mfma_f32_16x16x32_f16 with rows (query, hi/lo): lane (j, kb) scores
-// queries 2 kb and 2 kb + 1.
-template <int BITS, int D, bool QJL>
+// Table scores (3-7 bit keys).  The key's centroids are looked up in LDS as
+// fp16 hi + lo (c * 2^kCodeExp), its sign bytes as eight fp16 +-1; the
+// products run on v_mfma_f32_16x16x32_f16 with rows (query, hi/lo part of the
+// query): lane (j, kb) scores queries 2 kb and 2 kb + 1.  Up to 5 bits one
+// lookup serves two coordinates: an 8-byte entry (hi pair, lo pair) read with
+// one ds_read_b64, two entries making the lane's B quad (hi01, lo01, hi23,
+// lo23) against A slots (x0, x1, x0, x1, x2, x3, x2, x3), so the hi and lo
+// halves meet in one product over 16 coordinates.  From 6 bits one 4-byte
+// entry (hi | lo << 16) per coordinate, repacked into a hi and a lo operand.
+template <int BITS, int D, bool QJL, int TB = 8192>
 struct ScoreLut {
     using KW = KeyWords<BITS, D, QJL>;
     static constexpr int NQ = 2;
     static constexpr bool OCC3 = true;
     static constexpr int KS = D / 32;
     static constexpr bool PAIR = BITS <= 5;
-    // pair mode: a hi table and a lo table of packed (coordinate 2p, 2p + 1)
-    // fp16 pairs, so each lookup lands in its operand register; single mode:
-    // one table of (hi | lo << 16) per code
     static constexpr int NENT = PAIR ? (1 << (2 * BITS)) : (1 << BITS);
-    static constexpr int NTAB = PAIR ? 2 : 1;
-    // copies of the code tables, interleaved entry-major so that lane l reads
-    // copy l % COPIES: with 64 copies every lane owns its bank (no conflicts)
-    static constexpr int COPIES_RAW = 8192 / (NENT * 4 * NTAB);
-    static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 4 ? 4 : 1));
-    static constexpr int TAB1 = NENT * 4 * COPIES;                     // bytes of one code table
-    // the lo table starts 16 bytes past a multiple of 256 so that a hi and a lo
-    // lookup cannot be fused into one two-address read (which would land both
-    // in adjacent registers and cost moves into the two operand quads)
-    static constexpr int LO_OFF = TAB1 + 16;
-    static constexpr int CODE_TAB = PAIR ? LO_OFF + TAB1 : TAB1;
+    static constexpr int EBYTES = PAIR ? 8 : 4;                       // bytes per table entry
+    // copies of the code table within TB bytes, interleaved entry-major so
+    // that lane l reads copy l % COPIES (fewer lanes per bank).  The budget is
+    // 8 KB, and 4 KB at d = 128 with 4-bit values, whose larger value staging
+    // would otherwise leave room for two workgroups per CU instead of three.
+    static constexpr int COPIES_RAW = TB / (NENT * EBYTES);
+    static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 8 ? 8 : (COPIES_RAW >= 4 ? 4 : 1)));
+    static constexpr int CODE_TAB = NENT * EBYTES * COPIES;
     static constexpr int SIGN_TAB = QJL ? 256 * 16 : 0;
-    // the unit's A operands, [part][KS][64 lanes]: in registers for the
-    // first-stage format at d = 128 (one part, 16 VGPRs), else in LDS, shared
-    // by the four waves and read per k-step (registers for both parts cost a
-    // workgroup per CU, which measured slower)
+    // the unit's A operands, [step][64 lanes] with CODE_STEPS code steps then
+    // KS sign steps: in registers for the first-stage format at d = 128 (no
+    // sign steps), else in LDS, shared by the four waves and read per k-step
+    // (registers for both parts cost a workgroup per CU, which measured slower)
+    static constexpr int CODE_STEPS = PAIR ? 2 * KS : KS;
+    static constexpr int NSTEP = CODE_STEPS + KS;                     // per unit in the workspace
     static constexpr bool AREG = D == 128 && !QJL;
-    static constexpr int NPART = QJL ? 2 : 1;
-    static constexpr int AOP_BYTES = AREG ? 0 : NPART * KS * 64 * 16;
+    static constexpr int LSTEP = CODE_STEPS + (QJL ? KS : 0);         // steps kept in LDS
+    static constexpr int AOP_BYTES = AREG ? 0 : LSTEP * 64 * 16;
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     float scc[2], scs[2];
-    v4i areg[AREG ? NPART : 1][AREG ? KS : 1];
+    v4i areg[AREG ? CODE_STEPS : 1];
     const unsigned char *tab;
-    uint32_t copy4;            // byte offset of this lane's table copy within an entry
+    uint32_t copyb;            // byte offset of this lane's table copy within an entry
     int lane_;
 
     __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
@@ -569,17 +579,17 @@ struct ScoreLut {
     __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, float kappa, unsigned char *lds)
     {
         tab = lds;
-        copy4 = 4u * static_cast<uint32_t>(lane % COPIES);
+        copyb = static_cast<uint32_t>(EBYTES * (lane % COPIES));
         const int tid = threadIdx.x;
         constexpr int L = 1 << BITS;
         if (PAIR) {
-            uint32_t *th = reinterpret_cast<uint32_t *>(lds), *tl = reinterpret_cast<uint32_t *>(lds + LO_OFF);
+            uint2 *t2 = reinterpret_cast<uint2 *>(lds);
             for (int x = tid; x < L * L * COPIES; x += kThreads) {
                 const int i = x / COPIES;
                 const float c0 = ldexpf(a.centroids[i & (L - 1)], kCodeExp), c1 = ldexpf(a.centroids[i >> BITS], kCodeExp);
                 const _Float16 h0 = static_cast<_Float16>(c0), h1 = static_cast<_Float16>(c1);
-                th[x] = __builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-                tl[x] = f16_rn_bits(c0 - static_cast<float>(h0)) | (f16_rn_bits(c1 - static_cast<float>(h1)) << 16);
+                t2[x] = make_uint2(__builtin_bit_cast(uint16_t, h0) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16),
+                                   f16_rn_bits(c0 - static_cast<float>(h0)) | (f16_rn_bits(c1 - static_cast<float>(h1)) << 16));
             }
         } else {
             uint32_t *t1 = reinterpret_cast<uint32_t *>(lds);
@@ -596,15 +606,13 @@ struct ScoreLut {
             const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
             ts[i] = lo | (hi << 16);
         }
-        const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * 2 * KS * 64;
+        const v4i *src = reinterpret_cast<const v4i *>(a.mf.aops) + static_cast<int64_t>(unit) * NSTEP * 64;
         if constexpr (AREG) {
 #pragma unroll
-            for (int pt = 0; pt < NPART; ++pt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) areg[pt][ks] = src[(pt * KS + ks) * 64 + lane];
+            for (int st = 0; st < CODE_STEPS; ++st) areg[st] = src[st * 64 + lane];
         } else {
             v4i *adst = reinterpret_cast<v4i *>(lds + CODE_TAB + SIGN_TAB);
-            for (int i = tid; i < NPART * KS * 64; i += kThreads) adst[i] = src[i];
+            for (int i = tid; i < LSTEP * 64; i += kThreads) adst[i] = src[i];
         }
         lane_ = lane;
 #pragma unroll
@@ -623,7 +631,7 @@ struct ScoreLut {
     // lane's word array (o constant after unrolling): the field lands at bit
     // ESH = log2(entry stride) by one shift, so with the copy bits or-ed in the
     // offset costs a shift and an and-or
-    static constexpr int ESH = __builtin_ctz(4 * COPIES);
+    static constexpr int ESH = __builtin_ctz(EBYTES * COPIES);
     template <int W, int NW>
     __device__ uint32_t entry(const uint32_t (&w)[NW], int o) const
     {
@@ -632,13 +640,15 @@ struct ScoreLut {
         uint32_t x;
         if (s + W <= 32 || i + 1 >= NW) x = s >= ESH ? (w[i] >> (s - ESH)) : (w[i] << (ESH - s));
         else x = __builtin_amdgcn_alignbit(w[i + 1], w[i], s) << ESH;
-        return (x & mask) | copy4;
+        uint32_t off = (x & mask) | copyb;
+        // keeps the offset one v_and_or (the table base then folds into the
+        // LDS instruction's offset field instead of a separate add)
+        asm("" : "+v"(off));
+        return off;
     }
 
     __device__ void scores(const KW &kw, float (&sc)[2][2]) const
     {
-        const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
-        const uint32_t *tl = reinterpret_cast<const uint32_t *>(tab + LO_OFF);
         const v4i *ts = reinterpret_cast<const v4i *>(tab + CODE_TAB);
         const v4i *aop = reinterpret_cast<const v4i *>(tab + CODE_TAB + SIGN_TAB);
         v4f accc[2], accs[2];
@@ -646,33 +656,47 @@ struct ScoreLut {
         for (int c = 0; c < 2; ++c) accc[c] = accs[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            v8h acode, asign;
-            if constexpr (AREG) {
-                acode = __builtin_bit_cast(v8h, areg[0][ks]);
-                asign = __builtin_bit_cast(v8h, areg[NPART - 1][ks]);
+            if constexpr (PAIR) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int st = 2 * ks + m;
+                    v8h acode;
+                    if constexpr (AREG) acode = __builtin_bit_cast(v8h, areg[st]);
+                    else acode = __builtin_bit_cast(v8h, aop[st * 64 + lane_]);
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const uint2 t0 = *reinterpret_cast<const uint2 *>(
+                            tab + entry<2 * BITS>(kw.cw[c], 8 * BITS * ks + 2 * BITS * (2 * m)));
+                        const uint2 t1 = *reinterpret_cast<const uint2 *>(
+                            tab + entry<2 * BITS>(kw.cw[c], 8 * BITS * ks + 2 * BITS * (2 * m + 1)));
+                        const v4i b = {static_cast<int>(t0.x), static_cast<int>(t0.y), static_cast<int>(t1.x),
+                                       static_cast<int>(t1.y)};
+                        accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, b), accc[c], 0, 0, 0);
+                    }
+                }
             } else {
-                acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
-                asign = QJL ? __builtin_bit_cast(v8h, aop[(KS + ks) * 64 + lane_]) : acode;
-            }
+                v8h acode;
+                if constexpr (AREG) acode = __builtin_bit_cast(v8h, areg[ks]);
+                else acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
+                const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                v4i bhi, blo;
+                for (int c = 0; c < 2; ++c) {
+                    v4i bhi, blo;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    if (PAIR) {
-                        const uint32_t e = entry<2 * BITS>(kw.cw[c], 8 * BITS * ks + 2 * BITS * p);
-                        bhi[p] = static_cast<int>(*at_bytes(t1, e));
-                        blo[p] = static_cast<int>(*at_bytes(tl, e));
-                    } else {
+                    for (int p = 0; p < 4; ++p) {
                         const uint32_t e0 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p)));
                         const uint32_t e1 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1)));
                         bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
                         blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
                     }
+                    accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, bhi), accc[c], 0, 0, 0);
+                    accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, blo), accc[c], 0, 0, 0);
                 }
-                accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, bhi), accc[c], 0, 0, 0);
-                accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, blo), accc[c], 0, 0, 0);
-                if constexpr (QJL) {
+            }
+            if constexpr (QJL) {
+                const v8h asign = __builtin_bit_cast(v8h, aop[(CODE_STEPS + ks) * 64 + lane_]);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
                     const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
                     accs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accs[c], 0, 0, 0);
                 }
@@ -1507,6 +1531,8 @@ hipError_t launch_attend_b(const DecodeLaunch &a, hipStream_t s, float kappa, in
         return a.mf.mt == 1 ? launch_attend_v<ScoreBits<BITS, D, 1, QJL>, BITS, D>(a, s, kappa, chunk)
                             : launch_attend_v<ScoreBits<BITS, D, 2, QJL>, BITS, D>(a, s, kappa, chunk);
     } else {
+        if constexpr (D == 128)
+            if (a.vbits == 4) return launch_attend_t<ScoreLut<BITS, D, QJL, 4096>, BITS, D, 4>(a, s, kappa, chunk);
         return launch_attend_v<ScoreLut<BITS, D, QJL>, BITS, D>(a, s, kappa, chunk);
     }
 }
@@ -1566,7 +1592,10 @@ int mfma_row_tiles(int bits, int gc) { return bits <= 2 ? (gc + 3) / 4 : 1; }
 
 int mfma_score_steps(int d, int bits, int m)
 {
-    return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0) : 2 * (d / 32);
+    // table scores: code steps (two per 32 coordinates for pair tables) and
+    // the sign steps, reserved whether or not the format has them
+    return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0)
+                     : (bits <= 5 ? 3 : 2) * (d / 32);
 }
 
 template <int QB, int D>
