@@ -305,28 +305,30 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
     } else {
         // fp16 hi + lo rows (2 g, 2 g + 1) of the A operands of
         // v_mfma_f32_16x16x32_f16, aops[unit][step][lane][4 dwords] with the
-        // code steps first, then the sign steps.  Sign step ks (and the code
-        // step of single-code tables): k-block kb holds coordinates
-        // kb D/4 + 8 ks + e.  Pair tables (up to 5 bits) take two code steps
-        // per ks, m = 0, 1, over coordinates kb D/4 + 8 ks + 4 m + i, each
-        // slot pair repeated for the hi and lo halves of the centroid pair
-        // that the B operand holds: slots (x0, x1, x0, x1, x2, x3, x2, x3).
+        // code steps first, then the sign steps.  Sign step ks: k-block kb
+        // holds coordinates kb D/4 + 8 ks + e.  Code steps: two per ks, m =
+        // 0, 1, over coordinates kb D/4 + 8 ks + 4 m + i, each coordinate
+        // repeated for the hi and lo halves of its centroid in the B operand:
+        // slots (x0, x1, x0, x1, x2, x3, x2, x3) against pair entries (up to
+        // 5 bits), (x0, x0, x1, x1, x2, x2, x3, x3) against single entries.
         constexpr int KS = D / 32;
         const bool pair = a.bits <= 5;
-        const int code_steps = pair ? 2 * KS : KS;
+        const int code_steps = 2 * KS;
         const int nsteps = (part ? KS : code_steps);
         const int step0 = part ? code_steps : 0;
         uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * (code_steps + KS) * 256;
         for (int w = tid; w < nsteps * 64; w += kThreads) {
             const int r = w % 4, row = (w / 4) % 16, st = w / 64;
             const int g = row / 2, lo = row % 2;
-            // first coordinate of this dword's slot pair
-            const int c0 = (part || !pair) ? 8 * st + 2 * r : 8 * (st / 2) + 4 * (st % 2) + 2 * (r / 2);
+            // coordinates of this dword's two slots: c0 + h * dc
+            const int base = 8 * (st / 2) + 4 * (st % 2);
+            const int c0 = part ? 8 * st + 2 * r : (pair ? base + 2 * (r / 2) : base + r);
+            const int dc = (part || pair) ? 1 : 0;
             uint32_t dw = 0u;
             if (g < GQ) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float x = ldexpf(xv[g][c0 + h], s_f[g][part]);
+                    const float x = ldexpf(xv[g][c0 + h * dc], s_f[g][part]);
                     const _Float16 xh = static_cast<_Float16>(x);
                     const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
                     dw |= bits << (16 * h);
@@ -531,12 +533,13 @@ struct ScoreBits {
 // Table scores (3-7 bit keys).  The key's centroids are looked up in LDS as
 // fp16 hi + lo (c * 2^kCodeExp), its sign bytes as eight fp16 +-1; the
 // products run on v_mfma_f32_16x16x32_f16 with rows (query, hi/lo part of the
-// query): lane (j, kb) scores queries 2 kb and 2 kb + 1.  Up to 5 bits one
-// lookup serves two coordinates: an 8-byte entry (hi pair, lo pair) read with
-// one ds_read_b64, two entries making the lane's B quad (hi01, lo01, hi23,
-// lo23) against A slots (x0, x1, x0, x1, x2, x3, x2, x3), so the hi and lo
-// halves meet in one product over 16 coordinates.  From 6 bits one 4-byte
-// entry (hi | lo << 16) per coordinate, repacked into a hi and a lo operand.
+// query): lane (j, kb) scores queries 2 kb and 2 kb + 1.  The hi and lo
+// halves of the centroids share one product over 16 coordinates: up to 5 bits
+// an 8-byte entry (hi pair, lo pair) per two coordinates, read with one
+// ds_read_b64, two entries making the lane's B quad (hi01, lo01, hi23, lo23)
+// against A slots (x0, x1, x0, x1, x2, x3, x2, x3); from 6 bits a 4-byte
+// entry (hi | lo << 16) per coordinate, four making the quad against A slots
+// (x0, x0, x1, x1, x2, x2, x3, x3).
 template <int BITS, int D, bool QJL, int TB = 8192>
 struct ScoreLut {
     using KW = KeyWords<BITS, D, QJL>;
@@ -558,7 +561,7 @@ struct ScoreLut {
     // KS sign steps: in registers for the first-stage format at d = 128 (no
     // sign steps), else in LDS, shared by the four waves and read per k-step
     // (registers for both parts cost a workgroup per CU, which measured slower)
-    static constexpr int CODE_STEPS = PAIR ? 2 * KS : KS;
+    static constexpr int CODE_STEPS = 2 * KS;
     static constexpr int NSTEP = CODE_STEPS + KS;                     // per unit in the workspace
     static constexpr bool AREG = D == 128 && !QJL;
     static constexpr int LSTEP = CODE_STEPS + (QJL ? KS : 0);         // steps kept in LDS
@@ -675,22 +678,21 @@ struct ScoreLut {
                     }
                 }
             } else {
-                v8h acode;
-                if constexpr (AREG) acode = __builtin_bit_cast(v8h, areg[ks]);
-                else acode = __builtin_bit_cast(v8h, aop[ks * 64 + lane_]);
                 const uint32_t *t1 = reinterpret_cast<const uint32_t *>(tab);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    v4i bhi, blo;
+                for (int m = 0; m < 2; ++m) {
+                    const int st = 2 * ks + m;
+                    v8h acode;
+                    if constexpr (AREG) acode = __builtin_bit_cast(v8h, areg[st]);
+                    else acode = __builtin_bit_cast(v8h, aop[st * 64 + lane_]);
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t e0 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p)));
-                        const uint32_t e1 = *at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (2 * p + 1)));
-                        bhi[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x05040100u));
-                        blo[p] = static_cast<int>(__builtin_amdgcn_perm(e1, e0, 0x07060302u));
+                    for (int c = 0; c < 2; ++c) {
+                        v4i b;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            b[i] = static_cast<int>(*at_bytes(t1, entry<BITS>(kw.cw[c], 8 * BITS * ks + BITS * (4 * m + i))));
+                        accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, b), accc[c], 0, 0, 0);
                     }
-                    accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, bhi), accc[c], 0, 0, 0);
-                    accc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acode, __builtin_bit_cast(v8h, blo), accc[c], 0, 0, 0);
                 }
             }
             if constexpr (QJL) {
@@ -1592,10 +1594,9 @@ int mfma_row_tiles(int bits, int gc) { return bits <= 2 ? (gc + 3) / 4 : 1; }
 
 int mfma_score_steps(int d, int bits, int m)
 {
-    // table scores: code steps (two per 32 coordinates for pair tables) and
-    // the sign steps, reserved whether or not the format has them
-    return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0)
-                     : (bits <= 5 ? 3 : 2) * (d / 32);
+    // table scores: two code steps per 32 coordinates and one sign step,
+    // the sign steps reserved whether or not the format has them
+    return bits <= 2 ? 2 * code_dwords(d, bits) + (m > 0 ? 2 * sign_dwords(d) : 0) : 3 * (d / 32);
 }
 
 template <int QB, int D>
