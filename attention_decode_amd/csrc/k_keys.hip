@@ -40,10 +40,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-// 16-key tiles per workgroup: four (64 keys) up to d = 128; two at d = 256,
-// where the residual operands of 64 keys would leave room in LDS for a
-// single workgroup per CU
-template <int D> constexpr int key_tiles() { return D >= 256 ? 2 : 4; }
+// 16-key tiles per workgroup: four (64 keys), except fp32 keys at d = 256
+// (two), whose staged rows would leave room in LDS for one workgroup per CU
+template <int D, typename TIn> constexpr int key_tiles() { return D >= 256 ? (sizeof(TIn) == 2 ? 4 : 2) : 4; }
+// 16-key tiles whose residual operands share LDS at a time: at d = 256 with
+// 2-byte inputs a workgroup takes 64 keys and runs the residual and sign steps
+// in two passes of 32 (two workgroups per CU; every A fragment of Pi then
+// serves 64 keys instead of 32)
+template <int D, typename TIn, int KT> constexpr int key_pass_tiles() { return (D >= 256 && KT == 4) ? 2 : KT; }
+template <int D, typename TIn, int KT> constexpr int key_occupancy() { return key_pass_tiles<D, TIn, KT>() < KT ? 2 : 3; }
 
 // bf16 terms that represent one input element exactly
 template <typename TIn> struct KeyTerms;
@@ -166,7 +171,7 @@ constexpr int key_stage_stride() { return D * static_cast<int>(sizeof(TIn)) + 16
 template <int D, typename TIn, int KT>
 constexpr size_t key_union_bytes()
 {
-    const size_t rfrag = sizeof(uint4) * KT * (D / 32) * 2 * 64;
+    const size_t rfrag = sizeof(uint4) * key_pass_tiles<D, TIn, KT>() * (D / 32) * 2 * 64;
     const size_t stage = static_cast<size_t>(16 * KT) * key_stage_stride<D, TIn>();
     return rfrag > stage ? rfrag : stage;
 }
@@ -180,7 +185,7 @@ constexpr size_t key_smem_bytes()
 }
 
 template <int D, typename TIn, int BITS, int KT>
-__global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int64_t n_total)
+__global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
@@ -189,6 +194,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
     constexpr int CW = D * BITS / 32, SWN = D / 32;
     constexpr int kKT = KT;              // 16-key tiles of the workgroup
     constexpr int kKeys = 16 * kKT;      // keys of the workgroup
+    constexpr int KR = key_pass_tiles<D, TIn, KT>();   // key tiles per residual / sign pass
     constexpr int TPK = kThreads / kKeys;                              // threads per staged key
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup
@@ -340,9 +346,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
         for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
     }
 
-    // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
+    const bool qjl = a.m > 0;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
+    for (int kt0 = 0; kt0 < kKT; kt0 += KR) {
+    // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
+    // (key tiles kt0 .. kt0 + KR - 1 of this pass)
+#pragma unroll
+    for (int kt = kt0; kt < kt0 + KR; ++kt) {
         const int key = 16 * kt + col;
         float rr = 0.0f;
 #pragma unroll
@@ -393,8 +403,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
             atomicOr(&s.cw[key * CW + w], chunk << sh);
             if (sh + 4 * bits > 32) atomicOr(&s.cw[key * CW + w + 1], chunk >> (32 - sh));
             // residual as B operand of k-step rt/2: elements 4 (rt % 2) + r of this lane
-            uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 0) * 64 + lane]);
-            uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + rt / 2) * 2 + 1) * 64 + lane]);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 0) * 64 + lane]);
+            uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 1) * 64 + lane]);
             const int hw = 2 * (rt & 1);
             *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(h01, h23);
             *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(l01, l23);
@@ -408,18 +418,17 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
 
     // ---- 4. z = S r on this wave's rows; signs [z >= 0] (skipped for the
     // first-stage format, m = 0; the condition is uniform over the launch)
-    const bool qjl = a.m > 0;
     if (qjl) {
-    f32x4 zacc[RTW][kKT];
+    f32x4 zacc[RTW][KR];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kt = 0; kt < KR; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 2
     for (int ks = 0; ks < KS; ++ks) {
-        uint4 rf[kKT][2];
+        uint4 rf[KR][2];
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
+        for (int kt = 0; kt < KR; ++kt) {
             rf[kt][0] = s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + lane];
             rf[kt][1] = s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + lane];
         }
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
             const uint4 s0 = sfr[((rt * KS + ks) * 2 + 0) * 64 + lane];
             const uint4 s1 = sfr[((rt * KS + ks) * 2 + 1) * 64 + lane];
 #pragma unroll
-            for (int kt = 0; kt < kKT; ++kt) {
+            for (int kt = 0; kt < KR; ++kt) {
                 zacc[j][kt] = mfma_bf16(s0, rf[kt][0], zacc[j][kt]);
                 zacc[j][kt] = mfma_bf16(s0, rf[kt][1], zacc[j][kt]);
                 zacc[j][kt] = mfma_bf16(s1, rf[kt][0], zacc[j][kt]);
@@ -441,15 +450,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_compress_keys(KeyLaunch a, int6
         const int rt = wave * RTW + j;
         const int off = 16 * rt + 4 * kb;
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
+        for (int kt = 0; kt < KR; ++kt) {
             uint32_t nib = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
-            atomicOr(&s.sw[(16 * kt + col) * SWN + (off >> 5)], nib << (off & 31));
+            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWN + (off >> 5)], nib << (off & 31));
         }
     }
-    __syncthreads();
+    __syncthreads();   // (also: this pass's residual operands are read before the next pass writes them)
     }
+    }   // passes
 
     // ---- 5. store the WG's keys: contiguous rows of every plane, or (when
     // appending to a layout cache) each key at its own row
@@ -519,7 +529,7 @@ constexpr int64_t kSmallKeyGrid = 512;
 template <int D, typename TIn, int BITS>
 hipError_t launch_keys_t(const KeyLaunch &a, hipStream_t stream)
 {
-    constexpr int KT = key_tiles<D>();
+    constexpr int KT = key_tiles<D, TIn>();
     if constexpr (KT > 2) {
         const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
         if ((n + 16 * KT - 1) / (16 * KT) < kSmallKeyGrid) return launch_keys_k<D, TIn, BITS, 2>(a, stream);

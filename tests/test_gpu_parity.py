@@ -148,6 +148,35 @@ def test_strided_layouts_agree(torch_cuda):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["asym-d256", "long-1m"])
+def test_compressor_tilings_agree(torch_cuda, name):
+    """One large launch (64 keys per workgroup; at d = 256 the residual and
+    sign steps in two passes) and small launches of the same keys (32 keys per
+    workgroup) pack the same planes, bit for bit; sampled rows of the large
+    launch match the oracle."""
+    torch = torch_cuda
+    w = W.WORKLOADS[name].with_T(4096, B=4 if name == "asym-d256" else 1)
+    assert w.B * w.Hkv * w.T >= 64 * 512          # the large launch takes the 64-key tiling
+    fm = P.Formats(w, 0)
+    k = W.make_keys(w, device="cuda")
+    v = W.make_values(w, device="cuda")
+    kc, _ = P.gpu_compress(fm, k, v)
+    parts = []
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            one = tq.alloc_key_cache(fm.kf, 1, 1, 256, device="cuda")
+            tq.tq_compress_keys(fm.kf, k[b:b + 1, h:h + 1, :256], one)
+            parts.append(one)
+    torch.cuda.synchronize()
+    for i, one in enumerate(parts):
+        b, h = divmod(i, w.Hkv)
+        for big, small in [(kc.codes, one.codes), (kc.signs, one.signs), (kc.knorm, one.knorm), (kc.rnorm, one.rnorm)]:
+            assert torch.equal(big[b, h, :256], small[0, 0]), f"unit ({b}, {h})"
+    rows = np.random.default_rng(5).choice(w.B * w.Hkv * w.T, 48, replace=False)
+    kn = P.f64(k.cpu()).reshape(-1, w.d)
+    P.compare_keys(fm, kc, kn[rows], row_index=rows)
+
+
 def test_deterministic(torch_cuda):
     torch = torch_cuda
     w = _reduced("asym-d256")
