@@ -1509,6 +1509,8 @@ hipError_t launch_attend_t(const DecodeLaunch &a, hipStream_t stream, float kapp
     else if (S <= 16) hipLaunchKernelGGL((k_merge_rows<D, 16>), dim3(rows), dim3(D), 0, stream, a);
     else if (S <= 32) hipLaunchKernelGGL((k_merge_batch<32, 4>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     else if (S <= 64) hipLaunchKernelGGL((k_merge_batch<32, 8>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 128) hipLaunchKernelGGL((k_merge_batch<32, 16>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
+    else if (S <= 256) hipLaunchKernelGGL((k_merge_batch<32, 32>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((k_merge_splits<32, 16>), dim3(rows, a.d / 32), dim3(kThreads), 0, stream, a);
     prof_end(tok, stream);
     return hipGetLastError();
