@@ -27,6 +27,8 @@ CASES = [
     (128, 2, "dense", 1, 16, 2, 128, 300, "scaled", "bfloat16"),   # GQA 16, one-hot regime
     (128, 3, "dense", 1, 8, 2, 64, 400, "iid", "bfloat16"),        # 3-bit keys (pair table)
     (128, 4, "dense", 2, 8, 4, 32, 450, "iid", "bfloat16"),        # 4-bit keys (pair table)
+    (128, 3, "hadamard", 2, 8, 4, 32, 390, "iid", "bfloat16"),     # 3-bit keys, 4-bit values (4 KB table budget)
+    (128, 7, "dense", 1, 8, 4, 64, 270, "scaled", "bfloat16"),     # 7-bit keys at d 128 (single-code table, 4 KB budget)
     (128, 5, "hadamard", 1, 4, 2, 64, 290, "iid", "bfloat16"),     # 5-bit keys (largest pair table)
     (128, 6, "dense", 1, 2, 4, 32, 333, "iid", "float32"),         # 6-bit keys (single-code table)
     (256, 7, "dense", 2, 4, 4, 32, 260, "scaled", "bfloat16"),     # 7-bit keys (largest format), d 256
