@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: at least 3, and until 1.5 s of steps have run, so "
                          "that the GPU's clocks have settled under load)")
-    ap.add_argument("--workload", default="qwen25-3b-8k")
+    ap.add_argument("--workload", default="asym-d256",
+                    help="workload name (default: asym-d256, the largest single-GPU cache, 7.1 GB packed)")
     ap.add_argument("--key-format", choices=["full", "first-stage", "q8_0", "q4_0"], default="full",
                     help="full: Lloyd-Max codes + QJL signs (the default); first-stage: codes and "
                          "||k|| only (qjl_m = 0); q8_0 / q4_0: the rotated 8-bit / 4-bit block formats "
@@ -217,45 +218,69 @@ def read_ceiling():
     return None
 
 
+def _oracle_leg(w, small, rot, k, v, q, seconds: float):
+    """The oracle on (sequence 0, KV head h) units of `small` until the time
+    budget: keys compressed, values compressed, then decode attention of the
+    unit's G query heads over the oracle-packed unit."""
+    import oracle as O
+
+    key_time = val_time = dec_time = 0.0
+    vectors = 0
+    h = 0
+    t_start = time.perf_counter()
+    while h < small.Hkv and (h == 0 or time.perf_counter() - t_start < seconds):
+        t0 = time.perf_counter()
+        ok = O.compress_keys(k[h], w.k_bits, rot)
+        t1 = time.perf_counter()
+        ov = O.compress_values(v[h], w.v_bits, w.group)
+        t2 = time.perf_counter()
+        O.attend(q[h * w.G:(h + 1) * w.G], ok, w.k_bits, rot, ov, w.v_bits, w.group)
+        t3 = time.perf_counter()
+        key_time += t1 - t0
+        val_time += t2 - t1
+        dec_time += t3 - t2
+        vectors += small.T
+        h += 1
+    packed = vectors * (w.key_bytes() + w.value_bytes())
+    return {"decode_GBps": packed / dec_time / 1e9, "keys_compressed_per_s": vectors / key_time,
+            "values_compressed_per_s": vectors / val_time, "units": h, "seconds": round(time.perf_counter() - t_start, 2)}
+
+
 def cpu_baseline(w, seconds: float):
-    """The oracle (as is) on a bounded sample of the workload: one (sequence,
-    KV head) unit's keys compressed, then decode attention of its G query heads
-    over the oracle-packed unit, repeated over units until the time budget."""
-    import numpy as np
+    """The oracle (as is) on a bounded sample of the workload, on all the host
+    cores this process may use and then on one core: (sequence, KV head) units
+    of up to 8192 tokens, each compressed (keys, then values) and attended by
+    its G query heads.  The OpenMP thread count is set through the runtime the
+    oracle links (omp_set_num_threads), between the legs."""
+    import ctypes
     import oracle as O
     from attention_decode_amd import workloads as W
 
-    cores = len(os.sched_getaffinity(0))
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    allowed = len(os.sched_getaffinity(0))
+    threads = min(int(os.environ.get("OMP_NUM_THREADS", allowed)), allowed)
     small = w.with_T(min(w.T, 8192), B=1, layers=1)
     rot = O.rotation(w.rotation_seed(0), w.d, w.rot, m=w.qjl_m)
     O.codebook(w.d, w.k_bits)
     k = W.make_keys(small, 0).double().numpy()[0]
     v = W.make_values(small, 0).double().numpy()[0]
     q = W.make_queries(small, 0).double().numpy()[0]
-    key_time = dec_time = 0.0
-    keys = units = 0
-    h = 0
-    t_start = time.perf_counter()
-    while time.perf_counter() - t_start < seconds and h < small.Hkv:
-        # compress a bounded slice of keys, then decode over the unit
-        n_keys = small.T
-        t0 = time.perf_counter()
-        ok = O.compress_keys(k[h, :n_keys], w.k_bits, rot)
-        key_time += time.perf_counter() - t0
-        keys += n_keys
-        ov = O.compress_values(v[h, :n_keys], w.v_bits, w.group)
-        t0 = time.perf_counter()
-        O.attend(q[h * w.G:(h + 1) * w.G], ok, w.k_bits, rot, ov, w.v_bits, w.group)
-        dec_time += time.perf_counter() - t0
-        units += n_keys
-        h += 1
-    packed = units * (w.key_bytes() + w.value_bytes())
+    gomp = ctypes.CDLL("libgomp.so.1")      # the OpenMP runtime liboracle.so is linked with
+    gomp.omp_set_num_threads(threads)
+    many = _oracle_leg(w, small, rot, k, v, q, 0.6 * seconds)
+    gomp.omp_set_num_threads(1)
+    one = _oracle_leg(w, small, rot, k, v, q, 0.4 * seconds)
+    gomp.omp_set_num_threads(threads)
     return {
-        "value": packed / dec_time / 1e9, "unit": "GB/s", "cores": min(threads, cores), "kind": "oracle",
-        "sample": f"{h} (sequence, KV head) units x {min(w.T, 8192)} tokens of {w.name}: fp64 oracle "
-                  f"key compression then decode attention of {w.G} query heads",
-        "keys_compressed_per_s": keys / key_time,
+        "value": round(many["decode_GBps"], 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{many['units']} (sequence, KV head) units x {small.T} tokens of {w.name} on {threads} threads, "
+                  f"{one['units']} on 1 thread: fp64 oracle key and value compression, then decode attention of "
+                  f"{w.G} query heads over the unit (GB/s of packed KV read)",
+        "keys_compressed_per_s": round(many["keys_compressed_per_s"], 1),
+        "values_compressed_per_s": round(many["values_compressed_per_s"], 1),
+        "one_core": {"value": round(one["decode_GBps"], 5), "unit": "GB/s", "cores": 1,
+                     "keys_compressed_per_s": round(one["keys_compressed_per_s"], 1),
+                     "values_compressed_per_s": round(one["values_compressed_per_s"], 1)},
+        "nproc": os.cpu_count(), "affinity_cores": allowed,
         "cpu_model": _cpu_model(),
     }
 
@@ -419,14 +444,31 @@ def main():
     packed = w.packed_bytes()
     vectors = w.vectors()
     value = packed / (d_ms * 1e-3) / 1e9
-    # split-K attention kernel: algorithmic bytes per launch = packed K + V of one
-    # layer + q-prep rows read + split partials written
+    # split-K attention kernel: algorithmic bytes per launch = packed K + V
+    # planes of one layer + the queries read + the outputs written.  The
+    # workspace traffic of the launch (score operands and per-query scales read
+    # by every workgroup of a unit, split partials written for the merge) is
+    # reported beside it, not counted.
     per_layer_keys = w.B * w.Hkv * w.T
     splits = layers[0].splits
-    attn_bytes = (per_layer_keys * (w.key_bytes() + w.value_bytes())
-                  + w.B * w.Hq * 2 * w.d * 4 + w.B * w.Hq * splits * (w.d + 2) * 4)
+    in_bytes = 4 if w.dtype == "float32" else 2
+    q_bytes = w.B * w.Hq * w.d * in_bytes
+    out_bytes = w.B * w.Hq * w.d * 4
+    attn_bytes = per_layer_keys * (w.key_bytes() + w.value_bytes()) + q_bytes + out_bytes
+    overhead = {"split_partials_written": w.B * w.Hq * splits * (w.d + 2) * 4 if splits > 1 else 0,
+                "query_prep_rows": w.B * w.Hq * 2 * w.d * 4}
     attn_avg_s = attn_ms * 1e-3 / max(attn_n, 1)
     achieved = attn_bytes / attn_avg_s / 1e9
+    # key compressor: algorithmic flops per key 2 d^2 (dense rotation; d log2 d
+    # adds for a Walsh-Hadamard one) + 2 m d (QJL projection) against the bf16
+    # matrix-core peak, and its HBM bytes (key read, planes written)
+    import math
+    kq_avg_s = kq_ms * 1e-3 / max(kq_n, 1)
+    rot_flop = 2 * w.d * w.d if w.rot == "dense" else w.d * int(math.log2(w.d)) * (2 if w.rot == "hadamard2" else 1)
+    key_flop = rot_flop + 2 * w.qjl_m * w.d
+    key_io = in_bytes * w.d + w.key_bytes()
+    kq_tflops = per_layer_keys * key_flop / kq_avg_s / 1e12 if kq_n else None
+    kq_gbps = per_layer_keys * key_io / kq_avg_s / 1e9 if kq_n else None
     result = {
         "metric": "decode attention GB/s of packed KV read (% of HBM peak); keys compressed/s",
         "value": round(value, 2),
@@ -457,9 +499,17 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "tq_attend_splitk", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w), "bytes_per_launch": attn_bytes,
+                     "bytes_per_launch_terms": {"packed_kv": per_layer_keys * (w.key_bytes() + w.value_bytes()),
+                                                "queries": q_bytes, "outputs": out_bytes},
+                     "workspace_overhead_bytes": overhead,
                      "avg_launch_us": round(attn_avg_s * 1e6, 3), "launches": attn_n,
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
+        "compress_keys_roofline": None if not kq_n else {
+            "kernel": "tq_compress_keys", "bound": "mfma", "flop_per_key": key_flop,
+            "achieved": round(kq_tflops, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kq_tflops / 2500.0, 4),
+            "hbm_GBps": round(kq_gbps, 1), "hbm_frac": round(kq_gbps / HBM_PEAK_GBS, 4),
+            "keys_per_launch": per_layer_keys, "avg_launch_us": round(kq_avg_s * 1e6, 2)},
         "kernel_avg_us": {"tq_compress_keys": round(kq_ms * 1e3 / max(kq_n, 1), 3),
                           "tq_compress_values": round(vq_ms * 1e3 / max(vq_n, 1), 3),
                           "tq_qprep": round(qp_ms * 1e3 / max(qp_n, 1), 3),

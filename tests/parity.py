@@ -62,24 +62,48 @@ def gpu_compress(fm: Formats, k, v):
     return kc, vc
 
 
+def _rows_of(plane, row_index, ndim: int) -> np.ndarray:
+    """Rows of a packed plane (torch, any device) as numpy: the plane viewed
+    with `ndim` dimensions (rows first), gathered on the plane's device when
+    row_index is given, so that a few rows of a multi-GB plane cost little."""
+    import torch
+    shape = (-1,) + tuple(plane.shape[-(ndim - 1):]) if ndim > 1 else (-1,)
+    flat = plane.reshape(shape)
+    if row_index is not None:
+        flat = flat.index_select(0, torch.as_tensor(np.asarray(row_index, dtype=np.int64), device=plane.device))
+    return flat.cpu().numpy()
+
+
 def compare_keys(fm: Formats, kc, rows_k: np.ndarray, row_index=None):
     """kc: libtq key planes (torch); rows_k: [N, d] fp64 inputs of the rows to
     check; row_index: flat row numbers of those rows in kc (default: all)."""
     w = fm.w
     d, bits = w.d, w.k_bits
     ok = O.compress_keys(rows_k, bits, fm.orot, keep_aux=True)
-    sel = slice(None) if row_index is None else row_index
-    g_codes = kc.codes.reshape(-1, kc.codes.shape[-1]).cpu().numpy()[sel]
-    g_signs = kc.signs.reshape(-1, kc.signs.shape[-1]).cpu().numpy()[sel]
-    g_kn = kc.knorm.reshape(-1).cpu().numpy()[sel]
-    g_rn = kc.rnorm.reshape(-1).cpu().numpy()[sel]
+    g_codes = _rows_of(kc.codes, row_index, 2)
+    g_kn = _rows_of(kc.knorm, row_index, 1)
     n = rows_k.shape[0]
     gi, oi = unpack_le(g_codes, d, bits), unpack_le(ok.codes, d, bits)
-    dist = np.abs(ok.y[:, :, None] - fm.boundaries[None, None, :]).min(axis=2)
+    # distance of each rotated coordinate to its nearest boundary, without an
+    # [n, d, L - 1] temporary (boundaries are sorted)
+    pos = np.searchsorted(fm.boundaries, ok.y)
+    lo = fm.boundaries[np.clip(pos - 1, 0, fm.boundaries.size - 1)]
+    hi = fm.boundaries[np.clip(pos, 0, fm.boundaries.size - 1)]
+    dist = np.minimum(np.abs(ok.y - lo), np.abs(ok.y - hi))
     code_flip = gi != oi
     assert np.all(dist[code_flip] < FLIP_DIST), f"code mismatch away from a boundary: {dist[code_flip].max()}"
     # a boundary coordinate may take either adjacent cell, nothing else
     assert np.all(np.abs(gi[code_flip].astype(np.int64) - oi[code_flip].astype(np.int64)) == 1)
+    kn_ref = ok.knorm.astype(np.float64)
+    assert np.all(np.abs(g_kn - kn_ref) <= 1e-6 * np.maximum(kn_ref, 1e-30)), "knorm"
+    if kc.signs is None:
+        # first-stage format: codes and ||k|| only
+        flips = int(code_flip.sum())
+        assert flips <= FLIP_FRAC * n * d, f"{flips} flips over {n * d} coordinates"
+        return {"code_flips": flips, "sign_flips": 0, "flipped_keys": int(code_flip.any(axis=1).sum()),
+                "coords": n * d}
+    g_signs = _rows_of(kc.signs, row_index, 2)
+    g_rn = _rows_of(kc.rnorm, row_index, 1)
     flipped_key = code_flip.any(axis=1)
     # reference signs and ||r||: the oracle's encoding, or for a key with a
     # boundary flip the oracle's encoding under the other tie resolution
@@ -96,21 +120,31 @@ def compare_keys(fm: Formats, kc, rows_k: np.ndarray, row_index=None):
         f"sign mismatch away from z = 0: {np.abs(ref_z[sign_flip]).max()}"
     flips = int(code_flip.sum() + sign_flip.sum())
     assert flips <= FLIP_FRAC * n * d * 2, f"{flips} flips over {n * d * 2} coordinates"
-    kn_ref = ok.knorm.astype(np.float64)
-    assert np.all(np.abs(g_kn - kn_ref) <= 1e-6 * np.maximum(kn_ref, 1e-30)), "knorm"
     rel = np.abs(g_rn - ref_rho) / np.maximum(ref_rho, 1e-30)
     assert np.all(rel <= 1e-5), f"rnorm max rel {rel.max()}"
     return {"code_flips": int(code_flip.sum()), "sign_flips": int(sign_flip.sum()),
             "flipped_keys": int(flipped_key.sum()), "coords": n * d * 2}
 
 
+def compare_keys_chunked(fm: Formats, kc, rows_k: np.ndarray, row_index: np.ndarray, chunk: int = 65536):
+    """compare_keys over many rows in pieces (the oracle's auxiliary arrays of
+    a whole 2^20-token slice would take gigabytes); flips are summed, and the
+    flip budget is checked on each piece and on the total."""
+    tot = {"code_flips": 0, "sign_flips": 0, "flipped_keys": 0, "coords": 0}
+    for lo in range(0, rows_k.shape[0], chunk):
+        st = compare_keys(fm, kc, rows_k[lo:lo + chunk], row_index=row_index[lo:lo + chunk])
+        for key in tot:
+            tot[key] += st[key]
+    assert tot["code_flips"] + tot["sign_flips"] <= FLIP_FRAC * tot["coords"]
+    return tot
+
+
 def compare_values(fm: Formats, vc, rows_v: np.ndarray, row_index=None):
     w = fm.w
     d = w.d
     ov = O.compress_values(rows_v, w.v_bits, w.group, keep_aux=True)
-    sel = slice(None) if row_index is None else row_index
-    g_codes = vc.codes.reshape(-1, vc.codes.shape[-1]).cpu().numpy()[sel]
-    g_par = vc.params.reshape(-1, d // w.group, 2).cpu().numpy().view(np.uint16)[sel]
+    g_codes = _rows_of(vc.codes, row_index, 2)
+    g_par = _rows_of(vc.params.reshape(-1, d // w.group, 2), row_index, 3).view(np.uint16)
     assert np.array_equal(g_par, ov.params), "value scale/zero differ"
     gi, oi = unpack_le(g_codes, d, w.v_bits), unpack_le(ov.codes, d, w.v_bits)
     mism = gi != oi

@@ -86,6 +86,72 @@ def test_split_count_invariance(torch_cuda, splits):
     assert torch.allclose(out, ref, atol=1e-5, rtol=1e-5), (out - ref).abs().max()
 
 
+def _random_cache(w):
+    pc = W.random_packed_cache(w, 0, device="cuda")
+    return pc, tq.KeyCache(pc["codes"], pc["signs"], pc["knorm"], pc["rnorm"]), \
+        tq.ValueCache(pc["vcodes"], pc["vparams"])
+
+
+def _oracle_unit(w, fm, pc, q, b, h):
+    G = w.G
+    okc = O.KeyCache(pc["codes"][b, h].cpu().numpy(), pc["signs"][b, h].cpu().numpy(),
+                     pc["knorm"][b, h].cpu().numpy(), pc["rnorm"][b, h].cpu().numpy())
+    ovc = O.ValueCache(pc["vcodes"][b, h].cpu().numpy(), pc["vparams"][b, h].cpu().numpy().view(np.uint16))
+    qq = q[b, h * G:(h + 1) * G].double().cpu().numpy()
+    return O.attend(qq, okc, w.k_bits, fm.orot, ovc, w.v_bits, w.group)
+
+
+@pytest.mark.parametrize("splits", [257, 300, 1024])
+def test_many_splits_merge(torch_cuda, splits):
+    """More than 256 splits take the looping log-sum-exp merge: the output
+    equals the one-split decode and the oracle on whole units (a long-1m
+    shaped cache of 131072 tokens)."""
+    torch = torch_cuda
+    w = W.WORKLOADS["long-1m"].with_T(131072)
+    print(f"[parity] many splits {splits}: {w.B}x{w.Hkv}x{w.T}", flush=True)
+    fm = P.Formats(w, 0)
+    pc, kc, vc = _random_cache(w)
+    q = W.make_queries(w, 0, device="cuda")
+    ref = tq.tq_attend_decode(fm.kf, fm.vf, q, kc, vc, w.Hkv, w.T, n_splits=1)
+    out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc, vc, w.Hkv, w.T, n_splits=splits)
+    torch.cuda.synchronize()
+    G = w.G
+    errs = []
+    for b, h in [(0, 0), (0, w.Hkv - 1)]:
+        want = _oracle_unit(w, fm, pc, q, b, h)
+        errs.append(P.check_attention(out[b, h * G:(h + 1) * G].double().cpu().numpy(), want))
+        errs.append(P.check_attention(ref[b, h * G:(h + 1) * G].double().cpu().numpy(), want))
+    # One split sums 32768 tokens per wave in fp32 (softmax sum and value
+    # accumulators), many splits a few hundred per partial: the two orders of
+    # summation differ by up to about 2^-24 per addition in the long chain
+    # (1e-3 relative after 2^14 additions, outputs here are ~0.02), so they
+    # are compared at a tenth of the attention bar rather than bit for bit.
+    diff = float((out - ref).abs().max())
+    print(f"[parity] many splits {splits}: oracle errors (splits, one split) {errs}, |splits - one| {diff:.3g}",
+          flush=True)
+    assert diff <= 0.1 * P.ATTN_TOL
+
+
+def test_auto_plan_beyond_256_splits(torch_cuda):
+    """The automatic split plan of one long sequence with two KV heads (a
+    Qwen2.5-3B-shaped head layout at 64K tokens) picks more than 256 splits;
+    the decode still matches the oracle on every unit."""
+    torch = torch_cuda
+    w = W.WORKLOADS["qwen25-3b-8k"].with_T(65536, layers=1)
+    fm = P.Formats(w, 0)
+    auto = tq.tq_attend_splits(fm.kf, w.B, w.Hq, w.Hkv, w.T)
+    print(f"[parity] auto plan for {w.B}x{w.Hkv}x{w.T}, {w.Hq} query heads: {auto} splits", flush=True)
+    assert auto > 256
+    pc, kc, vc = _random_cache(w)
+    q = W.make_queries(w, 0, device="cuda")
+    out = tq.tq_attend_decode(fm.kf, fm.vf, q, kc, vc, w.Hkv, w.T)
+    torch.cuda.synchronize()
+    G = w.G
+    for h in range(w.Hkv):
+        want = _oracle_unit(w, fm, pc, q, 0, h)
+        P.check_attention(out[0, h * G:(h + 1) * G].double().cpu().numpy(), want)
+
+
 def test_edge_cases(torch_cuda):
     torch = torch_cuda
     w = W.WORKLOADS["tiny"].with_T(3)
