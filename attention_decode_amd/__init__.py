@@ -249,6 +249,18 @@ def tq_attend_decode(kfmt: KeyFormat, vfmt: ValueFormat, q, kc: KeyCache, vc: Va
     return out
 
 
+def tq_attend_decode_noalloc(kfmt: KeyFormat, vfmt: ValueFormat, q, kc: KeyCache, vc: ValueCache, Hkv: int,
+                             T: int, out, n_splits: int = 0, softmax_scale: float = 0.0, stream=None):
+    """tq_attend_decode with the library's static device scratch as its
+    workspace: allocates nothing (out [B, Hq, d] fp32 is the caller's)."""
+    B, Hq, _ = q.shape
+    kf, vf = kfmt.c(), vfmt.c()
+    check(lib().tq_attend_decode_noalloc(ctypes.byref(kf), ctypes.byref(vf), q.data_ptr(), _dtype_code(q), B, Hq,
+                                         Hkv, T, kc.c(), vc.c(), softmax_scale, n_splits, out.data_ptr(),
+                                         _stream(stream)), "tq_attend_decode_noalloc")
+    return out
+
+
 # ------------------------------------------------------------ serving caches
 @dataclass
 class CacheLayout:

@@ -71,6 +71,8 @@ SIGNATURES = {
     "tq_attend_workspace_bytes": (_sz, [_c.POINTER(KeyFmt), _i, _i, _i, _i64, _i]),
     "tq_attend_decode": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64,
                               KCache, VCache, _c.c_float, _i, _vp, _sz, _vp, _vp]),
+    "tq_attend_decode_noalloc": (_i, [_c.POINTER(KeyFmt), _c.POINTER(ValFmt), _vp, _i, _i, _i, _i, _i64,
+                                      KCache, VCache, _c.c_float, _i, _vp, _vp]),
     "tq_dequantize_keys": (_i, [_c.POINTER(KeyFmt), _i, _i, _i64, KCache, _vp, _vp]),
     "tq_append_keys": (_i, [_c.POINTER(KeyFmt), _vp, _i, _i, _i, _i, _i64, _i64, _i64, _c.POINTER(CacheLayout),
                             _vp, KCache, _vp]),

@@ -84,6 +84,7 @@ struct ProfRecord {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+thread_local bool g_prof_suppressed = false;
 std::vector<ProfRecord> g_prof_live;
 std::vector<ProfRecord> g_prof_free;
 
@@ -91,9 +92,12 @@ std::vector<ProfRecord> g_prof_free;
 
 namespace tq {
 
+void prof_suppress(bool on) { g_prof_suppressed = on; }
+
 void prof_begin(const char *name, hipStream_t stream, void **token)
 {
     *token = nullptr;
+    if (g_prof_suppressed) return;
     std::lock_guard<std::mutex> lock(g_prof_mu);
     if (!g_prof_on) return;
     ProfRecord r;
@@ -1009,7 +1013,7 @@ size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int
 static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype, int B,
                              int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
                              int n_splits, void *ws, size_t ws_bytes, float *out, const tq::CacheMap &map,
-                             void *stream, const char *who)
+                             void *stream, const char *who, bool use_scratch = false)
 {
     TQ_TRY(check_decode_common(kfmt, q, dtype, B, Hq, Hkv, T, kc, who));
     TQ_TRY(check_val_fmt(vfmt, who));
@@ -1036,11 +1040,22 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
         return e == hipSuccess ? TQ_OK : hip_fail(e, who);
     }
     TQ_TRY(check_vcache(vc, who));
-    if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
-    if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
+    if (!use_scratch) {
+        if (!ws) return fail(TQ_EINVAL, "%s: NULL workspace", who);
+        if (!aligned16(ws)) return fail(TQ_EALIGN, "%s: workspace must be 16-byte aligned", who);
+    }
     const DecodePlan plan = decode_plan(kfmt, B, Hq, Hkv, T, n_splits,
                                         map.mode == tq::CacheMap::kPaged ? map.bs : 0);
     const AttendLayout L = attend_layout(kfmt->d, kfmt->qjl_m, B, Hq, plan);
+    if (use_scratch) {
+        // the device's static scratch instead of a caller workspace
+        if (L.total > tq::scratch_capacity())
+            return fail(TQ_ENOMEM, "%s: this shape needs %zu B of workspace, more than the %zu B static scratch",
+                        who, L.total, tq::scratch_capacity());
+        const hipError_t se = tq::scratch_address(&ws);
+        if (se != hipSuccess) return hip_fail(se, "tq_attend_decode_noalloc: scratch address");
+        ws_bytes = tq::scratch_capacity();
+    }
     if (ws_bytes < L.total) return fail(TQ_ENOMEM, "%s: workspace %zu B < %zu B", who, ws_bytes, L.total);
     a.piT = kfmt->rot->d_piT;
     a.sT = kfmt->rot->d_sT;
@@ -1084,6 +1099,20 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
 {
     return attend_impl(kfmt, vfmt, q, dtype, B, Hq, Hkv, T, kc, vc, softmax_scale, n_splits, ws, ws_bytes, out,
                        tq::CacheMap{}, stream, "tq_attend_decode");
+}
+
+tq_status tq_attend_decode_noalloc(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,
+                                   int B, int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc,
+                                   float softmax_scale, int n_splits, float *out, void *stream)
+{
+    // the same kernels and split plan as tq_attend_decode; no event records
+    // either, even with the profiling hook on
+    struct Suppress {
+        Suppress() { tq::prof_suppress(true); }
+        ~Suppress() { tq::prof_suppress(false); }
+    } suppress;
+    return attend_impl(kfmt, vfmt, q, dtype, B, Hq, Hkv, T, kc, vc, softmax_scale, n_splits, nullptr, 0, out,
+                       tq::CacheMap{}, stream, "tq_attend_decode_noalloc", true);
 }
 
 tq_status tq_attend_decode_paged(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype,

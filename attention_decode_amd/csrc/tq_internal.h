@@ -194,5 +194,13 @@ hipError_t launch_decode_block(const DecodeLaunch &a, hipStream_t stream);
 // ---- profiling hooks (api.cpp)
 void prof_begin(const char *name, hipStream_t stream, void **token);
 void prof_end(void *token, hipStream_t stream);
+// while set on this thread, prof_begin records nothing (the allocation-free
+// entry point creates no events)
+void prof_suppress(bool on);
+
+// ---- static device scratch (scratch.hip): its size, and its address on the
+// current device (looked up once per device)
+size_t scratch_capacity();
+hipError_t scratch_address(void **out);
 
 }  // namespace tq

@@ -188,6 +188,24 @@ tq_status tq_attend_decode(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const
                            tq_vcache vc, float softmax_scale, int n_splits, void *ws,
                            size_t ws_bytes, float *out, void *stream);
 
+/* tq_attend_decode without a workspace argument, for callers that cannot
+   allocate device memory (code under HIP graph capture, serving loops or
+   harnesses that forbid hipMalloc).  Same arguments, kernels, split plan and
+   results as tq_attend_decode with the same n_splits; the workspace is a
+   static device array of 16 MiB that the library holds on each GPU it runs
+   on until the process ends (its address is looked up on the first call on
+   a device).  The call allocates nothing and records no profiling events.
+   Shapes whose workspace (tq_attend_workspace_bytes) exceeds 16 MiB return
+   TQ_ENOMEM before anything is launched.  Every call on one GPU shares that
+   GPU's array: calls that overlap on one GPU (several streams or host
+   threads) race and give undefined results; calls ordered on one stream are
+   safe.  Every workspace byte a call reads is written by that call first, so
+   nothing left by a previous call needs clearing. */
+tq_status tq_attend_decode_noalloc(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q,
+                                   tq_dtype dtype, int B, int Hq, int Hkv, int64_t T, tq_kcache kc,
+                                   tq_vcache vc, float softmax_scale, int n_splits, float *out,
+                                   void *stream);
+
 /* ------------------------------------------------- serving-style caches */
 
 /* Layout of a preallocated cache that grows by a few tokens per decode step,
