@@ -1,7 +1,8 @@
 """ctypes view of libtq.so (the C ABI declared in include/tq.h).
 
 Only argument marshalling lives here.  The library is loaded from this package
-directory; a missing library is an error, never a fallback.
+directory (or from the path in LIBTQ_PATH, e.g. an instrumented build of the
+same sources); a missing library is an error, never a fallback.
 """
 from __future__ import annotations
 
@@ -9,7 +10,7 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libtq.so")
+LIB_PATH = os.environ.get("LIBTQ_PATH") or os.path.join(PKG, "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_ENOMEM, TQ_EHIP, TQ_ENOTCONV = range(7)
 STATUS_NAMES = ["TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EALIGN", "TQ_ENOMEM", "TQ_EHIP",

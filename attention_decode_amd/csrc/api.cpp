@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -62,6 +63,44 @@ tq_status hip_fail(hipError_t e, const char *what)
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The integer a C caller passed for an enum parameter.  C lets any int travel
+// in an enum type; in C++ loading a value outside the enumerators' range is
+// undefined, so arguments are read through their bytes and range-checked
+// before they are used as the enum.
+template <class E>
+int enum_arg(const E &e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+// Failure injection for the failure-path tests, read from the environment
+// variable TQ_TEST_HOOK at each set-up call and before each launch (unset in
+// normal use):
+//   "codebook_iters=N"  caps the Lloyd-Max sweeps and Newton steps at N
+//                       (N = 0 leaves the start point: TQ_ENOTCONV)
+//   "host_alloc"        the host allocation of a new handle fails (TQ_ENOMEM)
+//   "launch"            an entry point that would launch kernels reports a
+//                       launch failure (TQ_EHIP) after its argument checks,
+//                       with nothing launched
+struct TestHook {
+    int codebook_iters = -1;
+    bool host_alloc = false, launch = false;
+};
+
+TestHook test_hook()
+{
+    TestHook h;
+    const char *s = std::getenv("TQ_TEST_HOOK");
+    if (!s) return h;
+    if (std::strncmp(s, "codebook_iters=", 15) == 0) h.codebook_iters = std::atoi(s + 15);
+    h.host_alloc = std::strcmp(s, "host_alloc") == 0;
+    h.launch = std::strcmp(s, "launch") == 0;
+    return h;
+}
 
 size_t dtype_size(tq_dtype t)
 {
@@ -169,7 +208,7 @@ tq_status tq_codebook_host(int d, int bits, double *centroids, double *boundarie
     if (bits < 1 || bits > 8) return fail(TQ_EINVAL, "codebook: bits=%d outside [1, 8]", bits);
     if (!centroids || !boundaries) return fail(TQ_EINVAL, "codebook: NULL output");
     double res = 0.0;
-    const tq_status st = tq::lloyd_max_codebook(d, bits, centroids, boundaries, &res);
+    const tq_status st = tq::lloyd_max_codebook(d, bits, centroids, boundaries, &res, test_hook().codebook_iters);
     if (st != TQ_OK) return fail(st, "codebook: Lloyd-Max residual %.3g after the iteration cap", res);
     return TQ_OK;
 }
@@ -178,7 +217,7 @@ tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
 {
     if (!out) return fail(TQ_EINVAL, "tq_build_codebook: NULL out");
     *out = nullptr;
-    auto *cb = new (std::nothrow) tq_codebook;
+    auto *cb = test_hook().host_alloc ? nullptr : new (std::nothrow) tq_codebook;
     if (!cb) return fail(TQ_ENOMEM, "tq_build_codebook: host allocation failed");
     cb->d = d;
     cb->bits = bits;
@@ -264,11 +303,13 @@ tq_status tq_codebook_tables(const tq_codebook *cb, double *centroids, double *b
 }
 
 // ------------------------------------------------------------------ rotation
-tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, double *s)
+tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind_arg, double *pi, double *s)
 {
     if (d < 2 || d > 4096) return fail(TQ_EINVAL, "rotation: d=%d outside [2, 4096]", d);
-    if (kind != TQ_ROT_DENSE && kind != TQ_ROT_HADAMARD && kind != TQ_ROT_HADAMARD2)
-        return fail(TQ_EINVAL, "rotation: bad kind %d", kind);
+    const int kv = enum_arg(kind_arg);
+    if (kv != TQ_ROT_DENSE && kv != TQ_ROT_HADAMARD && kv != TQ_ROT_HADAMARD2)
+        return fail(TQ_EINVAL, "rotation: bad kind %d", kv);
+    const tq_rot_kind kind = static_cast<tq_rot_kind>(kv);
     if (kind != TQ_ROT_DENSE && (d & (d - 1)) != 0)
         return fail(TQ_EUNSUPPORTED, "rotation: Hadamard needs a power-of-two d, got %d", d);
     if (pi) {
@@ -280,11 +321,15 @@ tq_status tq_rotation_host(uint64_t seed, int d, tq_rot_kind kind, double *pi, d
     return TQ_OK;
 }
 
-tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation **out)
+tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotation **out)
 {
     if (!out) return fail(TQ_EINVAL, "tq_make_rotation: NULL out");
     *out = nullptr;
     if (!supported_d(d)) return fail(TQ_EUNSUPPORTED, "tq_make_rotation: d=%d not in {64, 128, 256}", d);
+    const int kv = enum_arg(kind_arg);
+    if (kv != TQ_ROT_DENSE && kv != TQ_ROT_HADAMARD && kv != TQ_ROT_HADAMARD2)
+        return fail(TQ_EINVAL, "tq_make_rotation: bad kind %d", kv);
+    const tq_rot_kind kind = static_cast<tq_rot_kind>(kv);
     const size_t dd = static_cast<size_t>(d) * d;
     std::vector<double> pi(dd), s(dd);
     tq_status st = tq_rotation_host(seed, d, kind, pi.data(), s.data());
@@ -319,7 +364,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind, tq_rotation *
     }
     if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 5 * dd);
     else for (int j = 0; j < d; ++j) host[5 * dd + j] = 1.0f;
-    auto *rot = new (std::nothrow) tq_rotation;
+    auto *rot = test_hook().host_alloc ? nullptr : new (std::nothrow) tq_rotation;
     if (!rot) return fail(TQ_ENOMEM, "tq_make_rotation: host allocation failed");
     rot->seed = seed;
     rot->d = d;
@@ -468,9 +513,10 @@ tq_status check_val_fmt(const tq_val_fmt *f, const char *who)
     return TQ_OK;
 }
 
-tq_status check_dtype(tq_dtype t, const char *who)
+tq_status check_dtype(const tq_dtype &t, const char *who)
 {
-    if (dtype_size(t) == 0) return fail(TQ_EINVAL, "%s: bad dtype %d", who, static_cast<int>(t));
+    const int v = enum_arg(t);
+    if (v != TQ_F32 && v != TQ_BF16 && v != TQ_F16) return fail(TQ_EINVAL, "%s: bad dtype %d", who, v);
     return TQ_OK;
 }
 
@@ -510,6 +556,12 @@ tq_status check_vcache(const tq_vcache &vc, const char *who)
     do {                                     \
         const tq_status st_ = (expr);        \
         if (st_ != TQ_OK) return st_;        \
+    } while (0)
+
+// the "launch" test hook: report a launch failure where kernels would be launched
+#define TQ_LAUNCH_HOOK(who)                                                       \
+    do {                                                                          \
+        if (test_hook().launch) return hip_fail(hipErrorLaunchFailure, (who));    \
     } while (0)
 
 // Decode path and split count for a shape: the matrix-core path when the key
@@ -617,7 +669,7 @@ tq_status layout_map(const tq_cache_layout *lay, const int32_t *pos, bool decode
     return TQ_OK;
 }
 
-tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv, int64_t T,
+tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtype &dtype, int B, int Hkv, int64_t T,
                              int64_t sb, int64_t sh, int64_t st, tq_kcache out, const tq::CacheMap &map,
                              void *stream, const char *who)
 {
@@ -654,11 +706,12 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, tq_dtype dtyp
     a.sfrag = fmt->rot->d_sfrag;
     a.out = out;
     a.map = map;
+    TQ_LAUNCH_HOOK(who);
     const hipError_t e = tq::launch_compress_keys(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
 
-tq_status compress_values_impl(const tq_val_fmt *fmt, const void *v, tq_dtype dtype, int B, int Hkv, int64_t T,
+tq_status compress_values_impl(const tq_val_fmt *fmt, const void *v, const tq_dtype &dtype, int B, int Hkv, int64_t T,
                                int64_t sb, int64_t sh, int64_t st, tq_vcache out, const tq::CacheMap &map,
                                void *stream, const char *who)
 {
@@ -681,6 +734,7 @@ tq_status compress_values_impl(const tq_val_fmt *fmt, const void *v, tq_dtype dt
     a.group = fmt->group;
     a.out = out;
     a.map = map;
+    TQ_LAUNCH_HOOK(who);
     const hipError_t e = tq::launch_compress_values(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
@@ -722,7 +776,7 @@ tq_status tq_append_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtype,
     return compress_values_impl(fmt, v, dtype, B, Hkv, n_new, sb, sh, st, cache, m, stream, who);
 }
 
-static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq,
+static tq_status check_decode_common(const tq_key_fmt *fmt, const void *q, const tq_dtype &dtype, int B, int Hq,
                                      int Hkv, int64_t T, const tq_kcache &kc, const char *who)
 {
     TQ_TRY(check_key_fmt(fmt, who));
@@ -794,10 +848,12 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
         a.mf.aops = reinterpret_cast<uint32_t *>(base + L.aops);
         a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
         a.mf.lscale = 1.0f;
+        TQ_LAUNCH_HOOK(who);
         const hipError_t e = tq::launch_scores_mfma(a, s);
         return e == hipSuccess ? TQ_OK : hip_fail(e, who);
     }
     a.qprep = static_cast<float *>(ws);
+    TQ_LAUNCH_HOOK(who);
     hipError_t e = tq::launch_qprep(a, s);
     if (e == hipSuccess) e = tq::launch_scores(a, s);
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
@@ -880,6 +936,7 @@ tq_status tq_compress_keys_block(const tq_block_fmt *fmt, const void *k, tq_dtyp
     a.bits = fmt->bits;
     a.pi64T = fmt->rot->d_pi64T;
     a.out = out;
+    TQ_LAUNCH_HOOK(who);
     const hipError_t e = tq::launch_compress_keys_block(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
@@ -920,6 +977,7 @@ tq_status tq_attend_decode_block(const tq_block_fmt *kfmt, const tq_val_fmt *vfm
     a.out = out;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {
+        TQ_LAUNCH_HOOK(who);
         const hipError_t e = tq::launch_attend(a, s);
         return e == hipSuccess ? TQ_OK : hip_fail(e, who);
     }
@@ -954,6 +1012,7 @@ tq_status tq_attend_decode_block(const tq_block_fmt *kfmt, const tq_val_fmt *vfm
     a.mf.qscal = reinterpret_cast<float *>(base + L.qscal);
     a.qaux = reinterpret_cast<float *>(base + L.qaux);
     a.mf.lscale = a.scale * kLog2e;
+    TQ_LAUNCH_HOOK(who);
     const hipError_t e = tq::launch_decode_block(a, s);
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
@@ -983,6 +1042,7 @@ tq_status tq_dequantize_keys(const tq_key_fmt *fmt, int B, int Hkv, int64_t T, t
     a.knorm = kc.knorm;
     a.rnorm = kc.rnorm;
     a.out = out;
+    TQ_LAUNCH_HOOK(who);
     const hipError_t e = tq::launch_dequant_keys(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TQ_OK : hip_fail(e, who);
 }
@@ -1010,7 +1070,7 @@ size_t tq_attend_paged_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int
 
 // decode attention over T tokens per sequence (flat map) or over a layout
 // cache with T = its capacity
-static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, tq_dtype dtype, int B,
+static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, const void *q, const tq_dtype &dtype, int B,
                              int Hq, int Hkv, int64_t T, tq_kcache kc, tq_vcache vc, float softmax_scale,
                              int n_splits, void *ws, size_t ws_bytes, float *out, const tq::CacheMap &map,
                              void *stream, const char *who, bool use_scratch = false)
@@ -1036,6 +1096,7 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     a.out = out;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) {
+        TQ_LAUNCH_HOOK(who);
         const hipError_t e = tq::launch_attend(a, s);
         return e == hipSuccess ? TQ_OK : hip_fail(e, who);
     }
@@ -1083,6 +1144,7 @@ static tq_status attend_impl(const tq_key_fmt *kfmt, const tq_val_fmt *vfmt, con
     a.qaux = reinterpret_cast<float *>(base + L.qaux);
     a.mf.lscale = a.scale * kLog2e;
     a.map = map;
+    TQ_LAUNCH_HOOK(who);
     hipError_t e;
     if (plan.mfma) {
         e = tq::launch_decode_mfma(a, s);

@@ -133,8 +133,12 @@ struct Density {
 // Positive-half unknowns: c[0..K) are the centroids above 0 (K = L/2), the
 // cells are [e_i, e_{i+1}] with e_0 = 0, e_i = (c_{i-1}+c_i)/2, e_K = 1.
 tq_status lloyd_max_codebook(int d, int bits, double *centroids, double *boundaries,
-                             double *residual_out)
+                             double *residual_out, int max_iters)
 {
+    // iteration caps: 400 Lloyd sweeps, then 100 Newton steps (max_iters >= 0
+    // lowers both, for the host tests of the non-convergence status)
+    const int sweeps = max_iters >= 0 && max_iters < 400 ? max_iters : 400;
+    const int newton = max_iters >= 0 && max_iters < 100 ? max_iters : 100;
     const int L = 1 << bits, K = L / 2;
     const Density f(d);
     std::vector<double> c(K), e(K + 1), mean(K), mass(K);
@@ -154,14 +158,14 @@ tq_status lloyd_max_codebook(int d, int bits, double *centroids, double *boundar
     const double span = std::fmin(4.0 / std::sqrt(static_cast<double>(d)), 0.999);
     for (int i = 0; i < K; ++i) c[i] = span * (i + 0.5) / K;
     double res = evaluate(c);
-    for (int sweep = 0; sweep < 400 && res > 1e-10; ++sweep) {
+    for (int sweep = 0; sweep < sweeps && res > 1e-10; ++sweep) {
         c = mean;
         res = evaluate(c);
     }
     // Newton on F = c - mean(c); d mean_i / d e_i = f(e_i)(mean_i - e_i)/mass_i,
     // d mean_i / d e_{i+1} = f(e_{i+1})(e_{i+1} - mean_i)/mass_i, e_0 and e_K fixed.
     std::vector<double> sub(K), dia(K), sup(K), rhs(K), trial(K);
-    for (int it = 0; it < 100 && res > 1e-15; ++it) {
+    for (int it = 0; it < newton && res > 1e-15; ++it) {
         for (int i = 0; i < K; ++i) {
             const double lo = (i > 0) ? f.pdf(e[i]) * (mean[i] - e[i]) / mass[i] : 0.0;
             const double hi = (i < K - 1) ? f.pdf(e[i + 1]) * (e[i + 1] - mean[i]) / mass[i] : 0.0;

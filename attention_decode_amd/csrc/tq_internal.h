@@ -70,7 +70,7 @@ struct CacheMap {
 uint64_t rng_draw(uint64_t seed, int stream, uint64_t k);
 double rng_normal(uint64_t seed, int stream, uint64_t n);
 tq_status lloyd_max_codebook(int d, int bits, double *centroids, double *boundaries,
-                             double *residual_out);
+                             double *residual_out, int max_iters = -1);
 void dense_rotation(uint64_t seed, int d, double *pi);
 void hadamard_signs(uint64_t seed, int d, float *signs, int stream = 1);
 void hadamard_rotation(uint64_t seed, int d, double *pi, int stream = 1);

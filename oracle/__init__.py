@@ -28,6 +28,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# an instrumented build of tq_oracle.c (sanitizer runs) may stand in for it
+_LIB_OVERRIDE = os.environ.get("TQ_ORACLE_LIB")
 _lib = None
 
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
@@ -51,7 +53,7 @@ def _l():
     global _lib
     if _lib is not None:
         return _lib
-    lib = ctypes.CDLL(build())
+    lib = ctypes.CDLL(_LIB_OVERRIDE or build())
     u64, i32, i64 = ctypes.c_uint64, ctypes.c_int, ctypes.c_int64
     vp = ctypes.c_void_p
     lib.orc_splitmix_draw.restype = u64

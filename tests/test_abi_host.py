@@ -88,6 +88,12 @@ def test_errors_before_any_device_call():
                                   None) == L.TQ_EALIGN
     assert lib.tq_compress_values(ctypes.byref(vf), ctypes.c_void_p(0x1000), 1, 1, 1, 8, 0, 0, 132, vc,
                                   None) == L.TQ_EALIGN
+    # an enum argument outside its enumerators (a C caller may pass any int)
+    vf = L.ValFmt(128, 2, 32)
+    assert lib.tq_compress_values(ctypes.byref(vf), ctypes.c_void_p(0x1000), 9, 1, 1, 8, 0, 0, 128, vc,
+                                  None) == L.TQ_EINVAL
+    assert b"dtype" in lib.tq_last_error()
+    assert lib.tq_rotation_host(1, 64, -1, dp, dp) == L.TQ_EINVAL
     # T = 0 is a no-op that needs no planes
     assert lib.tq_compress_values(ctypes.byref(vf), None, 1, 1, 1, 0, 0, 0, 128, vc, None) == L.TQ_OK
     ms, n = ctypes.c_double(), ctypes.c_int64()
@@ -161,3 +167,62 @@ def test_split_policy_and_workspace():
     assert lib.tq_scores_workspace_bytes(ctypes.byref(kf3), 2, 8) >= need3
     assert lib.tq_scores_workspace_bytes(None, 2, 8) == 0
     assert lib.tq_scores_workspace_bytes(ctypes.byref(kf), 0, 8) == 0
+
+
+# ------------------------------------------------------ forced failure paths
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except L.TQError as e:
+        return e.status, str(e)
+    return L.TQ_OK, ""
+
+
+def test_forced_nonconvergence(monkeypatch):
+    """The Lloyd-Max iteration cap (TQ_TEST_HOOK=codebook_iters=N) gives
+    TQ_ENOTCONV with the residual in the message, and no handle."""
+    monkeypatch.setenv("TQ_TEST_HOOK", "codebook_iters=0")
+    st, msg = _status(tq.tq_codebook_host, 128, 3)
+    assert st == L.TQ_ENOTCONV and "residual" in msg
+    h = ctypes.c_void_p()
+    assert L.lib().tq_build_codebook(128, 3, ctypes.byref(h)) == L.TQ_ENOTCONV
+    assert h.value is None
+    # a few sweeps are not enough either at 7 bits
+    monkeypatch.setenv("TQ_TEST_HOOK", "codebook_iters=3")
+    assert _status(tq.tq_codebook_host, 256, 7)[0] == L.TQ_ENOTCONV
+    # without the hook the same tables converge
+    monkeypatch.delenv("TQ_TEST_HOOK")
+    c, t = tq.tq_codebook_host(256, 7)
+    assert np.abs(c - O.codebook(256, 7)[0]).max() < 1e-12
+
+
+def test_forced_handle_allocation_failure(monkeypatch):
+    """A failed host allocation in handle creation (TQ_TEST_HOOK=host_alloc)
+    gives TQ_ENOMEM and no handle; host-only calls are unaffected."""
+    monkeypatch.setenv("TQ_TEST_HOOK", "host_alloc")
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.tq_build_codebook(128, 2, ctypes.byref(h)) == L.TQ_ENOMEM
+    assert h.value is None and b"allocation" in lib.tq_last_error()
+    assert lib.tq_make_rotation(7, 128, L.TQ_ROT_DENSE, ctypes.byref(h)) == L.TQ_ENOMEM
+    assert h.value is None and b"allocation" in lib.tq_last_error()
+    c, _ = tq.tq_codebook_host(128, 2)
+    assert c.shape == (4,)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_device_errors_map_to_ehip():
+    """Without a GPU the device uploads of handle creation fail in the HIP
+    runtime: TQ_EHIP with the runtime's message, and no handle."""
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: the uploads succeed")
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.tq_build_codebook(128, 2, ctypes.byref(h)) == L.TQ_EHIP
+    assert h.value is None and b"device" in lib.tq_last_error()
+    assert lib.tq_make_rotation(7, 128, L.TQ_ROT_DENSE, ctypes.byref(h)) == L.TQ_EHIP
+    assert h.value is None
