@@ -334,7 +334,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
     std::vector<double> pi(dd), s(dd);
     tq_status st = tq_rotation_host(seed, d, kind, pi.data(), s.data());
     if (st != TQ_OK) return st;
-    std::vector<float> host(5 * dd + 3 * d);
+    std::vector<float> host(5 * dd + 5 * d);
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
             host[i * d + j] = static_cast<float>(pi[i * d + j]);            // Pi
@@ -364,6 +364,11 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
     }
     if (kind == TQ_ROT_HADAMARD) tq::hadamard_signs(seed, d, host.data() + 5 * dd);
     else for (int j = 0; j < d; ++j) host[5 * dd + j] = 1.0f;
+    // the sign vectors of the Walsh-Hadamard rounds (D1, then D2 of the second
+    // round) for the butterfly compressor; ones where a round is absent
+    for (int j = 0; j < 2 * d; ++j) host[5 * dd + 3 * d + j] = 1.0f;
+    if (kind != TQ_ROT_DENSE) tq::hadamard_signs(seed, d, host.data() + 5 * dd + 3 * d, 1);
+    if (kind == TQ_ROT_HADAMARD2) tq::hadamard_signs(seed, d, host.data() + 5 * dd + 4 * d, 3);
     auto *rot = test_hook().host_alloc ? nullptr : new (std::nothrow) tq_rotation;
     if (!rot) return fail(TQ_ENOMEM, "tq_make_rotation: host allocation failed");
     rot->seed = seed;
@@ -441,6 +446,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
     rot->d_dsign = base + 5 * dd;
     rot->d_pisum = base + 5 * dd + d;
     rot->d_spisum = base + 5 * dd + 2 * d;
+    rot->d_wht = base + 5 * dd + 3 * d;
     rot->sq_bound = static_cast<float>(rmax * (1.0 + 1e-6));
     *out = rot;
     return TQ_OK;
@@ -557,6 +563,17 @@ tq_status check_vcache(const tq_vcache &vc, const char *who)
         const tq_status st_ = (expr);        \
         if (st_ != TQ_OK) return st_;        \
     } while (0)
+
+// Implementation of the Walsh-Hadamard rotations in the key compressor
+// (TQ_HADAMARD_KERNEL, read at each call): "butterfly" (default) runs the
+// randomized butterfly in registers, "matrix" the +-1 sign matrix as one exact
+// bf16 term on the matrix cores.  Both compute the same rotation; their
+// roundings differ only in fp32 summation order.
+bool hadamard_butterfly()
+{
+    const char *s = std::getenv("TQ_HADAMARD_KERNEL");
+    return !(s && std::strcmp(s, "matrix") == 0);
+}
 
 // the "launch" test hook: report a launch failure where kernels would be launched
 #define TQ_LAUNCH_HOOK(who)                                                       \
@@ -696,6 +713,9 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     a.piT = fmt->rot->d_piT;
     a.sT = fmt->rot->d_sT;
     a.dsign = fmt->rot->d_dsign;
+    a.wht = fmt->rot->d_wht;
+    a.wht_rounds = fmt->rot->kind == TQ_ROT_HADAMARD2 ? 2 : fmt->rot->kind == TQ_ROT_HADAMARD ? 1 : 0;
+    a.wht_kernel = hadamard_butterfly();
     a.centroids = fmt->cb->d_centroids;
     a.boundaries = fmt->cb->d_boundaries;
     a.grid = fmt->cb->d_grid;

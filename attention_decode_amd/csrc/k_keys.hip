@@ -184,6 +184,151 @@ constexpr size_t key_smem_bytes()
            + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
 }
 
+
+// Code idx = #{t_i < y} of one rotated coordinate and its residual y - c[idx].
+// Up to 3 bits: |y| placed among the positive boundaries tp of the exactly
+// symmetric codebook by a binary search in registers, the centroid taken from
+// the positive ones cp, idx and the residual fixed by the sign of y (bit for
+// bit what the full count gives, up to exact ties).  From 4 bits: the uniform
+// grid gives a count at most two below the true one, and two exact
+// comparisons with the LDS boundaries finish it.
+template <int BITS>
+__device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BITS) / 2 > 1 ? (1 << BITS) / 2 - 1 : 1],
+                                            const float (&cp)[(1 << BITS) / 2], const KeySmem &s, const KeyLaunch &a,
+                                            float &res)
+{
+    constexpr int H = (1 << BITS) / 2;
+    int pos;
+    if constexpr (BITS <= 3) {
+        const float ay = fabsf(y);
+        int cnt = 0;          // positive boundaries below |y|
+        float c = cp[0];
+        if constexpr (BITS == 2) {
+            const bool b0 = ay > tp[0];
+            cnt = b0 ? 1 : 0;
+            c = b0 ? cp[1] : cp[0];
+        } else if constexpr (BITS == 3) {
+            const bool b1 = ay > tp[1];
+            const bool b0 = ay > (b1 ? tp[2] : tp[0]);
+            cnt = (b1 ? 2 : 0) + (b0 ? 1 : 0);
+            const float clo = b0 ? cp[1] : cp[0], chi = b0 ? cp[3] : cp[2];
+            c = b1 ? chi : clo;
+        }
+        const bool up = y > 0.0f;
+        pos = cnt ^ (up ? H : H - 1);     // H + cnt above zero, H - 1 - cnt below (cnt < H)
+        const float dv = ay - c;
+        res = up ? dv : -dv;
+    } else {
+        int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
+        c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
+        pos = s.grid[c];
+        pos += (y > s.bnd[pos]) ? 1 : 0;
+        pos += (y > s.bnd[pos]) ? 1 : 0;
+        res = y - s.cent[pos];
+    }
+    return pos;
+}
+
+// z = S r for the residual operands of key tiles kt0 .. kt0 + KR - 1 (LDS,
+// B-operand order) on this wave's rows of S; sign bits [z >= 0] OR-ed into
+// the sign words.  Ends with a workgroup barrier (the pass's residual operands
+// are read before the next pass writes them).
+template <int D, int KR>
+__device__ __forceinline__ void qjl_signs(const KeyLaunch &a, const KeySmem &s, int kt0, int wave, int lane)
+{
+    constexpr int KS = D / 32, RTW = D / 64, SWN = D / 32;
+    const int col = lane & 15, kb = lane >> 4;
+    const uint4 *sfr = reinterpret_cast<const uint4 *>(a.sfrag);
+    f32x4 zacc[RTW][KR];
+#pragma unroll
+    for (int j = 0; j < RTW; ++j)
+#pragma unroll
+        for (int kt = 0; kt < KR; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 rf[KR][2];
+#pragma unroll
+        for (int kt = 0; kt < KR; ++kt) {
+            rf[kt][0] = s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + lane];
+            rf[kt][1] = s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < RTW; ++j) {
+            const int rt = wave * RTW + j;
+            const uint4 s0 = sfr[((rt * KS + ks) * 2 + 0) * 64 + lane];
+            const uint4 s1 = sfr[((rt * KS + ks) * 2 + 1) * 64 + lane];
+#pragma unroll
+            for (int kt = 0; kt < KR; ++kt) {
+                zacc[j][kt] = mfma_bf16(s0, rf[kt][0], zacc[j][kt]);
+                zacc[j][kt] = mfma_bf16(s0, rf[kt][1], zacc[j][kt]);
+                zacc[j][kt] = mfma_bf16(s1, rf[kt][0], zacc[j][kt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RTW; ++j) {
+        const int rt = wave * RTW + j;
+        const int off = 16 * rt + 4 * kb;
+#pragma unroll
+        for (int kt = 0; kt < KR; ++kt) {
+            uint32_t nib = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
+            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWN + (off >> 5)], nib << (off & 31));
+        }
+    }
+    __syncthreads();
+}
+
+// The workgroup's KEYS packed keys to the planes: contiguous rows of every
+// plane, or (when appending to a layout cache) each key at its own row.
+// ||k||^2 and ||r||^2 arrive as NPN and NPR fp64 partial sums per key.
+template <int D, int BITS, int KEYS, int NPN, int NPR>
+__device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s, int64_t n0, int64_t n_total,
+                                           int64_t *s_row, bool qjl)
+{
+    constexpr int CW = D * BITS / 32, SWN = D / 32;
+    const int tid = threadIdx.x;
+    const int nk = static_cast<int>(n_total - n0 < KEYS ? n_total - n0 : KEYS);
+    if (a.map.mode == CacheMap::kFlat) {
+        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
+        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
+        if (qjl) {
+            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
+            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+        }
+        if (tid < nk) s_row[tid] = n0 + tid;
+    } else {
+        if (tid < nk) s_row[tid] = out_row(a.map, a.H, a.T, n0 + tid);
+        __syncthreads();
+        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes);
+        for (int i = tid; i < nk * CW; i += kThreads) {
+            const int64_t r = s_row[i / CW];
+            if (r >= 0) codes[r * CW + i % CW] = s.cw[i];
+        }
+        if (qjl) {
+            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs);
+            for (int i = tid; i < nk * SWN; i += kThreads) {
+                const int64_t r = s_row[i / SWN];
+                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[i];
+            }
+        }
+    }
+    if (tid < nk && s_row[tid] >= 0) {
+        const int64_t r = s_row[tid];
+        double n2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < NPN; ++q) n2 += s.nrm2[q * KEYS + tid];
+        a.out.knorm[r] = static_cast<float>(sqrt(n2));
+        if (qjl) {
+            double r2 = 0.0;
+#pragma unroll
+            for (int q = 0; q < NPR; ++q) r2 += s.rho2[q * KEYS + tid];
+            a.out.rnorm[r] = static_cast<float>(sqrt(r2));
+        }
+    }
+}
+
 template <int D, typename TIn, int BITS, int KT>
 __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
@@ -280,7 +425,6 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 
     // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r
     const uint4 *pif = reinterpret_cast<const uint4 *>(a.pifrag);
-    const uint4 *sfr = reinterpret_cast<const uint4 *>(a.sfrag);
     f32x4 acc[RTW][kKT];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
@@ -363,34 +507,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float y = acc[j][kt][r] * inv_n[kt];
-                int pos;
-                if constexpr (BITS <= 3) {
-                    const float ay = fabsf(y);
-                    int cnt = 0;          // positive boundaries below |y|
-                    float c = cp[0];
-                    if constexpr (BITS == 2) {
-                        const bool b0 = ay > tp[0];
-                        cnt = b0 ? 1 : 0;
-                        c = b0 ? cp[1] : cp[0];
-                    } else if constexpr (BITS == 3) {
-                        const bool b1 = ay > tp[1];
-                        const bool b0 = ay > (b1 ? tp[2] : tp[0]);
-                        cnt = (b1 ? 2 : 0) + (b0 ? 1 : 0);
-                        const float clo = b0 ? cp[1] : cp[0], chi = b0 ? cp[3] : cp[2];
-                        c = b1 ? chi : clo;
-                    }
-                    const bool up = y > 0.0f;
-                    pos = cnt ^ (up ? H : H - 1);     // H + cnt above zero, H - 1 - cnt below (cnt < H)
-                    const float dv = ay - c;
-                    res[r] = up ? dv : -dv;
-                } else {
-                    int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
-                    c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
-                    pos = s.grid[c];
-                    pos += (y > s.bnd[pos]) ? 1 : 0;
-                    pos += (y > s.bnd[pos]) ? 1 : 0;
-                    res[r] = y - s.cent[pos];
-                }
+                const int pos = encode_coord<BITS>(y, tp, cp, s, a, res[r]);
                 rr = fmaf(res[r], res[r], rr);
                 chunk |= static_cast<uint32_t>(pos) << (bits * r);
             }
@@ -418,92 +535,333 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 
     // ---- 4. z = S r on this wave's rows; signs [z >= 0] (skipped for the
     // first-stage format, m = 0; the condition is uniform over the launch)
-    if (qjl) {
-    f32x4 zacc[RTW][KR];
-#pragma unroll
-    for (int j = 0; j < RTW; ++j)
-#pragma unroll
-        for (int kt = 0; kt < KR; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 rf[KR][2];
-#pragma unroll
-        for (int kt = 0; kt < KR; ++kt) {
-            rf[kt][0] = s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + lane];
-            rf[kt][1] = s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + lane];
-        }
-#pragma unroll
-        for (int j = 0; j < RTW; ++j) {
-            const int rt = wave * RTW + j;
-            const uint4 s0 = sfr[((rt * KS + ks) * 2 + 0) * 64 + lane];
-            const uint4 s1 = sfr[((rt * KS + ks) * 2 + 1) * 64 + lane];
-#pragma unroll
-            for (int kt = 0; kt < KR; ++kt) {
-                zacc[j][kt] = mfma_bf16(s0, rf[kt][0], zacc[j][kt]);
-                zacc[j][kt] = mfma_bf16(s0, rf[kt][1], zacc[j][kt]);
-                zacc[j][kt] = mfma_bf16(s1, rf[kt][0], zacc[j][kt]);
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < RTW; ++j) {
-        const int rt = wave * RTW + j;
-        const int off = 16 * rt + 4 * kb;
-#pragma unroll
-        for (int kt = 0; kt < KR; ++kt) {
-            uint32_t nib = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
-            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWN + (off >> 5)], nib << (off & 31));
-        }
-    }
-    __syncthreads();   // (also: this pass's residual operands are read before the next pass writes them)
-    }
+    if (qjl) qjl_signs<D, KR>(a, s, kt0, wave, lane);
     }   // passes
 
-    // ---- 5. store the WG's keys: contiguous rows of every plane, or (when
-    // appending to a layout cache) each key at its own row
-    const int nk = static_cast<int>(n_total - n0 < kKeys ? n_total - n0 : kKeys);
-    if (a.map.mode == CacheMap::kFlat) {
-        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
-        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
-        if (qjl) {
-            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
-            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+    // ---- 5. store the WG's keys
+    store_keys<D, BITS, kKeys, TPK, 4>(a, s, n0, n_total, s_row, qjl);
+}
+
+
+// ---------------------------------------------------------------------------
+// Walsh-Hadamard rotations (TQ_ROT_HADAMARD: y = H D1 k / sqrt(d);
+// TQ_ROT_HADAMARD2: y = H D2 H D1 k / d) as a randomized butterfly in
+// registers (tproger.ru article, section "Implementations": the Walsh-Hadamard
+// transform as the O(d log d) rotation).
+//
+// A key's d coordinates sit in the 16 lanes of one DPP row, CPL = d / 16
+// consecutive coordinates per lane.  The stages over the coordinate bits below
+// log2(CPL) are add/sub pairs in registers; the four above them run across the
+// row as v_fmac_f32 with a DPP source: self + s * partner, partners along the
+// quad swaps (lane ^ 1, lane ^ 2), the half-row mirror (lane ^ 7) and the row
+// mirror (lane ^ 15), with s = +-1 per lane and stage (kWhtNeg).  Since the
+// mirrors pair lanes along 7 and 15 rather than 4 and 8, the lane stages give
+// Sylvester's H_16 up to a fixed relabelling of the lanes and a sign per lane:
+// lane p ends with sign(p) * (H_16 v)[out(p)], out(p) the nibble p of
+// kWhtOut, sign(p) = -1 where bit p of kWhtEps is set (H_16 is symmetric in
+// that relabelling, so a second round fed with the first round's lanes
+// undoes it and ends in natural order).  The lane holding output chunk c
+// then encodes coordinates [CPL c, CPL c + CPL) of its key directly: codes,
+// residual, and the residual's B-operand slots of the QJL product.
+constexpr uint32_t kWhtNeg[4] = {0x5a5au, 0x3c3cu, 0x0ff0u, 0xff00u};
+constexpr uint32_t kWhtEps = 0x9696u;
+constexpr uint64_t kWhtOut = 0x8deb7214c9af3650ull;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
+// sums over the 16 lanes of a DPP row, left in every lane of the row
+__device__ __forceinline__ double row16_sum_f64(double x)
+{
+    x += dpp_f64<0xB1>(x);
+    x += dpp_f64<0x4E>(x);
+    x += dpp_f64<0x141>(x);
+    return x + dpp_f64<0x140>(x);
+}
+
+__device__ __forceinline__ float row16_sum_f32(float x)
+{
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    return x + dpp_f32<0x140>(x);
+}
+
+// one round: the in-register stages, then the four lane stages
+template <int CPL>
+__device__ __forceinline__ void wht_round(float (&x)[CPL], const float (&sg)[4])
+{
+#pragma unroll
+    for (int h = 1; h < CPL; h *= 2)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+            if (!(e & h)) {
+                const float u = x[e], v = x[e + h];
+                x[e] = u + v;
+                x[e + h] = u - v;
+            }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0xB1>(x[e]), sg[0], x[e]);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x4E>(x[e]), sg[1], x[e]);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x141>(x[e]), sg[2], x[e]);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x140>(x[e]), sg[3], x[e]);
+}
+
+// CPL consecutive input elements as fp32 (16-byte aligned for CPL * size >= 16)
+template <typename TIn, int CPL>
+__device__ __forceinline__ void load_chunk(const TIn *p, float (&x)[CPL])
+{
+    if constexpr (CPL * sizeof(TIn) >= 16) {
+        constexpr int NV = sizeof(TIn) == 4 ? CPL / 4 : CPL / 8;     // 16-byte loads
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            if constexpr (sizeof(TIn) == 4) {
+                const float4 v = reinterpret_cast<const float4 *>(p)[c];
+                x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+            } else {
+                float v[8];
+                load8_as_f32(p + 8 * c, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * c + e] = v[e];
+            }
         }
-        if (tid < nk) s_row[tid] = n0 + tid;
     } else {
-        if (tid < nk) s_row[tid] = out_row(a.map, a.H, a.T, n0 + tid);
-        __syncthreads();
-        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes);
-        for (int i = tid; i < nk * CW; i += kThreads) {
-            const int64_t r = s_row[i / CW];
-            if (r >= 0) codes[r * CW + i % CW] = s.cw[i];
-        }
-        if (qjl) {
-            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs);
-            for (int i = tid; i < nk * SWN; i += kThreads) {
-                const int64_t r = s_row[i / SWN];
-                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[i];
+        // four 2-byte elements (d = 64)
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        const uint32_t u[2] = {w.x, w.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if constexpr (__is_same(TIn, bf16_t)) {
+                x[2 * i] = bf16_to_f32(u[i] & 0xffffu);
+                x[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+            } else {
+                x[2 * i] = f16_bits_to_f32(u[i] & 0xffffu);
+                x[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
             }
         }
     }
-    if (tid < nk && s_row[tid] >= 0) {
-        const int64_t r = s_row[tid];
-        double n2 = 0.0;
-#pragma unroll
-        for (int q = 0; q < TPK; ++q) n2 += s.nrm2[q * kKeys + tid];
-        a.out.knorm[r] = static_cast<float>(sqrt(n2));
-        if (qjl) {
-            const double r2 = s.rho2[tid] + s.rho2[kKeys + tid] + s.rho2[2 * kKeys + tid] + s.rho2[3 * kKeys + tid];
-            a.out.rnorm[r] = static_cast<float>(sqrt(r2));
-        }
+}
+
+template <int D, typename TIn, int KT>
+constexpr size_t key_smem_bytes_wht(int bits)
+{
+    constexpr size_t keys = 16 * KT;
+    const size_t rfrag = sizeof(uint4) * key_pass_tiles<D, TIn, KT>() * (D / 32) * 2 * 64;
+    return rfrag + sizeof(uint32_t) * keys * (D * bits / 32 + D / 32) + sizeof(double) * 2 * keys
+           + sizeof(float) * 512 + (bits >= 4 ? kMaxGrid : 0);
+}
+
+// One 256-thread workgroup encodes 16 KT keys; wave w takes keys 16 t + 4 w + g
+// of key tile t in lane row g.  Steps: load (each lane its CPL elements) and
+// ||k||^2 (exact squares in fp64, summed over the row); the butterfly;
+// codes, residual and ||r||^2 per lane; then, per pass of KR tiles, the QJL
+// product and the store shared with the matrix-core kernel.
+template <int D, typename TIn, int BITS, int KT, int ROUNDS>
+__global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_compress_keys_wht(KeyLaunch a, int64_t n_total)
+{
+    constexpr int CPL = D / 16;          // coordinates per lane
+    constexpr int KS = D / 32;
+    constexpr int L = 1 << BITS;
+    constexpr int H = L / 2;
+    constexpr int CW = D * BITS / 32, SWN = D / 32;
+    constexpr int kKeys = 16 * KT;
+    constexpr int KR = key_pass_tiles<D, TIn, KT>();
+    constexpr int NSW = (BITS * CPL + 31) / 32;   // code words of one lane's segment
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    __shared__ int64_t s_row[kKeys];
+    KeySmem s;
+    {
+        unsigned char *p = smem_raw;
+        s.rfrag = reinterpret_cast<uint4 *>(p);   p += sizeof(uint4) * KR * KS * 2 * 64;
+        s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kKeys;
+        s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kKeys;
+        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
+        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWN;
+        s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
+        s.bnd = reinterpret_cast<float *>(p);     p += sizeof(float) * 256;
+        s.grid = p;
     }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, pl = lane & 15;      // lane row (key of the round) and lane in the row
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kKeys;
+
+    // codebook tables, loaded ahead of the keys
+    const int ti = tid < L ? tid : L - 1;
+    const float cent_v = a.centroids[ti];
+    const float bnd_v = a.boundaries[ti];
+    uint4 grid_v = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BITS >= 4) {
+        const int ng16 = a.ngrid / 16;
+        grid_v = reinterpret_cast<const uint4 *>(a.grid)[tid < ng16 ? tid : ng16 - 1];
+    }
+    for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
+    for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
+
+    // this lane's elements of each of its KT keys (slots past the last key
+    // reload that key; their results are never stored)
+    const int last = static_cast<int>(n_total - 1 - n0 < kKeys - 1 ? n_total - 1 - n0 : kKeys - 1);
+    const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
+    float x[KT][CPL];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int kk = 16 * t + 4 * wave + g;
+        int64_t tt = t0 + (kk < last ? kk : last), h = bh0 % a.H, b = bh0 / a.H;
+        while (tt >= a.T) {
+            tt -= a.T;
+            if (++h == a.H) {
+                h = 0;
+                ++b;
+            }
+        }
+        load_chunk<TIn, CPL>(static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + tt * a.st + CPL * pl, x[t]);
+    }
+    // round signs of this lane: D1 of its input coordinates; for a second
+    // round D2 of the coordinates it holds after the first, times its sign
+    float d1[CPL], d2[ROUNDS == 2 ? CPL : 1];
+    const int out1 = static_cast<int>((kWhtOut >> (4 * pl)) & 15);
+    const float eps = ((kWhtEps >> pl) & 1u) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) d1[e] = a.wht[CPL * pl + e];
+    if constexpr (ROUNDS == 2) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) d2[e] = a.wht[D + CPL * out1 + e] * eps;
+    }
+    float sg[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sg[k] = ((kWhtNeg[k] >> pl) & 1u) ? -1.0f : 1.0f;
+    if (tid < L) {
+        s.cent[tid] = cent_v;
+        s.bnd[tid] = bnd_v;
+    }
+    if constexpr (BITS >= 4)
+        if (tid < a.ngrid / 16) reinterpret_cast<uint4 *>(s.grid)[tid] = grid_v;
+    __syncthreads();   // cleared words, codebook tables
+
+    float tp[H > 1 ? H - 1 : 1], cp[H];
+    if constexpr (BITS <= 3) {
+#pragma unroll
+        for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
+#pragma unroll
+        for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
+    }
+    // output chunk of this lane (one round: relabelled; two: natural)
+    const int chunk = ROUNDS == 1 ? out1 : pl;
+    const bool qjl = a.m > 0;
+#pragma unroll
+    for (int kt0 = 0; kt0 < KT; kt0 += KR) {
+#pragma unroll
+        for (int t = kt0; t < kt0 + KR; ++t) {
+            const int key = 16 * t + 4 * wave + g;
+            // ||k||^2: exact squares in fp64, summed over the key's 16 lanes
+            double ss = 0.0;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) ss = fma(static_cast<double>(x[t][e]), static_cast<double>(x[t][e]), ss);
+            ss = row16_sum_f64(ss);
+            float v[CPL];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) v[e] = x[t][e] * d1[e];
+            wht_round<CPL>(v, sg);
+            if constexpr (ROUNDS == 2) {
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) v[e] *= d2[e];
+                wht_round<CPL>(v, sg);
+            }
+            const float n2 = static_cast<float>(ss);
+            const float scale = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) * eps : 0.0f;
+            // codes and residual of coordinates [CPL chunk, CPL chunk + CPL)
+            float res[CPL];
+            uint32_t seg[NSW + 1];
+#pragma unroll
+            for (int i = 0; i <= NSW; ++i) seg[i] = 0u;
+            float rr = 0.0f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int pos = encode_coord<BITS>(v[e] * scale, tp, cp, s, a, res[e]);
+                rr = fmaf(res[e], res[e], rr);
+                const int bo = BITS * e;
+                seg[bo >> 5] |= static_cast<uint32_t>(pos) << (bo & 31);
+                if ((bo & 31) + BITS > 32) seg[(bo >> 5) + 1] |= static_cast<uint32_t>(pos) >> (32 - (bo & 31));
+            }
+            // the lane's CPL codes start at bit BITS CPL chunk of the key's row
+            const int bit0 = BITS * CPL * chunk, w0 = bit0 >> 5, sh0 = bit0 & 31;
+#pragma unroll
+            for (int i = 0; i <= NSW; ++i) {
+                const uint32_t word = sh0 ? ((seg[i] << sh0) | (i ? seg[i - 1] >> (32 - sh0) : 0u)) : seg[i];
+                if (word != 0u && w0 + i < CW) atomicOr(&s.cw[key * CW + w0 + i], word);
+            }
+            // residual as bf16 hi + lo terms in the B-operand slots of the QJL
+            // product: coordinate l at k-step l / 32, k-block (l / 4) % 4,
+            // element 4 ((l / 16) % 2) + l % 4 (the k order of the S fragments)
+            const int col = 4 * wave + g;
+#pragma unroll
+            for (int q = 0; q < CPL / 4; ++q) {
+                const int l = CPL * chunk + 4 * q;
+                const int rt = l >> 4, kbq = (l >> 2) & 3;
+                const uint32_t h01 = bf16x2(res[4 * q], res[4 * q + 1]), h23 = bf16x2(res[4 * q + 2], res[4 * q + 3]);
+                const uint32_t l01 = bf16x2(res[4 * q] - __uint_as_float(h01 << 16),
+                                            res[4 * q + 1] - __uint_as_float(h01 & 0xffff0000u));
+                const uint32_t l23 = bf16x2(res[4 * q + 2] - __uint_as_float(h23 << 16),
+                                            res[4 * q + 3] - __uint_as_float(h23 & 0xffff0000u));
+                const int slot = ((t - kt0) * KS + (rt >> 1)) * 2;
+                uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[(slot + 0) * 64 + col + 16 * kbq]);
+                uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[(slot + 1) * 64 + col + 16 * kbq]);
+                const int hw = 2 * (rt & 1);
+                *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(l01, l23);
+            }
+            rr = row16_sum_f32(rr);
+            if (pl == 0) {
+                s.nrm2[key] = ss;
+                s.rho2[key] = static_cast<double>(rr);
+            }
+        }
+        __syncthreads();
+        if (qjl) qjl_signs<D, KR>(a, s, kt0, wave, lane);
+    }
+    store_keys<D, BITS, kKeys, 1, 1>(a, s, n0, n_total, s_row, qjl);
+}
+
+template <int D, typename TIn, int BITS, int KT, int ROUNDS>
+hipError_t launch_keys_wht(const KeyLaunch &a, hipStream_t stream)
+{
+    const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
+    constexpr size_t smem = key_smem_bytes_wht<D, TIn, KT>(BITS);
+    auto kern = k_compress_keys_wht<D, TIn, BITS, KT, ROUNDS>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    constexpr int keys = 16 * KT;
+    const int64_t blocks = (n + keys - 1) / keys;
+    void *tok;
+    prof_begin("tq_compress_keys", stream, &tok);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), smem, stream, a, n);
+    prof_end(tok, stream);
+    return hipGetLastError();
 }
 
 template <int D, typename TIn, int BITS, int KT>
 hipError_t launch_keys_k(const KeyLaunch &a, hipStream_t stream)
 {
+    if (a.wht_kernel && a.wht_rounds == 1) return launch_keys_wht<D, TIn, BITS, KT, 1>(a, stream);
+    if (a.wht_kernel && a.wht_rounds == 2) return launch_keys_wht<D, TIn, BITS, KT, 2>(a, stream);
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
     constexpr size_t smem = key_smem_bytes<D, TIn, BITS, KT>();
     auto kern = k_compress_keys<D, TIn, BITS, KT>;

@@ -34,6 +34,7 @@ struct tq_rotation {
     float *d_spiT = nullptr;    // [d][m]  transpose of S Pi (Sq = S Pi q in one product)
     float *d_pisum = nullptr;   // [d]     column sums of Pi: sum_j (Pi q)_j = pisum . q
     float *d_spisum = nullptr;  // [d]     column sums of S Pi
+    float *d_wht = nullptr;     // [2][d]  signs D1, D2 of the Walsh-Hadamard rounds (+-1; ones if absent)
     float sq_bound = 0.0f;      // max row norm of S Pi (rounded up): |(S Pi q)_i| <= sq_bound |q|
     double *d_pi64T = nullptr;  // [d][d]  fp64 transpose of Pi (block-format compressor)
     // bf16 operand fragments of the matrix-core key compressor, in lane order
@@ -87,6 +88,9 @@ struct KeyLaunch {
     bool hadamard;              // Pi = integer matrix * rot_scale, exact in one bf16 term
     float rot_scale;            // 1/sqrt(d) (one Hadamard round), 1/d (two rounds)
     const float *piT, *sT, *dsign, *centroids, *boundaries;
+    const float *wht;           // [2][d] Walsh-Hadamard round signs D1, D2
+    int wht_rounds;             // 0 dense, 1 or 2 Walsh-Hadamard rounds
+    bool wht_kernel;            // Walsh-Hadamard rounds as the register butterfly (else the +-1 matrix product)
     const uint8_t *grid;
     int ngrid;
     float grid_lo, grid_scale;

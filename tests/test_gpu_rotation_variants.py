@@ -59,3 +59,43 @@ def test_two_round_hadamard_decode(torch_cuda, d, bits, Hkv, Hq, vb, g, T):
     sc = tq.tq_scores(fm.kf, q.cuda(), kc, w.Hkv, w.T)
     torch.cuda.synchronize()
     P.check_scores(sc.double().cpu().numpy(), osc, qn, ok.knorm.reshape(shape), w.Hkv)
+
+
+# Both implementations of the Walsh-Hadamard rotations in the key compressor:
+# the randomized butterfly in registers (DPP lane stages) and the +-1 sign
+# matrix on the matrix cores, each against the oracle under the flip rule, on
+# every head dim, input dtype, one and two rounds, both key tilings (64-key
+# workgroups for large launches, 32-key ones for small), ragged tails, and the
+# first-stage format (no QJL rows).
+HAD_CASES = [
+    # (d, bits, rot, dtype, B, Hkv, T, qjl)
+    (128, 2, "hadamard", "bfloat16", 2, 8, 777, True),
+    (128, 3, "hadamard", "float32", 1, 2, 300, True),
+    (64, 4, "hadamard", "bfloat16", 1, 3, 333, True),
+    (64, 2, "hadamard2", "float32", 2, 1, 129, True),
+    (256, 7, "hadamard", "bfloat16", 2, 2, 300, True),
+    (256, 2, "hadamard2", "bfloat16", 1, 2, 515, True),
+    (256, 5, "hadamard", "float32", 1, 1, 200, True),
+    (128, 2, "hadamard", "bfloat16", 64, 8, 128, True),     # 64-key workgroups (>= 512 of them)
+    (256, 7, "hadamard2", "bfloat16", 32, 4, 256, True),    # 64-key workgroups, two residual passes
+    (128, 3, "hadamard", "bfloat16", 2, 2, 301, False),     # first stage
+]
+
+
+@pytest.mark.parametrize("kernel", ["butterfly", "matrix"])
+@pytest.mark.parametrize("case", HAD_CASES, ids=lambda c: "d{}b{}{}{}B{}H{}T{}{}".format(
+    c[0], c[1], c[2], c[3][:4], c[4], c[5], c[6], "" if c[7] else "mse"))
+def test_hadamard_kernels_match_oracle(torch_cuda, monkeypatch, kernel, case):
+    torch = torch_cuda
+    d, bits, rot, dtype, B, Hkv, T, qjl = case
+    monkeypatch.setenv("TQ_HADAMARD_KERNEL", kernel)
+    w = replace(BASE, name="had", B=B, Hkv=Hkv, T=T, d=d, k_bits=bits, rot=rot, dtype=dtype, seed=67,
+                keys="scaled", kv_ratio=150.0, qjl=qjl)
+    fm = P.Formats(w, 0)
+    kf = tq.KeyFormat(d, bits, fm.cb, fm.rot, qjl_m=w.qjl_m)
+    k = W.make_keys(w, device="cuda")
+    kc = tq.alloc_key_cache(kf, B, Hkv, T)
+    tq.tq_compress_keys(kf, k, kc)
+    torch.cuda.synchronize()
+    st = P.compare_keys(fm, kc, P.f64(k.cpu()).reshape(-1, d))
+    print(f"[hadamard {kernel}] {case}: {st}", flush=True)
