@@ -25,11 +25,16 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+# Per-file code generation options (none at present).
+FILE_FLAGS: dict[str, list[str]] = {}
+
+
 def compile_cmd(src: str, obj: str) -> list[str]:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     return [hipcc(), *lang, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            *FILE_FLAGS.get(os.path.basename(src), []),
             "-I", os.path.join(PKG, "..", "include"), "-c", src, "-o", obj]
 
 

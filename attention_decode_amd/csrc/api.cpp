@@ -587,6 +587,9 @@ bool hadamard_butterfly()
 // stage multiplied by scale log2(e)
 constexpr float kLog2e = 1.4426950408889634f;
 
+// compute units of the target GPU (MI355X) the decode plan fills
+constexpr int64_t kDecodeCUs = 256;
+
 struct DecodePlan {
     bool mfma = false;
     int gc = 0, nqc = 0, mt = 0, units = 0, splits = 0, steps = 0;
@@ -610,11 +613,26 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     p.units = B * Hkv * p.nqc;
     p.steps = p.mfma ? tq::mfma_score_steps(fmt->d, fmt->mse_bits, fmt->qjl_m) : 0;
     // workgroups per launch: about eight per CU for the d = 128 matrix-core
-    // kernels (short enough splits that the last round is cheap), two for
-    // d = 256 (one workgroup per CU at a time, and a longer set-up), four for
-    // the scalar kernels
-    const int64_t target = p.mfma ? (fmt->d >= 256 ? 512 : 2048) : 1024;
+    // kernels (short enough splits that the last round is cheap), four for the
+    // scalar kernels; d = 256 below
+    const int64_t target = p.mfma ? 2048 : 1024;
     int64_t want = (target + p.units - 1) / p.units;
+    if (p.mfma && fmt->d >= 256) {
+        // one workgroup per CU at a time: the split count that minimises the
+        // rounds of workgroups times the tokens of each (ties to fewer splits,
+        // which need no or a smaller merge); the launch fills kDecodeCUs CUs
+        want = 1;
+        double best = 1e300;
+        const int64_t smax = std::max<int64_t>(16, 2 * ((kDecodeCUs + p.units - 1) / p.units));
+        for (int64_t s = 1; s <= smax && s <= 1024; ++s) {
+            const double rounds = static_cast<double>((p.units * s + kDecodeCUs - 1) / kDecodeCUs);
+            const double cost = rounds / static_cast<double>(s) * (1.0 + 1e-3 * static_cast<double>(s));
+            if (cost < best) {
+                best = cost;
+                want = s;
+            }
+        }
+    }
     if (want > tiles) want = tiles;
     if (want > 1024) want = 1024;
     p.splits = n_splits > 0 ? n_splits : static_cast<int>(want < 1 ? 1 : want);

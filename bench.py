@@ -57,6 +57,8 @@ def parse():
                          "block pool behind a shuffled block table, written with tq_append_* and read with "
                          "tq_attend_decode_paged")
     ap.add_argument("--block-size", type=int, default=64)
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split count of the decode (0: the library's plan)")
     ap.add_argument("--eager-decode", action="store_true",
                     help="launch the per-layer decode kernels one by one from the host instead of replaying "
                          "them from a captured HIP graph")
@@ -93,7 +95,7 @@ class Layer:
     """Inputs, formats and packed planes of one layer (flat, or a block pool
     behind a seeded shuffled block table)."""
 
-    def __init__(self, w, layer, tq, W, torch, paged_block=0):
+    def __init__(self, w, layer, tq, W, torch, paged_block=0, splits=0):
         self.cb = tq.tq_build_codebook(w.d, w.k_bits)
         self.rot = tq.tq_make_rotation(w.rotation_seed(layer), w.d, w.rot)
         self.kf = tq.KeyFormat(w.d, w.k_bits, self.cb, self.rot, qjl_m=w.qjl_m)
@@ -119,7 +121,7 @@ class Layer:
                        else tq.alloc_key_cache(self.kf, w.B, w.Hkv, w.T))
             self.vc = tq.alloc_value_cache(self.vf, w.B, w.Hkv, w.T)
             cap = w.T
-        self.splits = tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, cap)
+        self.splits = splits or tq.tq_attend_splits(self.kf, w.B, w.Hq, w.Hkv, cap)
         if self.bf:     # same split plan as the TurboQuant keys of this shape
             n = tq.tq_attend_block_workspace_bytes(self.bf, w.B, w.Hq, w.Hkv, cap, self.splits)
         else:
@@ -334,7 +336,7 @@ def main():
         w = replace(w, name=f"{w.name}-paged{paged}")
     if args.scores and (w.block_bits or paged):
         sys.exit("--scores times tq_scores on the flat TurboQuant key planes only")
-    layers = [Layer(w, l, tq, W, torch, paged) for l in range(w.layers)]
+    layers = [Layer(w, l, tq, W, torch, paged, args.splits) for l in range(w.layers)]
     torch.cuda.synchronize()
     if args.scores:
         print(json.dumps(scores_only(w, layers, tq, torch, args.steps)), flush=True)
