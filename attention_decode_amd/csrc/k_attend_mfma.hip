@@ -849,13 +849,15 @@ struct ScoreQ {
     }
 };
 
-// Workgroups per CU the register budget is fitted to: one at d = 256; three
-// for the table scores (OCC3), with a two-deep prefetch ring; otherwise two,
-// with a three-deep ring.  Per SIMD the tiles in flight stay at six either way.
-template <class SCORE, int D, bool TWO>
+// Workgroups per CU the register budget is fitted to: one at d = 256, two for
+// the spread-operand table scores there (SP: keys prefetched one tile ahead,
+// values loaded with their own tile); three for the table scores (OCC3) at
+// d = 128, with a two-deep prefetch ring; otherwise two, with a three-deep
+// ring.
+template <class SCORE, int D, bool TWO, bool SP = false>
 constexpr int attend_occupancy()
 {
-    return D == 256 ? 1 : SCORE::OCC3 ? 3 : 2;
+    return D == 256 ? (SP ? 2 : 1) : SCORE::OCC3 ? 3 : 2;
 }
 
 // SP (table scores, at most two query heads per unit, at least four value
@@ -867,7 +869,7 @@ constexpr int attend_occupancy()
 // SO: scores only (tq_scores): the same tiles and score products, the raw
 // scores written to a.scores [B, Hq, T]; no value loads, softmax or merge.
 template <class SCORE, int BITS, int D, int VBITS, bool TWO, bool SP = false, bool SO = false>
-__global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
+__global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) void k_attend(DecodeLaunch a, float kappa, int64_t chunk)
 {
     constexpr int NQ = SCORE::NQ;
     constexpr int TK = 32;                       // keys per wave tile
@@ -881,7 +883,12 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
     constexpr int NGM = D / 32;                  // most value groups per row (group >= 32)
     constexpr int PD = TK * NGM / 64;            // (scale, zero) dwords per lane per tile
     constexpr int VT_BYTES = TK * VSTR;
-    constexpr int AF_BYTES = NGM * 64 * 16;
+    // value-product A operand per group: 64 lanes x 16 B; in SP mode only the
+    // 16 lanes of rows 0-3 (queries 0 and 1, hi and lo) are stored, at a
+    // stride of 68 dwords (a bank skew between the groups the four row blocks
+    // write together), followed by 16 zero bytes the other lanes read
+    constexpr int AF_GSTRIDE = SP ? 68 : 256;     // dwords per group
+    constexpr int AF_BYTES = NGM * AF_GSTRIDE * 4 + (SP ? 16 : 0);
     constexpr int PS_BYTES = TK * NGM * 4;
     constexpr int WAVE_BYTES = VT_BYTES + AF_BYTES + PS_BYTES;
     constexpr int MERGE_BYTES = 4 * kMaxG * D * 4;
@@ -914,7 +921,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
     SCORE score;
     score.init(a, unit, row0, lane, kb, GC, kappa, stab);
     // value-product A rows of absent queries stay zero
-    for (int i = lane; i < NGM * 64 * 4; i += 64) afr[i] = 0u;
+    for (int i = lane; i < AF_BYTES / 4; i += 64) afr[i] = 0u;
     // Rows of the split's tiles, one formula for every cache: token t of the
     // unit lives at row (blk * Hkv + kvh) * rstride + (t & rmask) with blk =
     // s_blk[(t >> rshift) - blk0].  Flat and contiguous caches: one "block" per
@@ -971,12 +978,18 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
 #pragma unroll
         for (int part = 0; part < 2; ++part)
             awr[sl][part] = aslot(2 * SCORE::query(sl, kb) + part + 16 * (j / 4)) * 4 + (j % 4);
-    const int ard = aslot(lane) * 4;
+    // A-operand read of this lane: its row's slot, or (SP, rows 4-15) the zero block
+    const bool a_live = !SP || (lane % 16) < 4;
+    const uint32_t *abase = SP ? (a_live ? afr + (4 * (lane / 16) + lane % 16) * 4 : afr + NGM * AF_GSTRIDE)
+                               : afr + aslot(lane) * 4;
+    const int agstep = a_live ? AF_GSTRIDE : 0;
     int awq[2][2];                                // spread mode: slots of queries 0 and 1
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int part = 0; part < 2; ++part) awq[q][part] = aslot(2 * q + part + 16 * (j / 4)) * 4 + (j % 4);
+        for (int part = 0; part < 2; ++part)
+            awq[q][part] = SP ? (4 * (j / 4) + 2 * q + part) * 4 + (j % 4)
+                              : aslot(2 * q + part + 16 * (j / 4)) * 4 + (j % 4);
     // tr-read row of this lane in every value block: k-slot 8 kb + e holds the
     // token of slot order; lanes 2r, 2r + 1 address read row r, and row r lands
     // in half e(r) of the operand with e = {0, 2, 1, 3, 4, 6, 5, 7}
@@ -994,24 +1007,37 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
     // Loads of one tile, all unconditional: rows past the valid range are
     // clamped to the last valid row and masked where they are used; a tile
     // past the end reloads the wave's first tile.
-    auto fetch = [&](int64_t tile0, Prefetch &pf) {
+    // wave-uniform first row and valid keys of the tile starting at tile0: a
+    // tile never straddles a block (tiles start at multiples of 32 tokens,
+    // blocks hold a multiple of 32); nv = 0 for a block id outside the pool
+    // (the clamp only guards LDS: the host keeps every split within kStageBlocks blocks)
+    // (flat and contiguous caches skip the LDS read: their one block is the sequence)
+    auto tile_rows = [&](int64_t tile0, int64_t &n0, int &nv) {
         const int64_t tc = tile0 < t_end ? tile0 : first;
-        const int nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
-        // wave-uniform row of the tile: a tile never straddles a block (tiles
-        // start at multiples of 32 tokens, blocks hold a multiple of 32)
-        // (the clamp only guards LDS: the host keeps every split within kStageBlocks blocks)
-        // (flat and contiguous caches skip the LDS read: their one block is the sequence)
+        nv = static_cast<int>(t_end - tc < TK ? t_end - tc : TK);
         const int bi = min(static_cast<int>(tc >> rshift) - blk0, kStageBlocks - 1);
         const int blk = paged ? __builtin_amdgcn_readfirstlane(s_blk[bi]) : static_cast<int>(seq);
-        const int64_t n0 = blk >= 0 ? (static_cast<int64_t>(blk) * a.Hkv + kvh) * rstride
-                                          + (static_cast<uint32_t>(tc) & rmask) : 0;
-        pf.nvalid = blk >= 0 ? nv : 0;
+        n0 = blk >= 0 ? (static_cast<int64_t>(blk) * a.Hkv + kvh) * rstride + (static_cast<uint32_t>(tc) & rmask) : 0;
+        if (blk < 0) nv = 0;
+    };
+    auto fetch_keys = [&](int64_t tile0, Prefetch &pf) {
+        int64_t n0;
+        int nvv;
+        tile_rows(tile0, n0, nvv);
+        const int nv = nvv > 0 ? nvv : 1;      // loads stay in the tile's first row
+        pf.nvalid = nvv;
         const auto kbase = SCORE::KW::bases(a, n0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const uint32_t t = static_cast<uint32_t>(16 * c + j < nv ? 16 * c + j : nv - 1);
             pf.kw.load(kbase, t, kb, c);
         }
+    };
+    auto fetch_vals = [&](int64_t tile0, Prefetch &pf) {
+        int64_t n0;
+        int nvv;
+        tile_rows(tile0, n0, nvv);
+        const int nv = nvv > 0 ? nvv : 1;
         if constexpr (!SO) {
             const v4i *vsrc = reinterpret_cast<const v4i *>(a.vc.codes + n0 * VB);
 #pragma unroll
@@ -1029,8 +1055,31 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
             }
         }
     };
+    auto fetch = [&](int64_t tile0, Prefetch &pf) {
+        fetch_keys(tile0, pf);
+        fetch_vals(tile0, pf);
+    };
 
-    auto compute = [&](int64_t tile0, const Prefetch &cur) {
+    // staging of the tile's value codes and (scale, zero) words in this wave's LDS
+    auto stage_values = [&](const Prefetch &vals, int nv) {
+        wave_sync();        // the previous tile's LDS reads come before these writes
+#pragma unroll
+        for (int v = 0; v < VCL; ++v) {
+            const int i = lane + 64 * v;
+            *reinterpret_cast<v4i *>(vt + (i / (VB / 16)) * VSTR + (i % (VB / 16)) * 16) = vals.vcode[v];
+        }
+#pragma unroll
+        for (int k = 0; k < PD; ++k) {
+            const int idx = lane + 64 * k;
+            if (idx < TK * NG) pst[(idx >> lg_ng) * NGM + (idx & (NG - 1))] = idx < nv * NG ? vals.par[k] : 0u;
+        }
+        wave_sync();        // staged rows are read by other lanes below
+    };
+
+    // cur: the tile's key words; vals: its value words (the same buffer,
+    // except in SP mode, where the value words are staged after the scores and
+    // the buffer then takes the loads of the tile at next_vals)
+    auto compute = [&](int64_t tile0, const Prefetch &cur, Prefetch &vals, int64_t next_vals = -1) {
         (void)tile0;
         const int nv = cur.nvalid;
         if constexpr (SO) {
@@ -1046,19 +1095,8 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
                 }
             return;
         }
-        wave_sync();        // the previous tile's LDS reads come before these writes
         // ---- value codes and (scale, zero) words of the tile into this wave's LDS
-#pragma unroll
-        for (int v = 0; v < VCL; ++v) {
-            const int i = lane + 64 * v;
-            *reinterpret_cast<v4i *>(vt + (i / (VB / 16)) * VSTR + (i % (VB / 16)) * 16) = cur.vcode[v];
-        }
-#pragma unroll
-        for (int k = 0; k < PD; ++k) {
-            const int idx = lane + 64 * k;
-            if (idx < TK * NG) pst[(idx >> lg_ng) * NGM + (idx & (NG - 1))] = idx < nv * NG ? cur.par[k] : 0u;
-        }
-        wave_sync();        // staged rows are read by other lanes below
+        if constexpr (!SP) stage_values(vals, nv);
 
         // ---- scores of keys j and 16 + j for this lane's queries
         float lamv[NQ][2];
@@ -1121,6 +1159,13 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
             l_run[sl] += p[sl][0] + p[sl][1];
         }
 
+        // (SP: the tile's value words are staged now, after the scores, and
+        // the next tile's value loads go out at once)
+        if constexpr (SP) {
+            stage_values(vals, nv);
+            if (next_vals >= 0) fetch_vals(next_vals, vals);
+        }
+
         // ---- value-product A operand: p * scale as fp16 hi + lo in rows 2 q and
         // 2 q + 1, tokens j and 16 + j packed in dword j % 4 of k-block j / 4
         if constexpr (SP) {
@@ -1143,8 +1188,8 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
                         zsp[q][i] = fmaf(pq[q][0], z0, fmaf(pq[q][1], z1, zsp[q][i]));
                         const auto hi = __builtin_amdgcn_cvt_pkrtz(w0, w1);
                         const auto lo = __builtin_amdgcn_cvt_pkrtz(w0 - static_cast<float>(hi[0]), w1 - static_cast<float>(hi[1]));
-                        afr[gg * 256 + awq[q][0]] = __builtin_bit_cast(uint32_t, hi);
-                        afr[gg * 256 + awq[q][1]] = __builtin_bit_cast(uint32_t, lo);
+                        afr[gg * AF_GSTRIDE + awq[q][0]] = __builtin_bit_cast(uint32_t, hi);
+                        afr[gg * AF_GSTRIDE + awq[q][1]] = __builtin_bit_cast(uint32_t, lo);
                     }
                 }
             }
@@ -1181,10 +1226,10 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int g_lo = (NF * 16 * cb) >> (__builtin_ctz(a.group));
-            const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + g_lo * 256 + ard));
+            const v8h af0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(abase + g_lo * agstep));
             v8h af1 = af0;
             if constexpr (kTwoGroups)
-                af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(afr + (g_lo + 1) * 256 + ard));
+                af1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i *>(abase + (g_lo + 1) * agstep));
             const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(tr_base + 16 * cb));
             const uint32_t x0 = static_cast<uint32_t>(raw.x), x1 = static_cast<uint32_t>(raw.y);
             const uint32_t y0 = x0 >> 8, y1 = x1 >> 8;
@@ -1208,19 +1253,34 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
     // workgroups per CU, three at two).  Tiles left after the unrolled trips
     // are computed from the buffers that already hold them.
     constexpr int STEP = 4 * TK;
-    constexpr bool kRing2 = attend_occupancy<SCORE, D, TWO>() != 2;
+    constexpr bool kRing2 = attend_occupancy<SCORE, D, TWO, SP>() != 2;
     if (first < t_end) {
-        if constexpr (kRing2) {
+        if constexpr (SP) {
+            // two workgroups per CU: the key words one tile ahead; the value
+            // words of the next tile go out once the current tile's are staged
+            // (half a tile ahead: they are needed only after the scores)
+            Prefetch ka, kc, va;
+            fetch_keys(first, ka);
+            fetch_vals(first, va);
+            int64_t t = first;
+            for (; t + STEP < t_end; t += 2 * STEP) {
+                fetch_keys(t + STEP, kc);
+                compute(t, ka, va, t + STEP);
+                fetch_keys(t + 2 * STEP, ka);
+                compute(t + STEP, kc, va, t + 2 * STEP < t_end ? t + 2 * STEP : -1);
+            }
+            if (t < t_end) compute(t, ka, va);
+        } else if constexpr (kRing2) {
             Prefetch pa, pb;
             fetch(first, pa);
             int64_t t = first;
             for (; t + STEP < t_end; t += 2 * STEP) {
                 fetch(t + STEP, pb);
-                compute(t, pa);
+                compute(t, pa, pa);
                 fetch(t + 2 * STEP, pa);
-                compute(t + STEP, pb);
+                compute(t + STEP, pb, pb);
             }
-            if (t < t_end) compute(t, pa);
+            if (t < t_end) compute(t, pa, pa);
         } else {
             Prefetch p0, p1, p2;
             fetch(first, p0);
@@ -1228,14 +1288,14 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO>())) void
             int64_t t = first;
             for (; t + 2 * STEP < t_end; t += 3 * STEP) {
                 fetch(t + 2 * STEP, p2);
-                compute(t, p0);
+                compute(t, p0, p0);
                 fetch(t + 3 * STEP, p0);
-                compute(t + STEP, p1);
+                compute(t + STEP, p1, p1);
                 fetch(t + 4 * STEP, p1);
-                compute(t + 2 * STEP, p2);
+                compute(t + 2 * STEP, p2, p2);
             }
-            if (t < t_end) compute(t, p0);
-            if (t + STEP < t_end) compute(t + STEP, p1);
+            if (t < t_end) compute(t, p0, p0);
+            if (t + STEP < t_end) compute(t + STEP, p1, p1);
         }
     }
 
