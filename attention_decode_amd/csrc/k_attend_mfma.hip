@@ -554,7 +554,7 @@ struct ScoreLut {
     // 8 KB, and 4 KB at d = 128 with 4-bit values, whose larger value staging
     // would otherwise leave room for two workgroups per CU instead of three.
     static constexpr int COPIES_RAW = TB / (NENT * EBYTES);
-    static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 8 ? 8 : (COPIES_RAW >= 4 ? 4 : 1)));
+    static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 32 ? 32 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 8 ? 8 : (COPIES_RAW >= 4 ? 4 : 1))));
     static constexpr int CODE_TAB = NENT * EBYTES * COPIES;
     static constexpr int SIGN_TAB = QJL ? 256 * 16 : 0;
     // the unit's A operands, [step][64 lanes] with CODE_STEPS code steps then
@@ -567,6 +567,8 @@ struct ScoreLut {
     static constexpr int LSTEP = CODE_STEPS + (QJL ? KS : 0);         // steps kept in LDS
     static constexpr int AOP_BYTES = AREG ? 0 : LSTEP * 64 * 16;
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
+    template <int TB2>
+    using WithTable = ScoreLut<BITS, D, QJL, TB2>;
     float scc[2], scs[2];
     v4i areg[AREG ? CODE_STEPS : 1];
     const unsigned char *tab;
@@ -891,7 +893,8 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
     constexpr int AF_BYTES = NGM * AF_GSTRIDE * 4 + (SP ? 16 : 0);
     constexpr int PS_BYTES = TK * NGM * 4;
     constexpr int WAVE_BYTES = VT_BYTES + AF_BYTES + PS_BYTES;
-    constexpr int MERGE_BYTES = 4 * kMaxG * D * 4;
+    constexpr int MG = SP ? 2 : kMaxG;            // query rows of the merge area (SP: at most two)
+    constexpr int MERGE_BYTES = 4 * MG * D * 4;
     constexpr int SMEM = (4 * WAVE_BYTES > MERGE_BYTES) ? 4 * WAVE_BYTES : MERGE_BYTES;
 
     __shared__ __align__(16) unsigned char smem[SMEM];
@@ -1328,7 +1331,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
             }
     }
     __syncthreads();        // every wave is done with its tile buffers
-    float *wo = reinterpret_cast<float *>(smem);      // [4 waves][kMaxG][D]
+    float *wo = reinterpret_cast<float *>(smem);      // [4 waves][MG][D]
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt) {
         const int cb = nt / NF, f = nt % NF;
@@ -1343,7 +1346,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             const int g = 2 * kb + qq;
-            wo[(wave * kMaxG + g) * D + ch] = sc * (acc[2 * qq] + acc[2 * qq + 1]);
+            if (MG == kMaxG || g < MG) wo[(wave * MG + g) * D + ch] = sc * (acc[2 * qq] + acc[2 * qq + 1]);
         }
     }
     __syncthreads();
@@ -1357,7 +1360,7 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
         for (int w = 0; w < 4; ++w) {
             const float e = (s_wm[w][g] == -INFINITY) ? 0.0f : exp2_fast(s_wm[w][g] - mx);
             l = fmaf(e, s_wl[w][g], l);
-            o = fmaf(e, wo[(w * kMaxG + g) * D + ch] + s_wz[w][g][grp], o);
+            o = fmaf(e, wo[(w * MG + g) * D + ch] + s_wz[w][g][grp], o);
         }
         if (a.splits == 1) {
             a.out[(row0 + g) * D + ch] = l > 0.0f ? o / l : 0.0f;
@@ -1580,9 +1583,12 @@ template <class SCORE, int BITS, int D>
 hipError_t launch_attend_v(const DecodeLaunch &a, hipStream_t s, float kappa, int64_t chunk)
 {
     if constexpr (SCORE::TAB_BYTES > 0 && D == 256) {
+        // spread operand, two workgroups per CU: 16 KB of centroid tables (32
+        // copies) fit beside the smaller merge area
+        using SPS = typename SCORE::template WithTable<16384>;
         if (a.mf.gc <= 2 && a.d / a.group >= 4 && !(a.vbits == 2 && a.group == 32))
-            return a.vbits == 2 ? launch_attend_t<SCORE, BITS, D, 2, true>(a, s, kappa, chunk)
-                                : launch_attend_t<SCORE, BITS, D, 4, true>(a, s, kappa, chunk);
+            return a.vbits == 2 ? launch_attend_t<SPS, BITS, D, 2, true>(a, s, kappa, chunk)
+                                : launch_attend_t<SPS, BITS, D, 4, true>(a, s, kappa, chunk);
     }
     return a.vbits == 2 ? launch_attend_t<SCORE, BITS, D, 2>(a, s, kappa, chunk)
                         : launch_attend_t<SCORE, BITS, D, 4>(a, s, kappa, chunk);
