@@ -243,25 +243,36 @@ tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
         return hip_fail(e, "tq_build_codebook: device upload");
     }
     cb->d_boundaries = cb->d_centroids + L;
-    if (L >= 8) {
-        // grid over the fp32 boundaries the kernel compares with: cell c starts a
-        // bound below #{t_i < y}; its widened range holds at most two boundaries
+    if (L >= 16) {
+        // code cells over the fp32 boundaries the kernel compares with: the
+        // coarsest uniform grid (from 64 cells, doubling) whose cells, widened by
+        // 2 % of a cell on each side to absorb the rounding of the cell index,
+        // hold at most one boundary each
         const double lo = host[L], hi = host[L + L - 2];
-        std::vector<uint8_t> grid;
+        std::vector<float4> cells;
         int ng = 0;
         for (int n = 64; n <= tq::kMaxGrid && ng == 0; n *= 2) {
             const double w = (hi - lo) / n;
-            grid.assign(n, 0);
+            cells.assign(n, float4{});
             bool ok = true;
             for (int c = 0; c < n && ok; ++c) {
                 const double a = lo + (c - 0.02) * w, b = lo + (c + 1.02) * w;
-                int below = 0, inside = 0;
+                int below = 0, inside = 0, first = -1;
                 for (int i = 0; i < L - 1; ++i) {
-                    if (host[L + i] < a) ++below;
-                    else if (host[L + i] < b) ++inside;
+                    if (host[L + i] < a) {
+                        ++below;
+                    } else if (host[L + i] < b) {
+                        if (first < 0) first = i;
+                        ++inside;
+                    }
                 }
-                grid[c] = static_cast<uint8_t>(below);
-                ok = inside <= 2;
+                ok = inside <= 1;
+                float4 &e = cells[c];
+                e.x = inside ? host[L + first] : INFINITY;
+                e.y = host[below];
+                e.z = host[inside ? below + 1 : below];
+                int32_t bw = below;
+                std::memcpy(&e.w, &bw, sizeof(bw));
             }
             if (ok) ng = n;
         }
@@ -273,8 +284,8 @@ tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
         cb->ngrid = ng;
         cb->grid_lo = static_cast<float>(lo);
         cb->grid_scale = static_cast<float>(ng / (hi - lo));
-        e = hipMalloc(reinterpret_cast<void **>(&cb->d_grid), ng);
-        if (e == hipSuccess) e = hipMemcpy(cb->d_grid, grid.data(), ng, hipMemcpyHostToDevice);
+        e = hipMalloc(reinterpret_cast<void **>(&cb->d_grid), sizeof(float4) * ng);
+        if (e == hipSuccess) e = hipMemcpy(cb->d_grid, cells.data(), sizeof(float4) * ng, hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             if (cb->d_grid) hipFree(cb->d_grid);
             hipFree(cb->d_centroids);
@@ -713,6 +724,9 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
     if (T == 0) return TQ_OK;
     TQ_TRY(check_kcache(out, fmt->qjl_m, who));
+    if (fmt->mse_bits >= 4 && fmt->cb->ngrid > tq::kGridLds)
+        return fail(TQ_EUNSUPPORTED, "%s: codebook grid of %d cells exceeds the compressor's %d", who,
+                    fmt->cb->ngrid, tq::kGridLds);
     tq::KeyLaunch a{};
     a.k = k;
     a.dtype = dtype;

@@ -27,9 +27,10 @@
 //
 // Codes: idx = #{t_i < y}.  Up to 3 bits a binary search of |y| among the
 // positive boundaries of the symmetric codebook, in registers (at most two
-// comparisons, no LDS reads); from 4 bits a uniform grid over [t_0, t_{L-2}]
-// gives a lower bound of the count that is at most two below it, and two
-// exact comparisons finish it.
+// comparisons, no LDS reads); from 4 bits one 16-byte LDS read of the cell of
+// a uniform grid over [t_0, t_{L-2}] that holds y: the count below the cell,
+// the one boundary inside it and the centroids on either side, so one exact
+// comparison finishes the code and picks the centroid.
 #include "tq_internal.h"
 #include "tq_device.h"
 
@@ -150,15 +151,22 @@ __device__ __forceinline__ uint32_t bf16x2(float x0, float x1)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// LDS row strides of the code and sign words: one word past the row, an odd
+// stride, so that the 16 keys of one atomicOr (lanes 0-15 of a row of the
+// wave) land in 16 different banks (an even row of 8, 12 or 56 words puts
+// them in 2 to 8 banks)
+template <int D, int BITS> constexpr int cw_stride() { return D * BITS / 32 + 1; }
+template <int D> constexpr int sw_stride() { return D / 32 + 1; }
+
 struct KeySmem {
     uint4 *rfrag;       // [KT][KS][2][64]  residual B operands (two bf16 terms)
-    uint32_t *cw;       // [KEYS][D * bits / 32]  code words
-    uint32_t *sw;       // [KEYS][D / 32]         sign words
+    uint32_t *cw;       // [KEYS][cw_stride]  code words
+    uint32_t *sw;       // [KEYS][sw_stride]  sign words
     double *rho2;       // [4 waves][KEYS]
     double *nrm2;       // [256 / KEYS threads per key][KEYS]
     float *cent;        // [256]
     float *bnd;         // [256] (+inf after the last boundary)
-    uint8_t *grid;      // [kMaxGrid]
+    float4 *grid;       // [kGridLds] code cells {t, c_lo, c_hi, below}
 };
 
 // LDS row stride of a staged key: the row plus 16 bytes, so that the 16 keys
@@ -180,8 +188,8 @@ template <int D, typename TIn, int BITS, int KT>
 constexpr size_t key_smem_bytes()
 {
     constexpr size_t keys = 16 * KT;
-    return key_union_bytes<D, TIn, KT>() + sizeof(uint32_t) * keys * (D * BITS / 32 + D / 32)
-           + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? kMaxGrid : 0);
+    return key_union_bytes<D, TIn, KT>() + sizeof(uint32_t) * keys * (cw_stride<D, BITS>() + sw_stride<D>())
+           + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? sizeof(float4) * kGridLds : 0);
 }
 
 
@@ -189,9 +197,9 @@ constexpr size_t key_smem_bytes()
 // Up to 3 bits: |y| placed among the positive boundaries tp of the exactly
 // symmetric codebook by a binary search in registers, the centroid taken from
 // the positive ones cp, idx and the residual fixed by the sign of y (bit for
-// bit what the full count gives, up to exact ties).  From 4 bits: the uniform
-// grid gives a count at most two below the true one, and two exact
-// comparisons with the LDS boundaries finish it.
+// bit what the full count gives, up to exact ties).  From 4 bits: the cell of
+// the uniform grid that holds y gives the count below it and its one
+// boundary t, so the code is below + [y > t], the centroid c_lo or c_hi.
 template <int BITS>
 __device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BITS) / 2 > 1 ? (1 << BITS) / 2 - 1 : 1],
                                             const float (&cp)[(1 << BITS) / 2], const KeySmem &s, const KeyLaunch &a,
@@ -221,31 +229,78 @@ __device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BIT
     } else {
         int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
         c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
-        pos = s.grid[c];
-        pos += (y > s.bnd[pos]) ? 1 : 0;
-        pos += (y > s.bnd[pos]) ? 1 : 0;
-        res = y - s.cent[pos];
+        const float4 e = s.grid[c];
+        const bool up = y > e.x;
+        pos = __float_as_int(e.w) + (up ? 1 : 0);
+        res = y - (up ? e.z : e.y);
     }
     return pos;
 }
 
+// The A-fragment tables of Pi and S are read through buffer loads: the
+// lane's 16-byte slot is the one vector offset, the fragment's place in the
+// table a scalar offset (wave-uniform), so a fragment load costs no vector
+// address arithmetic and no address registers.  Records past the table's
+// size read as zero.
+static_assert(kGridLds <= kThreads, "one code cell per thread");
+constexpr int kBufWord3 = 0x00020000;     // raw 32-bit access, no format conversion
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t frag_table(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kBufWord3);
+}
+
+__device__ __forceinline__ uint4 frag_load(__amdgpu_buffer_rsrc_t t, int lane, int frag)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(t, lane * 16, frag * 1024, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// bytes of a table of A fragments for D rows x D columns with NT terms
+template <int D, int NT> constexpr int frag_table_bytes() { return (D / 16) * (D / 32) * NT * 1024; }
+
+// Rows 16 (RTW wave + j) .. + 15 of S, k-step ks, as the two bf16 A terms
+template <int D>
+__device__ __forceinline__ void load_s_frag(__amdgpu_buffer_rsrc_t st, int wave, int lane, int ks,
+                                            uint4 (&sf)[D / 64][2])
+{
+    constexpr int KS = D / 32, RTW = D / 64;
+#pragma unroll
+    for (int j = 0; j < RTW; ++j) {
+        const int rt = wave * RTW + j;
+        sf[j][0] = frag_load(st, lane, (rt * KS + ks) * 2 + 0);
+        sf[j][1] = frag_load(st, lane, (rt * KS + ks) * 2 + 1);
+    }
+}
+
 // z = S r for the residual operands of key tiles kt0 .. kt0 + KR - 1 (LDS,
 // B-operand order) on this wave's rows of S; sign bits [z >= 0] OR-ed into
-// the sign words.  Ends with a workgroup barrier (the pass's residual operands
-// are read before the next pass writes them).
+// the sign words.  sf0 holds the first k-step's S fragments, loaded by the
+// caller ahead of the residual work; each later k-step's fragments are in
+// flight while the previous k-step's products run.  Ends with a workgroup
+// barrier (the pass's residual operands are read before the next pass
+// writes them).
 template <int D, int KR>
-__device__ __forceinline__ void qjl_signs(const KeyLaunch &a, const KeySmem &s, int kt0, int wave, int lane)
+__device__ __forceinline__ void qjl_signs(__amdgpu_buffer_rsrc_t st, const KeySmem &s, int kt0, int wave, int lane,
+                                          const uint4 (&sf0)[D / 64][2])
 {
-    constexpr int KS = D / 32, RTW = D / 64, SWN = D / 32;
+    constexpr int KS = D / 32, RTW = D / 64, SWS = sw_stride<D>();
     const int col = lane & 15, kb = lane >> 4;
-    const uint4 *sfr = reinterpret_cast<const uint4 *>(a.sfrag);
     f32x4 zacc[RTW][KR];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
 #pragma unroll
         for (int kt = 0; kt < KR; ++kt) zacc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
+    uint4 sf[2][RTW][2];
+#pragma unroll
+    for (int j = 0; j < RTW; ++j) {
+        sf[0][j][0] = sf0[j][0];
+        sf[0][j][1] = sf0[j][1];
+    }
+#pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load_s_frag<D>(st, wave, lane, ks + 1, sf[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of this k-step's products
         uint4 rf[KR][2];
 #pragma unroll
         for (int kt = 0; kt < KR; ++kt) {
@@ -254,9 +309,7 @@ __device__ __forceinline__ void qjl_signs(const KeyLaunch &a, const KeySmem &s, 
         }
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
-            const int rt = wave * RTW + j;
-            const uint4 s0 = sfr[((rt * KS + ks) * 2 + 0) * 64 + lane];
-            const uint4 s1 = sfr[((rt * KS + ks) * 2 + 1) * 64 + lane];
+            const uint4 &s0 = sf[ks & 1][j][0], &s1 = sf[ks & 1][j][1];
 #pragma unroll
             for (int kt = 0; kt < KR; ++kt) {
                 zacc[j][kt] = mfma_bf16(s0, rf[kt][0], zacc[j][kt]);
@@ -274,7 +327,7 @@ __device__ __forceinline__ void qjl_signs(const KeyLaunch &a, const KeySmem &s, 
             uint32_t nib = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
-            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWN + (off >> 5)], nib << (off & 31));
+            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWS + (off >> 5)], nib << (off & 31));
         }
     }
     __syncthreads();
@@ -287,15 +340,15 @@ template <int D, int BITS, int KEYS, int NPN, int NPR>
 __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s, int64_t n0, int64_t n_total,
                                            int64_t *s_row, bool qjl)
 {
-    constexpr int CW = D * BITS / 32, SWN = D / 32;
+    constexpr int CW = D * BITS / 32, SWN = D / 32, CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
     const int tid = threadIdx.x;
     const int nk = static_cast<int>(n_total - n0 < KEYS ? n_total - n0 : KEYS);
     if (a.map.mode == CacheMap::kFlat) {
         uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
-        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[i];
+        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[(i / CW) * CWS + i % CW];
         if (qjl) {
             uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
-            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[i];
+            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[(i / SWN) * SWS + i % SWN];
         }
         if (tid < nk) s_row[tid] = n0 + tid;
     } else {
@@ -304,13 +357,13 @@ __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s,
         uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes);
         for (int i = tid; i < nk * CW; i += kThreads) {
             const int64_t r = s_row[i / CW];
-            if (r >= 0) codes[r * CW + i % CW] = s.cw[i];
+            if (r >= 0) codes[r * CW + i % CW] = s.cw[(i / CW) * CWS + i % CW];
         }
         if (qjl) {
             uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs);
             for (int i = tid; i < nk * SWN; i += kThreads) {
                 const int64_t r = s_row[i / SWN];
-                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[i];
+                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[(i / SWN) * SWS + i % SWN];
             }
         }
     }
@@ -329,14 +382,30 @@ __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s,
     }
 }
 
-template <int D, typename TIn, int BITS, int KT>
+// Rows 16 (RTW wave + j) .. + 15 of Pi, k-step ks, as NP bf16 A terms
+template <int D, int NP>
+__device__ __forceinline__ void load_pi_frag(__amdgpu_buffer_rsrc_t pt, int wave, int lane, int ks,
+                                             uint4 (&af)[D / 64][NP])
+{
+    constexpr int KS = D / 32, RTW = D / 64;
+#pragma unroll
+    for (int j = 0; j < RTW; ++j) {
+        const int rt = wave * RTW + j;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) af[j][p] = frag_load(pt, lane, (rt * KS + ks) * 3 + p);
+    }
+}
+
+// NP = 3: a dense Pi as three bf16 terms; NP = 1: the Hadamard sign matrix,
+// exact in one term
+template <int D, typename TIn, int BITS, int KT, int NP>
 __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
     constexpr int NK = KeyTerms<TIn>::n;
     constexpr int L = 1 << BITS;
-    constexpr int CW = D * BITS / 32, SWN = D / 32;
+    constexpr int CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
     constexpr int kKT = KT;              // 16-key tiles of the workgroup
     constexpr int kKeys = 16 * kKT;      // keys of the workgroup
     constexpr int KR = key_pass_tiles<D, TIn, KT>();   // key tiles per residual / sign pass
@@ -349,30 +418,32 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.rfrag = reinterpret_cast<uint4 *>(p);   p += key_union_bytes<D, TIn, KT>();
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * 4 * kKeys;
         s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kThreads;
-        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
-        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWN;
+        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CWS;
+        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWS;
         s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
         s.bnd = reinterpret_cast<float *>(p);     p += sizeof(float) * 256;
-        s.grid = p;
+        s.grid = reinterpret_cast<float4 *>(p);
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, kb = lane >> 4;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kKeys;
 
-    // codebook tables (L <= 128 entries, a grid of at most 4096 bytes in
-    // 16-byte pieces): loads issued unconditionally (indices clamped) ahead of
+    // codebook tables (L <= 128 entries, at most kGridLds = kThreads code
+    // cells of 16 bytes): loads issued unconditionally (indices clamped) ahead of
     // the keys, stored to LDS after them, so both share one round trip
     const int ti = tid < L ? tid : L - 1;
     const float cent_v = a.centroids[ti];
     const float bnd_v = a.boundaries[ti];      // entry L - 1 is +inf
-    uint4 grid_v = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (BITS >= 4) {
-        const int ng16 = a.ngrid / 16;
-        grid_v = reinterpret_cast<const uint4 *>(a.grid)[tid < ng16 ? tid : ng16 - 1];
-    }
-    for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
-    for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
+    float4 grid_v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
+    for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
+    for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
+    // Pi's fragments of the first k-step, in flight with the keys
+    const __amdgpu_buffer_rsrc_t pt = frag_table(a.pifrag, frag_table_bytes<D, 3>());
+    const __amdgpu_buffer_rsrc_t st = frag_table(a.sfrag, a.m > 0 ? frag_table_bytes<D, 2>() : 0);
+    uint4 af[2][RTW][NP];
+    load_pi_frag<D, NP>(pt, wave, lane, 0, af[0]);
 
     // ---- 0. the workgroup's keys into LDS, one HBM round trip: thread
     // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (rows
@@ -420,31 +491,22 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.bnd[tid] = bnd_v;
     }
     if constexpr (BITS >= 4)
-        if (tid < a.ngrid / 16) reinterpret_cast<uint4 *>(s.grid)[tid] = grid_v;
+        if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // staged keys, cleared words, codebook tables
 
-    // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r
-    const uint4 *pif = reinterpret_cast<const uint4 *>(a.pifrag);
+    // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r.
+    // Pi's A fragments come from L2, double-buffered: the next k-step's are
+    // in flight while this k-step's products run.
     f32x4 acc[RTW][kKT];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const bool three = !a.hadamard;
     const int bits = BITS;
-#pragma unroll 2
-    for (int ks = 0; ks < KS; ++ks) {
-        // A fragments of this k-step (the Hadamard sign matrix is one exact term)
-        uint4 af[RTW][3];
 #pragma unroll
-        for (int j = 0; j < RTW; ++j) {
-            const int rt = wave * RTW + j;
-            af[j][0] = pif[((rt * KS + ks) * 3 + 0) * 64 + lane];
-            if (three) {
-                af[j][1] = pif[((rt * KS + ks) * 3 + 1) * 64 + lane];
-                af[j][2] = pif[((rt * KS + ks) * 3 + 2) * 64 + lane];
-            }
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load_pi_frag<D, NP>(pt, wave, lane, ks + 1, af[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of this k-step's products
         uint4 kf[kKT][NK];
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
@@ -452,13 +514,12 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
 #pragma unroll
-            for (int pp = 0; pp < 3; ++pp) {
-                if (pp > 0 && !three) continue;
+            for (int pp = 0; pp < NP; ++pp) {
 #pragma unroll
                 for (int kq = 0; kq < NK; ++kq) {
-                    if (three && pp + kq > 2) continue;
+                    if (pp + kq > 2) continue;     // terms below fp32's resolution
 #pragma unroll
-                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af[j][pp], kf[kt][kq], acc[j][kt]);
+                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af[ks & 1][j][pp], kf[kt][kq], acc[j][kt]);
                 }
             }
         }
@@ -493,6 +554,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     const bool qjl = a.m > 0;
 #pragma unroll
     for (int kt0 = 0; kt0 < kKT; kt0 += KR) {
+    // S's fragments of the first k-step of step 4, in flight with step 3
+    uint4 sf0[RTW][2];
+    if (qjl) load_s_frag<D>(st, wave, lane, 0, sf0);
     // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
     // (key tiles kt0 .. kt0 + KR - 1 of this pass)
 #pragma unroll
@@ -517,8 +581,8 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             const uint32_t l23 = bf16x2(res[2] - __uint_as_float(h23 << 16), res[3] - __uint_as_float(h23 & 0xffff0000u));
             // 4 codes of `bits` bits at bit offset bits (16 rt + 4 kb) of the key's stream
             const int off = bits * (16 * rt + 4 * kb), w = off >> 5, sh = off & 31;
-            atomicOr(&s.cw[key * CW + w], chunk << sh);
-            if (sh + 4 * bits > 32) atomicOr(&s.cw[key * CW + w + 1], chunk >> (32 - sh));
+            atomicOr(&s.cw[key * CWS + w], chunk << sh);
+            if (sh + 4 * bits > 32) atomicOr(&s.cw[key * CWS + w + 1], chunk >> (32 - sh));
             // residual as B operand of k-step rt/2: elements 4 (rt % 2) + r of this lane
             uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 0) * 64 + lane]);
             uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 1) * 64 + lane]);
@@ -535,7 +599,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 
     // ---- 4. z = S r on this wave's rows; signs [z >= 0] (skipped for the
     // first-stage format, m = 0; the condition is uniform over the launch)
-    if (qjl) qjl_signs<D, KR>(a, s, kt0, wave, lane);
+    if (qjl) qjl_signs<D, KR>(st, s, kt0, wave, lane, sf0);
     }   // passes
 
     // ---- 5. store the WG's keys
@@ -664,8 +728,8 @@ constexpr size_t key_smem_bytes_wht(int bits)
 {
     constexpr size_t keys = 16 * KT;
     const size_t rfrag = sizeof(uint4) * key_pass_tiles<D, TIn, KT>() * (D / 32) * 2 * 64;
-    return rfrag + sizeof(uint32_t) * keys * (D * bits / 32 + D / 32) + sizeof(double) * 2 * keys
-           + sizeof(float) * 512 + (bits >= 4 ? kMaxGrid : 0);
+    return rfrag + sizeof(uint32_t) * keys * ((D * bits / 32 + 1) + sw_stride<D>()) + sizeof(double) * 2 * keys
+           + sizeof(float) * 512 + (bits >= 4 ? sizeof(float4) * kGridLds : 0);
 }
 
 // One 256-thread workgroup encodes 16 KT keys; wave w takes keys 16 t + 4 w + g
@@ -680,7 +744,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     constexpr int KS = D / 32;
     constexpr int L = 1 << BITS;
     constexpr int H = L / 2;
-    constexpr int CW = D * BITS / 32, SWN = D / 32;
+    constexpr int CW = D * BITS / 32, CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
     constexpr int kKeys = 16 * KT;
     constexpr int KR = key_pass_tiles<D, TIn, KT>();
     constexpr int NSW = (BITS * CPL + 31) / 32;   // code words of one lane's segment
@@ -692,11 +756,11 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.rfrag = reinterpret_cast<uint4 *>(p);   p += sizeof(uint4) * KR * KS * 2 * 64;
         s.rho2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kKeys;
         s.nrm2 = reinterpret_cast<double *>(p);   p += sizeof(double) * kKeys;
-        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CW;
-        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWN;
+        s.cw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * CWS;
+        s.sw = reinterpret_cast<uint32_t *>(p);   p += sizeof(uint32_t) * kKeys * SWS;
         s.cent = reinterpret_cast<float *>(p);    p += sizeof(float) * 256;
         s.bnd = reinterpret_cast<float *>(p);     p += sizeof(float) * 256;
-        s.grid = p;
+        s.grid = reinterpret_cast<float4 *>(p);
     }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -707,13 +771,10 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     const int ti = tid < L ? tid : L - 1;
     const float cent_v = a.centroids[ti];
     const float bnd_v = a.boundaries[ti];
-    uint4 grid_v = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (BITS >= 4) {
-        const int ng16 = a.ngrid / 16;
-        grid_v = reinterpret_cast<const uint4 *>(a.grid)[tid < ng16 ? tid : ng16 - 1];
-    }
-    for (int i = tid; i < kKeys * CW; i += kThreads) s.cw[i] = 0u;
-    for (int i = tid; i < kKeys * SWN; i += kThreads) s.sw[i] = 0u;
+    float4 grid_v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
+    for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
+    for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
 
     // this lane's elements of each of its KT keys (slots past the last key
     // reload that key; their results are never stored)
@@ -752,7 +813,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.bnd[tid] = bnd_v;
     }
     if constexpr (BITS >= 4)
-        if (tid < a.ngrid / 16) reinterpret_cast<uint4 *>(s.grid)[tid] = grid_v;
+        if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // cleared words, codebook tables
 
     float tp[H > 1 ? H - 1 : 1], cp[H];
@@ -765,8 +826,13 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     // output chunk of this lane (one round: relabelled; two: natural)
     const int chunk = ROUNDS == 1 ? out1 : pl;
     const bool qjl = a.m > 0;
+    const __amdgpu_buffer_rsrc_t st = frag_table(a.sfrag, qjl ? frag_table_bytes<D, 2>() : 0);
 #pragma unroll
     for (int kt0 = 0; kt0 < KT; kt0 += KR) {
+        // S's fragments of the first k-step of the sign product, in flight
+        // with the butterflies
+        uint4 sf0[D / 64][2];
+        if (qjl) load_s_frag<D>(st, wave, lane, 0, sf0);
 #pragma unroll
         for (int t = kt0; t < kt0 + KR; ++t) {
             const int key = 16 * t + 4 * wave + g;
@@ -805,7 +871,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
             for (int i = 0; i <= NSW; ++i) {
                 const uint32_t word = sh0 ? ((seg[i] << sh0) | (i ? seg[i - 1] >> (32 - sh0) : 0u)) : seg[i];
-                if (word != 0u && w0 + i < CW) atomicOr(&s.cw[key * CW + w0 + i], word);
+                if (word != 0u && w0 + i < CW) atomicOr(&s.cw[key * CWS + w0 + i], word);
             }
             // residual as bf16 hi + lo terms in the B-operand slots of the QJL
             // product: coordinate l at k-step l / 32, k-block (l / 4) % 4,
@@ -834,7 +900,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             }
         }
         __syncthreads();
-        if (qjl) qjl_signs<D, KR>(a, s, kt0, wave, lane);
+        if (qjl) qjl_signs<D, KR>(st, s, kt0, wave, lane, sf0);
     }
     store_keys<D, BITS, kKeys, 1, 1>(a, s, n0, n_total, s_row, qjl);
 }
@@ -864,7 +930,7 @@ hipError_t launch_keys_k(const KeyLaunch &a, hipStream_t stream)
     if (a.wht_kernel && a.wht_rounds == 2) return launch_keys_wht<D, TIn, BITS, KT, 2>(a, stream);
     const int64_t n = static_cast<int64_t>(a.B) * a.H * a.T;
     constexpr size_t smem = key_smem_bytes<D, TIn, BITS, KT>();
-    auto kern = k_compress_keys<D, TIn, BITS, KT>;
+    auto kern = a.hadamard ? k_compress_keys<D, TIn, BITS, KT, 1> : k_compress_keys<D, TIn, BITS, KT, 3>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;

@@ -13,9 +13,12 @@ struct tq_codebook {
     std::vector<double> centroids, boundaries;   // fp64 host tables
     float *d_centroids = nullptr;                // device fp32 [2^bits]
     float *d_boundaries = nullptr;               // device fp32 [2^bits - 1], then +inf
-    // uniform grid over [first, last boundary] for codes of 3+ bits: grid[c] is a
-    // lower bound of #{t_i < y} for every y of cell c, at most two below it
-    uint8_t *d_grid = nullptr;
+    // codes of 4+ bits: a uniform grid over [first, last boundary] whose cells,
+    // widened by 2 % of a cell on each side, hold at most one boundary each.
+    // Cell c = {t, c_lo, c_hi, below (int bits)}: every y of the cell has
+    // #{t_i < y} = below + [y > t], and centroid c_lo (c_hi above t); t = +inf
+    // and c_hi = c_lo where the cell holds no boundary
+    float4 *d_grid = nullptr;
     int ngrid = 0;
     float grid_lo = 0.0f, grid_scale = 0.0f;
     int device = 0;
@@ -91,7 +94,7 @@ struct KeyLaunch {
     const float *wht;           // [2][d] Walsh-Hadamard round signs D1, D2
     int wht_rounds;             // 0 dense, 1 or 2 Walsh-Hadamard rounds
     bool wht_kernel;            // Walsh-Hadamard rounds as the register butterfly (else the +-1 matrix product)
-    const uint8_t *grid;
+    const float4 *grid;         // code cells (tq_codebook::d_grid)
     int ngrid;
     float grid_lo, grid_scale;
     const uint16_t *pifrag, *sfrag;
@@ -99,7 +102,8 @@ struct KeyLaunch {
     CacheMap map;               // flat, or appending into a layout cache
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
-constexpr int kMaxGrid = 4096;     // cells of the code grid (bytes of LDS)
+constexpr int kMaxGrid = 8192;     // cells of a codebook's code grid
+constexpr int kGridLds = 256;      // cells the key compressor stages in LDS (every codebook of d >= 3, <= 7 bits)
 
 struct ValueLaunch {
     const void *v;
