@@ -39,12 +39,13 @@ def compile_cmd(src: str, obj: str) -> list[str]:
 
 
 CALIB = os.path.join(PKG, "calib_read")
+CALIB_PROGRAMS = ("calib_read", "calib_mfma")
 
 
-def calib_cmd(out: str) -> list[str]:
+def calib_cmd(out: str, name: str = "calib_read") -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            os.path.join(PKG, "calib_read.hip"), "-o", out]
+            os.path.join(PKG, name + ".hip"), "-o", out]
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -78,12 +79,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
-    # streaming-read calibration program (bench.py --calib-read)
-    r = subprocess.run(calib_cmd(CALIB + ".tmp"), stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
-    if r.returncode != 0:
-        print(r.stdout.decode(errors="replace"), file=sys.stderr)
-        raise RuntimeError("hipcc failed for calib_read.hip")
-    os.replace(CALIB + ".tmp", CALIB)
+    # calibration programs: streaming read (bench.py --calib-read) and matrix
+    # cores (bench.py --calib-mfma)
+    for name in CALIB_PROGRAMS:
+        prog = os.path.join(PKG, name)
+        r = subprocess.run(calib_cmd(prog + ".tmp", name), stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            print(r.stdout.decode(errors="replace"), file=sys.stderr)
+            raise RuntimeError(f"hipcc failed for {name}.hip")
+        os.replace(prog + ".tmp", prog)
     return LIB
 
 

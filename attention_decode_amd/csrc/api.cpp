@@ -163,6 +163,21 @@ void prof_end(void *token, hipStream_t stream)
 
 }  // namespace tq
 
+namespace {
+
+// Coordinate that row R of the compressor's fragment tables (Pi, S) holds:
+// wave w's row tile j, MFMA output row 4 kb + r takes coordinate
+// (d / 16)(4 w + kb) + 4 j + r, so that each lane of the key kernel ends with
+// d / 16 consecutive coordinates of a key (the natural order at d = 64).
+int compressor_row(int d, int R)
+{
+    const int rtw = d / 64, rt = R / 16, rho = R % 16;
+    const int w = rt / rtw, j = rt % rtw, kb = rho / 4, r = rho % 4;
+    return (d / 16) * (4 * w + kb) + 4 * j + r;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *tq_last_error(void) { return g_error.c_str(); }
@@ -394,7 +409,8 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
         delete rot;
         return hip_fail(e, "tq_make_rotation: device upload");
     }
-    // operand fragments of the matrix-core compressor: Pi as three bf16 terms
+    // operand fragments of the matrix-core compressor (rows in the order of
+    // compressor_row): Pi as three bf16 terms
     // (about 24 significant bits, so y keeps fp32 accuracy), S as two (16 bits;
     // the residual is split in two as well, see the key kernel)
     const int ks_n = d / 32, rt_n = d / 16;
@@ -404,7 +420,7 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
         for (int ks = 0; ks < ks_n; ++ks)
             for (int lane = 0; lane < 64; ++lane)
                 for (int el = 0; el < 8; ++el) {
-                    const int row = 16 * rt + lane % 16, kb = lane / 16;
+                    const int row = compressor_row(d, 16 * rt + lane % 16), kb = lane / 16;
                     uint16_t parts[3];
                     const double pv = pi[static_cast<size_t>(row) * d + 32 * ks + 8 * kb + el];
                     if (kind == TQ_ROT_HADAMARD) {
@@ -754,6 +770,8 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     a.ngrid = fmt->cb->ngrid;
     a.grid_lo = fmt->cb->grid_lo;
     a.grid_scale = fmt->cb->grid_scale;
+    a.grid_off = static_cast<float>(-static_cast<double>(fmt->cb->grid_lo) * fmt->cb->grid_scale);
+    a.grid_max = static_cast<float>(fmt->cb->ngrid > 0 ? fmt->cb->ngrid - 1 : 0);
     a.pifrag = fmt->rot->d_pifrag;
     a.sfrag = fmt->rot->d_sfrag;
     a.out = out;

@@ -174,12 +174,19 @@ struct KeySmem {
 template <int D, typename TIn>
 constexpr int key_stage_stride() { return D * static_cast<int>(sizeof(TIn)) + 16; }
 
-// the workgroup's raw keys (step 0-1) and the residual operands (steps 3-4)
-// share one region: the keys are dead before the first residual is written
+// d = 256: the matrix compressor writes its code and sign words straight to
+// the planes (each lane holds 16 consecutive coordinates of a key, two lanes
+// one run of whole words), so no LDS holds them and the residual operands of
+// all the workgroup's keys fit beside the staged keys: one sign product
+template <int D> constexpr bool key_direct_words() { return D == 256; }
+
+// the workgroup's raw keys (step 0-1) and the residual operands of all its
+// key tiles (steps 3-4) share one region: the keys are dead before the first
+// residual is written
 template <int D, typename TIn, int KT>
 constexpr size_t key_union_bytes()
 {
-    const size_t rfrag = sizeof(uint4) * key_pass_tiles<D, TIn, KT>() * (D / 32) * 2 * 64;
+    const size_t rfrag = sizeof(uint4) * KT * (D / 32) * 2 * 64;
     const size_t stage = static_cast<size_t>(16 * KT) * key_stage_stride<D, TIn>();
     return rfrag > stage ? rfrag : stage;
 }
@@ -188,8 +195,9 @@ template <int D, typename TIn, int BITS, int KT>
 constexpr size_t key_smem_bytes()
 {
     constexpr size_t keys = 16 * KT;
-    return key_union_bytes<D, TIn, KT>() + sizeof(uint32_t) * keys * (cw_stride<D, BITS>() + sw_stride<D>())
-           + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512 + (BITS >= 4 ? sizeof(float4) * kGridLds : 0);
+    constexpr size_t words = key_direct_words<D>() ? 0 : sizeof(uint32_t) * keys * (cw_stride<D, BITS>() + sw_stride<D>());
+    return key_union_bytes<D, TIn, KT>() + words + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512
+           + (BITS >= 4 ? sizeof(float4) * kGridLds : 0);
 }
 
 
@@ -227,9 +235,11 @@ __device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BIT
         const float dv = ay - c;
         res = up ? dv : -dv;
     } else {
-        int c = static_cast<int>((y - a.grid_lo) * a.grid_scale);
-        c = c < 0 ? 0 : (c >= a.ngrid ? a.ngrid - 1 : c);
-        const float4 e = s.grid[c];
+        // cell index (y - lo) / w as one fma, clamped to [0, ngrid - 1] before
+        // the conversion; its rounding (about 1e-5 of a cell) is inside the
+        // cells' 2 % widening
+        const float cf = __builtin_amdgcn_fmed3f(fmaf(y, a.grid_scale, a.grid_off), 0.0f, a.grid_max);
+        const float4 e = s.grid[static_cast<int>(cf)];
         const bool up = y > e.x;
         pos = __float_as_int(e.w) + (up ? 1 : 0);
         res = y - (up ? e.z : e.y);
@@ -273,19 +283,32 @@ __device__ __forceinline__ void load_s_frag(__amdgpu_buffer_rsrc_t st, int wave,
     }
 }
 
+// Row order of the compressor's fragment tables.  Wave w's row tile j, MFMA
+// output row 4 kb + r (lane col + 16 kb, element r) holds coordinate
+// SEGC (4 w + kb) + 4 j + r, SEGC = d / 16: each lane ends with SEGC
+// consecutive coordinates of each of its keys (the host orders the rows of
+// Pi and S so; at d = 64 this is the natural order).
+template <int D> constexpr int seg_coords() { return D / 16; }
+
 // z = S r for the residual operands of key tiles kt0 .. kt0 + KR - 1 (LDS,
-// B-operand order) on this wave's rows of S; sign bits [z >= 0] OR-ed into
-// the sign words.  sf0 holds the first k-step's S fragments, loaded by the
+// B-operand order) on this wave's rows of S; sign bits [z >= 0] of the
+// lane's SEGC consecutive rows OR-ed into the LDS sign words, or (DIRECT,
+// d = 256) paired with the next lane's 16 into one word stored to the key's
+// row of the sign plane (rows: the plane row of each of the workgroup's keys,
+// -1 to skip).  sf0 holds the first k-step's S fragments, loaded by the
 // caller ahead of the residual work; each later k-step's fragments are in
-// flight while the previous k-step's products run.  Ends with a workgroup
-// barrier (the pass's residual operands are read before the next pass
-// writes them).
-template <int D, int KR>
-__device__ __forceinline__ void qjl_signs(__amdgpu_buffer_rsrc_t st, const KeySmem &s, int kt0, int wave, int lane,
+// flight while the previous k-step's products run.  Without DIRECT, ends with
+// a workgroup barrier (the pass's residual operands are read before the next
+// pass writes them).
+template <int D, int KR, bool DIRECT>
+__device__ __forceinline__ void qjl_signs(__amdgpu_buffer_rsrc_t st, const KeySmem &s, const KeyLaunch &a,
+                                          const int64_t *rows, int kt0, int wave, int lane,
                                           const uint4 (&sf0)[D / 64][2])
 {
-    constexpr int KS = D / 32, RTW = D / 64, SWS = sw_stride<D>();
+    constexpr int KS = D / 32, RTW = D / 64, SWN = D / 32, SWS = sw_stride<D>(), SEGC = seg_coords<D>();
+    static_assert(!DIRECT || SEGC == 16, "direct sign words pair two lanes of 16 rows");
     const int col = lane & 15, kb = lane >> 4;
+    const int qb = SEGC * (4 * wave + kb);      // first row of S this lane holds
     f32x4 zacc[RTW][KR];
 #pragma unroll
     for (int j = 0; j < RTW; ++j)
@@ -319,65 +342,111 @@ __device__ __forceinline__ void qjl_signs(__amdgpu_buffer_rsrc_t st, const KeySm
         }
     }
 #pragma unroll
-    for (int j = 0; j < RTW; ++j) {
-        const int rt = wave * RTW + j;
-        const int off = 16 * rt + 4 * kb;
+    for (int kt = 0; kt < KR; ++kt) {
+        uint32_t bits = 0;        // bit 4 j + r: row qb + 4 j + r
 #pragma unroll
-        for (int kt = 0; kt < KR; ++kt) {
-            uint32_t nib = 0;
+        for (int j = 0; j < RTW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) nib |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << r;
-            atomicOr(&s.sw[(16 * (kt0 + kt) + col) * SWS + (off >> 5)], nib << (off & 31));
+            for (int r = 0; r < 4; ++r) bits |= (zacc[j][kt][r] >= 0.0f ? 1u : 0u) << (4 * j + r);
+        const int key = 16 * (kt0 + kt) + col;
+        if constexpr (DIRECT) {
+            const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(bits), 16));
+            const int64_t row = rows[key];
+            if (!(kb & 1) && row >= 0)
+                reinterpret_cast<uint32_t *>(a.out.signs)[row * SWN + (qb >> 5)] = bits | (other << 16);
+        } else {
+            atomicOr(&s.sw[key * SWS + (qb >> 5)], bits << (qb & 31));
         }
     }
-    __syncthreads();
+    if constexpr (!DIRECT) __syncthreads();
 }
 
-// The workgroup's KEYS packed keys to the planes: contiguous rows of every
-// plane, or (when appending to a layout cache) each key at its own row.
-// ||k||^2 and ||r||^2 arrive as NPN and NPR fp64 partial sums per key.
-template <int D, int BITS, int KEYS, int NPN, int NPR>
-__device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s, int64_t n0, int64_t n_total,
-                                           int64_t *s_row, bool qjl)
+// The code words of one lane's SEGC consecutive codes (seg: bit BITS e holds
+// the code of coordinate qb + e), for the key at plane row `row`.
+//   LDS (not DIRECT): OR-ed into the key's LDS code words at bit BITS qb.
+//   DIRECT (d = 256, SEGC = 16): straight to the plane.  With BITS even the
+//   lane's 16 codes are BITS / 2 whole words; with BITS odd the lanes kb, kb
+//   + 1 (kb even) hold one run of BITS words, the first lane's segment ending
+//   and the second's starting in the middle of word BITS / 2, so the second
+//   lane's low 16 bits move to the first (one lane shuffle).
+template <int D, int BITS, bool DIRECT, int NSEG>
+__device__ __forceinline__ void put_code_words(const KeySmem &s, const KeyLaunch &a, const uint32_t (&seg)[NSEG + 1],
+                                               int key, int64_t row, int qb, int kb)
 {
-    constexpr int CW = D * BITS / 32, SWN = D / 32, CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
-    const int tid = threadIdx.x;
-    const int nk = static_cast<int>(n_total - n0 < KEYS ? n_total - n0 : KEYS);
-    if (a.map.mode == CacheMap::kFlat) {
-        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes) + n0 * CW;
-        for (int i = tid; i < nk * CW; i += kThreads) codes[i] = s.cw[(i / CW) * CWS + i % CW];
-        if (qjl) {
-            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs) + n0 * SWN;
-            for (int i = tid; i < nk * SWN; i += kThreads) signs[i] = s.sw[(i / SWN) * SWS + i % SWN];
-        }
-        if (tid < nk) s_row[tid] = n0 + tid;
-    } else {
-        if (tid < nk) s_row[tid] = out_row(a.map, a.H, a.T, n0 + tid);
-        __syncthreads();
-        uint32_t *codes = reinterpret_cast<uint32_t *>(a.out.codes);
-        for (int i = tid; i < nk * CW; i += kThreads) {
-            const int64_t r = s_row[i / CW];
-            if (r >= 0) codes[r * CW + i % CW] = s.cw[(i / CW) * CWS + i % CW];
-        }
-        if (qjl) {
-            uint32_t *signs = reinterpret_cast<uint32_t *>(a.out.signs);
-            for (int i = tid; i < nk * SWN; i += kThreads) {
-                const int64_t r = s_row[i / SWN];
-                if (r >= 0) signs[r * SWN + i % SWN] = s.sw[(i / SWN) * SWS + i % SWN];
+    constexpr int CW = D * BITS / 32, CWS = cw_stride<D, BITS>();
+    if constexpr (DIRECT) {
+        static_assert(seg_coords<D>() == 16, "direct code words pair two lanes of 16 codes");
+        uint32_t *plane = reinterpret_cast<uint32_t *>(a.out.codes);
+        constexpr int NW = BITS / 2;
+        if constexpr (BITS % 2 == 0) {
+            if (row >= 0) {
+                uint32_t *dst = plane + row * CW + (BITS * qb >> 5);
+#pragma unroll
+                for (int i = 0; i < NW; ++i) dst[i] = seg[i];
+            }
+        } else {
+            const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(seg[0]), 16));
+            if (row >= 0) {
+                uint32_t *dst = plane + row * CW + BITS * (qb >> 5);      // the pair's first word
+                if (kb & 1) {
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) dst[NW + 1 + i] = (seg[i] >> 16) | (seg[i + 1] << 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) dst[i] = seg[i];
+                    dst[NW] = (seg[NW] & 0xffffu) | (other << 16);
+                }
             }
         }
+    } else {
+        const int bit0 = BITS * qb, w0 = bit0 >> 5, sh = bit0 & 31;
+#pragma unroll
+        for (int i = 0; i <= NSEG; ++i) {
+            const uint32_t word = sh ? ((seg[i] << sh) | (i ? seg[i - 1] >> (32 - sh) : 0u)) : seg[i];
+            if (word != 0u && w0 + i < CW) atomicOr(&s.cw[key * CWS + w0 + i], word);
+        }
     }
-    if (tid < nk && s_row[tid] >= 0) {
-        const int64_t r = s_row[tid];
+}
+
+// The workgroup's KEYS packed keys to the planes, each at its row s_row[key]
+// (-1: skipped): the code and sign words from LDS (WORDS; otherwise already
+// stored), ||k|| and ||r|| from NPN and NPR fp64 partial sums per key.
+template <int D, int BITS, int KEYS, int NPN, int NPR, bool WORDS>
+__device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s, const int64_t *s_row, bool qjl)
+{
+    constexpr int CW = D * BITS / 32, SWN = D / 32, CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
+    constexpr int TPK = kThreads / KEYS;            // threads per key
+    const int tid = threadIdx.x, kk = tid / TPK, q = tid % TPK;
+    const int64_t row = s_row[kk];
+    if (row < 0) return;
+    if constexpr (WORDS) {
+        // the TPK threads of a key copy its words round-robin (fixed offsets
+        // from one base per thread)
+        {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.out.codes) + row * CW + q;
+            const uint32_t *src = s.cw + kk * CWS + q;
+#pragma unroll
+            for (int it = 0; it < (CW + TPK - 1) / TPK; ++it)
+                if (CW % TPK == 0 || q + it * TPK < CW) dst[it * TPK] = src[it * TPK];
+        }
+        if (qjl) {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.out.signs) + row * SWN + q;
+            const uint32_t *src = s.sw + kk * SWS + q;
+#pragma unroll
+            for (int it = 0; it < (SWN + TPK - 1) / TPK; ++it)
+                if (SWN % TPK == 0 || q + it * TPK < SWN) dst[it * TPK] = src[it * TPK];
+        }
+    }
+    if (q == 0) {
         double n2 = 0.0;
 #pragma unroll
-        for (int q = 0; q < NPN; ++q) n2 += s.nrm2[q * KEYS + tid];
-        a.out.knorm[r] = static_cast<float>(sqrt(n2));
+        for (int p = 0; p < NPN; ++p) n2 += s.nrm2[p * KEYS + kk];
+        a.out.knorm[row] = static_cast<float>(sqrt(n2));
         if (qjl) {
             double r2 = 0.0;
 #pragma unroll
-            for (int q = 0; q < NPR; ++q) r2 += s.rho2[q * KEYS + tid];
-            a.out.rnorm[r] = static_cast<float>(sqrt(r2));
+            for (int p = 0; p < NPR; ++p) r2 += s.rho2[p * KEYS + kk];
+            a.out.rnorm[row] = static_cast<float>(sqrt(r2));
         }
     }
 }
@@ -405,13 +474,15 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
     constexpr int NK = KeyTerms<TIn>::n;
     constexpr int L = 1 << BITS;
-    constexpr int CWS = cw_stride<D, BITS>(), SWS = sw_stride<D>();
+    constexpr bool DIRECT = key_direct_words<D>();
+    constexpr int CWS = DIRECT ? 0 : cw_stride<D, BITS>(), SWS = DIRECT ? 0 : sw_stride<D>();
     constexpr int kKT = KT;              // 16-key tiles of the workgroup
     constexpr int kKeys = 16 * kKT;      // keys of the workgroup
-    constexpr int KR = key_pass_tiles<D, TIn, KT>();   // key tiles per residual / sign pass
     constexpr int TPK = kThreads / kKeys;                              // threads per staged key
+    constexpr int SEGC = seg_coords<D>();                              // consecutive coordinates per lane
+    constexpr int NSEG = (SEGC * BITS + 31) / 32;                      // words of a lane's codes
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup
+    __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup (-1: none)
     KeySmem s;
     {
         unsigned char *p = smem_raw;
@@ -439,6 +510,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
     for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
+    if (tid < kKeys) s_row[tid] = n0 + tid < n_total ? out_row(a.map, a.H, a.T, n0 + tid) : -1;
     // Pi's fragments of the first k-step, in flight with the keys
     const __amdgpu_buffer_rsrc_t pt = frag_table(a.pifrag, frag_table_bytes<D, 3>());
     const __amdgpu_buffer_rsrc_t st = frag_table(a.sfrag, a.m > 0 ? frag_table_bytes<D, 2>() : 0);
@@ -494,7 +566,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // staged keys, cleared words, codebook tables
 
-    // ---- 1. y = Pi k (unnormalised), this wave's rows 16 (RTW wave + j) + 4 kb + r.
+    // ---- 1. y = Pi k (unnormalised): acc[j][kt][r] of lane (col, kb) is
+    // coordinate SEGC (4 wave + kb) + 4 j + r of key 16 kt + col (the row order
+    // of the fragment table).
     // Pi's A fragments come from L2, double-buffered: the next k-step's are
     // in flight while this k-step's products run.
     f32x4 acc[RTW][kKT];
@@ -502,7 +576,6 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     for (int j = 0; j < RTW; ++j)
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int bits = BITS;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) load_pi_frag<D, NP>(pt, wave, lane, ks + 1, af[(ks + 1) & 1]);
@@ -552,44 +625,44 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     }
 
     const bool qjl = a.m > 0;
-#pragma unroll
-    for (int kt0 = 0; kt0 < kKT; kt0 += KR) {
     // S's fragments of the first k-step of step 4, in flight with step 3
     uint4 sf0[RTW][2];
     if (qjl) load_s_frag<D>(st, wave, lane, 0, sf0);
+    const int qb = SEGC * (4 * wave + kb);      // first coordinate this lane holds
     // ---- 3. codes idx = #{boundaries < y}, residual r = y - c[idx], ||r||
-    // (key tiles kt0 .. kt0 + KR - 1 of this pass)
 #pragma unroll
-    for (int kt = kt0; kt < kt0 + KR; ++kt) {
+    for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
         float rr = 0.0f;
+        uint32_t seg[NSEG + 1];               // code of coordinate qb + e at bit BITS e
+#pragma unroll
+        for (int i = 0; i <= NSEG; ++i) seg[i] = 0u;
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
-            const int rt = wave * RTW + j;
-            uint32_t chunk = 0;
             float res[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float y = acc[j][kt][r] * inv_n[kt];
-                const int pos = encode_coord<BITS>(y, tp, cp, s, a, res[r]);
+                const uint32_t pos = static_cast<uint32_t>(encode_coord<BITS>(y, tp, cp, s, a, res[r]));
                 rr = fmaf(res[r], res[r], rr);
-                chunk |= static_cast<uint32_t>(pos) << (bits * r);
+                const int b = BITS * (4 * j + r);
+                seg[b >> 5] |= pos << (b & 31);
+                if ((b & 31) + BITS > 32) seg[(b >> 5) + 1] |= pos >> (32 - (b & 31));
             }
-            // residual as two bf16 terms (hardware round to nearest even)
+            // residual as two bf16 terms (hardware round to nearest even), in
+            // the B-operand slots of coordinates q0 .. q0 + 3: k-step q0 / 32,
+            // k-block (q0 / 4) % 4 (the lane col + 16 k-block), elements
+            // 4 ((q0 / 16) % 2) + r
             const uint32_t h01 = bf16x2(res[0], res[1]), h23 = bf16x2(res[2], res[3]);
             const uint32_t l01 = bf16x2(res[0] - __uint_as_float(h01 << 16), res[1] - __uint_as_float(h01 & 0xffff0000u));
             const uint32_t l23 = bf16x2(res[2] - __uint_as_float(h23 << 16), res[3] - __uint_as_float(h23 & 0xffff0000u));
-            // 4 codes of `bits` bits at bit offset bits (16 rt + 4 kb) of the key's stream
-            const int off = bits * (16 * rt + 4 * kb), w = off >> 5, sh = off & 31;
-            atomicOr(&s.cw[key * CWS + w], chunk << sh);
-            if (sh + 4 * bits > 32) atomicOr(&s.cw[key * CWS + w + 1], chunk >> (32 - sh));
-            // residual as B operand of k-step rt/2: elements 4 (rt % 2) + r of this lane
-            uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 0) * 64 + lane]);
-            uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[(((kt - kt0) * KS + rt / 2) * 2 + 1) * 64 + lane]);
-            const int hw = 2 * (rt & 1);
+            const int q0 = qb + 4 * j, ks = q0 >> 5, bl = col + 16 * ((q0 >> 2) & 3), hw = 2 * ((q0 >> 4) & 1);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + bl]);
+            uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + bl]);
             *reinterpret_cast<uint2 *>(dst + hw) = make_uint2(h01, h23);
             *reinterpret_cast<uint2 *>(dst1 + hw) = make_uint2(l01, l23);
         }
+        put_code_words<D, BITS, DIRECT, NSEG>(s, a, seg, key, s_row[key], qb, kb);
         double rd = static_cast<double>(rr);
         rd += __shfl_xor(rd, 16);
         rd += __shfl_xor(rd, 32);
@@ -599,11 +672,10 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 
     // ---- 4. z = S r on this wave's rows; signs [z >= 0] (skipped for the
     // first-stage format, m = 0; the condition is uniform over the launch)
-    if (qjl) qjl_signs<D, KR>(st, s, kt0, wave, lane, sf0);
-    }   // passes
+    if (qjl) qjl_signs<D, kKT, DIRECT>(st, s, a, s_row, 0, wave, lane, sf0);
 
-    // ---- 5. store the WG's keys
-    store_keys<D, BITS, kKeys, TPK, 4>(a, s, n0, n_total, s_row, qjl);
+    // ---- 5. the workgroup's norms (and, from LDS, its code and sign words)
+    store_keys<D, BITS, kKeys, TPK, 4, !DIRECT>(a, s, s_row, qjl);
 }
 
 
@@ -775,6 +847,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
     for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
+    if (tid < kKeys) s_row[tid] = n0 + tid < n_total ? out_row(a.map, a.H, a.T, n0 + tid) : -1;
 
     // this lane's elements of each of its KT keys (slots past the last key
     // reload that key; their results are never stored)
@@ -900,9 +973,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             }
         }
         __syncthreads();
-        if (qjl) qjl_signs<D, KR>(st, s, kt0, wave, lane, sf0);
+        if (qjl) qjl_signs<D, KR, false>(st, s, a, s_row, kt0, wave, lane, sf0);
     }
-    store_keys<D, BITS, kKeys, 1, 1>(a, s, n0, n_total, s_row, qjl);
+    store_keys<D, BITS, kKeys, 1, 1, true>(a, s, s_row, qjl);
 }
 
 template <int D, typename TIn, int BITS, int KT, int ROUNDS>

@@ -97,6 +97,7 @@ struct KeyLaunch {
     const float4 *grid;         // code cells (tq_codebook::d_grid)
     int ngrid;
     float grid_lo, grid_scale;
+    float grid_off, grid_max;   // -grid_lo grid_scale (rounded once), ngrid - 1
     const uint16_t *pifrag, *sfrag;
     tq_kcache out;
     CacheMap map;               // flat, or appending into a layout cache

@@ -17,7 +17,7 @@ fp64 oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--key-format full|first-stage|q8_0|q4_0]
                     [--rotation dense|hadamard|hadamard2] [--layout flat|paged] [--block-size N]
-                    [--eager-decode] [--no-cpu-baseline] [--scores] [--calib-read]
+                    [--eager-decode] [--no-cpu-baseline] [--scores] [--calib-read] [--calib-mfma]
 """
 from __future__ import annotations
 
@@ -68,6 +68,8 @@ def parse():
                     help="run only a plain 1 GiB device copy (to calibrate HBM byte counters)")
     ap.add_argument("--calib-read", action="store_true",
                     help="run only the streaming-read calibration program (the practical HBM read ceiling)")
+    ap.add_argument("--calib-mfma", action="store_true",
+                    help="run only the matrix-core calibration program (sustained bf16 / f16 / i8 MFMA rates)")
     ap.add_argument("--scores", action="store_true",
                     help="time only tq_scores (query prep + raw scores [B, Hq, T]) over every layer's packed "
                          "keys and print its own JSON line")
@@ -304,11 +306,12 @@ def main():
               "(the path shards by sequence / KV head with no exchange, see the design notes)",
               file=sys.stderr)
         sys.exit(2)
-    if args.calib_read:
+    if args.calib_read or args.calib_mfma:
         import subprocess
-        prog = os.path.join(ROOT, "attention_decode_amd", "calib_read")
+        name = "calib_read" if args.calib_read else "calib_mfma"
+        prog = os.path.join(ROOT, "attention_decode_amd", name)
         if not os.path.exists(prog):
-            sys.exit("calib_read is not built (python -m attention_decode_amd.build)")
+            sys.exit(f"{name} is not built (python -m attention_decode_amd.build)")
         sys.exit(subprocess.call([prog]))
     import torch
     import attention_decode_amd as tq
