@@ -645,14 +645,19 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     const int64_t target = p.mfma ? 2048 : 1024;
     int64_t want = (target + p.units - 1) / p.units;
     if (p.mfma && fmt->d >= 256) {
-        // one workgroup per CU at a time: the split count that minimises the
-        // rounds of workgroups times the tokens of each (ties to fewer splits,
-        // which need no or a smaller merge); the launch fills kDecodeCUs CUs
+        // the split count that minimises the rounds of workgroups times the
+        // tokens of each (ties to fewer splits, which need no or a smaller
+        // merge).  A round is one workgroup per CU, or two for the table-score
+        // kernels of at most two query heads per unit (3+ bit keys), which fit
+        // two per CU at d = 256 when the value groups allow their spread
+        // operand; for value formats that do not, the extra splits only cost
+        // the merge.
+        const int64_t slots = kDecodeCUs * (fmt->mse_bits >= 3 && p.gc <= 2 ? 2 : 1);
         want = 1;
         double best = 1e300;
-        const int64_t smax = std::max<int64_t>(16, 2 * ((kDecodeCUs + p.units - 1) / p.units));
+        const int64_t smax = std::max<int64_t>(16, 2 * ((slots + p.units - 1) / p.units));
         for (int64_t s = 1; s <= smax && s <= 1024; ++s) {
-            const double rounds = static_cast<double>((p.units * s + kDecodeCUs - 1) / kDecodeCUs);
+            const double rounds = static_cast<double>((p.units * s + slots - 1) / slots);
             const double cost = rounds / static_cast<double>(s) * (1.0 + 1e-3 * static_cast<double>(s));
             if (cost < best) {
                 best = cost;

@@ -164,7 +164,10 @@ tq_status tq_compress_values(const tq_val_fmt *fmt, const void *v, tq_dtype dtyp
      score_t = ||k_t|| ( sum_j (Pi q)_j c[idx_tj]
                          + sqrt(pi/2)/m ||r_t|| sum_i (S Pi q)_i (2 s_ti - 1) ).
    scores: device fp32 [B, Hq, T].  ws: device workspace of at least
-   tq_scores_workspace_bytes() bytes. */
+   tq_scores_workspace_bytes() bytes.  (ws and ws_bytes extend the plain
+   queries + packed keys -> scores call: the rotated query operands are built
+   once per call into caller-owned memory, so that the call itself allocates
+   nothing; a too-small ws returns TQ_ENOMEM before any launch.) */
 size_t tq_scores_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq);
 tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B, int Hq, int Hkv,
                     int64_t T, tq_kcache kc, float *scores, void *ws, size_t ws_bytes,
@@ -179,7 +182,12 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
    writes zeros.  n_splits 0 picks the split count; otherwise the token axis
    is cut into n_splits ranges whose partial results are merged with a
    log-sum-exp combine.  ws: device workspace of at least
-   tq_attend_workspace_bytes() bytes (same n_splits). */
+   tq_attend_workspace_bytes() bytes (same n_splits).  (n_splits, ws and
+   ws_bytes extend the plain queries + packed K/V -> out call: the split count
+   is exposed so that a caller can fix the work partition (identical results
+   across calls, or a bounded workspace), and the query operands and split
+   partials live in caller-owned memory so that the call allocates nothing.
+   n_splits 0 and a workspace of the queried size give the plain call.) */
 int tq_attend_splits(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T);
 size_t tq_attend_workspace_bytes(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
                                  int n_splits);
