@@ -623,8 +623,12 @@ struct DecodePlan {
 };
 
 // paged_bs > 0: a paged cache with that block size, whose splits must each
-// span at most kStageBlocks blocks (their ids are staged in LDS)
-DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits, int paged_bs = 0)
+// span at most kStageBlocks blocks (their ids are staged in LDS).
+// scores_only: the plan of tq_scores, whose kernel (no value stage) fits at
+// least two workgroups per CU at d = 256 as at d = 128 and writes raw scores
+// per token (no merge), so it takes the d = 128 rule.
+DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T, int n_splits, int paged_bs = 0,
+                       bool scores_only = false)
 {
     DecodePlan p;
     const int G = Hq / Hkv;
@@ -644,7 +648,7 @@ DecodePlan decode_plan(const tq_key_fmt *fmt, int B, int Hq, int Hkv, int64_t T,
     // scalar kernels; d = 256 below
     const int64_t target = p.mfma ? 2048 : 1024;
     int64_t want = (target + p.units - 1) / p.units;
-    if (p.mfma && fmt->d >= 256) {
+    if (p.mfma && fmt->d >= 256 && !scores_only) {
         // the split count that minimises the rounds of workgroups times the
         // tokens of each (ties to fewer splits, which need no or a smaller
         // merge).  A round is one workgroup per CU, or two for the table-score
@@ -908,7 +912,7 @@ tq_status tq_scores(const tq_key_fmt *fmt, const void *q, tq_dtype dtype, int B,
     a.kc = kc;
     a.scores = scores;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const DecodePlan plan = decode_plan(fmt, B, Hq, Hkv, T, 0);
+    const DecodePlan plan = decode_plan(fmt, B, Hq, Hkv, T, 0, 0, true);
     if (plan.mfma) {
         // the matrix-core decode kernel with its value and softmax stages
         // compiled out: same tiles, same score products, raw scores out
