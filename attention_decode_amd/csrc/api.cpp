@@ -258,7 +258,7 @@ tq_status tq_build_codebook(int d, int bits, tq_codebook **out)
         return hip_fail(e, "tq_build_codebook: device upload");
     }
     cb->d_boundaries = cb->d_centroids + L;
-    if (L >= 16) {
+    if (L >= (1 << tq::kCellBits)) {
         // code cells over the fp32 boundaries the kernel compares with: the
         // coarsest uniform grid (from 64 cells, doubling) whose cells, widened by
         // 2 % of a cell on each side to absorb the rounding of the cell index,
@@ -749,7 +749,7 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     TQ_TRY(check_input(k, dtype, B, Hkv, T, sb, sh, st, fmt->d, who));
     if (T == 0) return TQ_OK;
     TQ_TRY(check_kcache(out, fmt->qjl_m, who));
-    if (fmt->mse_bits >= 4 && fmt->cb->ngrid > tq::kGridLds)
+    if (fmt->mse_bits >= tq::kCellBits && fmt->cb->ngrid > tq::kGridLds)
         return fail(TQ_EUNSUPPORTED, "%s: codebook grid of %d cells exceeds the compressor's %d", who,
                     fmt->cb->ngrid, tq::kGridLds);
     tq::KeyLaunch a{};
@@ -761,6 +761,7 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     a.sb = sb;
     a.sh = sh;
     a.st = st;
+    a.contig = st == fmt->d && sh == T * fmt->d && sb == static_cast<int64_t>(Hkv) * T * fmt->d;
     a.d = fmt->d;
     a.bits = fmt->mse_bits;
     a.m = fmt->qjl_m;

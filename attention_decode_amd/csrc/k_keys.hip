@@ -25,9 +25,9 @@
 // the exact fp32 squares (each wave takes a quarter of the k-steps); ||r||
 // in fp32 per lane and fp64 across lanes.
 //
-// Codes: idx = #{t_i < y}.  Up to 3 bits a binary search of |y| among the
-// positive boundaries of the symmetric codebook, in registers (at most two
-// comparisons, no LDS reads); from 4 bits one 16-byte LDS read of the cell of
+// Codes: idx = #{t_i < y}.  Up to 2 bits a comparison of |y| with the
+// positive boundary of the symmetric codebook, in registers (no LDS reads);
+// from 3 bits (kCellBits) one 16-byte LDS read of the cell of
 // a uniform grid over [t_0, t_{L-2}] that holds y: the count below the cell,
 // the one boundary inside it and the centroids on either side, so one exact
 // comparison finishes the code and picks the centroid.
@@ -197,15 +197,15 @@ constexpr size_t key_smem_bytes()
     constexpr size_t keys = 16 * KT;
     constexpr size_t words = key_direct_words<D>() ? 0 : sizeof(uint32_t) * keys * (cw_stride<D, BITS>() + sw_stride<D>());
     return key_union_bytes<D, TIn, KT>() + words + sizeof(double) * (4 * keys + kThreads) + sizeof(float) * 512
-           + (BITS >= 4 ? sizeof(float4) * kGridLds : 0);
+           + (BITS >= kCellBits ? sizeof(float4) * kGridLds : 0);
 }
 
 
 // Code idx = #{t_i < y} of one rotated coordinate and its residual y - c[idx].
-// Up to 3 bits: |y| placed among the positive boundaries tp of the exactly
-// symmetric codebook by a binary search in registers, the centroid taken from
-// the positive ones cp, idx and the residual fixed by the sign of y (bit for
-// bit what the full count gives, up to exact ties).  From 4 bits: the cell of
+// Up to 2 bits: |y| placed among the positive boundaries tp of the exactly
+// symmetric codebook in registers, the centroid taken from the positive ones
+// cp, idx and the residual fixed by the sign of y (bit for bit what the full
+// count gives, up to exact ties).  From 3 bits (kCellBits): the cell of
 // the uniform grid that holds y gives the count below it and its one
 // boundary t, so the code is below + [y > t], the centroid c_lo or c_hi.
 template <int BITS>
@@ -215,20 +215,15 @@ __device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BIT
 {
     constexpr int H = (1 << BITS) / 2;
     int pos;
-    if constexpr (BITS <= 3) {
+    if constexpr (BITS < kCellBits) {
         const float ay = fabsf(y);
         int cnt = 0;          // positive boundaries below |y|
         float c = cp[0];
+        static_assert(BITS <= 2, "register codes: one positive boundary at most");
         if constexpr (BITS == 2) {
             const bool b0 = ay > tp[0];
             cnt = b0 ? 1 : 0;
             c = b0 ? cp[1] : cp[0];
-        } else if constexpr (BITS == 3) {
-            const bool b1 = ay > tp[1];
-            const bool b0 = ay > (b1 ? tp[2] : tp[0]);
-            cnt = (b1 ? 2 : 0) + (b0 ? 1 : 0);
-            const float clo = b0 ? cp[1] : cp[0], chi = b0 ? cp[3] : cp[2];
-            c = b1 ? chi : clo;
         }
         const bool up = y > 0.0f;
         pos = cnt ^ (up ? H : H - 1);     // H + cnt above zero, H - 1 - cnt below (cnt < H)
@@ -507,7 +502,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     const float cent_v = a.centroids[ti];
     const float bnd_v = a.boundaries[ti];      // entry L - 1 is +inf
     float4 grid_v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
+    if constexpr (BITS >= kCellBits) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
     for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
     if (tid < kKeys) s_row[tid] = n0 + tid < n_total ? out_row(a.map, a.H, a.T, n0 + tid) : -1;
@@ -518,9 +513,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     load_pi_frag<D, NP>(pt, wave, lane, 0, af[0]);
 
     // ---- 0. the workgroup's keys into LDS, one HBM round trip: thread
-    // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (rows
-    // found with one divide per workgroup, then stepping across sequence /
-    // head boundaries) and adds the exact squares of its elements in fp64:
+    // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (row n
+    // at n d for densely packed inputs; otherwise found with one divide per
+    // workgroup, then stepping across sequence / head boundaries) and adds the exact squares of its elements in fp64:
     // partial q of ||k||^2.  Slots past the last key reload that key (loads
     // stay unconditional); their results are never stored.
     constexpr int RSTR = key_stage_stride<D, TIn>();
@@ -530,17 +525,23 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     {
         const int kk = tid / TPK, q = tid % TPK;
         const int last = static_cast<int>(n_total - 1 - n0 < kKeys - 1 ? n_total - 1 - n0 : kKeys - 1);
-        const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
-        int64_t t = t0 + (kk < last ? kk : last), h = bh0 % a.H, b = bh0 / a.H;
-        while (t >= a.T) {          // at most 64 / T + 1 steps
-            t -= a.T;
-            if (++h == a.H) {
-                h = 0;
-                ++b;
+        const int kr = kk < last ? kk : last;
+        const TIn *row;
+        if (a.contig) {
+            row = static_cast<const TIn *>(a.k) + (n0 + kr) * D;
+        } else {
+            const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
+            int64_t t = t0 + kr, h = bh0 % a.H, b = bh0 / a.H;
+            while (t >= a.T) {      // at most 64 / T + 1 steps
+                t -= a.T;
+                if (++h == a.H) {
+                    h = 0;
+                    ++b;
+                }
             }
+            row = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st;
         }
-        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + t * a.st)
-                           + q * CPT;
+        const uint4 *src = reinterpret_cast<const uint4 *>(row) + q * CPT;
         uint4 v[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) v[c] = src[c];
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.cent[tid] = cent_v;
         s.bnd[tid] = bnd_v;
     }
-    if constexpr (BITS >= 4)
+    if constexpr (BITS >= kCellBits)
         if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // staged keys, cleared words, codebook tables
 
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     // of y, bit for bit as the full count would give them (up to exact ties)
     constexpr int H = L / 2;
     float tp[H > 1 ? H - 1 : 1], cp[H];
-    if constexpr (BITS <= 3) {
+    if constexpr (BITS < kCellBits) {
 #pragma unroll
         for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
 #pragma unroll
@@ -801,7 +802,7 @@ constexpr size_t key_smem_bytes_wht(int bits)
     constexpr size_t keys = 16 * KT;
     const size_t rfrag = sizeof(uint4) * key_pass_tiles<D, TIn, KT>() * (D / 32) * 2 * 64;
     return rfrag + sizeof(uint32_t) * keys * ((D * bits / 32 + 1) + sw_stride<D>()) + sizeof(double) * 2 * keys
-           + sizeof(float) * 512 + (bits >= 4 ? sizeof(float4) * kGridLds : 0);
+           + sizeof(float) * 512 + (bits >= kCellBits ? sizeof(float4) * kGridLds : 0);
 }
 
 // One 256-thread workgroup encodes 16 KT keys; wave w takes keys 16 t + 4 w + g
@@ -844,7 +845,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     const float cent_v = a.centroids[ti];
     const float bnd_v = a.boundaries[ti];
     float4 grid_v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if constexpr (BITS >= 4) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
+    if constexpr (BITS >= kCellBits) grid_v = a.grid[tid < a.ngrid ? tid : a.ngrid - 1];
     for (int i = tid; i < kKeys * CWS; i += kThreads) s.cw[i] = 0u;
     for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
     if (tid < kKeys) s_row[tid] = n0 + tid < n_total ? out_row(a.map, a.H, a.T, n0 + tid) : -1;
@@ -852,20 +853,27 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     // this lane's elements of each of its KT keys (slots past the last key
     // reload that key; their results are never stored)
     const int last = static_cast<int>(n_total - 1 - n0 < kKeys - 1 ? n_total - 1 - n0 : kKeys - 1);
-    const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
     float x[KT][CPL];
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int kk = 16 * t + 4 * wave + g;
-        int64_t tt = t0 + (kk < last ? kk : last), h = bh0 % a.H, b = bh0 / a.H;
-        while (tt >= a.T) {
-            tt -= a.T;
-            if (++h == a.H) {
-                h = 0;
-                ++b;
+        const int kr = kk < last ? kk : last;
+        const TIn *row;
+        if (a.contig) {
+            row = static_cast<const TIn *>(a.k) + (n0 + kr) * D;
+        } else {
+            const int64_t bh0 = n0 / a.T, t0 = n0 - bh0 * a.T;
+            int64_t tt = t0 + kr, h = bh0 % a.H, b = bh0 / a.H;
+            while (tt >= a.T) {
+                tt -= a.T;
+                if (++h == a.H) {
+                    h = 0;
+                    ++b;
+                }
             }
+            row = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + tt * a.st;
         }
-        load_chunk<TIn, CPL>(static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + tt * a.st + CPL * pl, x[t]);
+        load_chunk<TIn, CPL>(row + CPL * pl, x[t]);
     }
     // round signs of this lane: D1 of its input coordinates; for a second
     // round D2 of the coordinates it holds after the first, times its sign
@@ -885,12 +893,12 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         s.cent[tid] = cent_v;
         s.bnd[tid] = bnd_v;
     }
-    if constexpr (BITS >= 4)
+    if constexpr (BITS >= kCellBits)
         if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // cleared words, codebook tables
 
     float tp[H > 1 ? H - 1 : 1], cp[H];
-    if constexpr (BITS <= 3) {
+    if constexpr (BITS < kCellBits) {
 #pragma unroll
         for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
 #pragma unroll

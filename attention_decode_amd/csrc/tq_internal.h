@@ -13,7 +13,7 @@ struct tq_codebook {
     std::vector<double> centroids, boundaries;   // fp64 host tables
     float *d_centroids = nullptr;                // device fp32 [2^bits]
     float *d_boundaries = nullptr;               // device fp32 [2^bits - 1], then +inf
-    // codes of 4+ bits: a uniform grid over [first, last boundary] whose cells,
+    // codes of kCellBits+ bits: a uniform grid over [first, last boundary] whose cells,
     // widened by 2 % of a cell on each side, hold at most one boundary each.
     // Cell c = {t, c_lo, c_hi, below (int bits)}: every y of the cell has
     // #{t_i < y} = below + [y > t], and centroid c_lo (c_hi above t); t = +inf
@@ -87,6 +87,7 @@ struct KeyLaunch {
     tq_dtype dtype;
     int B, H;
     int64_t T, sb, sh, st;      // element strides
+    bool contig;                // rows packed densely ([B, H, T, d] contiguous): row n at n d
     int d, bits, m;
     bool hadamard;              // Pi = integer matrix * rot_scale, exact in one bf16 term
     float rot_scale;            // 1/sqrt(d) (one Hadamard round), 1/d (two rounds)
@@ -103,6 +104,7 @@ struct KeyLaunch {
     CacheMap map;               // flat, or appending into a layout cache
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
+constexpr int kCellBits = 3;       // codes of kCellBits or more bits are read from code cells
 constexpr int kMaxGrid = 8192;     // cells of a codebook's code grid
 constexpr int kGridLds = 256;      // cells the key compressor stages in LDS (every codebook of d >= 3, <= 7 bits)
 
