@@ -704,10 +704,14 @@ constexpr uint32_t kWhtNeg[4] = {0x5a5au, 0x3c3cu, 0x0ff0u, 0xff00u};
 constexpr uint32_t kWhtEps = 0x9696u;
 constexpr uint64_t kWhtOut = 0x8deb7214c9af3650ull;
 
+// Lane permutations within a 16-lane row (quad swaps, half-row and row
+// mirrors): every source lane exists, so the move needs no "old" value and
+// the compiler can fold it into the consuming instruction as a DPP operand
+// (v_fmac_f32 with a DPP source, one instruction per butterfly stage)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
@@ -715,9 +719,9 @@ __device__ __forceinline__ double dpp_f64(double x)
 {
     const uint64_t u = __builtin_bit_cast(uint64_t, x);
     const uint32_t lo = static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+        __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, true));
     const uint32_t hi = static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false));
+        __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, true));
     return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
 }
 
