@@ -403,9 +403,28 @@ __device__ __forceinline__ void put_code_words(const KeySmem &s, const KeyLaunch
     }
 }
 
+// ||k||^2 of key kk from its NPN partials (fp32 values; NPN a power of two),
+// each an aligned subtree of one fixed pairwise tree over the key's groups of
+// eight elements, finished in that same tree, so that every tiling of the
+// keys gives the same bits
+template <int NPN>
+__device__ __forceinline__ float key_norm2(const double *nrm2, int stride, int kk)
+{
+    static_assert((NPN & (NPN - 1)) == 0, "partials of a power-of-two tree");
+    float p[NPN];
+#pragma unroll
+    for (int i = 0; i < NPN; ++i) p[i] = static_cast<float>(nrm2[i * stride + kk]);
+#pragma unroll
+    for (int w = 1; w < NPN; w *= 2)
+#pragma unroll
+        for (int i = 0; i < NPN; i += 2 * w) p[i] += p[i + w];
+    return p[0];
+}
+
 // The workgroup's KEYS packed keys to the planes, each at its row s_row[key]
 // (-1: skipped): the code and sign words from LDS (WORDS; otherwise already
-// stored), ||k|| and ||r|| from NPN and NPR fp64 partial sums per key.
+// stored), ||k|| from NPN partials of the key_norm2 tree and ||r|| from NPR
+// fp64 partial sums per key.
 template <int D, int BITS, int KEYS, int NPN, int NPR, bool WORDS>
 __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s, const int64_t *s_row, bool qjl)
 {
@@ -433,10 +452,7 @@ __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s,
         }
     }
     if (q == 0) {
-        double n2 = 0.0;
-#pragma unroll
-        for (int p = 0; p < NPN; ++p) n2 += s.nrm2[p * KEYS + kk];
-        a.out.knorm[row] = static_cast<float>(sqrt(n2));
+        a.out.knorm[row] = static_cast<float>(sqrt(static_cast<double>(key_norm2<NPN>(s.nrm2, KEYS, kk))));
         if (qjl) {
             double r2 = 0.0;
 #pragma unroll
@@ -515,9 +531,10 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     // ---- 0. the workgroup's keys into LDS, one HBM round trip: thread
     // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (row n
     // at n d for densely packed inputs; otherwise found with one divide per
-    // workgroup, then stepping across sequence / head boundaries) and adds the exact squares of its elements in fp64:
-    // partial q of ||k||^2.  Slots past the last key reload that key (loads
-    // stay unconditional); their results are never stored.
+    // workgroup, then stepping across sequence / head boundaries) and sums
+    // the squares of its elements: partial q of ||k||^2.  Slots past the last
+    // key reload that key (loads stay unconditional); their results are never
+    // stored.
     constexpr int RSTR = key_stage_stride<D, TIn>();
     constexpr int CH16 = D * static_cast<int>(sizeof(TIn)) / 16;     // 16-byte chunks per row
     constexpr int CPT = CH16 / TPK;                                    // chunks per thread
@@ -548,16 +565,31 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         uint4 *dst = reinterpret_cast<uint4 *>(kst + kk * RSTR) + q * CPT;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) dst[c] = v[c];
-        double ss = 0.0;
+        // partial q of ||k||^2 in fp32, one subtree of a fixed tree: each
+        // group of eight consecutive elements is one fma chain and the groups
+        // are summed pairwise (key_norm2 finishes the tree over the TPK
+        // partials).  A term passes through at most 7 + log2(D / 8) roundings
+        // of sums of non-negative terms (one more for an fp32 input's square;
+        // bf16 and fp16 squares are exact): 13 * 2^-24 < 8e-7 relative at
+        // d = 256, 4e-7 in ||k||
+        constexpr int EPC = 16 / static_cast<int>(sizeof(TIn));     // elements per chunk
+        constexpr int NG = CPT * EPC / 8;                              // groups of this thread
+        static_assert(NG >= 1 && (NG & (NG - 1)) == 0, "whole groups, a power of two per thread");
+        float gs[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) gs[g] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             float x[8];
             chunk_as_f32<TIn>(v, c, x);
 #pragma unroll
-            for (int e = 0; e < 16 / static_cast<int>(sizeof(TIn)); ++e)
-                ss = fma(static_cast<double>(x[e]), static_cast<double>(x[e]), ss);    // exact squares
+            for (int e = 0; e < EPC; ++e) gs[(c * EPC + e) / 8] = fmaf(x[e], x[e], gs[(c * EPC + e) / 8]);
         }
-        s.nrm2[q * kKeys + kk] = ss;
+#pragma unroll
+        for (int w = 1; w < NG; w *= 2)
+#pragma unroll
+            for (int g = 0; g < NG; g += 2 * w) gs[g] += gs[g + w];
+        s.nrm2[q * kKeys + kk] = static_cast<double>(gs[0]);
     }
     if (tid < L) {
         s.cent[tid] = cent_v;
@@ -604,11 +636,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
         // 1/||k|| only scales y: fp32 rsqrt (about 1 ulp) moves y by ~1e-7 at most,
-        // far inside the 1e-5 boundary band; the stored ||k|| is rounded from fp64
-        double n2d = 0.0;
-#pragma unroll
-        for (int q = 0; q < TPK; ++q) n2d += s.nrm2[q * kKeys + key];
-        const float n2 = static_cast<float>(n2d);
+        // far inside the 1e-5 boundary band; the stored ||k|| is the fp64 root
+        // of the same sum, rounded once
+        const float n2 = key_norm2<TPK>(s.nrm2, kKeys, key);
         inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
     }
     // 1-3 bits: the codebook is exactly symmetric (c[L-1-i] = -c[i], and so
@@ -706,34 +736,14 @@ constexpr uint64_t kWhtOut = 0x8deb7214c9af3650ull;
 
 // Lane permutations within a 16-lane row (quad swaps, half-row and row
 // mirrors): every source lane exists, so the move needs no "old" value and
-// the compiler can fold it into the consuming instruction as a DPP operand
-// (v_fmac_f32 with a DPP source, one instruction per butterfly stage)
+// the compiler folds it into the consuming v_add_f32 as a DPP operand
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = static_cast<uint32_t>(
-        __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, true));
-    const uint32_t hi = static_cast<uint32_t>(
-        __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, true));
-    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
-}
-
 // sums over the 16 lanes of a DPP row, left in every lane of the row
-__device__ __forceinline__ double row16_sum_f64(double x)
-{
-    x += dpp_f64<0xB1>(x);
-    x += dpp_f64<0x4E>(x);
-    x += dpp_f64<0x141>(x);
-    return x + dpp_f64<0x140>(x);
-}
-
 __device__ __forceinline__ float row16_sum_f32(float x)
 {
     x += dpp_f32<0xB1>(x);
@@ -742,10 +752,24 @@ __device__ __forceinline__ float row16_sum_f32(float x)
     return x + dpp_f32<0x140>(x);
 }
 
-// one round: the in-register stages, then the four lane stages
+// One lane stage on four values: x += s * (the partner lane's x), one
+// v_fmac_f32 with a DPP source per value (the compiler does not fold a DPP
+// move into v_fmac_f32, whose accumulator is tied to the destination, and
+// would spend a separate v_mov_b32_dpp on each).  The s_nop gives the two
+// wait states a DPP read needs after a VALU write of its source.
+#define TQ_WHT_FMAC(N, CTL) "v_fmac_f32_dpp %" #N ", %" #N ", %4 " CTL " row_mask:0xf bank_mask:0xf bound_ctrl:1"
+#define TQ_WHT_STAGE4(CTL, X, E, S)                                                                        \
+    asm("s_nop 1\n\t" TQ_WHT_FMAC(0, CTL) "\n\t" TQ_WHT_FMAC(1, CTL) "\n\t" TQ_WHT_FMAC(2, CTL) "\n\t"     \
+        TQ_WHT_FMAC(3, CTL)                                                                               \
+        : "+v"(X[E]), "+v"(X[E + 1]), "+v"(X[E + 2]), "+v"(X[E + 3])                                      \
+        : "v"(S))
+
+// one round: the in-register stages, then the four lane stages (partners
+// lane ^ 1, lane ^ 2, the half-row mirror and the row mirror)
 template <int CPL>
 __device__ __forceinline__ void wht_round(float (&x)[CPL], const float (&sg)[4])
 {
+    static_assert(CPL % 4 == 0, "lane stages take four values at a time");
 #pragma unroll
     for (int h = 1; h < CPL; h *= 2)
 #pragma unroll
@@ -756,14 +780,16 @@ __device__ __forceinline__ void wht_round(float (&x)[CPL], const float (&sg)[4])
                 x[e + h] = u - v;
             }
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0xB1>(x[e]), sg[0], x[e]);
+    for (int e = 0; e < CPL; e += 4) TQ_WHT_STAGE4("quad_perm:[1,0,3,2]", x, e, sg[0]);
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x4E>(x[e]), sg[1], x[e]);
+    for (int e = 0; e < CPL; e += 4) TQ_WHT_STAGE4("quad_perm:[2,3,0,1]", x, e, sg[1]);
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x141>(x[e]), sg[2], x[e]);
+    for (int e = 0; e < CPL; e += 4) TQ_WHT_STAGE4("row_half_mirror", x, e, sg[2]);
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) x[e] = fmaf(dpp_f32<0x140>(x[e]), sg[3], x[e]);
+    for (int e = 0; e < CPL; e += 4) TQ_WHT_STAGE4("row_mirror", x, e, sg[3]);
 }
+#undef TQ_WHT_STAGE4
+#undef TQ_WHT_FMAC
 
 // CPL consecutive input elements as fp32 (16-byte aligned for CPL * size >= 16)
 template <typename TIn, int CPL>
@@ -811,7 +837,7 @@ constexpr size_t key_smem_bytes_wht(int bits)
 
 // One 256-thread workgroup encodes 16 KT keys; wave w takes keys 16 t + 4 w + g
 // of key tile t in lane row g.  Steps: load (each lane its CPL elements) and
-// ||k||^2 (exact squares in fp64, summed over the row); the butterfly;
+// ||k||^2 (fp32, summed over the row); the butterfly;
 // codes, residual and ||r||^2 per lane; then, per pass of KR tiles, the QJL
 // product and the store shared with the matrix-core kernel.
 template <int D, typename TIn, int BITS, int KT, int ROUNDS>
@@ -921,11 +947,16 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
         for (int t = kt0; t < kt0 + KR; ++t) {
             const int key = 16 * t + 4 * wave + g;
-            // ||k||^2: exact squares in fp64, summed over the key's 16 lanes
-            double ss = 0.0;
+            // ||k||^2 in fp32: four interleaved fma chains per lane, summed
+            // pairwise, then over the key's 16 lanes in a DPP tree.  Every
+            // term passes through at most CPL / 4 + 6 roundings of sums of
+            // non-negative terms (one more for an fp32 input's square;
+            // bf16 and fp16 squares are exact), so the relative error stays
+            // below 11 * 2^-24 < 7e-7 at d = 256: under 4e-7 in ||k||
+            float q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) ss = fma(static_cast<double>(x[t][e]), static_cast<double>(x[t][e]), ss);
-            ss = row16_sum_f64(ss);
+            for (int e = 0; e < CPL; ++e) q4[e & 3] = fmaf(x[t][e], x[t][e], q4[e & 3]);
+            const float ss = row16_sum_f32((q4[0] + q4[1]) + (q4[2] + q4[3]));
             float v[CPL];
 #pragma unroll
             for (int e = 0; e < CPL; ++e) v[e] = x[t][e] * d1[e];
@@ -935,7 +966,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
                 for (int e = 0; e < CPL; ++e) v[e] *= d2[e];
                 wht_round<CPL>(v, sg);
             }
-            const float n2 = static_cast<float>(ss);
+            const float n2 = ss;
             const float scale = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) * eps : 0.0f;
             // codes and residual of coordinates [CPL chunk, CPL chunk + CPL)
             float res[CPL];
@@ -980,7 +1011,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             }
             rr = row16_sum_f32(rr);
             if (pl == 0) {
-                s.nrm2[key] = ss;
+                s.nrm2[key] = static_cast<double>(ss);
                 s.rho2[key] = static_cast<double>(rr);
             }
         }
