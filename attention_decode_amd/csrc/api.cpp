@@ -768,6 +768,8 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     a.hadamard = fmt->rot->kind != TQ_ROT_DENSE;
     a.rot_scale = fmt->rot->kind == TQ_ROT_HADAMARD2 ? 1.0f / fmt->d
                 : fmt->rot->kind == TQ_ROT_HADAMARD ? static_cast<float>(1.0 / std::sqrt(double(fmt->d))) : 1.0f;
+    a.inv_rot_scale = fmt->rot->kind == TQ_ROT_HADAMARD2 ? static_cast<float>(fmt->d)
+                    : fmt->rot->kind == TQ_ROT_HADAMARD ? static_cast<float>(std::sqrt(double(fmt->d))) : 1.0f;
     a.piT = fmt->rot->d_piT;
     a.sT = fmt->rot->d_sT;
     a.dsign = fmt->rot->d_dsign;

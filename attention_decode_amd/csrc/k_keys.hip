@@ -151,6 +151,18 @@ __device__ __forceinline__ uint32_t bf16x2(float x0, float x1)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// r0, r1 as two bf16 terms each (hardware round to nearest even), packed in
+// pairs: hi = (bf16(r0), bf16(r1)), lo = bf16 of the remainders.  The hi
+// terms come back to fp32 by a byte permute of the low half and a mask of the
+// high half (written as a shift, the compiler converts r0 a second time)
+__device__ __forceinline__ void split_bf16x2(float r0, float r1, uint32_t &hi, uint32_t &lo)
+{
+    hi = bf16x2(r0, r1);
+    const float h0 = __uint_as_float(__builtin_amdgcn_perm(hi, 0u, 0x05040c0cu));
+    const float h1 = __uint_as_float(hi & 0xffff0000u);
+    lo = bf16x2(r0 - h0, r1 - h1);
+}
+
 // LDS row strides of the code and sign words: one word past the row, an odd
 // stride, so that the 16 keys of one atomicOr (lanes 0-15 of a row of the
 // wave) land in 16 different banks (an even row of 8, 12 or 56 words puts
@@ -202,44 +214,52 @@ constexpr size_t key_smem_bytes()
 
 
 // Code idx = #{t_i < y} of one rotated coordinate and its residual y - c[idx].
-// Up to 2 bits: |y| placed among the positive boundaries tp of the exactly
-// symmetric codebook in registers, the centroid taken from the positive ones
-// cp, idx and the residual fixed by the sign of y (bit for bit what the full
-// count gives, up to exact ties).  From 3 bits (kCellBits): the cell of
-// the uniform grid that holds y gives the count below it and its one
-// boundary t, so the code is below + [y > t], the centroid c_lo or c_hi.
+// Up to 2 bits (encode_reg): |y| placed among the positive boundaries tp of
+// the exactly symmetric codebook in registers, the centroid taken from the
+// positive ones cp, idx and the residual fixed by the sign of y (bit for bit
+// what the full count gives, up to exact ties; y = 0 takes the code just below
+// zero).  From 3 bits (encode_cell, kCellBits): the cell of the uniform
+// grid that holds y gives the count below it and its one boundary t, so the
+// code is below + [y > t], the centroid c_lo or c_hi.
+// encode_reg takes the coordinate as y = v scale (scale > 0, one per key, or
+// 0 for a zero key) and the positive boundary as tv = tp / scale, so that no
+// product v scale is formed for the comparisons (their rounding differs from
+// y's by an ulp, far inside the 1e-5 band) and the residual is one fma.
 template <int BITS>
-__device__ __forceinline__ int encode_coord(float y, const float (&tp)[(1 << BITS) / 2 > 1 ? (1 << BITS) / 2 - 1 : 1],
-                                            const float (&cp)[(1 << BITS) / 2], const KeySmem &s, const KeyLaunch &a,
-                                            float &res)
+__device__ __forceinline__ uint32_t encode_reg(float v, float scale, float tv, const float (&cp)[(1 << BITS) / 2],
+                                               float &res)
 {
-    constexpr int H = (1 << BITS) / 2;
-    int pos;
-    if constexpr (BITS < kCellBits) {
-        const float ay = fabsf(y);
-        int cnt = 0;          // positive boundaries below |y|
-        float c = cp[0];
-        static_assert(BITS <= 2, "register codes: one positive boundary at most");
-        if constexpr (BITS == 2) {
-            const bool b0 = ay > tp[0];
-            cnt = b0 ? 1 : 0;
-            c = b0 ? cp[1] : cp[0];
-        }
-        const bool up = y > 0.0f;
-        pos = cnt ^ (up ? H : H - 1);     // H + cnt above zero, H - 1 - cnt below (cnt < H)
-        const float dv = ay - c;
-        res = up ? dv : -dv;
-    } else {
-        // cell index (y - lo) / w as one fma, clamped to [0, ngrid - 1] before
-        // the conversion; its rounding (about 1e-5 of a cell) is inside the
-        // cells' 2 % widening
-        const float cf = __builtin_amdgcn_fmed3f(fmaf(y, a.grid_scale, a.grid_off), 0.0f, a.grid_max);
-        const float4 e = s.grid[static_cast<int>(cf)];
-        const bool up = y > e.x;
-        pos = __float_as_int(e.w) + (up ? 1 : 0);
-        res = y - (up ? e.z : e.y);
+    static_assert(BITS <= 2, "register codes: one positive boundary at most");
+    constexpr uint32_t H = (1u << BITS) / 2;
+    const bool up = v > 0.0f;
+    float c = cp[0];
+    uint32_t cnt = 0u;                  // positive boundaries below |y|
+    if constexpr (BITS == 2) {
+        const bool b0 = fabsf(v) > tv;
+        c = b0 ? cp[1] : cp[0];
+        cnt = b0 ? 1u : 0u;
     }
-    return pos;
+    res = fmaf(v, scale, up ? -c : c);  // y - c[idx]: the centroid's sign is the side of zero
+    return cnt ^ (up ? H : H - 1);      // H + cnt above zero, H - 1 - cnt below (cnt < H)
+}
+
+// tp / scale for encode_reg from ||k||^2 (scale = rot_scale / ||k||), or 0 for
+// a zero key (whose v are all 0)
+__device__ __forceinline__ float reg_bound(float tp, float n2, float inv_rot_scale)
+{
+    return n2 > 0.0f ? tp * __builtin_amdgcn_sqrtf(n2) * inv_rot_scale : 0.0f;
+}
+
+__device__ __forceinline__ int encode_cell(float y, const KeySmem &s, const KeyLaunch &a, float &res)
+{
+    // cell index (y - lo) / w as one fma, clamped to [0, ngrid - 1] before
+    // the conversion; its rounding (about 1e-5 of a cell) is inside the
+    // cells' 2 % widening
+    const float cf = __builtin_amdgcn_fmed3f(fmaf(y, a.grid_scale, a.grid_off), 0.0f, a.grid_max);
+    const float4 e = s.grid[static_cast<int>(cf)];
+    const bool up = y > e.x;
+    res = y - (up ? e.z : e.y);
+    return __float_as_int(e.w) + (up ? 1 : 0);
 }
 
 // The A-fragment tables of Pi and S are read through buffer loads: the
@@ -631,7 +651,19 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         }
     }
     __syncthreads();   // every wave is done with the staged keys (the region takes the residuals next)
-    float inv_n[kKT];
+    // 1-2 bits: the codebook is exactly symmetric (c[L-1-i] = -c[i], and so
+    // the boundaries, with t[L/2-1] = 0), so |y| is placed against the one
+    // positive boundary in registers and the centroid taken from the H
+    // positive ones; idx and y - c[idx] follow from the sign of y, bit for bit
+    // as the full count would give them (up to exact ties)
+    constexpr int H = L / 2;
+    float cp[H];
+    const float tp0 = (BITS == 2) ? s.bnd[H] : 0.0f;
+    if constexpr (BITS < kCellBits) {
+#pragma unroll
+        for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
+    }
+    float inv_n[kKT], tv[kKT];
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
         const int key = 16 * kt + col;
@@ -640,19 +672,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         // of the same sum, rounded once
         const float n2 = key_norm2<TPK>(s.nrm2, kKeys, key);
         inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
-    }
-    // 1-3 bits: the codebook is exactly symmetric (c[L-1-i] = -c[i], and so
-    // the boundaries, with t[L/2-1] = 0), so |y| is placed among the H - 1
-    // positive boundaries by a binary search in registers and the centroid
-    // taken from the H positive ones; idx and y - c[idx] follow from the sign
-    // of y, bit for bit as the full count would give them (up to exact ties)
-    constexpr int H = L / 2;
-    float tp[H > 1 ? H - 1 : 1], cp[H];
-    if constexpr (BITS < kCellBits) {
-#pragma unroll
-        for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
-#pragma unroll
-        for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
+        tv[kt] = reg_bound(tp0, n2, a.inv_rot_scale);
     }
 
     const bool qjl = a.m > 0;
@@ -673,20 +693,24 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             float res[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float y = acc[j][kt][r] * inv_n[kt];
-                const uint32_t pos = static_cast<uint32_t>(encode_coord<BITS>(y, tp, cp, s, a, res[r]));
-                rr = fmaf(res[r], res[r], rr);
                 const int b = BITS * (4 * j + r);
-                seg[b >> 5] |= pos << (b & 31);
-                if ((b & 31) + BITS > 32) seg[(b >> 5) + 1] |= pos >> (32 - (b & 31));
+                if constexpr (BITS < kCellBits) {
+                    seg[b >> 5] |= encode_reg<BITS>(acc[j][kt][r], inv_n[kt], tv[kt], cp, res[r]) << (b & 31);
+                } else {
+                    const float y = acc[j][kt][r] * inv_n[kt];
+                    const uint32_t pos = static_cast<uint32_t>(encode_cell(y, s, a, res[r]));
+                    seg[b >> 5] |= pos << (b & 31);
+                    if ((b & 31) + BITS > 32) seg[(b >> 5) + 1] |= pos >> (32 - (b & 31));
+                }
+                rr = fmaf(res[r], res[r], rr);
             }
             // residual as two bf16 terms (hardware round to nearest even), in
             // the B-operand slots of coordinates q0 .. q0 + 3: k-step q0 / 32,
             // k-block (q0 / 4) % 4 (the lane col + 16 k-block), elements
             // 4 ((q0 / 16) % 2) + r
-            const uint32_t h01 = bf16x2(res[0], res[1]), h23 = bf16x2(res[2], res[3]);
-            const uint32_t l01 = bf16x2(res[0] - __uint_as_float(h01 << 16), res[1] - __uint_as_float(h01 & 0xffff0000u));
-            const uint32_t l23 = bf16x2(res[2] - __uint_as_float(h23 << 16), res[3] - __uint_as_float(h23 & 0xffff0000u));
+            uint32_t h01, l01, h23, l23;
+            split_bf16x2(res[0], res[1], h01, l01);
+            split_bf16x2(res[2], res[3], h23, l23);
             const int q0 = qb + 4 * j, ks = q0 >> 5, bl = col + 16 * ((q0 >> 2) & 3), hw = 2 * ((q0 >> 4) & 1);
             uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + ks) * 2 + 0) * 64 + bl]);
             uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[((kt * KS + ks) * 2 + 1) * 64 + bl]);
@@ -733,6 +757,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 constexpr uint32_t kWhtNeg[4] = {0x5a5au, 0x3c3cu, 0x0ff0u, 0xff00u};
 constexpr uint32_t kWhtEps = 0x9696u;
 constexpr uint64_t kWhtOut = 0x8deb7214c9af3650ull;
+constexpr int kWhtPartner[4] = {1, 2, 7, 15};    // lane stage k pairs lane p with p ^ kWhtPartner[k]
 
 // Lane permutations within a 16-lane row (quad swaps, half-row and row
 // mirrors): every source lane exists, so the move needs no "old" value and
@@ -905,20 +930,28 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         }
         load_chunk<TIn, CPL>(row + CPL * pl, x[t]);
     }
-    // round signs of this lane: D1 of its input coordinates; for a second
-    // round D2 of the coordinates it holds after the first, times its sign
+    // round signs of this lane.  The plain butterfly leaves lane p with
+    // eps(p) times its output chunk; instead every value the lane holds is kept
+    // times eps(p): the input D1 k times eps(p), and each lane stage's
+    // coefficient s(p) times eps(p) eps(partner), since eps(p) (x(p) + s x(q))
+    // = z(p) + s eps(p) eps(q) z(q) for z = eps x.  A round then ends with the
+    // chunk itself.  A second round takes D2 of the coordinates the lane holds
+    // after the first, again times eps(p).
     float d1[CPL], d2[ROUNDS == 2 ? CPL : 1];
     const int out1 = static_cast<int>((kWhtOut >> (4 * pl)) & 15);
     const float eps = ((kWhtEps >> pl) & 1u) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) d1[e] = a.wht[CPL * pl + e];
+    for (int e = 0; e < CPL; ++e) d1[e] = a.wht[CPL * pl + e] * eps;
     if constexpr (ROUNDS == 2) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) d2[e] = a.wht[D + CPL * out1 + e] * eps;
     }
     float sg[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sg[k] = ((kWhtNeg[k] >> pl) & 1u) ? -1.0f : 1.0f;
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t neg = (kWhtNeg[k] >> pl) ^ (kWhtEps >> pl) ^ (kWhtEps >> (pl ^ kWhtPartner[k]));
+        sg[k] = (neg & 1u) ? -1.0f : 1.0f;
+    }
     if (tid < L) {
         s.cent[tid] = cent_v;
         s.bnd[tid] = bnd_v;
@@ -927,10 +960,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         if (tid < a.ngrid) s.grid[tid] = grid_v;
     __syncthreads();   // cleared words, codebook tables
 
-    float tp[H > 1 ? H - 1 : 1], cp[H];
+    float cp[H];
+    const float tp0 = (BITS == 2) ? s.bnd[H] : 0.0f;
     if constexpr (BITS < kCellBits) {
-#pragma unroll
-        for (int i = 0; i < H - 1; ++i) tp[i] = s.bnd[H + i];
 #pragma unroll
         for (int i = 0; i < H; ++i) cp[i] = s.cent[H + i];
     }
@@ -967,7 +999,8 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
                 wht_round<CPL>(v, sg);
             }
             const float n2 = ss;
-            const float scale = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) * eps : 0.0f;
+            const float scale = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
+            const float tv = reg_bound(tp0, n2, a.inv_rot_scale);
             // codes and residual of coordinates [CPL chunk, CPL chunk + CPL)
             float res[CPL];
             uint32_t seg[NSW + 1];
@@ -976,11 +1009,16 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             float rr = 0.0f;
 #pragma unroll
             for (int e = 0; e < CPL; ++e) {
-                const int pos = encode_coord<BITS>(v[e] * scale, tp, cp, s, a, res[e]);
-                rr = fmaf(res[e], res[e], rr);
                 const int bo = BITS * e;
-                seg[bo >> 5] |= static_cast<uint32_t>(pos) << (bo & 31);
-                if ((bo & 31) + BITS > 32) seg[(bo >> 5) + 1] |= static_cast<uint32_t>(pos) >> (32 - (bo & 31));
+                if constexpr (BITS < kCellBits) {
+                    seg[bo >> 5] |= encode_reg<BITS>(v[e], scale, tv, cp, res[e]) << (bo & 31);
+                } else {
+                    const float y = v[e] * scale;
+                    const uint32_t pos = static_cast<uint32_t>(encode_cell(y, s, a, res[e]));
+                    seg[bo >> 5] |= pos << (bo & 31);
+                    if ((bo & 31) + BITS > 32) seg[(bo >> 5) + 1] |= pos >> (32 - (bo & 31));
+                }
+                rr = fmaf(res[e], res[e], rr);
             }
             // the lane's CPL codes start at bit BITS CPL chunk of the key's row
             const int bit0 = BITS * CPL * chunk, w0 = bit0 >> 5, sh0 = bit0 & 31;
@@ -997,11 +1035,9 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             for (int q = 0; q < CPL / 4; ++q) {
                 const int l = CPL * chunk + 4 * q;
                 const int rt = l >> 4, kbq = (l >> 2) & 3;
-                const uint32_t h01 = bf16x2(res[4 * q], res[4 * q + 1]), h23 = bf16x2(res[4 * q + 2], res[4 * q + 3]);
-                const uint32_t l01 = bf16x2(res[4 * q] - __uint_as_float(h01 << 16),
-                                            res[4 * q + 1] - __uint_as_float(h01 & 0xffff0000u));
-                const uint32_t l23 = bf16x2(res[4 * q + 2] - __uint_as_float(h23 << 16),
-                                            res[4 * q + 3] - __uint_as_float(h23 & 0xffff0000u));
+                uint32_t h01, l01, h23, l23;
+                split_bf16x2(res[4 * q], res[4 * q + 1], h01, l01);
+                split_bf16x2(res[4 * q + 2], res[4 * q + 3], h23, l23);
                 const int slot = ((t - kt0) * KS + (rt >> 1)) * 2;
                 uint32_t *dst = reinterpret_cast<uint32_t *>(&s.rfrag[(slot + 0) * 64 + col + 16 * kbq]);
                 uint32_t *dst1 = reinterpret_cast<uint32_t *>(&s.rfrag[(slot + 1) * 64 + col + 16 * kbq]);

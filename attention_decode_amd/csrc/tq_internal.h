@@ -90,7 +90,8 @@ struct KeyLaunch {
     bool contig;                // rows packed densely ([B, H, T, d] contiguous): row n at n d
     int d, bits, m;
     bool hadamard;              // Pi = integer matrix * rot_scale, exact in one bf16 term
-    float rot_scale;            // 1/sqrt(d) (one Hadamard round), 1/d (two rounds)
+    float rot_scale;            // 1/sqrt(d) (one Hadamard round), 1/d (two rounds), else 1
+    float inv_rot_scale;        // 1 / rot_scale (sqrt(d), d or 1)
     const float *piT, *sT, *dsign, *centroids, *boundaries;
     const float *wht;           // [2][d] Walsh-Hadamard round signs D1, D2
     int wht_rounds;             // 0 dense, 1 or 2 Walsh-Hadamard rounds
