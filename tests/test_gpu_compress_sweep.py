@@ -1,7 +1,7 @@
 """Key compression against the oracle at every code width the compressor
 takes (1 to 7 Lloyd-Max bits) and every head dimension (64, 128, 256), dense
-rotation with the QJL sign row, bf16 and fp32 inputs: the register search
-(up to 3 bits) and the code-cell table (from 4 bits) on each kernel shape.
+rotation with the QJL sign row, bf16 and fp32 inputs: the register codes
+(up to 2 bits) and the code-cell table (from 3 bits) on each kernel shape.
 Each case spans several 64-key workgroups and ends in a ragged one.
 
 Bars (the same as every compression test): codes bit-exact except
