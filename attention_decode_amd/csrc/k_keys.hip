@@ -91,6 +91,14 @@ __device__ __forceinline__ void split_terms(const float (&x)[8], uint4 (&t)[NT])
     }
 }
 
+// x0^2 + x1^2 + acc for the bf16 pair (x0, x1) packed in u (v_dot2c_f32_bf16)
+__device__ __forceinline__ float sq2_bf16(uint32_t u, float acc)
+{
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 x = __builtin_bit_cast(bf2, u);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
+
 // elements of 16-byte chunk c of a staged key row as fp32 (eight 16-bit
 // elements, or four fp32 ones in x[0..3])
 template <typename TIn, int N>
@@ -592,18 +600,29 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         // of sums of non-negative terms (one more for an fp32 input's square;
         // bf16 and fp16 squares are exact): 13 * 2^-24 < 8e-7 relative at
         // d = 256, 4e-7 in ||k||
+        // (bf16 keys: one v_dot2c_f32_bf16 per element pair, x0^2 + x1^2 + acc,
+        // at most two roundings per step, so still at most 8 in a group)
         constexpr int EPC = 16 / static_cast<int>(sizeof(TIn));     // elements per chunk
         constexpr int NG = CPT * EPC / 8;                              // groups of this thread
         static_assert(NG >= 1 && (NG & (NG - 1)) == 0, "whole groups, a power of two per thread");
         float gs[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) gs[g] = 0.0f;
+        if constexpr (__is_same(TIn, bf16_t)) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            float x[8];
-            chunk_as_f32<TIn>(v, c, x);
+            for (int c = 0; c < CPT; ++c) {
+                const uint32_t u[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) gs[(c * EPC + e) / 8] = fmaf(x[e], x[e], gs[(c * EPC + e) / 8]);
+                for (int i = 0; i < 4; ++i) gs[c] = sq2_bf16(u[i], gs[c]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                float x[8];
+                chunk_as_f32<TIn>(v, c, x);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) gs[(c * EPC + e) / 8] = fmaf(x[e], x[e], gs[(c * EPC + e) / 8]);
+            }
         }
 #pragma unroll
         for (int w = 1; w < NG; w *= 2)
@@ -816,40 +835,61 @@ __device__ __forceinline__ void wht_round(float (&x)[CPL], const float (&sg)[4])
 #undef TQ_WHT_STAGE4
 #undef TQ_WHT_FMAC
 
-// CPL consecutive input elements as fp32 (16-byte aligned for CPL * size >= 16)
+// CPL consecutive input elements of one lane as loaded: NW = CPL * size / 4
+// words, in 16-byte loads (8-byte ones for four 2-byte elements, d = 64)
 template <typename TIn, int CPL>
-__device__ __forceinline__ void load_chunk(const TIn *p, float (&x)[CPL])
-{
-    if constexpr (CPL * sizeof(TIn) >= 16) {
-        constexpr int NV = sizeof(TIn) == 4 ? CPL / 4 : CPL / 8;     // 16-byte loads
+struct LaneChunk {
+    static constexpr int NW = CPL * static_cast<int>(sizeof(TIn)) / 4;
+    uint32_t w[NW];
+
+    __device__ void load(const TIn *p)
+    {
+        if constexpr (NW >= 4) {
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
-            if constexpr (sizeof(TIn) == 4) {
-                const float4 v = reinterpret_cast<const float4 *>(p)[c];
-                x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
-            } else {
-                float v[8];
-                load8_as_f32(p + 8 * c, v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[8 * c + e] = v[e];
+            for (int c = 0; c < NW / 4; ++c) {
+                const uint4 u = reinterpret_cast<const uint4 *>(p)[c];
+                w[4 * c] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
             }
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2 *>(p);
+            w[0] = u.x; w[1] = u.y;
         }
-    } else {
-        // four 2-byte elements (d = 64)
-        const uint2 w = *reinterpret_cast<const uint2 *>(p);
-        const uint32_t u[2] = {w.x, w.y};
+    }
+
+    // the elements as fp32
+    __device__ void unpack(float (&x)[CPL]) const
+    {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if constexpr (__is_same(TIn, bf16_t)) {
-                x[2 * i] = bf16_to_f32(u[i] & 0xffffu);
-                x[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+        for (int i = 0; i < NW; ++i) {
+            if constexpr (sizeof(TIn) == 4) {
+                x[i] = __uint_as_float(w[i]);
+            } else if constexpr (__is_same(TIn, bf16_t)) {
+                x[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+                x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
             } else {
-                x[2 * i] = f16_bits_to_f32(u[i] & 0xffffu);
-                x[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
+                x[2 * i] = f16_bits_to_f32(w[i] & 0xffffu);
+                x[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
             }
         }
     }
-}
+
+    // the lane's share of ||k||^2 in fp32: interleaved chains summed pairwise
+    // (an fma per element in four chains; for bf16 one v_dot2c_f32_bf16 per
+    // pair, in two chains up to four pairs and four beyond)
+    __device__ float norm2(const float (&x)[CPL]) const
+    {
+        float q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (__is_same(TIn, bf16_t)) {
+            constexpr int NCH = NW > 4 ? 4 : 2;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) q4[i % NCH] = sq2_bf16(w[i], q4[i % NCH]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) q4[e & 3] = fmaf(x[e], x[e], q4[e & 3]);
+        }
+        return (q4[0] + q4[1]) + (q4[2] + q4[3]);
+    }
+};
 
 template <int D, typename TIn, int KT>
 constexpr size_t key_smem_bytes_wht(int bits)
@@ -908,7 +948,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     // this lane's elements of each of its KT keys (slots past the last key
     // reload that key; their results are never stored)
     const int last = static_cast<int>(n_total - 1 - n0 < kKeys - 1 ? n_total - 1 - n0 : kKeys - 1);
-    float x[KT][CPL];
+    LaneChunk<TIn, CPL> x[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int kk = 16 * t + 4 * wave + g;
@@ -928,7 +968,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
             }
             row = static_cast<const TIn *>(a.k) + b * a.sb + h * a.sh + tt * a.st;
         }
-        load_chunk<TIn, CPL>(row + CPL * pl, x[t]);
+        x[t].load(row + CPL * pl);
     }
     // round signs of this lane.  The plain butterfly leaves lane p with
     // eps(p) times its output chunk; instead every value the lane holds is kept
@@ -979,19 +1019,19 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
         for (int t = kt0; t < kt0 + KR; ++t) {
             const int key = 16 * t + 4 * wave + g;
-            // ||k||^2 in fp32: four interleaved fma chains per lane, summed
+            // ||k||^2 in fp32: four interleaved chains per lane, summed
             // pairwise, then over the key's 16 lanes in a DPP tree.  Every
             // term passes through at most CPL / 4 + 6 roundings of sums of
             // non-negative terms (one more for an fp32 input's square;
-            // bf16 and fp16 squares are exact), so the relative error stays
+            // bf16 and fp16 squares are exact; a bf16 pair step rounds at
+            // most twice for two elements), so the relative error stays
             // below 11 * 2^-24 < 7e-7 at d = 256: under 4e-7 in ||k||
-            float q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) q4[e & 3] = fmaf(x[t][e], x[t][e], q4[e & 3]);
-            const float ss = row16_sum_f32((q4[0] + q4[1]) + (q4[2] + q4[3]));
+            float xe[CPL];
+            x[t].unpack(xe);
+            const float ss = row16_sum_f32(x[t].norm2(xe));
             float v[CPL];
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) v[e] = x[t][e] * d1[e];
+            for (int e = 0; e < CPL; ++e) v[e] = xe[e] * d1[e];
             wht_round<CPL>(v, sg);
             if constexpr (ROUNDS == 2) {
 #pragma unroll

@@ -144,8 +144,9 @@ size_t tq_val_plane_bytes(const tq_val_fmt *fmt, int64_t n_vec, int plane);
    1; dtype f32/bf16/f16) into the planes of `out` (discosf article steps 1-3):
    n = ||k||, y = Pi k / n, idx_j = #{boundaries < y_j}, r = y - c[idx],
    sign_i = [(S r)_i >= 0], stored with fp32 n and fp32 ||r||.  A zero key
-   stores n = 0 and the codes of y = 0.  Keys must be finite with ||k|| below
-   2^64 (||k||^2 is summed in fp32).  T = 0 is a no-op.  Strides must be
+   stores n = 0 and the codes of y = 0.  Keys must be finite with ||k|| in
+   (2^-60, 2^64): ||k||^2 is summed in fp32, and bf16 squares below 2^-126
+   may be dropped.  T = 0 is a no-op.  Strides must be
    multiples of 16 bytes. */
 tq_status tq_compress_keys(const tq_key_fmt *fmt, const void *k, tq_dtype dtype, int B, int Hkv,
                            int64_t T, int64_t sb, int64_t sh, int64_t st, tq_kcache out,
