@@ -394,13 +394,15 @@ __device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off)
     return reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(base) + off);
 }
 
-// Value rows are read once per call, each load of a wave covering whole
-// cache lines: those loads carry the nontemporal hint (the "nt" bit), under
-// which the memory system streams the lines instead of keeping them like
-// reused data.  A streaming read of 2 GiB in contiguous per-workgroup chunks
-// runs at about 7.0 TB/s with it and 6.2 TB/s without.  The key rows are not
-// read that way (a line is spread over several loads of a wave: codes of one
-// quarter row per lane, one norm per key), and the hint made those slower.
+// The packed rows are read once per call.  Loads of a wave that cover whole
+// cache lines carry the nontemporal hint (the "nt" bit), under which the
+// memory system streams the lines instead of keeping them like reused data:
+// the value rows, and the code and sign rows of keys whose quarter row a lane
+// takes in one load (up to 16 bytes: 16 keys' whole rows per load).  A
+// streaming read of 2 GiB in contiguous per-workgroup chunks runs at about
+// 7.0 TB/s with the hint and 6.2 TB/s without.  Wider code rows (a line spread
+// over several loads of a wave) and the per-key norms (half a line per load)
+// keep plain loads: the hint made those slower.
 template <class T>
 __device__ __forceinline__ T ld_stream(const T *p)
 {
@@ -427,16 +429,17 @@ struct KeyWords {
                 reinterpret_cast<const uint32_t *>(a.kc.signs) + n0 * (D / 32), a.kc.knorm + n0, a.kc.rnorm + n0};
     }
     // key t of the tile (column c of this lane: key j or 16 + j), k-block kb
+    static constexpr bool STREAM = NC <= 4;     // a lane's quarter row in one load
     __device__ void load(const Bases &b, uint32_t t, int kb, int c)
     {
         const uint32_t *crow = at_bytes(b.c, 4u * (t * (D * BITS / 32) + kb * NC));
 #pragma unroll
-        for (int u = 0; u < NC; ++u) cw[c][u] = crow[u];
+        for (int u = 0; u < NC; ++u) cw[c][u] = STREAM ? ld_stream(crow + u) : crow[u];
         nrm[c] = *at_bytes(b.n, 4u * t);
         if constexpr (QJL) {
             const uint32_t *srow = at_bytes(b.s, 4u * (t * (D / 32) + kb * NS));
 #pragma unroll
-            for (int u = 0; u < NS; ++u) sw[c][u] = srow[u];
+            for (int u = 0; u < NS; ++u) sw[c][u] = ld_stream(srow + u);
             rho[c] = *at_bytes(b.r, 4u * t);
         } else {
             rho[c] = 0.0f;
