@@ -40,7 +40,7 @@ def test_fullsize_compression(torch_cuda, name):
     """Whole-tensor compression in the benchmark's launch configuration: one
     whole (sequence, KV head) slice (the last one, all T tokens) and a seeded
     sample of rows from everywhere else are re-encoded by the oracle and
-    compared under the flip rule; the flip budget is judged on the slice's
+    compared under the flip rule; the flip budget is checked on the slice's
     T x 2d coordinates."""
     torch = torch_cuda
     w = W.WORKLOADS[name]
