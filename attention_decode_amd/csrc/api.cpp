@@ -45,6 +45,17 @@ void bf16_split(double x, int parts, uint16_t *out)
     }
 }
 
+// split x into `parts` fp16 terms, each the rounding (to nearest even) of what
+// is left
+void f16_split(double x, int parts, uint16_t *out)
+{
+    for (int p = 0; p < parts; ++p) {
+        const _Float16 h = static_cast<_Float16>(x);
+        std::memcpy(&out[p], &h, 2);
+        x -= static_cast<double>(h);
+    }
+}
+
 tq_status fail(tq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 tq_status fail(tq_status st, const char *fmt, ...)
 {
@@ -410,12 +421,15 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
         return hip_fail(e, "tq_make_rotation: device upload");
     }
     // operand fragments of the matrix-core compressor (rows in the order of
-    // compressor_row): Pi as three bf16 terms
+    // compressor_row): Pi as three bf16 terms for fp32 keys and the Hadamard
+    // sign matrices
     // (about 24 significant bits, so y keeps fp32 accuracy), S as two (16 bits;
-    // the residual is split in two as well, see the key kernel)
+    // the residual is split in two as well, see the key kernel), and for 2-byte
+    // keys of a dense rotation Pi 2^kPiHalfExp as two fp16 terms (22 bits)
     const int ks_n = d / 32, rt_n = d / 16;
-    std::vector<uint16_t> frag(static_cast<size_t>(rt_n) * ks_n * 5 * 512);
-    uint16_t *pif = frag.data(), *sfr = frag.data() + static_cast<size_t>(rt_n) * ks_n * 3 * 512;
+    const size_t part_n = static_cast<size_t>(rt_n) * ks_n * 512;
+    std::vector<uint16_t> frag(part_n * 7);
+    uint16_t *pif = frag.data(), *sfr = frag.data() + part_n * 3, *pih = frag.data() + part_n * 5;
     for (int rt = 0; rt < rt_n; ++rt)
         for (int ks = 0; ks < ks_n; ++ks)
             for (int lane = 0; lane < 64; ++lane)
@@ -436,6 +450,9 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
                         bf16_split(pv, 3, parts);
                     }
                     for (int p = 0; p < 3; ++p) pif[(((rt * ks_n + ks) * 3 + p) * 64 + lane) * 8 + el] = parts[p];
+                    uint16_t hparts[2] = {0, 0};
+                    if (kind == TQ_ROT_DENSE) f16_split(std::ldexp(pv, tq::kPiHalfExp), 2, hparts);
+                    for (int p = 0; p < 2; ++p) pih[(((rt * ks_n + ks) * 2 + p) * 64 + lane) * 8 + el] = hparts[p];
                     const int col = 16 * (2 * ks + el / 4) + 4 * kb + el % 4;
                     bf16_split(s[static_cast<size_t>(row) * d + col], 2, parts);
                     for (int p = 0; p < 2; ++p) sfr[(((rt * ks_n + ks) * 2 + p) * 64 + lane) * 8 + el] = parts[p];
@@ -463,7 +480,8 @@ tq_status tq_make_rotation(uint64_t seed, int d, tq_rot_kind kind_arg, tq_rotati
         return hip_fail(e, "tq_make_rotation: fp64 upload");
     }
     rot->d_pifrag = static_cast<uint16_t *>(rot->d_frag_block);
-    rot->d_sfrag = rot->d_pifrag + static_cast<size_t>(rt_n) * ks_n * 3 * 512;
+    rot->d_sfrag = rot->d_pifrag + part_n * 3;
+    rot->d_pihfrag = rot->d_pifrag + part_n * 5;
     float *base = static_cast<float *>(rot->d_block);
     rot->d_pi = base;
     rot->d_piT = base + dd;
@@ -786,6 +804,7 @@ tq_status compress_keys_impl(const tq_key_fmt *fmt, const void *k, const tq_dtyp
     a.grid_max = static_cast<float>(fmt->cb->ngrid > 0 ? fmt->cb->ngrid - 1 : 0);
     a.pifrag = fmt->rot->d_pifrag;
     a.sfrag = fmt->rot->d_sfrag;
+    a.pihfrag = fmt->rot->d_pihfrag;
     a.out = out;
     a.map = map;
     TQ_LAUNCH_HOOK(who);

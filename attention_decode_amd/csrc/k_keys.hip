@@ -7,23 +7,25 @@
 // One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 at d = 256,
 // and in launches too small to give every CU two workgroups) and stages them
 // in LDS first, in one round trip to HBM.  Both products run
-// as v_mfma_f32_16x16x32_bf16 with the keys / residuals as the B operand
-// (lane = key column) and the matrix as the A operand, so that every A
-// fragment read from L2 serves all keys of the workgroup; the four waves split
-// the output rows.
+// as 16x16x32 MFMAs (bf16, or fp16 for the y product of 2-byte keys under a
+// dense rotation) with the keys / residuals as the B operand (lane = key
+// column) and the matrix as the A operand, so that every A fragment read from
+// L2 serves all keys of the workgroup; the four waves split the output rows.
 //
-// Accuracy: the bf16 operands are made exact or near-fp32 by splitting.
-//   * y:  Pi = P0 + P1 + P2 (three bf16 terms, about 24 significant bits); a
-//         bf16 key is one exact term, an fp16 key two, an fp32 key three.  The
-//         products kept are those whose term ranks sum to at most 2, i.e. every
-//         product down to about 2^-24 of the leading one.  The Hadamard sign
-//         matrix H D is exact in one term and its 1/sqrt(d) joins 1/||k||.
+// Accuracy: the 16-bit operands are made exact or near-fp32 by splitting.
+//   * y, 2-byte keys, dense Pi:  Pi 2^14 = F0 + F1 (two fp16 terms, about 22
+//         significant bits) against the key times 2^ex, one exact fp16 term
+//         (key_half_y).
+//   * y otherwise:  Pi = P0 + P1 + P2 (three bf16 terms, about 24 significant
+//         bits); an fp32 key is three terms.  The products kept are those whose
+//         term ranks sum to at most 2, i.e. every product down to about 2^-24
+//         of the leading one.  The Hadamard sign matrix H D is exact in one
+//         term and its 1/sqrt(d) joins 1/||k||.
 //   * z:  S = S0 + S1, r = R0 + R1 (16 bits each); S0 R0 + S0 R1 + S1 R0 leaves
 //         an error near 2^-16 of |z| per term, far inside the resolution at
 //         which a sign can legitimately flip.
-// All sums accumulate in fp32 inside the MFMA.  ||k|| is summed in fp64 from
-// the exact fp32 squares (each wave takes a quarter of the k-steps); ||r||
-// in fp32 per lane and fp64 across lanes.
+// All sums accumulate in fp32 inside the MFMA.  ||k||^2 is summed in fp32
+// along one fixed tree per key; ||r|| in fp32 per lane and fp64 across lanes.
 //
 // Codes: idx = #{t_i < y}.  Up to 2 bits a comparison of |y| with the
 // positive boundary of the symmetric codebook, in registers (no LDS reads);
@@ -70,6 +72,47 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint4 &a, const uint4 &b, const
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f16(const uint4 &a, const uint4 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Dense rotations of 2-byte keys run y = Pi k on fp16 operands: Pi 2^kPiHalfExp
+// as two fp16 terms (22 significant bits; the bf16 form needs three terms for
+// 24) against the key times a power of two 2^ex of its own, chosen so that
+// ||k|| 2^ex < 2^kKeyHalfExp.  A bf16 or fp16 element then fits fp16's
+// 11-bit significand exactly unless it falls below fp16's normal range,
+// i.e. below about ||k|| 2^-28, where it is rounded on the subnormal grid
+// (an error under ||k|| 2^-37).  Two products per fragment instead of three.
+constexpr int kKeyHalfExp = 14;
+template <int NP, typename TIn> constexpr bool key_half_y() { return NP == 3 && sizeof(TIn) == 2; }
+
+// the eight 16-bit elements of a staged chunk times 2^ex, as packed fp16
+// (v_cvt_pkrtz_f16_f32: exact for normal fp16 results, toward zero below)
+template <typename TIn>
+__device__ __forceinline__ uint4 chunk_as_f16(const uint4 &v, int ex)
+{
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x0, x1;
+        if constexpr (__is_same(TIn, bf16_t)) {
+            x0 = __uint_as_float(u[i] << 16);
+            x1 = __uint_as_float(u[i] & 0xffff0000u);
+        } else {
+            x0 = f16_bits_to_f32(u[i] & 0xffffu);
+            x1 = f16_bits_to_f32(u[i] >> 16);
+        }
+        o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_ldexpf(x0, ex),
+                                                                      __builtin_amdgcn_ldexpf(x1, ex)));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // split eight fp32 values into NT bf16x8 terms (x = t0 + t1 + ...)
@@ -491,7 +534,8 @@ __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s,
 }
 
 // Rows 16 (RTW wave + j) .. + 15 of Pi, k-step ks, as NP bf16 A terms
-template <int D, int NP>
+// the first NP of the NT terms of Pi's fragments, rows of this wave, k-step ks
+template <int D, int NP, int NT>
 __device__ __forceinline__ void load_pi_frag(__amdgpu_buffer_rsrc_t pt, int wave, int lane, int ks,
                                              uint4 (&af)[D / 64][NP])
 {
@@ -500,18 +544,21 @@ __device__ __forceinline__ void load_pi_frag(__amdgpu_buffer_rsrc_t pt, int wave
     for (int j = 0; j < RTW; ++j) {
         const int rt = wave * RTW + j;
 #pragma unroll
-        for (int p = 0; p < NP; ++p) af[j][p] = frag_load(pt, lane, (rt * KS + ks) * 3 + p);
+        for (int p = 0; p < NP; ++p) af[j][p] = frag_load(pt, lane, (rt * KS + ks) * NT + p);
     }
 }
 
-// NP = 3: a dense Pi as three bf16 terms; NP = 1: the Hadamard sign matrix,
-// exact in one term
+// NP = 3: a dense Pi as three bf16 terms (two fp16 terms for 2-byte keys,
+// key_half_y); NP = 1: the Hadamard sign matrix, exact in one term
 template <int D, typename TIn, int BITS, int KT, int NP>
 __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_compress_keys(KeyLaunch a, int64_t n_total)
 {
     constexpr int KS = D / 32;           // k-steps of 32 channels
     constexpr int RTW = D / 64;          // 16-row output tiles per wave
-    constexpr int NK = KeyTerms<TIn>::n;
+    constexpr bool HALF = key_half_y<NP, TIn>();
+    constexpr int NPA = HALF ? 2 : NP;   // A terms of Pi per fragment
+    constexpr int NTAB = HALF ? 2 : 3;   // terms per fragment in Pi's table
+    constexpr int NK = HALF ? 1 : KeyTerms<TIn>::n;
     constexpr int L = 1 << BITS;
     constexpr bool DIRECT = key_direct_words<D>();
     constexpr int CWS = DIRECT ? 0 : cw_stride<D, BITS>(), SWS = DIRECT ? 0 : sw_stride<D>();
@@ -522,6 +569,7 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     constexpr int NSEG = (SEGC * BITS + 31) / 32;                      // words of a lane's codes
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __shared__ int64_t s_row[kKeys];              // plane row of each key of the workgroup (-1: none)
+    __shared__ int s_kexp[HALF ? kKeys : 1];      // each key's staging exponent ex (fp16 y product)
     KeySmem s;
     {
         unsigned char *p = smem_raw;
@@ -551,10 +599,10 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
     for (int i = tid; i < kKeys * SWS; i += kThreads) s.sw[i] = 0u;
     if (tid < kKeys) s_row[tid] = n0 + tid < n_total ? out_row(a.map, a.H, a.T, n0 + tid) : -1;
     // Pi's fragments of the first k-step, in flight with the keys
-    const __amdgpu_buffer_rsrc_t pt = frag_table(a.pifrag, frag_table_bytes<D, 3>());
+    const __amdgpu_buffer_rsrc_t pt = frag_table(HALF ? a.pihfrag : a.pifrag, frag_table_bytes<D, NTAB>());
     const __amdgpu_buffer_rsrc_t st = frag_table(a.sfrag, a.m > 0 ? frag_table_bytes<D, 2>() : 0);
-    uint4 af[2][RTW][NP];
-    load_pi_frag<D, NP>(pt, wave, lane, 0, af[0]);
+    uint4 af[2][RTW][NPA];
+    load_pi_frag<D, NPA, NTAB>(pt, wave, lane, 0, af[0]);
 
     // ---- 0. the workgroup's keys into LDS, one HBM round trip: thread
     // (key kk, quarter q) loads quarter q of row kk as 16-byte chunks (row n
@@ -591,8 +639,10 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
         for (int c = 0; c < CPT; ++c) v[c] = src[c];
         uint4 *dst = reinterpret_cast<uint4 *>(kst + kk * RSTR) + q * CPT;
+        if constexpr (!HALF) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) dst[c] = v[c];
+            for (int c = 0; c < CPT; ++c) dst[c] = v[c];
+        }
         // partial q of ||k||^2 in fp32, one subtree of a fixed tree: each
         // group of eight consecutive elements is one fma chain and the groups
         // are summed pairwise (key_norm2 finishes the tree over the TPK
@@ -629,6 +679,19 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
 #pragma unroll
             for (int g = 0; g < NG; g += 2 * w) gs[g] += gs[g + w];
         s.nrm2[q * kKeys + kk] = static_cast<double>(gs[0]);
+        if constexpr (HALF) {
+            // the key's ||k||^2 from its TPK threads (consecutive lanes; each
+            // xor step adds the same two values in either order, so every
+            // thread of the key gets the same bits and the same exponent):
+            // ||k||^2 < 2^E, so ||k|| < 2^ceil(E/2) and ||k|| 2^ex < 2^kKeyHalfExp
+            float n2 = gs[0];
+#pragma unroll
+            for (int o = 1; o < TPK; o *= 2) n2 += __shfl_xor(n2, o);
+            const int ex = kKeyHalfExp - ((__builtin_amdgcn_frexp_expf(n2) + 1) >> 1);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) dst[c] = chunk_as_f16<TIn>(v[c], ex);
+            if (q == 0) s_kexp[kk] = ex;
+        }
     }
     if (tid < L) {
         s.cent[tid] = cent_v;
@@ -650,21 +713,27 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) load_pi_frag<D, NP>(pt, wave, lane, ks + 1, af[(ks + 1) & 1]);
+        if (ks + 1 < KS) load_pi_frag<D, NPA, NTAB>(pt, wave, lane, ks + 1, af[(ks + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of this k-step's products
         uint4 kf[kKT][NK];
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-            key_frag_lds<TIn, NK>(kst + (16 * kt + col) * RSTR + (32 * ks + 8 * kb) * static_cast<int>(sizeof(TIn)), kf[kt]);
+        for (int kt = 0; kt < kKT; ++kt) {
+            const unsigned char *kp = kst + (16 * kt + col) * RSTR + (32 * ks + 8 * kb) * static_cast<int>(sizeof(TIn));
+            if constexpr (HALF) kf[kt][0] = *reinterpret_cast<const uint4 *>(kp);     // staged as fp16
+            else key_frag_lds<TIn, NK>(kp, kf[kt]);
+        }
 #pragma unroll
         for (int j = 0; j < RTW; ++j) {
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp) {
+            for (int pp = 0; pp < NPA; ++pp) {
 #pragma unroll
                 for (int kq = 0; kq < NK; ++kq) {
                     if (pp + kq > 2) continue;     // terms below fp32's resolution
 #pragma unroll
-                    for (int kt = 0; kt < kKT; ++kt) acc[j][kt] = mfma_bf16(af[ks & 1][j][pp], kf[kt][kq], acc[j][kt]);
+                    for (int kt = 0; kt < kKT; ++kt) {
+                        if constexpr (HALF) acc[j][kt] = mfma_f16(af[ks & 1][j][pp], kf[kt][kq], acc[j][kt]);
+                        else acc[j][kt] = mfma_bf16(af[ks & 1][j][pp], kf[kt][kq], acc[j][kt]);
+                    }
                 }
             }
         }
@@ -692,6 +761,12 @@ __global__ __launch_bounds__(kThreads, (key_occupancy<D, TIn, KT>())) void k_com
         const float n2 = key_norm2<TPK>(s.nrm2, kKeys, key);
         inv_n[kt] = (n2 > 0.0f) ? a.rot_scale * __builtin_amdgcn_rsqf(n2) : 0.0f;
         tv[kt] = reg_bound(tp0, n2, a.inv_rot_scale);
+        if constexpr (HALF) {
+            // acc is y 2^(kPiHalfExp + ex): both factors are exact powers of two
+            const int sh = kPiHalfExp + s_kexp[key];
+            inv_n[kt] = __builtin_amdgcn_ldexpf(inv_n[kt], -sh);
+            tv[kt] = __builtin_amdgcn_ldexpf(tv[kt], sh);
+        }
     }
 
     const bool qjl = a.m > 0;

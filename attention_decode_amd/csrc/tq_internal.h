@@ -45,8 +45,11 @@ struct tq_rotation {
     //   pifrag [d/16 row tiles][d/32 k-steps][3 parts][64][8]: Pi = hi + mid + lo
     //   sfrag  [m/16 row tiles][d/32 k-steps][2 parts][64][8]: S = hi + mid, with
     //          k element e of k-block kb at coordinate 16 (2 ks + e/4) + 4 kb + e%4
+    //   pihfrag [d/16 row tiles][d/32 k-steps][2 parts][64][8]: fp16 bits,
+    //          Pi 2^kPiHalfExp = hi + lo (dense rotations; zeros otherwise)
     uint16_t *d_pifrag = nullptr;
     uint16_t *d_sfrag = nullptr;
+    uint16_t *d_pihfrag = nullptr;
     void *d_frag_block = nullptr;
     void *d_block = nullptr;
     int device = 0;
@@ -101,10 +104,16 @@ struct KeyLaunch {
     float grid_lo, grid_scale;
     float grid_off, grid_max;   // -grid_lo grid_scale (rounded once), ngrid - 1
     const uint16_t *pifrag, *sfrag;
+    const uint16_t *pihfrag;    // Pi 2^kPiHalfExp as two fp16 terms (dense rotations)
     tq_kcache out;
     CacheMap map;               // flat, or appending into a layout cache
 };
 hipError_t launch_compress_keys(const KeyLaunch &a, hipStream_t stream);
+// power of two that lifts Pi (|entries| <= 1) for its two fp16 terms: the
+// leading term stays at or below 2^14 (fp16's largest finite value is
+// 65504), and the second one, about 2^-11 of it, stays out of fp16's
+// subnormal range for every entry above 2^-17
+constexpr int kPiHalfExp = 14;
 constexpr int kCellBits = 3;       // codes of kCellBits or more bits are read from code cells
 constexpr int kMaxGrid = 8192;     // cells of a codebook's code grid
 constexpr int kGridLds = 256;      // cells the key compressor stages in LDS (every codebook of d >= 3, <= 7 bits)
