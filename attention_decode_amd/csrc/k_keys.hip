@@ -4,9 +4,9 @@
 // steps 1-3 (y = Pi k/||k||, nearest-centroid codes, signs of S r with
 // r = y - c[idx]).
 //
-// One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 at d = 256,
-// and in launches too small to give every CU two workgroups) and stages them
-// in LDS first, in one round trip to HBM.  Both products run
+// One 256-thread workgroup encodes 64 keys (four 16-key tiles; 32 for fp32
+// keys at d = 256 and in launches too small to give every CU two workgroups)
+// and stages them in LDS first, in one round trip to HBM.  Both products run
 // as 16x16x32 MFMAs (bf16, or fp16 for the y product of 2-byte keys under a
 // dense rotation) with the keys / residuals as the B operand (lane = key
 // column) and the matrix as the A operand, so that every A fragment read from
@@ -85,10 +85,11 @@ __device__ __forceinline__ f32x4 mfma_f16(const uint4 &a, const uint4 &b, const 
 // Dense rotations of 2-byte keys run y = Pi k on fp16 operands: Pi 2^kPiHalfExp
 // as two fp16 terms (22 significant bits; the bf16 form needs three terms for
 // 24) against the key times a power of two 2^ex of its own, chosen so that
-// ||k|| 2^ex < 2^kKeyHalfExp.  A bf16 or fp16 element then fits fp16's
-// 11-bit significand exactly unless it falls below fp16's normal range,
-// i.e. below about ||k|| 2^-28, where it is rounded on the subnormal grid
-// (an error under ||k|| 2^-37).  Two products per fragment instead of three.
+// 2^(kKeyHalfExp - 1) <= ||k|| 2^ex < 2^kKeyHalfExp.  A bf16 or fp16 element
+// then fits fp16's 11-bit significand exactly unless it falls below fp16's
+// normal range, i.e. below ||k|| 2^-27, where it is rounded on the subnormal
+// grid (an error under ||k|| 2^-37).  Two products per fragment instead of
+// three.
 constexpr int kKeyHalfExp = 14;
 template <int NP, typename TIn> constexpr bool key_half_y() { return NP == 3 && sizeof(TIn) == 2; }
 
@@ -533,8 +534,8 @@ __device__ __forceinline__ void store_keys(const KeyLaunch &a, const KeySmem &s,
     }
 }
 
-// Rows 16 (RTW wave + j) .. + 15 of Pi, k-step ks, as NP bf16 A terms
-// the first NP of the NT terms of Pi's fragments, rows of this wave, k-step ks
+// Rows 16 (RTW wave + j) .. + 15 of Pi, k-step ks: the first NP of the NT
+// terms that each fragment of the table holds
 template <int D, int NP, int NT>
 __device__ __forceinline__ void load_pi_frag(__amdgpu_buffer_rsrc_t pt, int wave, int lane, int ks,
                                              uint4 (&af)[D / 64][NP])
