@@ -133,10 +133,13 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
     float mv[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) mv[i] = mtx[(jp * NR + i) * D + kb * CB + cl];
-    // column sums for the constant terms (bit-plane scores, written by the
-    // (part 0, quarter 0) workgroup): coordinates lane + 64 i of this lane
+    // table scores at d = 256 take int8 sign products (ScoreLut::I8S)
+    constexpr bool kI8S = D == 256;
+    // column sums for the constant terms (bit-plane codes, and the int8 QJL
+    // sign sums, written by the (part 0, quarter 0) workgroup): coordinates
+    // lane + 64 i of this lane
     const bool head = blockIdx.y == 0;
-    const bool sums = head && bitplane;
+    const bool sums = head && (bitplane || (kI8S && !a.kfmt_block));
     float psum[D / 64], pssum[D / 64];
     if (sums) {
 #pragma unroll
@@ -193,12 +196,16 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
             const float qn = sqrtf(s2) * (1.0f + 0x1p-16f);      // >= max_j |q_rot_j|, rounding included
             const float mc = bitplane ? qn * fmaxf(fabsf(s_acoef[0]), fabsf(s_acoef[1])) : qn;
             const float ms = qn * a.sq_bound;
-            const int top = (bitplane || a.kfmt_block) ? 26 : 10; // |scaled value| < 2^top
+            // |scaled value| < 2^top: 2^26 for int8 digit rows (bit-plane and
+            // block codes, bit-plane and d = 256 table signs), 2^10 for fp16
+            // rows (table codes, d = 128 table signs)
+            const int topc = (bitplane || a.kfmt_block) ? 26 : 10;
+            const int tops = (bitplane || kI8S) ? 26 : 10;
             int ec = 0, es = 0;
             frexpf(mc, &ec);
             frexpf(ms, &es);
-            const int fc = (mc > 0.0f) ? top - ec : 0;
-            const int fs = (ms > 0.0f) ? top - es : 0;
+            const int fc = (mc > 0.0f) ? topc - ec : 0;
+            const int fs = (ms > 0.0f) ? tops - es : 0;
             s_f[g][0] = fc;
             s_f[g][1] = fs;
             if (head) {
@@ -209,6 +216,11 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
                 } else if (bitplane) {
                     sc4[0] = ldexpf(1.0f, -fc);
                     sc4[1] = a.centroids[0] * sc;
+                    sc4[2] = ldexpf(1.0f, -fs);
+                    sc4[3] = ss;
+                } else if (kI8S) {
+                    sc4[0] = ldexpf(1.0f, -(fc + kCodeExp));
+                    sc4[1] = 0.0f;
                     sc4[2] = ldexpf(1.0f, -fs);
                     sc4[3] = ss;
                 } else {
@@ -303,38 +315,94 @@ __global__ __launch_bounds__(kThreads) void k_qprep(DecodeLaunch a)
             }
         }
     } else {
-        // fp16 hi + lo rows (2 g, 2 g + 1) of the A operands of
-        // v_mfma_f32_16x16x32_f16, aops[unit][step][lane][4 dwords] with the
-        // code steps first, then the sign steps.  Sign step ks: k-block kb
-        // holds coordinates kb D/4 + 8 ks + e.  Code steps: two per ks, m =
-        // 0, 1, over coordinates kb D/4 + 8 ks + 4 m + i, each coordinate
-        // repeated for the hi and lo halves of its centroid in the B operand:
-        // slots (x0, x1, x0, x1, x2, x3, x2, x3) against pair entries (up to
-        // 5 bits), (x0, x0, x1, x1, x2, x2, x3, x3) against single entries.
+        // Table scores, aops[unit][step][lane][4 dwords] with the code steps
+        // first, then the sign steps.
+        // Code steps: fp16 hi + lo rows of the A operands of
+        // v_mfma_f32_16x16x32_f16, row 4 kk + r holding query kk + 4 (r / 2)
+        // at d = 256, 2 kk + r / 2 at d = 128, part r % 2 (kk the row block).
+        // Two steps per ks, m = 0, 1, over
+        // coordinates kb D/4 + 8 ks + 4 m + i, each coordinate repeated for the
+        // hi and lo halves of its centroid in the B operand: slots (x0, x1, x0,
+        // x1, x2, x3, x2, x3) against pair entries (up to 5 bits), (x0, x0, x1,
+        // x1, x2, x2, x3, x3) against single entries.
+        // Sign steps, d = 256: int8 digit rows of v_mfma_i32_16x16x64_i8 as
+        // in the bit-plane scores, two row tiles of four queries (query g in
+        // lanes 16 kb + 4 (g % 4) + digit of tile g / 4), tile-major; step sl
+        // of a tile reads sign dword u = sl / 2 of the quarter, dword r of a
+        // lane holding coordinates 32 u + 8 K + 4 (sl % 2) + r, K = 0..3.
+        // Sign steps, d = 128: fp16 hi + lo rows in the code rows' order, step
+        // ks holding coordinates kb D/4 + 8 ks + e of Sq.
         constexpr int KS = D / 32;
         const bool pair = a.bits <= 5;
         const int code_steps = 2 * KS;
-        const int nsteps = (part ? KS : code_steps);
-        const int step0 = part ? code_steps : 0;
         uint32_t *out = a.mf.aops + static_cast<int64_t>(unit) * (code_steps + KS) * 256;
-        for (int w = tid; w < nsteps * 64; w += kThreads) {
-            const int r = w % 4, row = (w / 4) % 16, st = w / 64;
-            const int g = row / 2, lo = row % 2;
-            // coordinates of this dword's two slots: c0 + h * dc
-            const int base = 8 * (st / 2) + 4 * (st % 2);
-            const int c0 = part ? 8 * st + 2 * r : (pair ? base + 2 * (r / 2) : base + r);
-            const int dc = (part || pair) ? 1 : 0;
-            uint32_t dw = 0u;
-            if (g < GQ) {
+        if (part == 0) {
+            for (int w = tid; w < code_steps * 64; w += kThreads) {
+                const int r = w % 4, row = (w / 4) % 16, st = w / 64;
+                const int g = kI8S ? (row >> 2) + 4 * ((row >> 1) & 1) : row >> 1, lo = row & 1;
+                // coordinates of this dword's two slots: c0 + h * dc
+                const int base = 8 * (st / 2) + 4 * (st % 2);
+                const int c0 = pair ? base + 2 * (r / 2) : base + r;
+                const int dc = pair ? 1 : 0;
+                uint32_t dw = 0u;
+                if (g < GQ) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float x = ldexpf(xv[g][c0 + h * dc], s_f[g][part]);
-                    const _Float16 xh = static_cast<_Float16>(x);
-                    const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
-                    dw |= bits << (16 * h);
+                    for (int h = 0; h < 2; ++h) {
+                        const float x = ldexpf(xv[g][c0 + h * dc], s_f[g][0]);
+                        const _Float16 xh = static_cast<_Float16>(x);
+                        const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
+                        dw |= bits << (16 * h);
+                    }
+                }
+                out[(st * 64 + 16 * kb + row) * 4 + r] = dw;
+            }
+        } else if (!kI8S) {
+            for (int w = tid; w < KS * 64; w += kThreads) {
+                const int r = w % 4, row = (w / 4) % 16, st = w / 64;
+                const int g = row >> 1, lo = row & 1;
+                uint32_t dw = 0u;
+                if (g < GQ) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float x = ldexpf(xv[g][8 * st + 2 * r + h], s_f[g][1]);
+                        const _Float16 xh = static_cast<_Float16>(x);
+                        const uint32_t bits = lo ? f16_rn_bits(x - static_cast<float>(xh)) : __builtin_bit_cast(uint16_t, xh);
+                        dw |= bits << (16 * h);
+                    }
+                }
+                out[((code_steps + st) * 64 + 16 * kb + row) * 4 + r] = dw;
+            }
+        } else {
+            constexpr int SS = D / 64;           // two steps per sign dword of a quarter
+            uint32_t *sout = out + code_steps * 256;
+            for (int w = tid; w < 2 * 4 * SS * 4; w += kThreads) {
+                const int r = w % 4, sl = (w / 4) % SS, g = w / (4 * SS);
+                const int u = sl / 2, h = sl % 2;
+                uint32_t dw[4] = {0u, 0u, 0u, 0u};
+                if (g < GQ) {
+                    const int f = s_f[g][1];
+#pragma unroll
+                    for (int K = 0; K < 4; ++K) {
+                        // the sign bit arrives as byte 2^sh (masked in place):
+                        // weight Sq 2^-sh, negated for sh = 7 (the byte reads -128)
+                        const int sh = 4 * h + r;
+                        int x = static_cast<int>(rintf(ldexpf(xv[g][32 * u + 8 * K + sh], f - sh)));
+                        if (sh == 7) x = -x;
+#pragma unroll
+                        for (int limb = 0; limb < 3; ++limb) {
+                            const int d = ((x + 64) & 127) - 64;
+                            dw[limb] |= (static_cast<uint32_t>(d) & 0xffu) << (8 * K);
+                            x = (x - d) >> 7;
+                        }
+                        dw[3] |= (static_cast<uint32_t>(x) & 0xffu) << (8 * K);
+                    }
+                }
+#pragma unroll
+                for (int limb = 0; limb < 4; ++limb) {
+                    const int l = 16 * kb + 4 * (g % 4) + limb;
+                    sout[((g / 4) * SS + sl) * 256 + l * 4 + r] = dw[limb];
                 }
             }
-            out[((step0 + st) * 64 + 16 * kb + row) * 4 + r] = dw;
         }
     }
 }
@@ -547,9 +615,20 @@ struct ScoreBits {
 };
 
 // Table scores (3-7 bit keys).  The key's centroids are looked up in LDS as
-// fp16 hi + lo (c * 2^kCodeExp), its sign bytes as eight fp16 +-1; the
-// products run on v_mfma_f32_16x16x32_f16 with rows (query, hi/lo part of the
-// query): lane (j, kb) scores queries 2 kb and 2 kb + 1.  The hi and lo
+// fp16 hi + lo (c * 2^kCodeExp); the code products run on
+// v_mfma_f32_16x16x32_f16 with rows (query, hi/lo part of the query).
+// The QJL sign bits:
+//   d = 128: each sign byte indexes a 256-entry LDS table of eight fp16 +-1,
+//     in a product with the same rows; row 4 kb + r holds query 2 kb + r / 2,
+//     part r % 2, so lane (j, kb) scores queries 2 kb and 2 kb + 1.
+//   d = 256 (I8S): as in the bit-plane scores, masked in place into int8
+//     operands against int8 digit rows of Sq (v_mfma_i32_16x16x64_i8, row
+//     tile t holding queries 4 t .. 4 t + 3, lane block kb the digits of query
+//     4 t + kb), with no table; the code rows follow, row 4 kb + r holding
+//     query kb + 4 (r / 2), so lane (j, kb) scores queries kb and kb + 4.  With
+//     at most four query heads one int8 tile takes the 32 x 8 sign bits of a
+//     key in half the products of the fp16 form.
+// The hi and lo
 // halves of the centroids share one product over 16 coordinates: up to 5 bits
 // an 8-byte entry (hi pair, lo pair) per two coordinates, read with one
 // ds_read_b64, two entries making the lane's B quad (hi01, lo01, hi23, lo23)
@@ -572,29 +651,50 @@ struct ScoreLut {
     static constexpr int COPIES_RAW = TB / (NENT * EBYTES);
     static constexpr int COPIES = COPIES_RAW >= 64 ? 64 : (COPIES_RAW >= 32 ? 32 : (COPIES_RAW >= 16 ? 16 : (COPIES_RAW >= 8 ? 8 : (COPIES_RAW >= 4 ? 4 : 1))));
     static constexpr int CODE_TAB = NENT * EBYTES * COPIES;
-    static constexpr int SIGN_TAB = QJL ? 256 * 16 : 0;
+    static constexpr bool I8S = QJL && D == 256;                      // int8 sign products
+    static constexpr int SIGN_TAB = (QJL && !I8S) ? 256 * 16 : 0;
+    // int8 sign K-steps: two per sign dword of a lane (the bits at positions
+    // 0-3 and 4-7 of each byte), for each of the two row tiles
+    static constexpr int SS = I8S ? 2 * (D / 128) : 0;
     // the unit's A operands, [step][64 lanes] with CODE_STEPS code steps then
-    // KS sign steps: in registers for the first-stage format at d = 128 (no
-    // sign steps), else in LDS, shared by the four waves and read per k-step
-    // (registers for both parts cost a workgroup per CU, which measured slower)
+    // KS sign steps (fp16; or int8, 2 SS = KS, tile-major): in registers for
+    // the first-stage format at d = 128 (no sign steps), else in LDS, shared
+    // by the four waves and read per k-step (registers for both parts cost a
+    // workgroup per CU, which measured slower)
     static constexpr int CODE_STEPS = 2 * KS;
     static constexpr int NSTEP = CODE_STEPS + KS;                     // per unit in the workspace
+    static_assert(!I8S || 2 * SS == KS, "two int8 sign tiles fill the workspace's KS sign steps");
     static constexpr bool AREG = D == 128 && !QJL;
     static constexpr int LSTEP = CODE_STEPS + (QJL ? KS : 0);         // steps kept in LDS
     static constexpr int AOP_BYTES = AREG ? 0 : LSTEP * 64 * 16;
     static constexpr int TAB_BYTES = CODE_TAB + SIGN_TAB + AOP_BYTES;
     template <int TB2>
     using WithTable = ScoreLut<BITS, D, QJL, TB2>;
-    float scc[2], scs[2];
+    float scc[2], scs[2], ssq[2];
     v4i areg[AREG ? CODE_STEPS : 1];
     const unsigned char *tab;
     uint32_t copyb;            // byte offset of this lane's table copy within an entry
     int lane_;
+    bool two_;                 // I8S: the second sign tile (queries 4-7) holds a query of the unit
 
-    __device__ static int query(int slot, int kb) { return 2 * kb + slot; }
+    __device__ static int query(int slot, int kb) { return I8S ? kb + 4 * slot : 2 * kb + slot; }
 
-    // queries 2 kb and 2 kb + 1 are this lane's own slots
-    __device__ static float for_query(const float (&v)[2], int q, int) { return v[q % 2]; }
+    // the lane (of column j) and the slot that score query q
+    __device__ static constexpr int lane_of(int q, int j) { return I8S ? 16 * (q % 4) + j : 16 * (q / 2) + j; }
+    __device__ static constexpr int slot_of(int q) { return I8S ? q / 4 : q % 2; }
+
+    // value of a per-slot quantity for query q, fetched from a lane that
+    // scores q (d = 128: the callers ask for queries 2 kb and 2 kb + 1, this
+    // lane's own slots)
+    __device__ static float for_query(const float (&v)[2], int q, int j)
+    {
+        if constexpr (!I8S) {
+            return v[q % 2];
+        } else {
+            const float t0 = __shfl(v[0], lane_of(q, j)), t1 = __shfl(v[1], lane_of(q, j));
+            return slot_of(q) ? t1 : t0;
+        }
+    }
 
     // builds the tables (all threads; the caller synchronises) and loads the operands
     __device__ void init(const DecodeLaunch &a, int unit, int64_t row0, int lane, int kb, int GC, float kappa, unsigned char *lds)
@@ -621,7 +721,7 @@ struct ScoreLut {
             }
         }
         uint32_t *ts = reinterpret_cast<uint32_t *>(lds + CODE_TAB);
-        for (int i = tid; i < (QJL ? 256 * 4 : 0); i += kThreads) {
+        for (int i = tid; i < (SIGN_TAB ? 256 * 4 : 0); i += kThreads) {
             const int e = i / 4, r = i % 4;
             const uint32_t lo = ((e >> (2 * r)) & 1) ? 0x3C00u : 0xBC00u;
             const uint32_t hi = ((e >> (2 * r + 1)) & 1) ? 0x3C00u : 0xBC00u;
@@ -636,15 +736,18 @@ struct ScoreLut {
             for (int i = tid; i < LSTEP * 64; i += kThreads) adst[i] = src[i];
         }
         lane_ = lane;
+        two_ = GC > 4;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
-            const int g = 2 * kb + qq;
+            const int g = query(qq, kb);
             const bool ok = g < GC;
             const float4 sc = *reinterpret_cast<const float4 *>(a.mf.qscal + (row0 + (ok ? g : 0)) * 4);
-            // scores leave in log2 units of the softmax (scale log2(e) folded in)
-            const float f = a.mf.lscale;
+            // scores leave in log2 units of the softmax (scale log2(e) folded
+            // in); the int8 sign sum is 2 sum Sq s - sum Sq for bits s in {0, 1}
+            const float f = a.mf.lscale, fk = f * kappa;
             scc[qq] = ok ? sc.x * f : 0.0f;
-            scs[qq] = ok ? sc.y * f * kappa : 0.0f;
+            scs[qq] = ok ? (I8S ? 2.0f * sc.z : sc.y) * fk : 0.0f;
+            ssq[qq] = ok && I8S ? sc.w * fk : 0.0f;
         }
     }
 
@@ -672,9 +775,14 @@ struct ScoreLut {
     {
         const v4i *ts = reinterpret_cast<const v4i *>(tab + CODE_TAB);
         const v4i *aop = reinterpret_cast<const v4i *>(tab + CODE_TAB + SIGN_TAB);
-        v4f accc[2], accs[2];
+        v4f accc[2], accf[2];     // code products; fp16 sign products (d = 128)
+        v4i accs[2][I8S ? 2 : 1]; // int8 sign products [key column][sign tile]
 #pragma unroll
-        for (int c = 0; c < 2; ++c) accc[c] = accs[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < 2; ++c) {
+            accc[c] = accf[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < (I8S ? 2 : 1); ++t) accs[c][t] = v4i{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if constexpr (PAIR) {
@@ -713,23 +821,54 @@ struct ScoreLut {
                     }
                 }
             }
-            if constexpr (QJL) {
+            if constexpr (QJL && !I8S) {
                 const v8h asign = __builtin_bit_cast(v8h, aop[(CODE_STEPS + ks) * 64 + lane_]);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const uint32_t sb = (kw.sw[c][ks / 4] >> (8 * (ks % 4))) & 0xffu;
-                    accs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accs[c], 0, 0, 0);
+                    accf[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asign, __builtin_bit_cast(v8h, ts[sb]), accf[c], 0, 0, 0);
                 }
             }
         }
-        // rows 4 kb + r: (query 2 kb + r / 2, part r % 2)
+        if constexpr (I8S) {
+            // sign step s: the bits at 4 (s % 2) .. 4 (s % 2) + 3 of each byte of
+            // sign dword s / 2, masked in place (byte value 2^k; the digit rows
+            // carry 2^-k, negated for k = 7)
+            const v4i *asg = aop + CODE_STEPS * 64 + lane_;
+#pragma unroll
+            for (int st = 0; st < SS; ++st) {
+                const int h = 4 * (st % 2);
+                const v4i a0 = asg[st * 64];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const uint32_t dw = kw.sw[c][st / 2];
+                    const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                                     static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
+                    accs[c][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bop, accs[c][0], 0, 0, 0);
+                }
+                if (two_) {
+                    const v4i a1 = asg[(SS + st) * 64];
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const uint32_t dw = kw.sw[c][st / 2];
+                        const v4i bop = {static_cast<int>(dw & (0x01010101u << h)), static_cast<int>(dw & (0x01010101u << (h + 1))),
+                                         static_cast<int>(dw & (0x01010101u << (h + 2))), static_cast<int>(dw & (0x01010101u << (h + 3)))};
+                        accs[c][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bop, accs[c][1], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // code and fp16 sign rows 4 kb + r: (query(r / 2, kb), part r % 2);
+        // int8 sign tile qq: lane block kb holds the four digits of query kb + 4 qq
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
                 const float dcode = (accc[c][2 * qq] + accc[c][2 * qq + 1]) * scc[qq];
                 if constexpr (QJL) {
-                    const float dsign = (accs[c][2 * qq] + accs[c][2 * qq + 1]) * scs[qq];
+                    float dsign;
+                    if constexpr (I8S) dsign = fmaf(limbs_to_float(accs[c][qq]), scs[qq], -ssq[qq]);
+                    else dsign = (accf[c][2 * qq] + accf[c][2 * qq + 1]) * scs[qq];
                     sc[c][qq] = kw.nrm[c] * fmaf(kw.rho[c], dsign, dcode);
                 } else {
                     sc[c][qq] = kw.nrm[c] * dcode;
@@ -1151,10 +1290,10 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
                 m_run[sl] = m_new[sl];
             }
             if constexpr (SP) {
-                // queries 0 and 1 live in slots 0 and 1 of lane (j, 0)
+                // queries 0 and 1, from the lanes that score them
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const float aq = __shfl(alpha[q], j);
+                    const float aq = __shfl(alpha[SCORE::slot_of(q)], SCORE::lane_of(q, j));
 #pragma unroll
                     for (int i = 0; i < NSP; ++i) zsp[q][i] *= aq;
                 }
@@ -1191,8 +1330,8 @@ __global__ __launch_bounds__(kThreads, (attend_occupancy<SCORE, D, TWO, SP>())) 
             float pq[2][2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                pq[q][0] = __shfl(p[q][0], j);
-                pq[q][1] = __shfl(p[q][1], j);
+                pq[q][0] = __shfl(p[SCORE::slot_of(q)][0], SCORE::lane_of(q, j));
+                pq[q][1] = __shfl(p[SCORE::slot_of(q)][1], SCORE::lane_of(q, j));
             }
 #pragma unroll
             for (int i = 0; i < NSP; ++i) {
