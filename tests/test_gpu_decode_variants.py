@@ -38,9 +38,14 @@ CASES = [
     (64, 2, "dense", 1, 4, 2, 32, 260, "iid", "float32"),          # d 64 (general kernel)
     # the decode plan splits a GQA group into smaller query chunks while the
     # grid has fewer than 256 (unit, tile) pairs, so the short cases above run
-    # with small chunks; these two keep chunks of 8 (2 x 8 heads x 17 tiles)
+    # with small chunks; the cases below keep chunks of 4 or 8 (2 x 8 heads x
+    # 17 tiles)
     (128, 2, "dense", 8, 64, 2, 32, 2100, "iid", "bfloat16"),      # bit-plane scores, two row tiles
     (128, 3, "dense", 8, 64, 2, 64, 2100, "iid", "bfloat16"),      # table scores, eight queries per unit
+    # d 256 table scores score the QJL signs on int8 tiles of four queries:
+    # four heads per unit fill one tile, eight take both
+    (256, 7, "dense", 8, 32, 4, 32, 2100, "scaled", "bfloat16"),   # table scores d 256, four queries per unit
+    (256, 5, "dense", 8, 64, 2, 64, 2100, "iid", "bfloat16"),      # table scores d 256, eight queries per unit
 ]
 
 
