@@ -95,3 +95,28 @@ def test_fp16_queries(torch_cuda):
     torch.cuda.synchronize()
     _, oat = P.oracle_units(fm, P.f64(q), ok, ov, shape)
     P.check_attention(out.double().cpu().numpy(), oat)
+
+
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_fp16_queries_d256_table(torch_cuda, Hq):
+    """fp16 queries on the d = 256 table scores (int8 QJL sign digits built
+    from the fp16 query): four and eight query heads per KV head, so one and
+    both sign tiles; attention and scores against the oracle."""
+    torch = torch_cuda
+    w = replace(BASE, name="variant16d256", B=2, Hkv=8, Hq=Hq, T=2100, d=256, k_bits=5, rot="dense", v_bits=4,
+                group=32, dtype="bfloat16", seed=13)
+    fm = P.Formats(w, 0)
+    k, v = W.make_keys(w), W.make_values(w)
+    q = W.make_queries(w).to(torch.float16)
+    ok = O.compress_keys(P.f64(k).reshape(-1, w.d), w.k_bits, fm.orot)
+    ov = O.compress_values(P.f64(v).reshape(-1, w.d), w.v_bits, w.group)
+    shape = (w.B, w.Hkv, w.T)
+    kc, vc = P.to_device_cache(ok, ov, shape, "cuda")
+    qn = P.f64(q)
+    osc, oat = P.oracle_units(fm, qn, ok, ov, shape)
+    out = tq.tq_attend_decode(fm.kf, fm.vf, q.cuda(), kc, vc, w.Hkv, w.T)
+    sc = tq.tq_scores(fm.kf, q.cuda(), kc, w.Hkv, w.T)
+    torch.cuda.synchronize()
+    err = P.check_attention(out.double().cpu().numpy(), oat)
+    P.check_scores(sc.double().cpu().numpy(), osc, qn, ok.knorm.reshape(shape), w.Hkv)
+    print(f"[fp16 q d256] Hq={Hq}: attention max abs err {err:.3g}", flush=True)
